@@ -1,0 +1,157 @@
+/*
+ * mi_attn.h: C ABI of the masked FlashAttention forward for AMD MI355X (gfx950).
+ *
+ * The operation is softmax attention with an additive mask, computed tile by tile
+ * with an online (running max / running sum) softmax, as the ExecuTorch pull request
+ * #10466 page describes in its "Summary" (query and key dimensions both split into
+ * chunks, the softmax state rescaled as chunks arrive and finalised at the end), with
+ * the guard that page asks for: a chunk whose logits are all -inf must not create NaN.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller. The library keeps no
+ *    pointer after a call returns.
+ *  - Every call validates its arguments on the host first. On a non-zero return nothing
+ *    has been enqueued and no output was touched; attn_last_error() gives a message.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL means the default stream). The
+ *    library never synchronises the stream. Temporary device memory (split-KV partial
+ *    results, top-k ranks) is taken with hipMallocAsync/hipFreeAsync on that stream.
+ *  - Layouts are row-major and contiguous:
+ *      q, out      [B, Hq,  Lq, d]   elements of `dtype`
+ *      k, v        [B, Hkv, Lk, d]   elements of `dtype`
+ *      lse         [B, Hq,  Lq]      fp32
+ *      mask        [Lq, Lk]          fp32, the same for every batch and head
+ *      zero_hold   [B, Hkv, Lk]      fp32, one value per key of each KV head
+ *  - Query row i sits at absolute key position p_i = Lk - Lq + i (bottom-right
+ *    alignment). This is how causal attention over past keys works without padding
+ *    the queries (FastChat pull request #2315 page, "Enable use_cache support with
+ *    Flash-Attention"). When Lq == Lk it is the ordinary top-left causal mask.
+ *  - Query head h reads KV head h / (Hq / Hkv): MHA when Hq == Hkv, GQA/MQA when
+ *    Hq % Hkv == 0, an error otherwise (InfiniTrain pull request #193 page,
+ *    "Framework and autograd").
+ */
+#ifndef MI_ATTN_H
+#define MI_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MI_ATTN_ABI_VERSION 1
+
+/* element types of q, k, v, out */
+#define MI_ATTN_F32 0
+#define MI_ATTN_F16 1
+#define MI_ATTN_BF16 2
+
+/* mask kinds */
+#define MI_ATTN_MASK_NONE 0   /* every key visible                                        */
+#define MI_ATTN_MASK_CAUSAL 1 /* key j visible iff j <= p_i                                */
+#define MI_ATTN_MASK_WINDOW 2 /* key j visible iff p_i - window_left <= j <= p_i           */
+#define MI_ATTN_MASK_DENSE 3  /* logit += mask[i, j]; -inf hides the key                   */
+#define MI_ATTN_MASK_TOPK 4   /* causal, and j in the row's dynamic top-k: logit += zh[j]  */
+
+/* return codes */
+#define MI_ATTN_OK 0
+#define MI_ATTN_EINVAL (-1)       /* invalid argument                                  */
+#define MI_ATTN_EUNSUPPORTED (-2) /* valid but not supported by this build (e.g. d)   */
+#define MI_ATTN_EHIP (-3)         /* a HIP runtime call or a launch failed            */
+
+/*
+ * attn_fwd: out = softmax(scale * q k^T + M) v, and lse = log-sum-exp of that row (natural
+ * log) over the same masked, biased, scaled logits.
+ *
+ *   M is chosen by mask_kind (see MI_ATTN_MASK_*). For the dense kind `mask` is added to
+ *   the scaled logits before the softmax, as the ExecuTorch page ("Summary") and the
+ *   flash-sparse-attention issue #11 page ("Next Steps", item 1) require; finite non-zero
+ *   values are allowed and only -inf hides a key. For the top-k kind the mask is built
+ *   from zero_hold as dynamic_mask_topk() defines it, with keep_k keys per row.
+ *
+ *   A row in which every key is hidden gets out = 0 and lse = -inf, never NaN.
+ *
+ *   q, k, v, out   device pointers, layouts above, element type `dtype`.
+ *   lse            device pointer to fp32 [B,Hq,Lq], or NULL to skip writing it.
+ *   scale          multiplies q k^T (typically 1/sqrt(d)); must be finite.
+ *   window_left    used by MI_ATTN_MASK_WINDOW only; must be >= 0.
+ *   mask           required (non-NULL) for MI_ATTN_MASK_DENSE, ignored otherwise.
+ *   zero_hold      required for MI_ATTN_MASK_TOPK, ignored otherwise.
+ *   keep_k         used by MI_ATTN_MASK_TOPK only; must be >= 1.
+ *   dtype          MI_ATTN_F32, MI_ATTN_F16 or MI_ATTN_BF16. fp32 inputs are computed
+ *                  in fp32 throughout; fp16/bf16 inputs use fp32 accumulation and the
+ *                  output is rounded to nearest-even in the input type.
+ *   stream         hipStream_t (as void*), NULL for the default stream.
+ *
+ *   Supported head dims: fp16/bf16: 64 and 128; fp32: any multiple of 4 up to 256.
+ *   Returns MI_ATTN_OK, MI_ATTN_EINVAL (sizes <= 0, Hq % Hkv != 0, non-finite scale,
+ *   unknown mask_kind or dtype, a required pointer NULL, keep_k < 1, window_left < 0),
+ *   MI_ATTN_EUNSUPPORTED (head dim not in the list above) or MI_ATTN_EHIP.
+ *   A mask argument is never silently ignored: the kinds that need one reject NULL.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+             int B, int Hq, int Hkv, int Lq, int Lk, int d, float scale,
+             int mask_kind, int window_left, const float* mask, const float* zero_hold,
+             int keep_k, int dtype, void* stream);
+
+/*
+ * dynamic_mask_topk: the dynamic top-k mask on its own, as the flash-sparse-attention
+ * issue #11 page ("Overview", "Current Status") separates it from the attention kernel:
+ * zero_hold values computed ahead of time select, per query row, which keys stay visible.
+ *
+ *   Total order of the keys of one (b, h): zero_hold descending, ties to the lower key
+ *   index, -0.0 equal to +0.0. rank[b,h,j] is key j's place in that order (0 = first).
+ *   Row i allows keys j <= p_i when causal != 0, every key otherwise. If the row allows
+ *   more than keep_k keys, tau[b,h,i] is the keep_k-th smallest rank among them (keys
+ *   with rank <= tau are kept); otherwise it is INT32_MAX and every allowed key is kept.
+ *
+ *   zero_hold  device fp32 [B,H,Lk] (no NaN).
+ *   rank       device int32 [B,H,Lk], written.
+ *   tau        device int32 [B,H,Lq], written.
+ *   keep_bits  device uint32 [B,H,Lq,ceil(Lk/32)] or NULL; when given, bit (j % 32) of
+ *              word j / 32 is set iff row i keeps key j.
+ *   Returns MI_ATTN_OK, MI_ATTN_EINVAL or MI_ATTN_EHIP.
+ */
+int dynamic_mask_topk(const float* zero_hold, int B, int H, int Lq, int Lk, int keep_k,
+                      int causal, int32_t* rank, int32_t* tau, uint32_t* keep_bits,
+                      void* stream);
+
+/* which kernels attn_fwd would run for a shape (host-only query, no GPU work) */
+typedef struct {
+  int path;          /* 0 fp32 row kernel, 1 MFMA prefill, 2 split-KV decode + LSE merge */
+  int block_m;       /* query rows per workgroup (rows of all heads sharing a KV head)   */
+  int block_n;       /* keys per KV tile                                                 */
+  int splits;        /* key-range splits (decode path), 1 otherwise                      */
+  int grid;          /* workgroups of the main kernel                                    */
+  int mask_summary;  /* 1 when a per-tile dense-mask summary kernel runs first            */
+  size_t workspace_bytes; /* temporary device memory the call takes                     */
+} attn_plan_t;
+
+/*
+ * attn_fwd_plan: fill *plan for the arguments attn_fwd would get (pointers are not
+ * needed). Validates exactly as attn_fwd does and returns the same error codes. Runs on
+ * the host only; usable without a GPU.
+ */
+int attn_fwd_plan(int B, int Hq, int Hkv, int Lq, int Lk, int d, int mask_kind,
+                  int window_left, int keep_k, int dtype, attn_plan_t* plan);
+
+/*
+ * attn_set_debug: process-wide debug switches (not thread-safe; for tests and tuning).
+ *   no_skip      1: visit every KV tile, even ones the mask hides entirely.
+ *   force_path   -1: automatic; 0/1/2 force the path numbers of attn_plan_t (a forced
+ *                path that cannot run the arguments makes attn_fwd return
+ *                MI_ATTN_EUNSUPPORTED).
+ *   force_splits 0: automatic; n > 0 forces n key-range splits on the decode path.
+ */
+void attn_set_debug(int no_skip, int force_path, int force_splits);
+
+/* message for the last non-zero return on the calling thread ("" if none) */
+const char* attn_last_error(void);
+
+/* MI_ATTN_ABI_VERSION of the loaded library, for the caller to assert semantics */
+int attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MI_ATTN_H */

@@ -1,0 +1,169 @@
+"""Masked FlashAttention forward for AMD MI355X (gfx950): Python binding.
+
+A thin ctypes layer over ``libmi_attn.so`` (declared in ``include/mi_attn.h``).
+Torch tensors supply device memory and the stream; every step of the
+computation runs in the library's HIP kernels. If the library has not been
+built, every call raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmi_attn.so")
+
+F32, F16, BF16 = 0, 1, 2
+MASK_KINDS = {"none": 0, "causal": 1, "window": 2, "dense": 3, "topk": 4}
+PATH_NAMES = {0: "row", 1: "mfma_prefill", 2: "splitkv_decode"}
+OK, EINVAL, EUNSUPPORTED, EHIP = 0, -1, -2, -3
+
+
+class MiAttnError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"mi_attn error {code}: {msg}")
+        self.code = code
+
+
+class AttnPlan(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int), ("block_m", ctypes.c_int), ("block_n", ctypes.c_int),
+                ("splits", ctypes.c_int), ("grid", ctypes.c_int), ("mask_summary", ctypes.c_int),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+_lib = None
+
+_SIGS = {
+    "attn_fwd": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_void_p] + [ctypes.c_int] * 6 + [ctypes.c_float]
+                 + [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                    ctypes.c_void_p]),
+    "dynamic_mask_topk": (ctypes.c_int, [ctypes.c_void_p] + [ctypes.c_int] * 6
+                          + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "attn_fwd_plan": (ctypes.c_int, [ctypes.c_int] * 10 + [ctypes.POINTER(AttnPlan)]),
+    "attn_set_debug": (None, [ctypes.c_int] * 3),
+    "attn_last_error": (ctypes.c_char_p, []),
+    "attn_abi_version": (ctypes.c_int, []),
+}
+EXPORTED = tuple(_SIGS)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise MiAttnError(EHIP, f"{LIB_PATH} is missing: build it with "
+                                    "`python -m masked_flashattention_forward_amd.build`")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(l, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = l
+    return _lib
+
+
+def _check(rc: int):
+    if rc != OK:
+        raise MiAttnError(rc, lib().attn_last_error().decode())
+
+
+def abi_version() -> int:
+    return lib().attn_abi_version()
+
+
+def set_debug(no_skip: bool = False, force_path: int = -1, force_splits: int = 0):
+    lib().attn_set_debug(int(bool(no_skip)), int(force_path), int(force_splits))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def plan(B, Hq, Hkv, Lq, Lk, d, mask_kind="causal", window_left=0, keep_k=0, dtype=BF16) -> dict:
+    """Which kernels attn_fwd runs for a shape (host-only)."""
+    p = AttnPlan()
+    mk = MASK_KINDS[mask_kind] if isinstance(mask_kind, str) else int(mask_kind)
+    _check(lib().attn_fwd_plan(B, Hq, Hkv, Lq, Lk, d, mk, window_left, keep_k, dtype, ctypes.byref(p)))
+    return {"path": PATH_NAMES[p.path], "block_m": p.block_m, "block_n": p.block_n, "splits": p.splits,
+            "grid": p.grid, "mask_summary": bool(p.mask_summary), "workspace_bytes": p.workspace_bytes}
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(device, stream):
+    import torch
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def attn_fwd(q, k, v, *, scale=None, mask_kind="causal", window_left=0, mask=None, zero_hold=None,
+             keep_k=0, out=None, lse=None, return_lse=True, stream=None):
+    """Masked attention forward.
+
+    q ``[B,Hq,Lq,d]``, k/v ``[B,Hkv,Lk,d]`` (fp32, fp16 or bf16, contiguous, on one
+    GPU); mask ``[Lq,Lk]`` fp32 for ``mask_kind="dense"``; zero_hold ``[B,Hkv,Lk]``
+    fp32 and ``keep_k`` for ``"topk"``. Returns ``(out, lse)``; lse is fp32
+    ``[B,Hq,Lq]`` (natural log) or None when ``return_lse`` is false.
+    """
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-D GPU tensor")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share a dtype")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k and v must be on one device")
+    B, Hq, Lq, d = q.shape
+    Bk, Hkv, Lk, dk = k.shape
+    if (Bk, dk) != (B, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    mk = MASK_KINDS[mask_kind] if isinstance(mask_kind, str) else int(mask_kind)
+    if mask is not None:
+        if mask.dtype != torch.float32 or tuple(mask.shape) != (Lq, Lk) or not mask.is_contiguous() \
+                or mask.device != q.device:
+            raise ValueError("mask must be a contiguous fp32 [Lq, Lk] tensor on q's device")
+    if zero_hold is not None:
+        if zero_hold.dtype != torch.float32 or tuple(zero_hold.shape) != (B, Hkv, Lk) \
+                or not zero_hold.is_contiguous() or zero_hold.device != q.device:
+            raise ValueError("zero_hold must be a contiguous fp32 [B, Hkv, Lk] tensor on q's device")
+    if out is None:
+        out = torch.empty_like(q)
+    elif tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must match q")
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    if lse is not None and (tuple(lse.shape) != (B, Hq, Lq) or lse.dtype != torch.float32
+                            or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous fp32 [B, Hq, Lq] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    rc = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Lq, Lk, d,
+                        float(scale), mk, int(window_left), _ptr(mask), _ptr(zero_hold), int(keep_k),
+                        _dtype_code(q), _stream_handle(q.device, stream))
+    _check(rc)
+    return out, lse
+
+
+def dynamic_mask_topk(zero_hold, Lq, keep_k, causal=True, with_bits=False, stream=None):
+    """Ranks ``[B,H,Lk]`` int32, thresholds ``[B,H,Lq]`` int32 and, if asked, the keep
+    bitmask ``[B,H,Lq,ceil(Lk/32)]`` (as int32 words) of the dynamic top-k mask."""
+    import torch
+    if zero_hold.dtype != torch.float32 or zero_hold.dim() != 3 or not zero_hold.is_contiguous() \
+            or not zero_hold.is_cuda:
+        raise ValueError("zero_hold must be a contiguous fp32 [B, H, Lk] GPU tensor")
+    B, H, Lk = zero_hold.shape
+    dev = zero_hold.device
+    rank = torch.empty((B, H, Lk), dtype=torch.int32, device=dev)
+    tau = torch.empty((B, H, Lq), dtype=torch.int32, device=dev)
+    bits = torch.empty((B, H, Lq, (Lk + 31) // 32), dtype=torch.int32, device=dev) if with_bits else None
+    _check(lib().dynamic_mask_topk(_ptr(zero_hold), B, H, Lq, Lk, int(keep_k), int(bool(causal)),
+                                   _ptr(rank), _ptr(tau), _ptr(bits), _stream_handle(dev, stream)))
+    return rank, tau, bits

@@ -1,0 +1,247 @@
+// Host side of the C ABI: argument validation, path planning, temporary device memory
+// and kernel launches on the caller's stream.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+using namespace mi_attn;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MI_ATTN_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// debug switches (attn_set_debug)
+int g_no_skip = 0;
+int g_force_path = -1;
+int g_force_splits = 0;
+
+struct Shape {
+  int B, Hq, Hkv, Lq, Lk, d, mask_kind, window_left, keep_k, dtype;
+};
+
+int validate(const Shape& s) {
+  if (s.B <= 0 || s.Hq <= 0 || s.Hkv <= 0 || s.Lq <= 0 || s.Lk <= 0 || s.d <= 0)
+    return fail(MI_ATTN_EINVAL, "sizes must be positive (B=%d Hq=%d Hkv=%d Lq=%d Lk=%d d=%d)", s.B, s.Hq, s.Hkv,
+                s.Lq, s.Lk, s.d);
+  if (s.Hq % s.Hkv != 0)
+    return fail(MI_ATTN_EINVAL, "Hq (%d) must be a multiple of Hkv (%d)", s.Hq, s.Hkv);
+  if (s.mask_kind < MI_ATTN_MASK_NONE || s.mask_kind > MI_ATTN_MASK_TOPK)
+    return fail(MI_ATTN_EINVAL, "unknown mask_kind %d", s.mask_kind);
+  if (s.dtype < MI_ATTN_F32 || s.dtype > MI_ATTN_BF16) return fail(MI_ATTN_EINVAL, "unknown dtype %d", s.dtype);
+  if (s.mask_kind == MI_ATTN_MASK_WINDOW && s.window_left < 0)
+    return fail(MI_ATTN_EINVAL, "window_left must be >= 0 (got %d)", s.window_left);
+  if (s.mask_kind == MI_ATTN_MASK_TOPK && s.keep_k < 1)
+    return fail(MI_ATTN_EINVAL, "keep_k must be >= 1 (got %d)", s.keep_k);
+  const double elems_q = static_cast<double>(s.B) * s.Hq * s.Lq * s.d;
+  const double elems_kv = static_cast<double>(s.B) * s.Hkv * s.Lk * s.d;
+  if (elems_q > 9.0e15 || elems_kv > 9.0e15) return fail(MI_ATTN_EINVAL, "tensor too large");
+  if (s.dtype == MI_ATTN_F32) {
+    if (s.d % 4 != 0 || s.d > 256)
+      return fail(MI_ATTN_EUNSUPPORTED, "fp32 head dim must be a multiple of 4 up to 256 (got %d)", s.d);
+  } else if (s.d != 64 && s.d != 128) {
+    return fail(MI_ATTN_EUNSUPPORTED, "fp16/bf16 head dim must be 64 or 128 (got %d)", s.d);
+  }
+  if (s.mask_kind == MI_ATTN_MASK_TOPK && s.Lk > 65536)
+    return fail(MI_ATTN_EUNSUPPORTED, "top-k mask supports Lk <= 65536 (got %d)", s.Lk);
+  return MI_ATTN_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+struct Plan {
+  attn_plan_t pub;
+  int q_per_block;     // query positions per workgroup (dense-mask summary granularity)
+  size_t off_rank, off_tau, off_tmin, off_flags, off_pout, off_plse;
+};
+
+int make_plan(const Shape& s, Plan* pl) {
+  *pl = Plan{};
+  attn_plan_t& p = pl->pub;
+  const int G = s.Hq / s.Hkv;
+  int path = 0;
+  if (s.dtype != MI_ATTN_F32) path = choose_half_path(s.B, s.Hkv, G, s.Lq, s.Lk, s.d, s.mask_kind);
+  if (g_force_path >= 0) {
+    if (g_force_path == 0) {
+      path = 0;
+    } else if (s.dtype == MI_ATTN_F32) {
+      return fail(MI_ATTN_EUNSUPPORTED, "forced path %d needs fp16/bf16 inputs", g_force_path);
+    } else if (!half_path_available(g_force_path, s.d, G, s.Lq)) {
+      return fail(MI_ATTN_EUNSUPPORTED, "forced path %d cannot run d=%d G*Lq=%d", g_force_path, s.d, G * s.Lq);
+    } else {
+      path = g_force_path;
+    }
+  }
+  p.path = path;
+  p.splits = 1;
+  HalfPlan hp{};
+  if (path == 0) {
+    p.block_m = 4;
+    p.block_n = 64;
+    p.grid = static_cast<int>((static_cast<long>(s.B) * s.Hq * s.Lq + 3) / 4);
+    pl->q_per_block = 1;
+  } else {
+    hp = plan_half_path(path, s.B, s.Hkv, G, s.Lq, s.Lk, s.d, s.mask_kind, s.window_left, g_force_splits);
+    p.block_m = hp.block_m;
+    p.block_n = hp.block_n;
+    p.grid = hp.grid;
+    p.splits = hp.splits;
+    pl->q_per_block = hp.q_per_block;
+  }
+  // workspace layout
+  size_t off = 0;
+  const long bh = static_cast<long>(s.B) * s.Hkv;
+  if (s.mask_kind == MI_ATTN_MASK_TOPK) {
+    pl->off_rank = off; off = align256(off + sizeof(int32_t) * bh * s.Lk);
+    pl->off_tau = off;  off = align256(off + sizeof(int32_t) * bh * s.Lq);
+    pl->off_tmin = off; off = align256(off + sizeof(int32_t) * bh * ((s.Lk + p.block_n - 1) / p.block_n));
+  }
+  if (s.mask_kind == MI_ATTN_MASK_DENSE && path != 0) {
+    p.mask_summary = 1;
+    pl->off_flags = off;
+    off = align256(off + static_cast<size_t>((s.Lq + pl->q_per_block - 1) / pl->q_per_block) *
+                             ((s.Lk + p.block_n - 1) / p.block_n));
+  }
+  if (p.splits > 1) {
+    const size_t rows = static_cast<size_t>(s.B) * s.Hq * s.Lq;
+    pl->off_pout = off; off = align256(off + sizeof(float) * p.splits * rows * s.d);
+    pl->off_plse = off; off = align256(off + sizeof(float) * p.splits * rows);
+  }
+  p.workspace_bytes = off;
+  return MI_ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return MI_ATTN_ABI_VERSION; }
+
+const char* attn_last_error(void) { return g_err.c_str(); }
+
+void attn_set_debug(int no_skip, int force_path, int force_splits) {
+  g_no_skip = no_skip ? 1 : 0;
+  g_force_path = (force_path >= 0 && force_path <= 2) ? force_path : -1;
+  g_force_splits = force_splits > 0 ? force_splits : 0;
+}
+
+int attn_fwd_plan(int B, int Hq, int Hkv, int Lq, int Lk, int d, int mask_kind, int window_left, int keep_k,
+                  int dtype, attn_plan_t* plan) {
+  g_err.clear();
+  if (plan == nullptr) return fail(MI_ATTN_EINVAL, "plan must not be NULL");
+  const Shape s{B, Hq, Hkv, Lq, Lk, d, mask_kind, window_left, keep_k, dtype};
+  int rc = validate(s);
+  if (rc != MI_ATTN_OK) return rc;
+  Plan pl;
+  rc = make_plan(s, &pl);
+  if (rc != MI_ATTN_OK) return rc;
+  *plan = pl.pub;
+  return MI_ATTN_OK;
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv, int Lq,
+             int Lk, int d, float scale, int mask_kind, int window_left, const float* mask, const float* zero_hold,
+             int keep_k, int dtype, void* stream) {
+  g_err.clear();
+  const Shape s{B, Hq, Hkv, Lq, Lk, d, mask_kind, window_left, keep_k, dtype};
+  int rc = validate(s);
+  if (rc != MI_ATTN_OK) return rc;
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
+    return fail(MI_ATTN_EINVAL, "q, k, v and out must not be NULL");
+  if (!std::isfinite(scale)) return fail(MI_ATTN_EINVAL, "scale must be finite");
+  if (mask_kind == MI_ATTN_MASK_DENSE && mask == nullptr)
+    return fail(MI_ATTN_EINVAL, "mask_kind DENSE needs a mask pointer");
+  if (mask_kind == MI_ATTN_MASK_TOPK && zero_hold == nullptr)
+    return fail(MI_ATTN_EINVAL, "mask_kind TOPK needs a zero_hold pointer");
+  Plan pl;
+  rc = make_plan(s, &pl);
+  if (rc != MI_ATTN_OK) return rc;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = nullptr;
+  if (pl.pub.workspace_bytes > 0) {
+    hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&ws), pl.pub.workspace_bytes, st);
+    if (e != hipSuccess) return hip_fail(e, "hipMallocAsync(workspace)");
+  }
+
+  AttnParams p{};
+  p.q = q; p.k = k; p.v = v; p.out = out; p.lse = lse;
+  p.mask = mask; p.zero_hold = zero_hold;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Lq = Lq; p.Lk = Lk; p.d = d; p.G = Hq / Hkv;
+  p.scale = scale; p.mask_kind = mask_kind; p.window_left = window_left; p.keep_k = keep_k;
+  p.no_skip = g_no_skip;
+  p.splits = pl.pub.splits;
+  {
+    const int tiles = (Lk + pl.pub.block_n - 1) / pl.pub.block_n;
+    p.keys_per_split = ((tiles + pl.pub.splits - 1) / pl.pub.splits) * pl.pub.block_n;
+  }
+  p.block_n = pl.pub.block_n;
+  p.q_per_block = pl.q_per_block;
+
+  hipError_t e = hipSuccess;
+  const char* what = "";
+  if (mask_kind == MI_ATTN_MASK_TOPK) {
+    int32_t* rank = reinterpret_cast<int32_t*>(ws + pl.off_rank);
+    int32_t* tau = reinterpret_cast<int32_t*>(ws + pl.off_tau);
+    int32_t* tmin = reinterpret_cast<int32_t*>(ws + pl.off_tmin);
+    what = "top-k selection";
+    e = launch_topk(zero_hold, B * Hkv, Lq, Lk, keep_k, 1, rank, tau, nullptr, st);
+    if (e == hipSuccess) e = launch_tile_min_rank(rank, B * Hkv, Lk, pl.pub.block_n, tmin, st);
+    p.rank = rank; p.tau = tau; p.tile_min_rank = tmin;
+  }
+  if (e == hipSuccess && pl.pub.mask_summary) {
+    uint8_t* flags = reinterpret_cast<uint8_t*>(ws + pl.off_flags);
+    what = "dense-mask summary";
+    e = launch_mask_summary(mask, Lq, Lk, pl.q_per_block, pl.pub.block_n, flags, st);
+    p.tile_live = flags;
+  }
+  if (e == hipSuccess) {
+    if (pl.pub.splits > 1) {
+      p.part_out = reinterpret_cast<float*>(ws + pl.off_pout);
+      p.part_lse = reinterpret_cast<float*>(ws + pl.off_plse);
+    }
+    what = "attention kernel";
+    e = (pl.pub.path == 0) ? launch_row_kernel(p, dtype, st) : launch_half_path(pl.pub.path, p, dtype, st);
+  }
+  if (ws != nullptr) {
+    const hipError_t ef = hipFreeAsync(ws, st);
+    if (e == hipSuccess && ef != hipSuccess) return hip_fail(ef, "hipFreeAsync(workspace)");
+  }
+  if (e != hipSuccess) return hip_fail(e, what);
+  return MI_ATTN_OK;
+}
+
+int dynamic_mask_topk(const float* zero_hold, int B, int H, int Lq, int Lk, int keep_k, int causal, int32_t* rank,
+                      int32_t* tau, uint32_t* keep_bits, void* stream) {
+  g_err.clear();
+  if (B <= 0 || H <= 0 || Lq <= 0 || Lk <= 0)
+    return fail(MI_ATTN_EINVAL, "sizes must be positive (B=%d H=%d Lq=%d Lk=%d)", B, H, Lq, Lk);
+  if (keep_k < 1) return fail(MI_ATTN_EINVAL, "keep_k must be >= 1 (got %d)", keep_k);
+  if (zero_hold == nullptr || rank == nullptr || tau == nullptr)
+    return fail(MI_ATTN_EINVAL, "zero_hold, rank and tau must not be NULL");
+  if (Lk > 65536) return fail(MI_ATTN_EUNSUPPORTED, "Lk must be <= 65536 (got %d)", Lk);
+  if (static_cast<double>(B) * H * Lq * ((Lk + 31) / 32) > 2.0e9) return fail(MI_ATTN_EINVAL, "tensor too large");
+  const hipError_t e = launch_topk(zero_hold, B * H, Lq, Lk, keep_k, causal ? 1 : 0, rank, tau, keep_bits,
+                                   static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "dynamic_mask_topk");
+  return MI_ATTN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,123 @@
+// Shared device helpers and launch declarations of the masked attention library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mi_attn.h"
+
+namespace mi_attn {
+
+// ------------------------------------------------------------------ element types
+// Storage types are raw 16-bit patterns for fp16/bf16; conversions below are exact
+// (upcast) or round-to-nearest-even (downcast).
+struct bf16_t { uint16_t bits; };
+struct f16_t { uint16_t bits; };
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) {
+  return __uint_as_float(static_cast<uint32_t>(x.bits) << 16);
+}
+__device__ __forceinline__ float to_f32(f16_t x) {
+  _Float16 h;
+  __builtin_memcpy(&h, &x.bits, 2);
+  return static_cast<float>(h);
+}
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
+  uint32_t u = __float_as_uint(x);
+  bf16_t r;
+  if ((u & 0x7fffffffu) > 0x7f800000u) {
+    r.bits = 0x7fc0;  // NaN stays NaN
+  } else {
+    u += 0x7fffu + ((u >> 16) & 1u);
+    r.bits = static_cast<uint16_t>(u >> 16);
+  }
+  return r;
+}
+template <> __device__ __forceinline__ f16_t from_f32<f16_t>(float x) {
+  _Float16 h = static_cast<_Float16>(x);  // v_cvt_f16_f32: round to nearest even
+  f16_t r;
+  __builtin_memcpy(&r.bits, &h, 2);
+  return r;
+}
+
+// ------------------------------------------------------------------ wave helpers
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+  return x;
+}
+
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ------------------------------------------------------------------ problem description
+// Everything a kernel needs to know about one attn_fwd call.
+struct AttnParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;
+  const float* mask;       // dense [Lq, Lk]
+  const float* zero_hold;  // [B, Hkv, Lk]
+  const int32_t* rank;     // top-k: [B, Hkv, Lk]
+  const int32_t* tau;      // top-k: [B, Hkv, Lq]
+  const int32_t* tile_min_rank;  // top-k: [B, Hkv, ceil(Lk / block_n)]
+  const uint8_t* tile_live;      // dense: [ceil(Lq / q_per_block), ceil(Lk / block_n)]
+  float* part_out;         // split-KV partials [splits, B, Hq, Lq, d] fp32
+  float* part_lse;         // split-KV partials [splits, B, Hq, Lq] fp32 (natural log)
+  int B, Hq, Hkv, Lq, Lk, d;
+  int G;                   // Hq / Hkv
+  float scale;
+  int mask_kind;
+  int window_left;
+  int keep_k;
+  int no_skip;
+  int splits;
+  int keys_per_split;
+  int block_n;
+  int q_per_block;         // query positions per workgroup (summary granularity)
+};
+
+// Visible key range [lo, hi) for a contiguous span of query positions [p0, p1]
+// (positions are bottom-right aligned). Keys outside the range are hidden for every
+// row of the span; keys inside may still be hidden per element.
+__host__ __device__ inline void key_range(int mask_kind, int window_left, int Lk, int p0, int p1,
+                                          int* lo, int* hi) {
+  int a = 0, b = Lk;
+  if (mask_kind == MI_ATTN_MASK_CAUSAL || mask_kind == MI_ATTN_MASK_TOPK ||
+      mask_kind == MI_ATTN_MASK_WINDOW) {
+    b = p1 + 1 < Lk ? p1 + 1 : Lk;
+    if (b < 0) b = 0;
+  }
+  if (mask_kind == MI_ATTN_MASK_WINDOW) {
+    a = p0 - window_left;
+    if (a < 0) a = 0;
+  }
+  if (a > b) a = b;
+  *lo = a;
+  *hi = b;
+}
+
+// ------------------------------------------------------------------ launchers
+hipError_t launch_row_kernel(const AttnParams& p, int dtype, hipStream_t s);
+hipError_t launch_topk(const float* zh, int BH, int Lq, int Lk, int keep_k, int causal,
+                       int32_t* rank, int32_t* tau, uint32_t* keep_bits, hipStream_t s);
+hipError_t launch_tile_min_rank(const int32_t* rank, int BH, int Lk, int block_n, int32_t* out,
+                                hipStream_t s);
+hipError_t launch_mask_summary(const float* mask, int Lq, int Lk, int q_per_block, int block_n,
+                               uint8_t* flags, hipStream_t s);
+
+}  // namespace mi_attn

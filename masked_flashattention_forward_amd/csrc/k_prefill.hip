@@ -1,0 +1,437 @@
+// MFMA prefill kernel for fp16/bf16 inputs, head dim 64 or 128, every mask kind.
+//
+// Work unit: one workgroup = 4 wavefronts = up to 128 query rows of ONE (batch, KV head)
+// group. Rows are the query heads sharing that KV head, packed query-major
+// (row r -> query i = r / G, head g*G + r % G), so a K/V tile staged once in LDS serves
+// all G heads (InfiniTrain page, "Transformer integration": the flash path keeps the
+// original KV heads instead of expanding them).
+//
+// Per KV tile of BN keys (ExecuTorch page, "Summary": chunks along the key dimension,
+// online softmax finalised at the end):
+//   S^T = K Q^T      v_mfma_f32_32x32x16 (K from LDS as the A operand, Q^T from registers).
+//                    Each lane then holds one query column and 16 keys per 32-key block,
+//                    so the row max/sum is in-lane plus one exchange with lane ^ 32.
+//   mask             only on tiles the mask does not cover entirely (boundary tiles).
+//   online softmax   running max m and sum l per row in the log2 domain, guarded so an
+//                    all -inf tile (or row) never produces exp(-inf - -inf).
+//   O^T += V^T P^T   P^T straight from the S^T registers (packed to 16 bit) as the B
+//                    operand; V is written to LDS transposed, with keys permuted so each
+//                    lane's eight keys match the ones its P registers hold.
+// Tiles that the mask hides entirely are never loaded: their range comes from the causal
+// / window bounds, the dense-mask summary or the top-k minimum rank per tile.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace mi_attn {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x16_t mfma32(bf16_t, const u32x4_t& a, const u32x4_t& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+__device__ __forceinline__ f32x16_t mfma32(f16_t, const u32x4_t& a, const u32x4_t& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c, 0,
+                                                0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack2(bf16_t, float a, float b) {
+  f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+__device__ __forceinline__ uint32_t pack2(f16_t, float a, float b) {
+  f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;
+constexpr int kBlockM = 32 * kWaves;  // query rows per workgroup
+
+template <int D, int BN>
+struct Tile {
+  static constexpr int kStride = D + 8;                // K row stride in 16-bit elements (16 B pad)
+  static constexpr int vStride = BN + 8;               // V^T row stride
+  static constexpr int kElems = BN * kStride;
+  static constexpr int vElems = D * vStride;
+  static constexpr int stage = kElems + vElems;
+  static constexpr int kChunks = BN * D / 8 / kThreads;  // 16-byte K loads per thread
+  static constexpr int vKeyGroups = BN / 4;               // V loaded as 4-key x 8-dim blocks
+  static_assert(vKeyGroups * (D / 8) == kThreads, "one V block per thread");
+  static_assert(kChunks * kThreads * 8 == BN * D, "K tile split evenly");
+};
+
+// Storage position of key offset `kk` (multiple of 4) inside a V^T row: within each group
+// of 16 keys the 4-key quarters are stored in the order 0, 2, 1, 3, so that lane half 0
+// reads keys {0-3, 8-11} and lane half 1 keys {4-7, 12-15} as one 16-byte run.
+__device__ __forceinline__ int vperm(int kk) {
+  const int q4 = (kk >> 2) & 3;
+  return (kk & ~15) + ((q4 & 1) << 3) + ((q4 >> 1) << 2);
+}
+
+template <typename T, int D, int BN>
+__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
+  using TL = Tile<D, BN>;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * TL::stage];
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid % kWave;
+  const int l32 = lane & 31;
+  const int hf = lane >> 5;  // lane half
+
+  // ---- work unit: (b, g, query block, split); heavy query blocks first
+  const int nqb = (p.Lq + p.q_per_block - 1) / p.q_per_block;
+  const int qb = nqb - 1 - static_cast<int>(blockIdx.x % nqb);
+  const int bg = static_cast<int>(blockIdx.x / nqb);
+  const int b = bg / p.Hkv;
+  const int g = bg % p.Hkv;
+  const int split = blockIdx.y;
+  const int i_first = qb * p.q_per_block;
+  const int i_last = min(p.Lq, i_first + p.q_per_block) - 1;
+  const int rows_blk = (i_last - i_first + 1) * p.G;
+  const int P0 = p.Lk - p.Lq + i_first;
+  const int P1 = p.Lk - p.Lq + i_last;
+
+  // ---- this lane's query row (the S^T column it owns)
+  const int rloc = wave * 32 + l32;
+  const bool row_ok = rloc < rows_blk;
+  const int i_row = i_first + (row_ok ? rloc / p.G : 0);
+  const int h_row = g * p.G + (row_ok ? rloc % p.G : 0);
+  const int pos = p.Lk - p.Lq + i_row;
+  const long row_index = (static_cast<long>(b) * p.Hq + h_row) * p.Lq + i_row;
+
+  // ---- Q^T operand in registers: lane holds 8 dims (dc*16 + hf*8 ..) of its row
+  const T* Q = static_cast<const T*>(p.q);
+  const bool negate = p.scale < 0.f;  // fold the sign into Q so the log2-domain scale is > 0
+  const float cexp = fabsf(p.scale) * kLog2e;
+  u32x4_t qreg[D / 16];
+#pragma unroll
+  for (int dc = 0; dc < D / 16; ++dc) {
+    u32x4_t x = {0u, 0u, 0u, 0u};
+    if (row_ok) x = *reinterpret_cast<const u32x4_t*>(Q + row_index * D + dc * 16 + hf * 8);
+    if (negate) x ^= 0x80008000u;
+    qreg[dc] = x;
+  }
+
+  // ---- key range of this block (and split)
+  int lo, hi;
+  key_range(p.mask_kind, p.window_left, p.Lk, P0, P1, &lo, &hi);
+  if (p.no_skip) { lo = 0; hi = p.Lk; }
+  if (p.splits > 1) {
+    const int s0 = split * p.keys_per_split;
+    const int s1 = min(p.Lk, s0 + p.keys_per_split);
+    lo = max(lo, s0);
+    hi = min(hi, s1);
+    if (hi < lo) hi = lo;
+  }
+  const int ntiles_all = (p.Lk + BN - 1) / BN;
+  const int t_lo = lo / BN;
+  // an empty range visits no tile (a rounded-up end would reach into the next split)
+  const int t_hi = (hi > lo) ? (hi + BN - 1) / BN : t_lo;
+
+  const long kv_base = static_cast<long>(bg) * p.Lk * D;
+  const T* K = static_cast<const T*>(p.k) + kv_base;
+  const T* V = static_cast<const T*>(p.v) + kv_base;
+
+  // top-k: the block's largest threshold (thresholds do not grow with the row position)
+  const long bg_l = bg;
+  int32_t tau_row = 0, tau_blk = 0;
+  if (p.mask_kind == MI_ATTN_MASK_TOPK) {
+    tau_row = p.tau[bg_l * p.Lq + i_row];
+    tau_blk = p.tau[bg_l * p.Lq + i_first];
+  }
+  auto tile_live = [&](int t) -> bool {
+    if (p.no_skip) return true;
+    if (p.mask_kind == MI_ATTN_MASK_DENSE) return p.tile_live[static_cast<long>(qb) * ntiles_all + t] != 0;
+    if (p.mask_kind == MI_ATTN_MASK_TOPK) return p.tile_min_rank[bg_l * ntiles_all + t] <= tau_blk;
+    return true;
+  };
+  auto next_live = [&](int t) -> int {
+    while (t < t_hi && !tile_live(t)) ++t;
+    return t;
+  };
+
+  // ---- cooperative tile loads: K as [key][d] rows, V as V^T [d][permuted key]
+  const int vkg = tid / (D / 8);  // V key group (4 keys)
+  const int vdc = tid % (D / 8);  // V dim chunk (8 dims)
+  u32x4_t kbuf[TL::kChunks];
+  u32x4_t vbuf[4];
+  auto load_tile = [&](int t) {
+    const int j0 = t * BN;
+#pragma unroll
+    for (int c = 0; c < TL::kChunks; ++c) {
+      const int flat = c * kThreads + tid;
+      const int key = flat / (D / 8);
+      const int dch = flat % (D / 8);
+      u32x4_t x = {0u, 0u, 0u, 0u};
+      if (j0 + key < p.Lk) x = *reinterpret_cast<const u32x4_t*>(K + static_cast<long>(j0 + key) * D + dch * 8);
+      kbuf[c] = x;
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int key = j0 + vkg * 4 + a;
+      u32x4_t x = {0u, 0u, 0u, 0u};
+      if (key < p.Lk) x = *reinterpret_cast<const u32x4_t*>(V + static_cast<long>(key) * D + vdc * 8);
+      vbuf[a] = x;
+    }
+  };
+  auto store_tile = [&](int stage) {
+    uint16_t* ks = smem + stage * TL::stage;
+    uint16_t* vs = ks + TL::kElems;
+#pragma unroll
+    for (int c = 0; c < TL::kChunks; ++c) {
+      const int flat = c * kThreads + tid;
+      const int key = flat / (D / 8);
+      const int dch = flat % (D / 8);
+      *reinterpret_cast<u32x4_t*>(ks + key * TL::kStride + dch * 8) = kbuf[c];
+    }
+    // transpose 4 keys x 8 dims -> 8 rows of 4 keys
+    const int col = vperm(vkg * 4);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int w = e >> 1;
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;  // high or low halves
+      u32x2_t o;
+      o.x = __builtin_amdgcn_perm(vbuf[1][w], vbuf[0][w], sel);
+      o.y = __builtin_amdgcn_perm(vbuf[3][w], vbuf[2][w], sel);
+      *reinterpret_cast<u32x2_t*>(vs + (vdc * 8 + e) * TL::vStride + col) = o;
+    }
+  };
+
+  // ---- running state
+  constexpr int NKB = BN / 32;  // 32-key blocks per tile
+  constexpr int NDB = D / 32;   // 32-dim blocks of O^T
+  f32x16_t oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16_t{};
+  float m_run = kNegInf;  // running max, log2 domain
+  float l_run = 0.f;      // this lane's partial running sum
+
+  int t = next_live(t_lo);
+  int stage = 0;
+  if (t < t_hi) {
+    load_tile(t);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  while (t < t_hi) {
+    const int tn = next_live(t + 1);
+    if (tn < t_hi) load_tile(tn);  // prefetch into registers while this tile computes
+
+    const uint16_t* ks = smem + stage * TL::stage;
+    const uint16_t* vs = ks + TL::kElems;
+    const int j0 = t * BN;
+
+    // S^T = K Q^T
+    f32x16_t sacc[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      f32x16_t acc = f32x16_t{};
+#pragma unroll
+      for (int dc = 0; dc < D / 16; ++dc) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(ks + (kb * 32 + l32) * TL::kStride + dc * 16 + hf * 8);
+        acc = mfma32(T{}, a, qreg[dc], acc);
+      }
+      sacc[kb] = acc;
+    }
+
+    // mask (boundary tiles only); masked tiles move to the log2 domain here (cm = 1)
+    const int j_end = j0 + BN - 1;
+    bool need_mask = p.no_skip || j_end >= p.Lk || p.mask_kind == MI_ATTN_MASK_DENSE ||
+                     p.mask_kind == MI_ATTN_MASK_TOPK;
+    if (p.mask_kind == MI_ATTN_MASK_CAUSAL || p.mask_kind == MI_ATTN_MASK_WINDOW) need_mask |= j_end > P0;
+    if (p.mask_kind == MI_ATTN_MASK_WINDOW) need_mask |= j0 < P1 - p.window_left;
+    float cm = cexp;
+    if (need_mask) {
+      cm = 1.f;
+      const long bgk = bg_l * p.Lk;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int jb = j0 + kb * 32 + r4 * 8 + hf * 4;  // first of 4 consecutive keys
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = jb + e;
+            float s = sacc[kb][r4 * 4 + e] * cexp;
+            bool vis = j < p.Lk;
+            switch (p.mask_kind) {
+              case MI_ATTN_MASK_CAUSAL: vis = vis && j <= pos; break;
+              case MI_ATTN_MASK_WINDOW: vis = vis && j <= pos && j >= pos - p.window_left; break;
+              case MI_ATTN_MASK_DENSE:
+                if (vis) s += p.mask[static_cast<long>(i_row) * p.Lk + j] * kLog2e;
+                break;
+              case MI_ATTN_MASK_TOPK:
+                vis = vis && j <= pos && p.rank[bgk + j] <= tau_row;
+                if (vis) s += p.zero_hold[bgk + j] * kLog2e;
+                break;
+              default: break;
+            }
+            sacc[kb][r4 * 4 + e] = vis ? s : kNegInf;
+          }
+        }
+      }
+    }
+
+    // online softmax (log2 domain), guarded against all -inf tiles
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    const float m_new = fmaxf(m_run, mx * cm);
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    float psum = 0.f;
+    u32x4_t preg[BN / 16];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pv[e] = fast_exp2(fmaf(sacc[kb][half * 8 + e], cm, -m_use));
+          psum += pv[e];
+        }
+        u32x4_t pk;
+        pk.x = pack2(T{}, pv[0], pv[1]);
+        pk.y = pack2(T{}, pv[2], pv[3]);
+        pk.z = pack2(T{}, pv[4], pv[5]);
+        pk.w = pack2(T{}, pv[6], pv[7]);
+        preg[kb * 2 + half] = pk;
+      }
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int kc = 0; kc < BN / 16; ++kc) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(vs + (db * 32 + l32) * TL::vStride + kc * 16 + hf * 8);
+        oacc[db] = mfma32(T{}, a, preg[kc], oacc[db]);
+      }
+    }
+
+    if (tn < t_hi) store_tile(stage ^ 1);
+    __syncthreads();
+    t = tn;
+    stage ^= 1;
+  }
+
+  // ---- epilogue: combine the two lane halves' partial sums, normalise, store
+  const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
+  if (!row_ok) return;
+  const bool dead = !(l_tot > 0.f);
+  const float inv = dead ? 0.f : 1.f / l_tot;
+  const float lse = dead ? kNegInf : (m_run + fast_log2(l_tot)) * kLn2;
+  if (p.splits > 1) {
+    const long rows_all = static_cast<long>(p.B) * p.Hq * p.Lq;
+    float* po = p.part_out + (static_cast<long>(split) * rows_all + row_index) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = db * 32 + r4 * 8 + hf * 4;
+        float4 v = {oacc[db][r4 * 4] * inv, oacc[db][r4 * 4 + 1] * inv, oacc[db][r4 * 4 + 2] * inv,
+                    oacc[db][r4 * 4 + 3] * inv};
+        *reinterpret_cast<float4*>(po + d0) = v;
+      }
+    if (hf == 0) p.part_lse[split * rows_all + row_index] = lse;
+    return;
+  }
+  T* O = static_cast<T*>(p.out) + row_index * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d0 = db * 32 + r4 * 8 + hf * 4;
+      u32x2_t w;
+      w.x = pack2(T{}, oacc[db][r4 * 4] * inv, oacc[db][r4 * 4 + 1] * inv);
+      w.y = pack2(T{}, oacc[db][r4 * 4 + 2] * inv, oacc[db][r4 * 4 + 3] * inv);
+      *reinterpret_cast<u32x2_t*>(O + d0) = w;
+    }
+  if (hf == 0 && p.lse != nullptr) p.lse[row_index] = lse;
+}
+
+// Split-KV combine: one thread per (row, 4 dims). lse = log sum_s exp(lse_s) (all -inf
+// gives -inf and output 0); out = sum_s exp(lse_s - lse) o_s.
+template <typename T>
+__global__ __launch_bounds__(256) void lse_merge_kernel(AttnParams p) {
+  const int D = p.d;
+  const long rows_all = static_cast<long>(p.B) * p.Hq * p.Lq;
+  const long t = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int per_row = D / 4;
+  if (t >= rows_all * per_row) return;
+  const long row = t / per_row;
+  const int d0 = static_cast<int>(t % per_row) * 4;
+  float mx = kNegInf;
+  for (int s = 0; s < p.splits; ++s) mx = fmaxf(mx, p.part_lse[s * rows_all + row]);
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
+  float tot = 0.f;
+  if (mx != kNegInf) {
+    for (int s = 0; s < p.splits; ++s) {
+      const float w = __expf(p.part_lse[s * rows_all + row] - mx);
+      const float4 o = *reinterpret_cast<const float4*>(p.part_out + (s * rows_all + row) * D + d0);
+      acc.x += w * o.x; acc.y += w * o.y; acc.z += w * o.z; acc.w += w * o.w;
+      tot += w;
+    }
+  }
+  const bool dead = !(tot > 0.f);
+  const float inv = dead ? 0.f : 1.f / tot;
+  T* O = static_cast<T*>(p.out) + row * D + d0;
+  O[0] = from_f32<T>(acc.x * inv);
+  O[1] = from_f32<T>(acc.y * inv);
+  O[2] = from_f32<T>(acc.z * inv);
+  O[3] = from_f32<T>(acc.w * inv);
+  if (d0 == 0 && p.lse != nullptr) p.lse[row] = dead ? kNegInf : mx + logf(tot);
+}
+
+template <typename T>
+hipError_t launch_prefill_t(const AttnParams& p, hipStream_t s) {
+  const int nqb = (p.Lq + p.q_per_block - 1) / p.q_per_block;
+  const long blocks = static_cast<long>(p.B) * p.Hkv * nqb;
+  if (blocks > 0x7fffffffL || p.splits > 65535) return hipErrorInvalidValue;
+  dim3 grid(static_cast<unsigned>(blocks), p.splits), block(kThreads);
+  if (p.d == 128)
+    hipLaunchKernelGGL((prefill_kernel<T, 128, 64>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((prefill_kernel<T, 64, 128>), grid, block, 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.splits <= 1) return e;
+  const long n = static_cast<long>(p.B) * p.Hq * p.Lq * (p.d / 4);
+  hipLaunchKernelGGL(lse_merge_kernel<T>, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int prefill_block_n(int d) { return d == 128 ? 64 : 128; }
+int prefill_block_m() { return kBlockM; }
+
+hipError_t launch_prefill(const AttnParams& p, int dtype, hipStream_t s) {
+  if (dtype == MI_ATTN_BF16) return launch_prefill_t<bf16_t>(p, s);
+  if (dtype == MI_ATTN_F16) return launch_prefill_t<f16_t>(p, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mi_attn

@@ -1,0 +1,133 @@
+// Row kernel: one wavefront per query row, online softmax over 64-key chunks.
+//
+// This is the plain GPU form of the chunked forward (ExecuTorch pull request #10466 page,
+// "Summary"): keys arrive in chunks, the row keeps a running max m and running sum l,
+// and the unnormalised output is rescaled whenever m grows. It serves the fp32 inputs
+// (computed in fp32 end to end) and, through the debug switch, cross-checks the MFMA
+// kernels for fp16/bf16. Every mask kind is applied per element.
+#include "common.hpp"
+
+namespace mi_attn {
+
+namespace {
+
+constexpr int kRowsPerBlock = 4;  // one row per wavefront
+constexpr int kMaxD = 256;
+
+template <typename T>
+__global__ __launch_bounds__(kRowsPerBlock * kWave) void row_kernel(AttnParams p) {
+  __shared__ float sq[kRowsPerBlock][kMaxD];
+  __shared__ float sp[kRowsPerBlock][kWave];
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const long row = static_cast<long>(blockIdx.x) * kRowsPerBlock + wave;
+  const long nrows = static_cast<long>(p.B) * p.Hq * p.Lq;
+  if (row >= nrows) return;  // whole wavefront leaves together; no block barrier below
+
+  const int i = static_cast<int>(row % p.Lq);
+  const int h = static_cast<int>((row / p.Lq) % p.Hq);
+  const int b = static_cast<int>(row / (static_cast<long>(p.Lq) * p.Hq));
+  const int g = h / p.G;
+  const int d = p.d;
+  const int pos = p.Lk - p.Lq + i;  // bottom-right aligned absolute position
+
+  const T* qrow = static_cast<const T*>(p.q) + row * d;
+  const long kv_off = (static_cast<long>(b) * p.Hkv + g) * p.Lk * d;
+  const T* kb = static_cast<const T*>(p.k) + kv_off;
+  const T* vb = static_cast<const T*>(p.v) + kv_off;
+
+  for (int c = lane; c < d; c += kWave) sq[wave][c] = to_f32(qrow[c]);
+  __builtin_amdgcn_wave_barrier();
+
+  int lo, hi;
+  key_range(p.mask_kind, p.window_left, p.Lk, pos, pos, &lo, &hi);
+  if (p.no_skip) { lo = 0; hi = p.Lk; }
+
+  const long bg = static_cast<long>(b) * p.Hkv + g;
+  const int32_t tau = (p.mask_kind == MI_ATTN_MASK_TOPK) ? p.tau[bg * p.Lq + i] : 0;
+
+  float m = kNegInf, l = 0.f;
+  float acc[kMaxD / kWave];
+#pragma unroll
+  for (int t = 0; t < kMaxD / kWave; ++t) acc[t] = 0.f;
+
+  for (int j0 = lo; j0 < hi; j0 += kWave) {
+    const int j = j0 + lane;
+    float s = kNegInf;
+    if (j < hi) {
+      const T* kr = kb + static_cast<long>(j) * d;
+      float dot = 0.f;
+      for (int c = 0; c < d; ++c) dot = fmaf(sq[wave][c], to_f32(kr[c]), dot);
+      s = dot * p.scale;
+      switch (p.mask_kind) {
+        case MI_ATTN_MASK_CAUSAL:
+          if (j > pos) s = kNegInf;
+          break;
+        case MI_ATTN_MASK_WINDOW:
+          if (j > pos || j < pos - p.window_left) s = kNegInf;
+          break;
+        case MI_ATTN_MASK_DENSE:
+          s += p.mask[static_cast<long>(i) * p.Lk + j];
+          break;
+        case MI_ATTN_MASK_TOPK:
+          if (j <= pos && p.rank[bg * p.Lk + j] <= tau)
+            s += p.zero_hold[bg * p.Lk + j];
+          else
+            s = kNegInf;
+          break;
+        default:
+          break;
+      }
+    }
+    const float m_new = fmaxf(m, wave_max(s));
+    // Guard: a chunk whose logits are all -inf leaves m_new = -inf. Subtracting a
+    // finite stand-in keeps exp(-inf - ref) = 0 instead of exp(-inf + inf) = NaN.
+    const float ref = (m_new == kNegInf) ? 0.f : m_new;
+    const float alpha = expf(m - ref);
+    const float pj = expf(s - ref);
+    l = alpha * l + wave_sum(pj);
+    m = m_new;
+    sp[wave][lane] = pj;
+    __builtin_amdgcn_wave_barrier();
+    const int nk = (hi - j0) < kWave ? (hi - j0) : kWave;
+#pragma unroll
+    for (int t = 0; t < kMaxD / kWave; ++t) {
+      const int c = lane + t * kWave;
+      if (c < d) {
+        float a = acc[t] * alpha;
+        for (int jj = 0; jj < nk; ++jj)
+          a = fmaf(sp[wave][jj], to_f32(vb[static_cast<long>(j0 + jj) * d + c]), a);
+        acc[t] = a;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  T* orow = static_cast<T*>(p.out) + row * d;
+  const bool dead = (l == 0.f);
+  const float inv = dead ? 0.f : 1.f / l;
+#pragma unroll
+  for (int t = 0; t < kMaxD / kWave; ++t) {
+    const int c = lane + t * kWave;
+    if (c < d) orow[c] = from_f32<T>(dead ? 0.f : acc[t] * inv);
+  }
+  if (p.lse != nullptr && lane == 0) p.lse[row] = dead ? kNegInf : (m + logf(l));
+}
+
+}  // namespace
+
+hipError_t launch_row_kernel(const AttnParams& p, int dtype, hipStream_t s) {
+  const long nrows = static_cast<long>(p.B) * p.Hq * p.Lq;
+  const long blocks = (nrows + kRowsPerBlock - 1) / kRowsPerBlock;
+  if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
+  dim3 grid(static_cast<unsigned>(blocks)), block(kRowsPerBlock * kWave);
+  switch (dtype) {
+    case MI_ATTN_F32: hipLaunchKernelGGL(row_kernel<float>, grid, block, 0, s, p); break;
+    case MI_ATTN_F16: hipLaunchKernelGGL(row_kernel<f16_t>, grid, block, 0, s, p); break;
+    case MI_ATTN_BF16: hipLaunchKernelGGL(row_kernel<bf16_t>, grid, block, 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mi_attn

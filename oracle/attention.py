@@ -51,7 +51,7 @@ def mask_matrix(kind: str, Lq: int, Lk: int, *, window_left: int = 0, dense=None
         return np.asarray(dense, dtype=np.float64)[rows]
     if kind == "topk":
         from .topk import topk_kept_ref
-        kept = topk_kept_ref(zh_row, Lq, keep_k, causal=True)[rows]
+        kept = topk_kept_ref(zh_row, Lq, keep_k, causal=True, rows=rows)
         return np.where(kept, np.asarray(zh_row, dtype=np.float64)[None, :], NEG_INF)
     raise ValueError(kind)
 

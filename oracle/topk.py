@@ -33,8 +33,8 @@ def _canon(zh_row: np.ndarray) -> np.ndarray:
     return z
 
 
-def topk_kept_ref(zh_row: np.ndarray, Lq: int, keep_k: int, causal: bool = True) -> np.ndarray:
-    """bool [Lq, Lk]: the kept set of every query row, by the definition itself.
+def topk_kept_ref(zh_row: np.ndarray, Lq: int, keep_k: int, causal: bool = True, rows=None) -> np.ndarray:
+    """bool [Lq, Lk] (or [len(rows), Lk]): the kept set of each query row, by the definition.
 
     For each row: list the allowed keys, stable-sort them by descending
     zero_hold (a stable sort keeps lower indices first among ties), keep the
@@ -44,14 +44,15 @@ def topk_kept_ref(zh_row: np.ndarray, Lq: int, keep_k: int, causal: bool = True)
     z = _canon(zh_row)
     Lk = z.shape[0]
     pos = query_positions(Lq, Lk)
-    kept = np.zeros((Lq, Lk), dtype=bool)
-    for i in range(Lq):
+    rows = np.arange(Lq) if rows is None else np.asarray(rows)
+    kept = np.zeros((rows.size, Lk), dtype=bool)
+    for r, i in enumerate(rows):
         n_allowed = (min(Lk, pos[i] + 1) if pos[i] >= 0 else 0) if causal else Lk
         if n_allowed <= 0:
             continue
         cand = np.arange(n_allowed)
         order = cand[np.argsort(-z[:n_allowed], kind="stable")]
-        kept[i, order[:keep_k]] = True
+        kept[r, order[:keep_k]] = True
     return kept
 
 

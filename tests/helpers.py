@@ -1,0 +1,82 @@
+"""Shared test helpers: move a synthetic problem to the GPU, run the HIP path through the
+binding, run the oracle on the same stored inputs, and compare to the stated bounds."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle
+import synth
+
+# Bounds: fp32 inputs 1e-5 on the output; fp16/bf16 inputs 2e-2 on the output and 1e-3
+# on the LSE; an LSE of -inf must match exactly and no NaN may appear.
+TOL = {"fp32": (1e-5, 1e-5), "fp16": (2e-2, 1e-3), "bf16": (2e-2, 1e-3)}
+
+
+def say(msg: str):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def to_device(arr: np.ndarray, dtype: str, device="cuda"):
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(arr.view(np.int16).copy()).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(arr)).to(device)
+
+
+def out_to_f64(t, dtype: str) -> np.ndarray:
+    import torch
+    return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+
+
+def run_gpu(p: synth.Problem, *, out_fill=None, return_tensors=False):
+    import torch
+    import masked_flashattention_forward_amd as mfa
+    q, k, v = (to_device(getattr(p, n), p.dtype) for n in ("q", "k", "v"))
+    mask = None if p.mask is None else torch.from_numpy(p.mask).cuda()
+    zh = None if p.zero_hold is None else torch.from_numpy(p.zero_hold).cuda()
+    out = torch.empty_like(q)
+    lse = torch.empty((p.B, p.Hq, p.Lq), dtype=torch.float32, device=q.device)
+    if out_fill is not None:
+        out.fill_(out_fill)
+        lse.fill_(out_fill)
+    mfa.attn_fwd(q, k, v, scale=p.scale, mask_kind=p.mask_kind, window_left=p.window_left,
+                 mask=mask if p.mask_kind == "dense" else None,
+                 zero_hold=zh if p.mask_kind == "topk" else None,
+                 keep_k=p.keep_k, out=out, lse=lse)
+    torch.cuda.synchronize()
+    if return_tensors:
+        return out, lse
+    return out_to_f64(out, p.dtype), lse.cpu().numpy().astype(np.float64)
+
+
+def run_oracle(p: synth.Problem, rows=None, heads=None):
+    return oracle.attention_ref(p.f64("q"), p.f64("k"), p.f64("v"), p.scale64, p.mask_kind,
+                                window_left=p.window_left,
+                                mask=None if p.mask is None else p.mask.astype(np.float64),
+                                zero_hold=None if p.zero_hold is None else p.zero_hold.astype(np.float64),
+                                keep_k=p.keep_k, rows=rows, heads=heads)
+
+
+def compare(p: synth.Problem, out, lse, ref_out, ref_lse, rows=None, heads=None, label=""):
+    """Element-wise comparison on the computed (rows, heads) subset; returns the errors."""
+    tol_o, tol_l = TOL[p.dtype]
+    sel = ~np.isnan(ref_lse)
+    if rows is not None or heads is not None:
+        assert sel.any()
+    go, gl = out[sel], lse[sel]
+    ro, rl = ref_out[sel], ref_lse[sel]
+    assert not np.isnan(go).any(), f"{label}: NaN in output"
+    assert not np.isnan(gl).any(), f"{label}: NaN in LSE"
+    dead = rl == -np.inf
+    assert np.array_equal(gl == -np.inf, dead), f"{label}: -inf LSE pattern differs"
+    assert np.all(go[dead] == 0.0), f"{label}: fully masked rows must be 0"
+    err_o = float(np.abs(go - ro).max()) if go.size else 0.0
+    err_l = float(np.abs(gl[~dead] - rl[~dead]).max()) if (~dead).any() else 0.0
+    print(f"[parity] {label or p.name}: max|out err|={err_o:.3e} (tol {tol_o}) "
+          f"max|lse err|={err_l:.3e} (tol {tol_l}) dead_rows={int(dead.sum())}", flush=True)
+    assert err_o <= tol_o, f"{label}: output error {err_o} > {tol_o}"
+    assert err_l <= tol_l, f"{label}: LSE error {err_l} > {tol_l}"
+    return err_o, err_l

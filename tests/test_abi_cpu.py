@@ -1,0 +1,135 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol, and rejects
+invalid arguments before any GPU work. No kernel is launched here."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import masked_flashattention_forward_amd as mfa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mi_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "defined")))
+
+
+def header_define(name):
+    m = re.search(rf"#define\s+{name}\s+\(?(-?\d+)\)?", open(HEADER).read())
+    return int(m.group(1))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mfa.LIB_PATH):
+        pytest.fail("libmi_attn.so is not built; run __graft_entry__.build()")
+    return mfa.lib()
+
+
+def test_header_declares_the_expected_entry_points():
+    assert declared_functions() == sorted(mfa.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", mfa.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_abi_version_matches_header(lib):
+    assert mfa.abi_version() == header_define("MI_ATTN_ABI_VERSION")
+    assert header_define("MI_ATTN_EINVAL") == mfa.EINVAL
+    assert header_define("MI_ATTN_EUNSUPPORTED") == mfa.EUNSUPPORTED
+
+
+def plan_rc(**kw):
+    args = dict(B=1, Hq=4, Hkv=2, Lq=16, Lk=32, d=64, mask_kind=1, window_left=0, keep_k=1, dtype=2)
+    args.update(kw)
+    p = mfa.AttnPlan()
+    rc = mfa.lib().attn_fwd_plan(*args.values(), ctypes.byref(p))
+    return rc, p
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Hq=3, Hkv=2), -1),          # Hq % Hkv != 0 (InfiniTrain page: an error)
+    (dict(B=0), -1), (dict(Lq=0), -1), (dict(Lk=-5), -1), (dict(d=0), -1), (dict(Hkv=0), -1),
+    (dict(mask_kind=7), -1), (dict(mask_kind=-1), -1),
+    (dict(dtype=5), -1),
+    (dict(mask_kind=2, window_left=-1), -1),
+    (dict(mask_kind=4, keep_k=0), -1),
+    (dict(d=96), -2), (dict(d=256), -2), (dict(d=32), -2),
+    (dict(dtype=0, d=260), -2), (dict(dtype=0, d=66), -2),
+    (dict(mask_kind=4, keep_k=4, Lk=70000), -2),
+])
+def test_plan_rejects_invalid_arguments(lib, kw, code):
+    rc, _ = plan_rc(**kw)
+    assert rc == code
+    assert lib.attn_last_error().decode() != ""
+
+
+def test_plan_accepts_supported_shapes(lib):
+    for kw in (dict(), dict(dtype=0, d=64), dict(dtype=0, d=4), dict(dtype=0, d=256), dict(d=128, dtype=1),
+               dict(mask_kind=0), dict(mask_kind=2, window_left=0), dict(mask_kind=3), dict(mask_kind=4, keep_k=3)):
+        rc, p = plan_rc(**kw)
+        assert rc == 0, (kw, lib.attn_last_error())
+        assert lib.attn_last_error().decode() == ""
+        assert p.path in (0, 1, 2) and p.grid >= 1 and p.splits >= 1
+
+
+def test_fp32_takes_the_row_kernel(lib):
+    assert mfa.plan(1, 2, 2, 128, 128, 64, "causal", dtype=mfa.F32)["path"] == "row"
+
+
+def test_forced_path_errors_are_reported(lib):
+    try:
+        mfa.set_debug(force_path=1)
+        rc, _ = plan_rc(dtype=0)
+        assert rc == -2
+    finally:
+        mfa.set_debug()
+
+
+def call_attn(**kw):
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+    args = dict(q=fake, k=fake, v=fake, out=fake, lse=None, B=1, Hq=2, Hkv=2, Lq=8, Lk=8, d=64, scale=0.125,
+                mask_kind=1, window_left=0, mask=None, zero_hold=None, keep_k=0, dtype=2, stream=None)
+    args.update(kw)
+    return mfa.lib().attn_fwd(*args.values())
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=None), dict(out=None), dict(v=None),
+    dict(scale=float("nan")), dict(scale=float("inf")),
+    dict(mask_kind=3, mask=None),                 # a dense mask is never silently ignored
+    dict(mask_kind=4, zero_hold=None, keep_k=4),
+    dict(mask_kind=4, zero_hold=ctypes.c_void_p(0x2000), keep_k=0),
+    dict(Hq=3, Hkv=2),
+])
+def test_attn_fwd_rejects_before_any_gpu_work(lib, kw):
+    assert call_attn(**kw) == -1
+    assert lib.attn_last_error().decode() != ""
+
+
+def test_topk_rejects_invalid_arguments(lib):
+    fake = ctypes.c_void_p(0x1000)
+    f = lib.dynamic_mask_topk
+    assert f(fake, 1, 1, 4, 4, 0, 1, fake, fake, None, None) == -1
+    assert f(None, 1, 1, 4, 4, 2, 1, fake, fake, None, None) == -1
+    assert f(fake, 1, 1, 0, 4, 2, 1, fake, fake, None, None) == -1
+    assert f(fake, 1, 1, 4, 4, 2, 1, None, fake, None, None) == -1
+    assert f(fake, 1, 1, 4, 70000, 2, 1, fake, fake, None, None) == -2
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(mfa, "LIB_PATH", "/nonexistent/libmi_attn.so")
+    monkeypatch.setattr(mfa, "_lib", None)
+    with pytest.raises(mfa.MiAttnError):
+        mfa.lib()

@@ -1,0 +1,152 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle, element by
+element, on seeded inputs. Small shapes span several tiles with ragged tails; the
+full-size workloads are compared on sampled heads and rows."""
+import numpy as np
+import pytest
+
+import synth
+from helpers import compare, run_gpu, run_oracle, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import masked_flashattention_forward_amd as mfa
+    mfa.lib()
+    mfa.set_debug()
+    yield
+    mfa.set_debug()
+
+
+def dense_mask(seed, Lq, Lk):
+    rng = np.random.default_rng(seed)
+    m = rng.standard_normal((Lq, Lk)).astype(np.float32)
+    m[rng.random((Lq, Lk)) < 0.4] = -np.inf
+    m[1] = -np.inf                       # a fully masked row
+    m[2, :] = -np.inf
+    m[2, Lk // 2:Lk // 2 + 3] = 1.5      # a row with three finite, non-zero entries
+    return m
+
+
+SMALL = []
+for dtype, d in (("bf16", 128), ("bf16", 64), ("fp16", 128), ("fp16", 64), ("fp32", 64), ("fp32", 40)):
+    for kind in ("none", "causal", "window", "dense", "topk"):
+        SMALL.append((dtype, d, kind))
+
+
+@pytest.mark.parametrize("dtype,d,kind", SMALL)
+def test_small_ragged(dtype, d, kind):
+    B, Hq, Hkv, Lq, Lk = 2, 4, 2, 77, 203
+    p = synth.make_problem(f"small {dtype} d{d} {kind}", B, Hq, Hkv, Lq, Lk, d, dtype, kind, 100 + d,
+                           window_left=37, keep_k=17, with_zero_hold=kind == "topk",
+                           mask=dense_mask(7, Lq, Lk) if kind == "dense" else None)
+    say(p.name)
+    out, lse = run_gpu(p, out_fill=float("nan"))
+    ref_o, ref_l = run_oracle(p)
+    compare(p, out, lse, ref_o, ref_l, label=p.name)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("Lq,Lk,kind", [(130, 50, "causal"), (1, 1000, "causal"), (3, 517, "window"),
+                                         (64, 64, "topk"), (1, 1, "none"), (200, 129, "topk")])
+def test_edge_shapes(dtype, Lq, Lk, kind):
+    d = 128 if dtype == "bf16" else 64
+    p = synth.make_problem(f"edge {dtype} Lq{Lq} Lk{Lk} {kind}", 1, 8, 1, Lq, Lk, d, dtype, kind, 200 + Lq,
+                           window_left=5, keep_k=9, with_zero_hold=kind == "topk")
+    say(p.name)
+    out, lse = run_gpu(p, out_fill=float("nan"))
+    ref_o, ref_l = run_oracle(p)
+    compare(p, out, lse, ref_o, ref_l, label=p.name)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c2b", "c2c", "c2w"])
+def test_small_configs_full(name):
+    p = synth.config(name)
+    say(f"config {name}: {p.name}")
+    out, lse = run_gpu(p, out_fill=float("nan"))
+    ref_o, ref_l = run_oracle(p)
+    compare(p, out, lse, ref_o, ref_l, label=name)
+    if name == "c2b":
+        assert np.all(out == 0) and np.all(lse == -np.inf)
+    if name == "c2c":   # one visible key per row: out = v[pos] rounded, lse = its logit
+        v = p.f64("v")
+        for i in range(p.Lq):
+            np.testing.assert_allclose(out[:, :, i], np.repeat(v[:, :, 572 + i], p.Hq // p.Hkv, axis=1),
+                                       rtol=0, atol=1e-2)
+
+
+def test_c2_dense_equals_window_kind():
+    """Two routes on the GPU: the dense window mask over 700 keys and the window kind
+    over the first 576 keys give the same result."""
+    a = run_gpu(synth.config("c2"))
+    b = run_gpu(synth.config("c2w"))
+    np.testing.assert_allclose(a[0], b[0], rtol=0, atol=2e-2)
+    np.testing.assert_allclose(a[1], b[1], rtol=0, atol=1e-3)
+
+
+def test_no_skip_switch_changes_nothing():
+    import masked_flashattention_forward_amd as mfa
+    for kind in ("causal", "window", "dense", "topk"):
+        p = synth.make_problem(f"noskip {kind}", 1, 4, 1, 100, 700, 128, "bf16", kind, 300,
+                               window_left=60, keep_k=30, with_zero_hold=kind == "topk",
+                               mask=synth.window_dense_mask(100, 700, 500, 60) if kind == "dense" else None)
+        say(p.name)
+        a = run_gpu(p)
+        try:
+            mfa.set_debug(no_skip=True)
+            b = run_gpu(p)
+        finally:
+            mfa.set_debug()
+        # Skipping only drops keys that are -inf for every row of a tile, but it can move
+        # the chunk boundaries, so fp32 summation order (and a bf16 rounding) may change.
+        np.testing.assert_array_equal(a[1] == -np.inf, b[1] == -np.inf)
+        np.testing.assert_allclose(a[0], b[0], rtol=0, atol=1e-3)
+        fin = np.isfinite(a[1])
+        np.testing.assert_allclose(a[1][fin], b[1][fin], rtol=0, atol=1e-4)
+
+
+def test_runs_are_bitwise_deterministic():
+    p = synth.make_problem("determinism", 2, 8, 2, 300, 900, 128, "bf16", "causal", 301)
+    say(p.name)
+    a = run_gpu(p)
+    b = run_gpu(p)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("kind", ["causal", "window", "dense", "topk", "none"])
+@pytest.mark.parametrize("splits", [2, 3, 7])
+def test_forced_split_kv_merge(kind, splits):
+    """Split-KV with the LSE merge, including splits whose key range is empty or fully
+    masked (window), against the oracle."""
+    import masked_flashattention_forward_amd as mfa
+    Lq, Lk = 5, 1111
+    p = synth.make_problem(f"split{splits} {kind}", 2, 8, 2, Lq, Lk, 128, "bf16", kind, 400 + splits,
+                           window_left=70, keep_k=50, with_zero_hold=kind == "topk",
+                           mask=synth.window_dense_mask(Lq, Lk, 900, 100) if kind == "dense" else None)
+    say(p.name)
+    try:
+        mfa.set_debug(force_path=2, force_splits=splits)
+        out, lse = run_gpu(p, out_fill=float("nan"))
+    finally:
+        mfa.set_debug()
+    ref_o, ref_l = run_oracle(p)
+    compare(p, out, lse, ref_o, ref_l, label=p.name)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_row_kernel_and_mfma_agree(dtype):
+    import masked_flashattention_forward_amd as mfa
+    p = synth.make_problem(f"paths {dtype}", 1, 4, 4, 150, 333, 64, dtype, "causal", 500)
+    say(p.name)
+    a = run_gpu(p)
+    try:
+        mfa.set_debug(force_path=0)
+        b = run_gpu(p)
+    finally:
+        mfa.set_debug()
+    np.testing.assert_allclose(a[0], b[0], rtol=0, atol=2e-2)
+    np.testing.assert_allclose(a[1], b[1], rtol=0, atol=1e-3)
