@@ -1,0 +1,315 @@
+"""Benchmark of the masked attention forward on one MI355X.
+
+Headline (the JSON line's ``value``): causal prefill with past keys, bottom-right
+aligned -- B=8, Hq=32, Hkv=8, Lq=512, Lk=4096, d=128, bf16 -- in TFLOP/s of
+algorithmic work (4*d flops per visible (row, key) pair). One step is one
+``attn_fwd`` call on that batch, inputs resident in HBM before timing starts.
+
+The same line carries:
+  roofline      the prefill kernel's achieved TFLOP/s against the bf16 dense MFMA peak,
+                timed with events on the stream the library launches on;
+  cpu_baseline  the fp64 oracle on a bounded sample of the same workload;
+  configs       every other workload (decode GB/s, long causal, top-k, dense window,
+                tiny fp32), each checked against the oracle on sampled rows first.
+
+Usage: python bench.py [--steps K] [--warmup W] [--only NAME] [--no-cpu-baseline]
+                       [--no-configs] [--copy-calibration BYTES]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attn fwd TFLOP/s (prefill, % MFMA peak); decode KV GB/s (% HBM peak)"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 flop/clk/CU (published 2.5 PFLOP/s dense)
+PEAK_HBM_GBS = 8000.0       # 8 TB/s HBM3E
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def visible_pairs(p) -> int:
+    """(row, key) pairs the mask leaves visible, summed over batch and heads."""
+    Lq, Lk = p.Lq, p.Lk
+    pos = np.arange(Lq) + (Lk - Lq)
+    if p.mask_kind == "none":
+        per = Lq * Lk
+    elif p.mask_kind == "causal":
+        per = int(np.clip(pos + 1, 0, Lk).sum())
+    elif p.mask_kind == "window":
+        hi = np.clip(pos + 1, 0, Lk)
+        lo = np.clip(pos - p.window_left, 0, Lk)
+        per = int(np.maximum(hi - lo, 0).sum())
+    elif p.mask_kind == "dense":
+        per = int(np.isfinite(p.mask).sum())
+    elif p.mask_kind == "topk":
+        per = int(np.minimum(np.clip(pos + 1, 0, Lk), p.keep_k).sum())
+    else:
+        raise ValueError(p.mask_kind)
+    return per * p.B * p.Hq
+
+
+def causal_pairs(p) -> int:
+    pos = np.arange(p.Lq) + (p.Lk - p.Lq)
+    return int(np.clip(pos + 1, 0, p.Lk).sum()) * p.B * p.Hq
+
+
+def algorithmic_bytes(p) -> int:
+    """Q + out + LSE + the distinct K/V rows some row can see (+ mask / zero_hold)."""
+    es = 4 if p.dtype == "fp32" else 2
+    q = p.B * p.Hq * p.Lq * p.d * es
+    lse = p.B * p.Hq * p.Lq * 4
+    pos = np.arange(p.Lq) + (p.Lk - p.Lq)
+    if p.mask_kind in ("causal", "topk"):
+        keys = min(p.Lk, int(pos.max()) + 1) if pos.max() >= 0 else 0
+    elif p.mask_kind == "window":
+        keys = min(p.Lk, int(pos.max()) + 1) - max(0, int(pos.min()) - p.window_left)
+    elif p.mask_kind == "dense":
+        keys = int(np.isfinite(p.mask).any(axis=0).sum())
+    else:
+        keys = p.Lk
+    kv = 2 * p.B * p.Hkv * keys * p.d * es
+    extra = 0
+    if p.mask_kind == "dense":
+        extra = p.mask.nbytes
+    if p.mask_kind == "topk":
+        extra = p.zero_hold.nbytes
+    return int(2 * q + lse + kv + extra)
+
+
+class Runner:
+    """Device copies of one problem and a bound attn_fwd call."""
+
+    def __init__(self, p):
+        import torch
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        self.p = p
+        dev = "cuda"
+
+        def t(a):
+            if p.dtype == "bf16":
+                return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+            return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+        self.q, self.k, self.v = t(p.q), t(p.k), t(p.v)
+        self.mask = torch.from_numpy(p.mask).to(dev) if p.mask is not None else None
+        self.zh = torch.from_numpy(p.zero_hold).to(dev) if p.zero_hold is not None else None
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty((p.B, p.Hq, p.Lq), dtype=torch.float32, device=dev)
+
+    def __call__(self):
+        import masked_flashattention_forward_amd as mfa
+        p = self.p
+        mfa.attn_fwd(self.q, self.k, self.v, scale=p.scale, mask_kind=p.mask_kind, window_left=p.window_left,
+                     mask=self.mask if p.mask_kind == "dense" else None,
+                     zero_hold=self.zh if p.mask_kind == "topk" else None, keep_k=p.keep_k,
+                     out=self.out, lse=self.lse)
+
+    def event_time_ms(self, iters: int, fn=None) -> float:
+        """Average duration per call from events on torch's current stream, which is the
+        stream the library launches on."""
+        import torch
+        fn = fn or self
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(iters):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / iters
+
+    def check(self, n_rows=8, n_heads=3, seed=0):
+        """Oracle comparison on sampled (head, row) pairs; returns (max out err, max lse err)."""
+        import oracle
+        import torch
+        p = self.p
+        rng = np.random.default_rng(seed)
+        heads = sorted({(int(rng.integers(p.B)), int(rng.integers(p.Hq))) for _ in range(n_heads)})
+        rows = np.unique(np.concatenate([[0, p.Lq - 1], rng.integers(0, p.Lq, size=n_rows)]))
+        ro, rl = oracle.attention_ref(p.f64("q"), p.f64("k"), p.f64("v"), p.scale64, p.mask_kind,
+                                      window_left=p.window_left,
+                                      mask=None if p.mask is None else p.mask.astype(np.float64),
+                                      zero_hold=None if p.zero_hold is None else p.zero_hold.astype(np.float64),
+                                      keep_k=p.keep_k, rows=rows, heads=heads)
+        go = self.out.to(torch.float32).cpu().numpy()
+        gl = self.lse.cpu().numpy()
+        eo = el = 0.0
+        for b, h in heads:
+            o, l = go[b, h, rows], gl[b, h, rows]
+            r_o, r_l = ro[b, h, rows], rl[b, h, rows]
+            assert not np.isnan(o).any() and not np.isnan(l).any(), "NaN in GPU output"
+            assert np.array_equal(np.isneginf(l), np.isneginf(r_l)), "-inf LSE pattern differs"
+            eo = max(eo, float(np.abs(o - r_o).max()))
+            fin = np.isfinite(r_l)
+            if fin.any():
+                el = max(el, float(np.abs(l[fin] - r_l[fin]).max()))
+        tol_o, tol_l = (1e-5, 1e-5) if p.dtype == "fp32" else (2e-2, 1e-3)
+        if eo > tol_o or el > tol_l:
+            raise AssertionError(f"{p.name}: parity failed out {eo} lse {el}")
+        return eo, el
+
+
+def cpu_baseline(p, budget_s: float = 12.0) -> dict:
+    """The fp64 oracle, as it stands, on the first (b, h) heads of the workload in order,
+    until about ``budget_s`` seconds of CPU work; scaled to TFLOP/s of algorithmic work."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    q, k, v = p.f64("q"), p.f64("k"), p.f64("v")
+    per_head_pairs = visible_pairs(p) / (p.B * p.Hq)
+    done, t0 = 0, time.perf_counter()
+    heads = [(b, h) for b in range(p.B) for h in range(p.Hq)]
+    G = p.Hq // p.Hkv
+    A = oracle.mask_matrix(p.mask_kind, p.Lq, p.Lk, window_left=p.window_left)
+    for b, h in heads:
+        oracle.attention_rows_ref(q[b, h], k[b, h // G], v[b, h // G], p.scale64, A)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = 4.0 * p.d * per_head_pairs * done
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 oracle on the first {done} of {len(heads)} (b,h) heads of the headline workload "
+                      f"(all {p.Lq} rows each), {dt:.1f} s"}
+
+
+def bench_config(name, iters=20):
+    import synth
+    p = synth.config(name)
+    r = Runner(p)
+    r()
+    import torch
+    torch.cuda.synchronize()
+    eo, el = r.check()
+    for _ in range(3):
+        r()
+    ms = r.event_time_ms(iters)
+    res = {"workload": p.name, "B": p.B, "Hq": p.Hq, "Hkv": p.Hkv, "Lq": p.Lq, "Lk": p.Lk, "d": p.d,
+           "dtype": p.dtype, "mask": p.mask_kind, "us": round(ms * 1e3, 2),
+           "parity_sampled": {"max_out_err": eo, "max_lse_err": el}}
+    flops = 4.0 * p.d * visible_pairs(p)
+    byts = algorithmic_bytes(p)
+    res["tflops"] = round(flops / ms / 1e9, 2)
+    res["pct_mfma_peak"] = round(100 * flops / ms / 1e9 / PEAK_BF16_TFLOPS, 2)
+    res["gbs"] = round(byts / ms / 1e6, 1)
+    res["pct_hbm_peak"] = round(100 * byts / ms / 1e6 / PEAK_HBM_GBS, 2)
+    if p.mask_kind == "topk":
+        cf = 4.0 * p.d * causal_pairs(p)
+        res["tflops_causal_tiles"] = round(cf / ms / 1e9, 2)
+        import masked_flashattention_forward_amd as mfa
+        zt = r.zh
+        ms_topk = r.event_time_ms(iters, lambda: mfa.dynamic_mask_topk(zt, p.Lq, p.keep_k))
+        res["dynamic_mask_topk_us"] = round(ms_topk * 1e3, 2)
+    import masked_flashattention_forward_amd as mfa
+    res["plan"] = mfa.plan(p.B, p.Hq, p.Hkv, p.Lq, p.Lk, p.d, p.mask_kind, p.window_left, p.keep_k,
+                           synth.DTYPE_CODES[p.dtype])
+    del r
+    torch.cuda.empty_cache()
+    log(f"{name}: {json.dumps(res)}")
+    return res
+
+
+def copy_calibration(nbytes: int, iters: int):
+    """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    x = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(iters):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    log(f"copied {nbytes} bytes x {iters}")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", default="c3p", help="headline workload name (see synth.CONFIG_NAMES)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (--gpus {args.gpus} requested)",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, max(1, args.steps))
+        return
+
+    import torch
+    import masked_flashattention_forward_amd as mfa
+    import synth
+    mfa.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    log(f"generating {args.only}")
+    p = synth.config(args.only)
+    r = Runner(p)
+    r()
+    torch.cuda.synchronize()
+    eo, el = r.check()
+    log(f"headline parity (sampled rows vs oracle): out {eo:.2e} lse {el:.2e}")
+    for _ in range(args.warmup):
+        r()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        r()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    kern_ms = r.event_time_ms(args.steps)
+    flops = 4.0 * p.d * visible_pairs(p)
+    value = flops / wall_ms / 1e9
+    achieved = flops / kern_ms / 1e9
+    plan = mfa.plan(p.B, p.Hq, p.Hkv, p.Lq, p.Lk, p.d, p.mask_kind, p.window_left, p.keep_k,
+                    synth.DTYPE_CODES[p.dtype])
+    log(f"headline: {wall_ms * 1e3:.1f} us/step wall, {kern_ms * 1e3:.1f} us/kernel, {value:.1f} TFLOP/s")
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall_ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": p.dtype, "data": "synthetic (seeded numpy normal, RNE to bf16)",
+        "config": {"workload": p.name, "B": p.B, "Hq": p.Hq, "Hkv": p.Hkv, "Lq": p.Lq, "Lk": p.Lk, "d": p.d,
+                   "mask": p.mask_kind, "seed": p.meta.get("seed"), "flops_per_step": flops,
+                   "plan": plan},
+        "roofline": {"bound": "mfma", "kernel": "prefill_kernel<bf16,128,64>", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "avg_kernel_us": round(kern_ms * 1e3, 2)},
+        "parity_sampled": {"max_out_err": eo, "max_lse_err": el},
+    }
+    del r
+    torch.cuda.empty_cache()
+    if not args.no_configs:
+        configs = {}
+        for name in ("c3d", "c4_d128_bf16", "c4_d64_bf16", "c4_d128_fp16", "c4_d64_fp16", "c5", "c2", "c2w",
+                     "c1"):
+            log(f"config {name}")
+            configs[name] = bench_config(name)
+        line["configs"] = configs
+        d = configs["c3d"]
+        line["decode"] = {"workload": d["workload"], "value": d["gbs"], "unit": "GB/s",
+                          "frac_hbm_peak": round(d["gbs"] / PEAK_HBM_GBS, 4)}
+    if not args.no_cpu_baseline:
+        log("cpu baseline (fp64 oracle)")
+        line["cpu_baseline"] = cpu_baseline(p)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
