@@ -66,11 +66,13 @@ struct Tile {
   static constexpr int vStride = BN + 8;               // V^T row stride
   static constexpr int kElems = BN * kStride;
   static constexpr int vElems = D * vStride;
-  static constexpr int stage = kElems + vElems;
+  static constexpr int xElems = 4 * BN;                // top-k side data: BN int32 ranks + BN fp32 values
+  static constexpr int stage = kElems + vElems + xElems;
   static constexpr int kChunks = BN * D / 8 / kThreads;  // 16-byte K loads per thread
   static constexpr int vKeyGroups = BN / 4;               // V loaded as 4-key x 8-dim blocks
   static_assert(vKeyGroups * (D / 8) == kThreads, "one V block per thread");
   static_assert(kChunks * kThreads * 8 == BN * D, "K tile split evenly");
+  static_assert(BN <= kThreads, "one top-k side entry per thread");
 };
 
 // Storage position of key offset `kk` (multiple of 4) inside a V^T row: within each group
@@ -81,7 +83,22 @@ __device__ __forceinline__ int vperm(int kk) {
   return (kk & ~15) + ((q4 & 1) << 3) + ((q4 >> 1) << 2);
 }
 
-template <typename T, int D, int BN>
+// The running max only moves when a row's maximum grows by more than 2^8 (log2 units).
+// Between moves, p = exp2(s - m) stays below 2^8, which fp32 sums and 16-bit P hold
+// without loss of relative precision; l and the output use the same m, so the result is
+// unchanged up to rounding, and most tiles skip rescaling the output accumulator.
+constexpr float kRescaleThreshold = 8.0f;
+
+// Workgroup -> (KV group, query block). Workgroups are handed to the 8 XCDs round-robin;
+// the remap gives each XCD a contiguous run of KV groups (their K/V stays in that XCD's
+// L2), and inside a KV group the query blocks with the most tiles start first.
+__device__ __forceinline__ unsigned logical_block(unsigned bid, unsigned nblk) {
+  const unsigned per = nblk / 8u;
+  if (bid < per * 8u) return (bid % 8u) * per + bid / 8u;
+  return bid;
+}
+
+template <typename T, int D, int BN, int MK>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
   using TL = Tile<D, BN>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * TL::stage];
@@ -92,10 +109,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
   const int l32 = lane & 31;
   const int hf = lane >> 5;  // lane half
 
-  // ---- work unit: (b, g, query block, split); heavy query blocks first
+  // ---- work unit: (b, g, query block, split)
   const int nqb = (p.Lq + p.q_per_block - 1) / p.q_per_block;
-  const int qb = nqb - 1 - static_cast<int>(blockIdx.x % nqb);
-  const int bg = static_cast<int>(blockIdx.x / nqb);
+  const unsigned lb = logical_block(blockIdx.x, gridDim.x);
+  const int qb = nqb - 1 - static_cast<int>(lb % nqb);
+  const int bg = static_cast<int>(lb / nqb);
   const int b = bg / p.Hkv;
   const int g = bg % p.Hkv;
   const int split = blockIdx.y;
@@ -128,7 +146,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
 
   // ---- key range of this block (and split)
   int lo, hi;
-  key_range(p.mask_kind, p.window_left, p.Lk, P0, P1, &lo, &hi);
+  key_range(MK, p.window_left, p.Lk, P0, P1, &lo, &hi);
   if (p.no_skip) { lo = 0; hi = p.Lk; }
   if (p.splits > 1) {
     const int s0 = split * p.keys_per_split;
@@ -145,18 +163,19 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
   const long kv_base = static_cast<long>(bg) * p.Lk * D;
   const T* K = static_cast<const T*>(p.k) + kv_base;
   const T* V = static_cast<const T*>(p.v) + kv_base;
+  const long bgk = static_cast<long>(bg) * p.Lk;
 
   // top-k: the block's largest threshold (thresholds do not grow with the row position)
-  const long bg_l = bg;
   int32_t tau_row = 0, tau_blk = 0;
-  if (p.mask_kind == MI_ATTN_MASK_TOPK) {
-    tau_row = p.tau[bg_l * p.Lq + i_row];
-    tau_blk = p.tau[bg_l * p.Lq + i_first];
+  if constexpr (MK == MI_ATTN_MASK_TOPK) {
+    tau_row = p.tau[static_cast<long>(bg) * p.Lq + i_row];
+    tau_blk = p.tau[static_cast<long>(bg) * p.Lq + i_first];
   }
   auto tile_live = [&](int t) -> bool {
     if (p.no_skip) return true;
-    if (p.mask_kind == MI_ATTN_MASK_DENSE) return p.tile_live[static_cast<long>(qb) * ntiles_all + t] != 0;
-    if (p.mask_kind == MI_ATTN_MASK_TOPK) return p.tile_min_rank[bg_l * ntiles_all + t] <= tau_blk;
+    if constexpr (MK == MI_ATTN_MASK_DENSE) return p.tile_live[static_cast<long>(qb) * ntiles_all + t] != 0;
+    if constexpr (MK == MI_ATTN_MASK_TOPK)
+      return p.tile_min_rank[static_cast<long>(bg) * ntiles_all + t] <= tau_blk;
     return true;
   };
   auto next_live = [&](int t) -> int {
@@ -165,10 +184,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
   };
 
   // ---- cooperative tile loads: K as [key][d] rows, V as V^T [d][permuted key]
-  const int vkg = tid / (D / 8);  // V key group (4 keys)
-  const int vdc = tid % (D / 8);  // V dim chunk (8 dims)
+  // V thread map: 16 consecutive lanes take 16 different 4-key groups of one 8-dim chunk, so
+  // the transposed LDS writes of a 32-lane pass cover two whole V^T rows (all 64 banks).
+  const int vkg = tid % TL::vKeyGroups;  // V key group (4 keys)
+  const int vdc = tid / TL::vKeyGroups;  // V dim chunk (8 dims)
   u32x4_t kbuf[TL::kChunks];
   u32x4_t vbuf[4];
+  int32_t xrank = 0;
+  float xzh = 0.f;
   auto load_tile = [&](int t) {
     const int j0 = t * BN;
 #pragma unroll
@@ -186,6 +209,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
       u32x4_t x = {0u, 0u, 0u, 0u};
       if (key < p.Lk) x = *reinterpret_cast<const u32x4_t*>(V + static_cast<long>(key) * D + vdc * 8);
       vbuf[a] = x;
+    }
+    if constexpr (MK == MI_ATTN_MASK_TOPK) {
+      if (tid < BN) {
+        const int key = j0 + tid;
+        xrank = key < p.Lk ? p.rank[bgk + key] : 0x7fffffff;
+        xzh = key < p.Lk ? p.zero_hold[bgk + key] : 0.f;
+      }
     }
   };
   auto store_tile = [&](int stage) {
@@ -209,6 +239,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
       o.y = __builtin_amdgcn_perm(vbuf[3][w], vbuf[2][w], sel);
       *reinterpret_cast<u32x2_t*>(vs + (vdc * 8 + e) * TL::vStride + col) = o;
     }
+    if constexpr (MK == MI_ATTN_MASK_TOPK) {
+      if (tid < BN) {
+        int32_t* xr = reinterpret_cast<int32_t*>(vs + TL::vElems);
+        xr[tid] = xrank;
+        reinterpret_cast<float*>(xr + BN)[tid] = xzh;
+      }
+    }
   };
 
   // ---- running state
@@ -217,7 +254,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
   f32x16_t oacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) oacc[db] = f32x16_t{};
-  float m_run = kNegInf;  // running max, log2 domain
+  float m_run = kNegInf;  // running max, log2 domain (may lag the true max by < 2^8)
   float l_run = 0.f;      // this lane's partial running sum
 
   int t = next_live(t_lo);
@@ -249,37 +286,45 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
       sacc[kb] = acc;
     }
 
-    // mask (boundary tiles only); masked tiles move to the log2 domain here (cm = 1)
+    // mask (tiles the mask does not cover entirely); masked tiles move to the log2
+    // domain here (cm = 1), unmasked ones are scaled inside the exponent (cm = cexp)
     const int j_end = j0 + BN - 1;
-    bool need_mask = p.no_skip || j_end >= p.Lk || p.mask_kind == MI_ATTN_MASK_DENSE ||
-                     p.mask_kind == MI_ATTN_MASK_TOPK;
-    if (p.mask_kind == MI_ATTN_MASK_CAUSAL || p.mask_kind == MI_ATTN_MASK_WINDOW) need_mask |= j_end > P0;
-    if (p.mask_kind == MI_ATTN_MASK_WINDOW) need_mask |= j0 < P1 - p.window_left;
+    bool need_mask = p.no_skip || j_end >= p.Lk || MK == MI_ATTN_MASK_DENSE || MK == MI_ATTN_MASK_TOPK;
+    if constexpr (MK == MI_ATTN_MASK_CAUSAL || MK == MI_ATTN_MASK_WINDOW) need_mask = need_mask || j_end > P0;
+    if constexpr (MK == MI_ATTN_MASK_WINDOW) need_mask = need_mask || j0 < P1 - p.window_left;
     float cm = cexp;
     if (need_mask) {
       cm = 1.f;
-      const long bgk = bg_l * p.Lk;
+      const int32_t* xr = reinterpret_cast<const int32_t*>(vs + TL::vElems);
+      const float* xz = reinterpret_cast<const float*>(xr + BN);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const int jb = j0 + kb * 32 + r4 * 8 + hf * 4;  // first of 4 consecutive keys
+          const int kk = kb * 32 + r4 * 8 + hf * 4;  // first of 4 consecutive keys in the tile
+          const int jb = j0 + kk;
+          int4 rk4 = {0, 0, 0, 0};
+          float4 zh4 = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (MK == MI_ATTN_MASK_TOPK) {
+            rk4 = *reinterpret_cast<const int4*>(xr + kk);
+            zh4 = *reinterpret_cast<const float4*>(xz + kk);
+          }
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int j = jb + e;
             float s = sacc[kb][r4 * 4 + e] * cexp;
             bool vis = j < p.Lk;
-            switch (p.mask_kind) {
-              case MI_ATTN_MASK_CAUSAL: vis = vis && j <= pos; break;
-              case MI_ATTN_MASK_WINDOW: vis = vis && j <= pos && j >= pos - p.window_left; break;
-              case MI_ATTN_MASK_DENSE:
-                if (vis) s += p.mask[static_cast<long>(i_row) * p.Lk + j] * kLog2e;
-                break;
-              case MI_ATTN_MASK_TOPK:
-                vis = vis && j <= pos && p.rank[bgk + j] <= tau_row;
-                if (vis) s += p.zero_hold[bgk + j] * kLog2e;
-                break;
-              default: break;
+            if constexpr (MK == MI_ATTN_MASK_CAUSAL) vis = vis && j <= pos;
+            if constexpr (MK == MI_ATTN_MASK_WINDOW) vis = vis && j <= pos && j >= pos - p.window_left;
+            if constexpr (MK == MI_ATTN_MASK_DENSE) {
+              const float mv = vis ? p.mask[static_cast<long>(i_row) * p.Lk + j] : 0.f;
+              s = fmaf(mv, kLog2e, s);
+            }
+            if constexpr (MK == MI_ATTN_MASK_TOPK) {
+              const int32_t rk = e == 0 ? rk4.x : e == 1 ? rk4.y : e == 2 ? rk4.z : rk4.w;
+              const float zv = e == 0 ? zh4.x : e == 1 ? zh4.y : e == 2 ? zh4.z : zh4.w;
+              vis = vis && j <= pos && rk <= tau_row;
+              s = fmaf(zv, kLog2e, s);
             }
             sacc[kb][r4 * 4 + e] = vis ? s : kNegInf;
           }
@@ -287,16 +332,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
       }
     }
 
-    // online softmax (log2 domain), guarded against all -inf tiles
+    // online softmax (log2 domain), guarded against all -inf tiles and rows
     float mx = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    const float m_new = fmaxf(m_run, mx * cm);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * cm;
+    const float m_next = (mx > m_run + kRescaleThreshold) ? mx : m_run;
+    const float m_use = (m_next == kNegInf) ? 0.f : m_next;
+    const float alpha = fast_exp2(m_run - m_use);  // 1 when the max did not move, 0 from -inf
     float psum = 0.f;
     u32x4_t preg[BN / 16];
 #pragma unroll
@@ -318,9 +363,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
       }
     }
     l_run = l_run * alpha + psum;
-    m_run = m_new;
+    m_run = m_next;
+    if (!__all(alpha == 1.f)) {
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+    }
 
     // O^T += V^T P^T
 #pragma unroll
@@ -412,10 +459,23 @@ hipError_t launch_prefill_t(const AttnParams& p, hipStream_t s) {
   const long blocks = static_cast<long>(p.B) * p.Hkv * nqb;
   if (blocks > 0x7fffffffL || p.splits > 65535) return hipErrorInvalidValue;
   dim3 grid(static_cast<unsigned>(blocks), p.splits), block(kThreads);
-  if (p.d == 128)
-    hipLaunchKernelGGL((prefill_kernel<T, 128, 64>), grid, block, 0, s, p);
-  else
-    hipLaunchKernelGGL((prefill_kernel<T, 64, 128>), grid, block, 0, s, p);
+  if (p.d == 128) {
+    switch (p.mask_kind) {
+      case MI_ATTN_MASK_NONE: hipLaunchKernelGGL((prefill_kernel<T, 128, 64, 0>), grid, block, 0, s, p); break;
+      case MI_ATTN_MASK_CAUSAL: hipLaunchKernelGGL((prefill_kernel<T, 128, 64, 1>), grid, block, 0, s, p); break;
+      case MI_ATTN_MASK_WINDOW: hipLaunchKernelGGL((prefill_kernel<T, 128, 64, 2>), grid, block, 0, s, p); break;
+      case MI_ATTN_MASK_DENSE: hipLaunchKernelGGL((prefill_kernel<T, 128, 64, 3>), grid, block, 0, s, p); break;
+      default: hipLaunchKernelGGL((prefill_kernel<T, 128, 64, 4>), grid, block, 0, s, p); break;
+    }
+  } else {
+    switch (p.mask_kind) {
+      case MI_ATTN_MASK_NONE: hipLaunchKernelGGL((prefill_kernel<T, 64, 128, 0>), grid, block, 0, s, p); break;
+      case MI_ATTN_MASK_CAUSAL: hipLaunchKernelGGL((prefill_kernel<T, 64, 128, 1>), grid, block, 0, s, p); break;
+      case MI_ATTN_MASK_WINDOW: hipLaunchKernelGGL((prefill_kernel<T, 64, 128, 2>), grid, block, 0, s, p); break;
+      case MI_ATTN_MASK_DENSE: hipLaunchKernelGGL((prefill_kernel<T, 64, 128, 3>), grid, block, 0, s, p); break;
+      default: hipLaunchKernelGGL((prefill_kernel<T, 64, 128, 4>), grid, block, 0, s, p); break;
+    }
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits <= 1) return e;
   const long n = static_cast<long>(p.B) * p.Hq * p.Lq * (p.d / 4);
