@@ -58,6 +58,9 @@ int validate(const Shape& s) {
       return fail(MI_ATTN_EUNSUPPORTED, "fp32 head dim must be a multiple of 4 up to 256 (got %d)", s.d);
   } else if (s.d != 64 && s.d != 128) {
     return fail(MI_ATTN_EUNSUPPORTED, "fp16/bf16 head dim must be 64 or 128 (got %d)", s.d);
+  } else if (static_cast<double>(s.Lk) * s.d * 2 > 2147483647.0) {
+    // one (batch, KV head) slice of K or V is addressed with 32-bit byte offsets
+    return fail(MI_ATTN_EUNSUPPORTED, "Lk * d * 2 must stay below 2^31 bytes (Lk=%d d=%d)", s.Lk, s.d);
   }
   if (s.mask_kind == MI_ATTN_MASK_TOPK && s.Lk > 65536)
     return fail(MI_ATTN_EUNSUPPORTED, "top-k mask supports Lk <= 65536 (got %d)", s.Lk);

@@ -53,6 +53,24 @@ __device__ __forceinline__ uint32_t pack2(f16_t, float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
 }
 
+// max over lanes l and l ^ 32 (v_permlane32_swap, no LDS round trip)
+__device__ __forceinline__ float max_halves(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+// Buffer resource over `bytes` bytes at `base`: loads past the end return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, int byte_offset) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, 0));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
@@ -62,25 +80,39 @@ constexpr int kBlockM = 32 * kWaves;  // query rows per workgroup
 
 template <int D, int BN>
 struct Tile {
-  static constexpr int kStride = D + 8;                // K row stride in 16-bit elements (16 B pad)
-  static constexpr int vStride = BN + 8;               // V^T row stride
-  static constexpr int kElems = BN * kStride;
-  static constexpr int vElems = D * vStride;
-  static constexpr int xElems = 4 * BN;                // top-k side data: BN int32 ranks + BN fp32 values
-  static constexpr int stage = kElems + vElems + xElems;
-  static constexpr int kChunks = BN * D / 8 / kThreads;  // 16-byte K loads per thread
-  static constexpr int vKeyGroups = BN / 4;               // V loaded as 4-key x 8-dim blocks
-  static_assert(vKeyGroups * (D / 8) == kThreads, "one V block per thread");
-  static_assert(kChunks * kThreads * 8 == BN * D, "K tile split evenly");
+  static constexpr int rowBytes = D * 2;
+  static constexpr int kBytes = BN * rowBytes;          // K tile, [key][d], no padding
+  static constexpr int vBytes = BN * rowBytes;          // V tile, [key][d], no padding
+  static constexpr int xBytes = 8 * BN;                 // top-k side data: BN int32 ranks + BN fp32 values
+  static constexpr int stage = kBytes + vBytes + xBytes;
+  static constexpr int rowsPerWaveLoad = 1024 / rowBytes;  // one wave's 64 x 16 B direct load
+  static constexpr int loadRounds = kBytes / (kThreads * 16);
+  static_assert(loadRounds * kThreads * 16 == kBytes, "tile split evenly across direct loads");
   static_assert(BN <= kThreads, "one top-k side entry per thread");
 };
 
-// Storage position of key offset `kk` (multiple of 4) inside a V^T row: within each group
-// of 16 keys the 4-key quarters are stored in the order 0, 2, 1, 3, so that lane half 0
-// reads keys {0-3, 8-11} and lane half 1 keys {4-7, 12-15} as one 16-byte run.
-__device__ __forceinline__ int vperm(int kk) {
-  const int q4 = (kk >> 2) & 3;
-  return (kk & ~15) + ((q4 & 1) << 3) + ((q4 >> 1) << 2);
+// 16-byte slot swizzle of a tile row. Rows are stored unpadded; slot s of row r lives at
+// slot s ^ swz(r). With 64 banks (16 lanes per cycle for 128-bit reads, 32 lanes for
+// 64-bit reads) it makes both operand reads conflict-free: the K read (16 consecutive
+// rows, one slot each) and the transposed V read (4 consecutive rows x 4 aligned slots).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int slot) {
+  return r * (D * 2) + ((slot ^ swz<D>(r)) << 4);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+// Transposed 64-bit LDS read: within each 16-lane group, lane j receives element j % 4 of
+// the 8-byte rows read by lanes j / 4, 4 + j / 4, 8 + j / 4 and 12 + j / 4.
+__device__ __forceinline__ u32x2_t lds_read_tr16(const unsigned char* p) {
+  const bf16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)(p));
+  return __builtin_bit_cast(u32x2_t, v);
 }
 
 // The running max only moves when a row's maximum grows by more than 2^8 (log2 units).
@@ -101,7 +133,7 @@ __device__ __forceinline__ unsigned logical_block(unsigned bid, unsigned nblk) {
 template <typename T, int D, int BN, int MK>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
   using TL = Tile<D, BN>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * TL::stage];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * TL::stage];
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
@@ -183,32 +215,25 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
     return t;
   };
 
-  // ---- cooperative tile loads: K as [key][d] rows, V as V^T [d][permuted key]
-  // V thread map: 16 consecutive lanes take 16 different 4-key groups of one 8-dim chunk, so
-  // the transposed LDS writes of a 32-lane pass cover two whole V^T rows (all 64 banks).
-  const int vkg = tid % TL::vKeyGroups;  // V key group (4 keys)
-  const int vdc = tid / TL::vKeyGroups;  // V dim chunk (8 dims)
-  u32x4_t kbuf[TL::kChunks];
-  u32x4_t vbuf[4];
+  // ---- tile loads straight into LDS (buffer_load ... lds): each wave instruction fills
+  // 1 KB of the tile; lane i of it takes the global 16-byte chunk that belongs in slot i
+  // of the swizzled layout. Rows at or past Lk read as zeros (buffer range check).
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K, p.Lk * D * 2);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V, p.Lk * D * 2);
   int32_t xrank = 0;
   float xzh = 0.f;
-  auto load_tile = [&](int t) {
+  auto issue_tile = [&](int t, int stg) {
     const int j0 = t * BN;
+    unsigned char* kst = smem + stg * TL::stage;
+    unsigned char* vst = kst + TL::kBytes;
 #pragma unroll
-    for (int c = 0; c < TL::kChunks; ++c) {
-      const int flat = c * kThreads + tid;
-      const int key = flat / (D / 8);
-      const int dch = flat % (D / 8);
-      u32x4_t x = {0u, 0u, 0u, 0u};
-      if (j0 + key < p.Lk) x = *reinterpret_cast<const u32x4_t*>(K + static_cast<long>(j0 + key) * D + dch * 8);
-      kbuf[c] = x;
-    }
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int key = j0 + vkg * 4 + a;
-      u32x4_t x = {0u, 0u, 0u, 0u};
-      if (key < p.Lk) x = *reinterpret_cast<const u32x4_t*>(V + static_cast<long>(key) * D + vdc * 8);
-      vbuf[a] = x;
+    for (int c = 0; c < TL::loadRounds; ++c) {
+      const int blk = c * kWaves + wave;             // 1 KB block of the tile
+      const int r = blk * TL::rowsPerWaveLoad + lane / (D / 8);
+      const int ps = lane % (D / 8);                 // physical slot this lane fills
+      const int gofs = ((j0 + r) * D + ((ps ^ swz<D>(r)) << 3)) * 2;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(kst + blk * 1024), 16, gofs, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(vst + blk * 1024), 16, gofs, 0, 0, 0);
     }
     if constexpr (MK == MI_ATTN_MASK_TOPK) {
       if (tid < BN) {
@@ -218,34 +243,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
       }
     }
   };
-  auto store_tile = [&](int stage) {
-    uint16_t* ks = smem + stage * TL::stage;
-    uint16_t* vs = ks + TL::kElems;
-#pragma unroll
-    for (int c = 0; c < TL::kChunks; ++c) {
-      const int flat = c * kThreads + tid;
-      const int key = flat / (D / 8);
-      const int dch = flat % (D / 8);
-      *reinterpret_cast<u32x4_t*>(ks + key * TL::kStride + dch * 8) = kbuf[c];
-    }
-    // transpose 4 keys x 8 dims -> 8 rows of 4 keys
-    const int col = vperm(vkg * 4);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int w = e >> 1;
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;  // high or low halves
-      u32x2_t o;
-      o.x = __builtin_amdgcn_perm(vbuf[1][w], vbuf[0][w], sel);
-      o.y = __builtin_amdgcn_perm(vbuf[3][w], vbuf[2][w], sel);
-      *reinterpret_cast<u32x2_t*>(vs + (vdc * 8 + e) * TL::vStride + col) = o;
-    }
+  auto finish_tile = [&](int stg) {
     if constexpr (MK == MI_ATTN_MASK_TOPK) {
       if (tid < BN) {
-        int32_t* xr = reinterpret_cast<int32_t*>(vs + TL::vElems);
+        int32_t* xr = reinterpret_cast<int32_t*>(smem + stg * TL::stage + TL::kBytes + TL::vBytes);
         xr[tid] = xrank;
         reinterpret_cast<float*>(xr + BN)[tid] = xzh;
       }
     }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
   };
 
   // ---- running state
@@ -260,17 +266,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
   int t = next_live(t_lo);
   int stage = 0;
   if (t < t_hi) {
-    load_tile(t);
-    store_tile(0);
+    issue_tile(t, 0);
+    finish_tile(0);
   }
   __syncthreads();
 
   while (t < t_hi) {
     const int tn = next_live(t + 1);
-    if (tn < t_hi) load_tile(tn);  // prefetch into registers while this tile computes
+    if (tn < t_hi) issue_tile(tn, stage ^ 1);  // lands in the other stage while this tile computes
 
-    const uint16_t* ks = smem + stage * TL::stage;
-    const uint16_t* vs = ks + TL::kElems;
+    const unsigned char* ks = smem + stage * TL::stage;
+    const unsigned char* vs = ks + TL::kBytes;
     const int j0 = t * BN;
 
     // S^T = K Q^T
@@ -280,7 +286,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
       f32x16_t acc = f32x16_t{};
 #pragma unroll
       for (int dc = 0; dc < D / 16; ++dc) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(ks + (kb * 32 + l32) * TL::kStride + dc * 16 + hf * 8);
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(ks + tile_off<D>(kb * 32 + l32, dc * 2 + hf));
         acc = mfma32(T{}, a, qreg[dc], acc);
       }
       sacc[kb] = acc;
@@ -295,7 +301,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
     float cm = cexp;
     if (need_mask) {
       cm = 1.f;
-      const int32_t* xr = reinterpret_cast<const int32_t*>(vs + TL::vElems);
+      const int32_t* xr = reinterpret_cast<const int32_t*>(vs + TL::vBytes);
       const float* xz = reinterpret_cast<const float*>(xr + BN);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
@@ -333,16 +339,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
     }
 
     // online softmax (log2 domain), guarded against all -inf tiles and rows
-    float mx = kNegInf;
+    float mx4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};  // four independent chains
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * cm;
+      for (int e = 0; e < 16; ++e) mx4[e & 3] = fmaxf(mx4[e & 3], sacc[kb][e]);
+    float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
+    mx = max_halves(mx) * cm;
     const float m_next = (mx > m_run + kRescaleThreshold) ? mx : m_run;
     const float m_use = (m_next == kNegInf) ? 0.f : m_next;
     const float alpha = fast_exp2(m_run - m_use);  // 1 when the max did not move, 0 from -inf
-    float psum = 0.f;
+    float ps4[4] = {0.f, 0.f, 0.f, 0.f};  // four independent chains
     u32x4_t preg[BN / 16];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
@@ -352,7 +359,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           pv[e] = fast_exp2(fmaf(sacc[kb][half * 8 + e], cm, -m_use));
-          psum += pv[e];
+          ps4[e & 3] += pv[e];
         }
         u32x4_t pk;
         pk.x = pack2(T{}, pv[0], pv[1]);
@@ -362,31 +369,40 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
         preg[kb * 2 + half] = pk;
       }
     }
-    l_run = l_run * alpha + psum;
+    l_run = fmaf(l_run, alpha, (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]));
     m_run = m_next;
     if (!__all(alpha == 1.f)) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
     }
 
-    // O^T += V^T P^T
+    // O^T += V^T P^T. The V^T operand comes from two transposed reads: lane (16 * g + i)
+    // reads 8 bytes of key row R0 + i / 4 at dims D0 + 4 * (i % 4) and receives keys
+    // R0..R0+3 of dim D0 + i. Keys 4*hf+0..3 and 8+4*hf+0..3 of the 16-key chunk are what
+    // its P registers hold.
+    const int tr_row = 4 * hf + (lane & 15) / 4;
+    const int tr_dim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
       for (int kc = 0; kc < BN / 16; ++kc) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(vs + (db * 32 + l32) * TL::vStride + kc * 16 + hf * 8);
+        const int d0 = db * 32 + tr_dim;
+        const int r0 = kc * 16 + tr_row;
+        const u32x2_t lo = lds_read_tr16(vs + tile_off<D>(r0, d0 >> 3) + ((d0 & 7) << 1));
+        const u32x2_t hi2 = lds_read_tr16(vs + tile_off<D>(r0 + 8, d0 >> 3) + ((d0 & 7) << 1));
+        const u32x4_t a = {lo.x, lo.y, hi2.x, hi2.y};
         oacc[db] = mfma32(T{}, a, preg[kc], oacc[db]);
       }
     }
 
-    if (tn < t_hi) store_tile(stage ^ 1);
+    if (tn < t_hi) finish_tile(stage ^ 1);
     __syncthreads();
     t = tn;
     stage ^= 1;
   }
 
   // ---- epilogue: combine the two lane halves' partial sums, normalise, store
-  const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
+  const float l_tot = sum_halves(l_run);
   if (!row_ok) return;
   const bool dead = !(l_tot > 0.f);
   const float inv = dead ? 0.f : 1.f / l_tot;
