@@ -118,10 +118,11 @@ int dynamic_mask_topk(const float* zero_hold, int B, int H, int Lq, int Lk, int 
 
 /* which kernels attn_fwd would run for a shape (host-only query, no GPU work) */
 typedef struct {
-  int path;          /* 0 fp32 row kernel, 1 MFMA prefill, 2 split-KV decode + LSE merge */
+  int path;          /* 0 fp32 row kernel; 1 MFMA prefill (split over keys, with an LSE merge,
+                        when there are few workgroups); 2 split-KV decode + LSE merge        */
   int block_m;       /* query rows per workgroup (rows of all heads sharing a KV head)   */
   int block_n;       /* keys per KV tile                                                 */
-  int splits;        /* key-range splits (decode path), 1 otherwise                      */
+  int splits;        /* key-range splits merged by log-sum-exp (paths 1, 2); 1 if unsplit */
   int grid;          /* workgroups of the main kernel                                    */
   int mask_summary;  /* 1 when a per-tile dense-mask summary kernel runs first            */
   size_t workspace_bytes; /* temporary device memory the call takes                     */
@@ -140,8 +141,9 @@ int attn_fwd_plan(int B, int Hq, int Hkv, int Lq, int Lk, int d, int mask_kind,
  *   no_skip      1: visit every KV tile, even ones the mask hides entirely.
  *   force_path   -1: automatic; 0/1/2 force the path numbers of attn_plan_t (a forced
  *                path that cannot run the arguments makes attn_fwd return
- *                MI_ATTN_EUNSUPPORTED).
- *   force_splits 0: automatic; n > 0 forces n key-range splits on the decode path.
+ *                MI_ATTN_EUNSUPPORTED; path 2 needs (Hq / Hkv) * Lq <= 32).
+ *   force_splits 0: automatic; n > 0 asks for n key-range splits on paths 1 and 2 (fewer
+ *                when the key range has fewer tiles).
  */
 void attn_set_debug(int no_skip, int force_path, int force_splits);
 

@@ -1,0 +1,326 @@
+// Split-KV decode kernel: few query rows per KV head (G * Lq <= 32), long key range.
+//
+// This is the decode step of the chunked forward (ExecuTorch pull request #10466 page,
+// "Summary") with past keys and Lq << Lk (FastChat pull request #2315 page): the cost is
+// streaming K and V once from HBM. A workgroup takes one (batch, KV head) and one key
+// range ("split"); its 4 wavefronts stream disjoint 32-key tiles of that range
+// independently, each with its own online-softmax state for all G * Lq rows:
+//   K tile   loaded straight into registers in the 32x32x16 MFMA A-operand layout;
+//   V tile   loaded straight into a private 2-stage LDS ring (buffer_load ... lds) and read
+//            back transposed (ds_read_b64_tr_b16) as the V^T operand;
+//   S^T = K Q^T and O^T += V^T P^T on MFMA, softmax guarded as in the prefill kernel.
+// No workgroup barrier is needed while streaming; at the end the four states are merged
+// through LDS by log-sum-exp, giving the split's partial (o, lse) or, with one split, the
+// output itself.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "mfma_common.hpp"
+
+namespace mi_attn {
+
+hipError_t launch_lse_merge(const AttnParams& p, int dtype, hipStream_t s);
+
+namespace {
+
+using namespace mfma;
+
+constexpr int kDecWaves = 4;
+constexpr int kDecThreads = kDecWaves * kWave;
+constexpr int kDecBN = 32;  // keys per wavefront tile
+
+// s_waitcnt immediate for "at most n vector-memory operations outstanding" (gfx9
+// encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their maximum).
+constexpr int vmcnt_imm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
+
+template <int D>
+struct DecTile {
+  static constexpr int vBytes = kDecBN * D * 2;     // one V tile in LDS
+  static constexpr int vLoads = vBytes / 1024;      // 1 KB direct loads per V tile
+  static constexpr int kLoads = D / 16;             // 16-byte K loads per lane per tile
+  static constexpr int waveBytes = 2 * vBytes;      // 2-stage ring per wavefront
+  static constexpr int lds = kDecWaves * waveBytes;
+  static constexpr int NDB = D / 32;
+  // merge area (reuses the rings): per non-zero wave, O^T registers + m + l per lane
+  static constexpr int mergeFloats = (NDB * 16 + 2) * kWave;
+  static_assert((kDecWaves - 1) * mergeFloats * 4 <= lds, "merge area fits in the rings");
+};
+
+template <typename T, int D, int MK>
+__global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(AttnParams p) {
+  using TL = DecTile<D>;
+  constexpr int NDB = TL::NDB;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[TL::lds];
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid % kWave;
+  const int l32 = lane & 31;
+  const int hf = lane >> 5;
+
+  const int bg = blockIdx.x;
+  const int b = bg / p.Hkv;
+  const int g = bg % p.Hkv;
+  const int split = blockIdx.y;
+  const int rows = p.G * p.Lq;
+  const int P0 = p.Lk - p.Lq;      // position of the first query row
+  const int P1 = p.Lk - 1;         // position of the last
+
+  // this lane's row (query-major: row r -> query r / G, head g*G + r % G)
+  const bool row_ok = l32 < rows;
+  const int i_row = row_ok ? l32 / p.G : 0;
+  const int h_row = g * p.G + (row_ok ? l32 % p.G : 0);
+  const int pos = p.Lk - p.Lq + i_row;
+  const long row_index = (static_cast<long>(b) * p.Hq + h_row) * p.Lq + i_row;
+
+  const T* Q = static_cast<const T*>(p.q);
+  const bool negate = p.scale < 0.f;
+  const float cexp = fabsf(p.scale) * kLog2e;
+  u32x4_t qreg[D / 16];
+#pragma unroll
+  for (int dc = 0; dc < D / 16; ++dc) {
+    u32x4_t x = {0u, 0u, 0u, 0u};
+    if (row_ok) x = *reinterpret_cast<const u32x4_t*>(Q + row_index * D + dc * 16 + hf * 8);
+    if (negate) x ^= 0x80008000u;
+    qreg[dc] = x;
+  }
+
+  // key range of this split
+  int lo, hi;
+  key_range(MK, p.window_left, p.Lk, P0, P1, &lo, &hi);
+  if (p.no_skip) { lo = 0; hi = p.Lk; }
+  {
+    const int s0 = split * p.keys_per_split;
+    const int s1 = min(p.Lk, s0 + p.keys_per_split);
+    lo = max(lo, s0);
+    hi = min(hi, s1);
+  }
+  const int t_lo = lo / kDecBN;
+  const int t_hi = (hi > lo) ? (hi + kDecBN - 1) / kDecBN : t_lo;
+  const int ntiles_all = (p.Lk + kDecBN - 1) / kDecBN;
+
+  const long kv_base = static_cast<long>(bg) * p.Lk * D;
+  const long bgk = static_cast<long>(bg) * p.Lk;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(static_cast<const T*>(p.k) + kv_base, p.Lk * D * 2);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(static_cast<const T*>(p.v) + kv_base, p.Lk * D * 2);
+
+  int32_t tau_row = 0, tau_blk = 0;
+  if constexpr (MK == MI_ATTN_MASK_TOPK) {
+    tau_row = p.tau[static_cast<long>(bg) * p.Lq + i_row];
+    tau_blk = p.tau[static_cast<long>(bg) * p.Lq];
+  }
+  auto tile_live = [&](int t) -> bool {
+    if (p.no_skip) return true;
+    if constexpr (MK == MI_ATTN_MASK_DENSE) return p.tile_live[t] != 0;  // one query block
+    if constexpr (MK == MI_ATTN_MASK_TOPK) return p.tile_min_rank[static_cast<long>(bg) * ntiles_all + t] <= tau_blk;
+    return true;
+  };
+  // this wavefront's tiles: t_lo + wave, then every 4th, skipping dead ones
+  auto next_tile = [&](int t) -> int {
+    while (t < t_hi && !tile_live(t)) t += kDecWaves;
+    return t;
+  };
+
+  unsigned char* const ring = smem + wave * TL::waveBytes;
+  auto issue = [&](int t, u32x4_t* kr, int stg) {
+    const int j0 = t * kDecBN;
+    // K: lane holds key j0 + l32, dims dc*16 + hf*8 .. +8 (the A operand of S^T = K Q^T)
+#pragma unroll
+    for (int dc = 0; dc < TL::kLoads; ++dc) kr[dc] = buffer_load16(krs, ((j0 + l32) * D + dc * 16 + hf * 8) * 2);
+    // V: 1 KB direct loads into the swizzled [key][d] tile
+    unsigned char* dst = ring + stg * TL::vBytes;
+#pragma unroll
+    for (int c = 0; c < TL::vLoads; ++c) {
+      const int r = c * (1024 / (D * 2)) + lane / (D / 8);
+      const int ps = lane % (D / 8);
+      const int gofs = ((j0 + r) * D + ((ps ^ swz<D>(r)) << 3)) * 2;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(dst + c * 1024), 16, gofs, 0, 0, 0);
+    }
+  };
+  constexpr int kLoadsPerTile = TL::kLoads + TL::vLoads;
+
+  f32x16_t oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16_t{};
+  float m_run = kNegInf;
+  float l_run = 0.f;
+
+  u32x4_t kcur[TL::kLoads], knext[TL::kLoads];
+  int t = next_tile(t_lo + wave);
+  int stg = 0;
+  if (t < t_hi) issue(t, kcur, 0);
+  const int tr_row = 4 * hf + (lane & 15) / 4;
+  const int tr_dim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  while (t < t_hi) {
+    const int tn = next_tile(t + kDecWaves);
+    if (tn < t_hi) {
+      issue(tn, knext, stg ^ 1);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerTile));  // tile t has landed
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+    const int j0 = t * kDecBN;
+
+    // S^T = K Q^T (32 keys x 32 rows)
+    f32x16_t sacc[1];
+    {
+      f32x16_t acc = f32x16_t{};
+#pragma unroll
+      for (int dc = 0; dc < D / 16; ++dc) acc = mfma32(T{}, kcur[dc], qreg[dc], acc);
+      sacc[0] = acc;
+    }
+    float cm = cexp;
+    if (tile_needs_mask<MK, kDecBN>(p, j0, P0, P1)) {
+      const int32_t* xr = nullptr;
+      const float* xz = nullptr;
+      if constexpr (MK == MI_ATTN_MASK_TOPK) {
+        xr = p.rank + bgk + j0;
+        xz = p.zero_hold + bgk + j0;
+      }
+      mask_tile<MK, 1>(sacc, p, j0, hf, pos, i_row, tau_row, cexp, xr, xz);
+      cm = 1.f;
+    }
+
+    float mx4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mx4[e & 3] = fmaxf(mx4[e & 3], sacc[0][e]);
+    float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
+    mx = max_halves(mx) * cm;
+    const float m_next = (mx > m_run + kRescaleThreshold) ? mx : m_run;
+    const float m_use = (m_next == kNegInf) ? 0.f : m_next;
+    const float alpha = fast_exp2(m_run - m_use);
+    m_run = m_next;
+    if (!__all(alpha == 1.f)) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+    }
+    float ps4[4] = {0.f, 0.f, 0.f, 0.f};
+    u32x4_t preg[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      float pv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pv[e] = fast_exp2(fmaf(sacc[0][half * 8 + e], cm, -m_use));
+        ps4[e & 3] += pv[e];
+      }
+      preg[half] = u32x4_t{pack2(T{}, pv[0], pv[1]), pack2(T{}, pv[2], pv[3]), pack2(T{}, pv[4], pv[5]),
+                           pack2(T{}, pv[6], pv[7])};
+    }
+    l_run = fmaf(l_run, alpha, (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]));
+
+    // O^T += V^T P^T (transposed V reads; see the prefill kernel for the lane mapping)
+    const unsigned char* vs = ring + stg * TL::vBytes;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const int d0 = db * 32 + tr_dim;
+        const int r0 = kc * 16 + tr_row;
+        const u32x2_t lo2 = lds_read_tr16(vs + tile_off<D>(r0, d0 >> 3) + ((d0 & 7) << 1));
+        const u32x2_t hi2 = lds_read_tr16(vs + tile_off<D>(r0 + 8, d0 >> 3) + ((d0 & 7) << 1));
+        oacc[db] = mfma32(T{}, u32x4_t{lo2.x, lo2.y, hi2.x, hi2.y}, preg[kc], oacc[db]);
+      }
+    }
+#pragma unroll
+    for (int dc = 0; dc < TL::kLoads; ++dc) kcur[dc] = knext[dc];
+    t = tn;
+    stg ^= 1;
+  }
+
+  // ---- merge the four wavefronts' states (log-sum-exp), then store
+  __syncthreads();  // every wavefront is done with its ring
+  float* mf = reinterpret_cast<float*>(smem);
+  if (wave > 0) {
+    float* dst = mf + (wave - 1) * TL::mergeFloats;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dst[(db * 16 + i) * kWave + lane] = oacc[db][i];
+    dst[(NDB * 16) * kWave + lane] = m_run;
+    dst[(NDB * 16 + 1) * kWave + lane] = l_run;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float m_all = m_run;
+#pragma unroll
+  for (int w = 1; w < kDecWaves; ++w) m_all = fmaxf(m_all, mf[(w - 1) * TL::mergeFloats + (NDB * 16) * kWave + lane]);
+  const float m_ref = (m_all == kNegInf) ? 0.f : m_all;
+  const float s0 = fast_exp2(m_run - m_ref);
+  float l_all = l_run * s0;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) oacc[db] *= s0;
+#pragma unroll
+  for (int w = 1; w < kDecWaves; ++w) {
+    const float* src = mf + (w - 1) * TL::mergeFloats;
+    const float sw = fast_exp2(src[(NDB * 16) * kWave + lane] - m_ref);
+    l_all = fmaf(src[(NDB * 16 + 1) * kWave + lane], sw, l_all);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[db][i] = fmaf(src[(db * 16 + i) * kWave + lane], sw, oacc[db][i]);
+  }
+  const float l_tot = sum_halves(l_all);
+  if (!row_ok) return;
+  const bool dead = !(l_tot > 0.f);
+  const float inv = dead ? 0.f : 1.f / l_tot;
+  const float lse = dead ? kNegInf : (m_all + fast_log2(l_tot)) * kLn2;
+  if (p.splits > 1) {
+    const long rows_all = static_cast<long>(p.B) * p.Hq * p.Lq;
+    float* po = p.part_out + (static_cast<long>(split) * rows_all + row_index) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = db * 32 + r4 * 8 + hf * 4;
+        *reinterpret_cast<float4*>(po + d0) = float4{oacc[db][r4 * 4] * inv, oacc[db][r4 * 4 + 1] * inv,
+                                                     oacc[db][r4 * 4 + 2] * inv, oacc[db][r4 * 4 + 3] * inv};
+      }
+    if (hf == 0) p.part_lse[split * rows_all + row_index] = lse;
+    return;
+  }
+  T* O = static_cast<T*>(p.out) + row_index * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d0 = db * 32 + r4 * 8 + hf * 4;
+      *reinterpret_cast<u32x2_t*>(O + d0) =
+          u32x2_t{pack2(T{}, oacc[db][r4 * 4] * inv, oacc[db][r4 * 4 + 1] * inv),
+                  pack2(T{}, oacc[db][r4 * 4 + 2] * inv, oacc[db][r4 * 4 + 3] * inv)};
+    }
+  if (hf == 0 && p.lse != nullptr) p.lse[row_index] = lse;
+}
+
+template <typename T, int D>
+void launch_decode_d(const AttnParams& p, hipStream_t s) {
+  dim3 grid(p.B * p.Hkv, p.splits), block(kDecThreads);
+  switch (p.mask_kind) {
+    case MI_ATTN_MASK_NONE: hipLaunchKernelGGL((decode_kernel<T, D, 0>), grid, block, 0, s, p); break;
+    case MI_ATTN_MASK_CAUSAL: hipLaunchKernelGGL((decode_kernel<T, D, 1>), grid, block, 0, s, p); break;
+    case MI_ATTN_MASK_WINDOW: hipLaunchKernelGGL((decode_kernel<T, D, 2>), grid, block, 0, s, p); break;
+    case MI_ATTN_MASK_DENSE: hipLaunchKernelGGL((decode_kernel<T, D, 3>), grid, block, 0, s, p); break;
+    default: hipLaunchKernelGGL((decode_kernel<T, D, 4>), grid, block, 0, s, p); break;
+  }
+}
+
+}  // namespace
+
+int decode_block_n() { return kDecBN; }
+int decode_max_rows() { return 32; }
+
+hipError_t launch_decode(const AttnParams& p, int dtype, hipStream_t s) {
+  if (static_cast<long>(p.B) * p.Hkv > 0x7fffffffL || p.splits > 65535) return hipErrorInvalidValue;
+  if (dtype == MI_ATTN_BF16) {
+    if (p.d == 128) launch_decode_d<bf16_t, 128>(p, s); else launch_decode_d<bf16_t, 64>(p, s);
+  } else if (dtype == MI_ATTN_F16) {
+    if (p.d == 128) launch_decode_d<f16_t, 128>(p, s); else launch_decode_d<f16_t, 64>(p, s);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.splits <= 1) return e;
+  return launch_lse_merge(p, dtype, s);
+}
+
+}  // namespace mi_attn

@@ -21,58 +21,13 @@
 // / window bounds, the dense-mask summary or the top-k minimum rank per tile.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "mfma_common.hpp"
 
 namespace mi_attn {
 
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ f32x16_t mfma32(bf16_t, const u32x4_t& a, const u32x4_t& b, const f32x16_t& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
-                                                 0, 0, 0);
-}
-__device__ __forceinline__ f32x16_t mfma32(f16_t, const u32x4_t& a, const u32x4_t& b, const f32x16_t& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c, 0,
-                                                0, 0);
-}
-
-__device__ __forceinline__ uint32_t pack2(bf16_t, float a, float b) {
-  f32x2_t v = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-}
-__device__ __forceinline__ uint32_t pack2(f16_t, float a, float b) {
-  f32x2_t v = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
-}
-
-// max over lanes l and l ^ 32 (v_permlane32_swap, no LDS round trip)
-__device__ __forceinline__ float max_halves(float x) {
-  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
-}
-__device__ __forceinline__ float sum_halves(float x) {
-  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
-}
-
-// Buffer resource over `bytes` bytes at `base`: loads past the end return zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes, 0x00020000);
-}
-__device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, int byte_offset) {
-  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, 0));
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+using namespace mfma;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
@@ -84,56 +39,20 @@ struct Tile {
   static constexpr int kBytes = BN * rowBytes;          // K tile, [key][d], no padding
   static constexpr int vBytes = BN * rowBytes;          // V tile, [key][d], no padding
   static constexpr int xBytes = 8 * BN;                 // top-k side data: BN int32 ranks + BN fp32 values
-  static constexpr int stage = kBytes + vBytes + xBytes;
   static constexpr int rowsPerWaveLoad = 1024 / rowBytes;  // one wave's 64 x 16 B direct load
   static constexpr int loadRounds = kBytes / (kThreads * 16);
   static_assert(loadRounds * kThreads * 16 == kBytes, "tile split evenly across direct loads");
   static_assert(BN <= kThreads, "one top-k side entry per thread");
 };
 
-// 16-byte slot swizzle of a tile row. Rows are stored unpadded; slot s of row r lives at
-// slot s ^ swz(r). With 64 banks (16 lanes per cycle for 128-bit reads, 32 lanes for
-// 64-bit reads) it makes both operand reads conflict-free: the K read (16 consecutive
-// rows, one slot each) and the transposed V read (4 consecutive rows x 4 aligned slots).
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-}
-template <int D>
-__device__ __forceinline__ int tile_off(int r, int slot) {
-  return r * (D * 2) + ((slot ^ swz<D>(r)) << 4);
-}
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-
-// Transposed 64-bit LDS read: within each 16-lane group, lane j receives element j % 4 of
-// the 8-byte rows read by lanes j / 4, 4 + j / 4, 8 + j / 4 and 12 + j / 4.
-__device__ __forceinline__ u32x2_t lds_read_tr16(const unsigned char* p) {
-  const bf16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)(p));
-  return __builtin_bit_cast(u32x2_t, v);
-}
-
-// The running max only moves when a row's maximum grows by more than 2^8 (log2 units).
-// Between moves, p = exp2(s - m) stays below 2^8, which fp32 sums and 16-bit P hold
-// without loss of relative precision; l and the output use the same m, so the result is
-// unchanged up to rounding, and most tiles skip rescaling the output accumulator.
-constexpr float kRescaleThreshold = 8.0f;
-
-// Workgroup -> (KV group, query block). Workgroups are handed to the 8 XCDs round-robin;
-// the remap gives each XCD a contiguous run of KV groups (their K/V stays in that XCD's
-// L2), and inside a KV group the query blocks with the most tiles start first.
-__device__ __forceinline__ unsigned logical_block(unsigned bid, unsigned nblk) {
-  const unsigned per = nblk / 8u;
-  if (bid < per * 8u) return (bid % 8u) * per + bid / 8u;
-  return bid;
-}
-
 template <typename T, int D, int BN, int MK>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
   using TL = Tile<D, BN>;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * TL::stage];
+  // LDS: two K slots, two V slots, two top-k side-data slots. K runs one tile ahead of V.
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * TL::kBytes + 2 * TL::vBytes + 2 * TL::xBytes];
+  unsigned char* const kslot0 = smem;
+  unsigned char* const vslot0 = smem + 2 * TL::kBytes;
+  unsigned char* const xslot0 = vslot0 + 2 * TL::vBytes;
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
@@ -220,67 +139,44 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
   // of the swizzled layout. Rows at or past Lk read as zeros (buffer range check).
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(K, p.Lk * D * 2);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V, p.Lk * D * 2);
-  int32_t xrank = 0;
-  float xzh = 0.f;
-  auto issue_tile = [&](int t, int stg) {
+  auto issue = [&](__amdgpu_buffer_rsrc_t rs, int t, unsigned char* dst) {
     const int j0 = t * BN;
-    unsigned char* kst = smem + stg * TL::stage;
-    unsigned char* vst = kst + TL::kBytes;
 #pragma unroll
     for (int c = 0; c < TL::loadRounds; ++c) {
-      const int blk = c * kWaves + wave;             // 1 KB block of the tile
+      const int blk = c * kWaves + wave;  // 1 KB block of the tile
       const int r = blk * TL::rowsPerWaveLoad + lane / (D / 8);
-      const int ps = lane % (D / 8);                 // physical slot this lane fills
+      const int ps = lane % (D / 8);      // physical slot this lane fills
       const int gofs = ((j0 + r) * D + ((ps ^ swz<D>(r)) << 3)) * 2;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(kst + blk * 1024), 16, gofs, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(vst + blk * 1024), 16, gofs, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + blk * 1024), 16, gofs, 0, 0, 0);
     }
+  };
+  // top-k side data (rank, zero_hold of the tile's keys) travels with K, through registers
+  int32_t xrank = 0;
+  float xzh = 0.f;
+  auto side_load = [&](int t) {
     if constexpr (MK == MI_ATTN_MASK_TOPK) {
       if (tid < BN) {
-        const int key = j0 + tid;
+        const int key = t * BN + tid;
         xrank = key < p.Lk ? p.rank[bgk + key] : 0x7fffffff;
         xzh = key < p.Lk ? p.zero_hold[bgk + key] : 0.f;
       }
     }
   };
-  auto finish_tile = [&](int stg) {
+  auto side_store = [&](int slot) {
     if constexpr (MK == MI_ATTN_MASK_TOPK) {
       if (tid < BN) {
-        int32_t* xr = reinterpret_cast<int32_t*>(smem + stg * TL::stage + TL::kBytes + TL::vBytes);
+        int32_t* xr = reinterpret_cast<int32_t*>(xslot0 + slot * TL::xBytes);
         xr[tid] = xrank;
         reinterpret_cast<float*>(xr + BN)[tid] = xzh;
       }
     }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
   };
 
-  // ---- running state
   constexpr int NKB = BN / 32;  // 32-key blocks per tile
   constexpr int NDB = D / 32;   // 32-dim blocks of O^T
-  f32x16_t oacc[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16_t{};
-  float m_run = kNegInf;  // running max, log2 domain (may lag the true max by < 2^8)
-  float l_run = 0.f;      // this lane's partial running sum
 
-  int t = next_live(t_lo);
-  int stage = 0;
-  if (t < t_hi) {
-    issue_tile(t, 0);
-    finish_tile(0);
-  }
-  __syncthreads();
-
-  while (t < t_hi) {
-    const int tn = next_live(t + 1);
-    if (tn < t_hi) issue_tile(tn, stage ^ 1);  // lands in the other stage while this tile computes
-
-    const unsigned char* ks = smem + stage * TL::stage;
-    const unsigned char* vs = ks + TL::kBytes;
-    const int j0 = t * BN;
-
-    // S^T = K Q^T
-    f32x16_t sacc[NKB];
+  // S^T = K Q^T for one tile held in `ks`
+  auto qk = [&](const unsigned char* ks, f32x16_t* sacc) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       f32x16_t acc = f32x16_t{};
@@ -291,65 +187,82 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
       }
       sacc[kb] = acc;
     }
+  };
 
-    // mask (tiles the mask does not cover entirely); masked tiles move to the log2
-    // domain here (cm = 1), unmasked ones are scaled inside the exponent (cm = cexp)
-    const int j_end = j0 + BN - 1;
-    bool need_mask = p.no_skip || j_end >= p.Lk || MK == MI_ATTN_MASK_DENSE || MK == MI_ATTN_MASK_TOPK;
-    if constexpr (MK == MI_ATTN_MASK_CAUSAL || MK == MI_ATTN_MASK_WINDOW) need_mask = need_mask || j_end > P0;
-    if constexpr (MK == MI_ATTN_MASK_WINDOW) need_mask = need_mask || j0 < P1 - p.window_left;
-    float cm = cexp;
-    if (need_mask) {
-      cm = 1.f;
-      const int32_t* xr = reinterpret_cast<const int32_t*>(vs + TL::vBytes);
-      const float* xz = reinterpret_cast<const float*>(xr + BN);
+  // Mask one tile's S^T in place where the mask does not cover the whole tile; such a
+  // tile moves to the log2 domain here and the returned exponent scale is 1, otherwise
+  // the raw dot products stay and the scale is cexp.
+  auto apply_mask = [&](int t, const unsigned char* xs, f32x16_t* sacc) -> float {
+    const int j0 = t * BN;
+    if (!tile_needs_mask<MK, BN>(p, j0, P0, P1)) return cexp;
+    const int32_t* xr = reinterpret_cast<const int32_t*>(xs);
+    mask_tile<MK, NKB>(sacc, p, j0, hf, pos, i_row, tau_row, cexp, xr, reinterpret_cast<const float*>(xr + BN));
+    return 1.f;
+  };
+
+  // ---- running state
+  f32x16_t oacc[NDB];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int kk = kb * 32 + r4 * 8 + hf * 4;  // first of 4 consecutive keys in the tile
-          const int jb = j0 + kk;
-          int4 rk4 = {0, 0, 0, 0};
-          float4 zh4 = {0.f, 0.f, 0.f, 0.f};
-          if constexpr (MK == MI_ATTN_MASK_TOPK) {
-            rk4 = *reinterpret_cast<const int4*>(xr + kk);
-            zh4 = *reinterpret_cast<const float4*>(xz + kk);
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int j = jb + e;
-            float s = sacc[kb][r4 * 4 + e] * cexp;
-            bool vis = j < p.Lk;
-            if constexpr (MK == MI_ATTN_MASK_CAUSAL) vis = vis && j <= pos;
-            if constexpr (MK == MI_ATTN_MASK_WINDOW) vis = vis && j <= pos && j >= pos - p.window_left;
-            if constexpr (MK == MI_ATTN_MASK_DENSE) {
-              const float mv = vis ? p.mask[static_cast<long>(i_row) * p.Lk + j] : 0.f;
-              s = fmaf(mv, kLog2e, s);
-            }
-            if constexpr (MK == MI_ATTN_MASK_TOPK) {
-              const int32_t rk = e == 0 ? rk4.x : e == 1 ? rk4.y : e == 2 ? rk4.z : rk4.w;
-              const float zv = e == 0 ? zh4.x : e == 1 ? zh4.y : e == 2 ? zh4.z : zh4.w;
-              vis = vis && j <= pos && rk <= tau_row;
-              s = fmaf(zv, kLog2e, s);
-            }
-            sacc[kb][r4 * 4 + e] = vis ? s : kNegInf;
-          }
-        }
-      }
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16_t{};
+  float m_run = kNegInf;  // running max, log2 domain (may lag the true max by < 2^8)
+  float l_run = 0.f;      // this lane's partial running sum
+
+  // ---- prologue: K and V of the first live tile, K of the second
+  int t = next_live(t_lo);
+  int tn = (t < t_hi) ? next_live(t + 1) : t_hi;
+  f32x16_t scur[NKB];
+  float cm_cur = cexp;
+  if (t < t_hi) {
+    issue(krs, t, kslot0);
+    issue(vrs, t, vslot0);
+    side_load(t);
+    side_store(0);
+    if (tn < t_hi) {
+      issue(krs, tn, kslot0 + TL::kBytes);
+      side_load(tn);
+      side_store(1);
     }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    qk(kslot0, scur);
+    cm_cur = apply_mask(t, xslot0, scur);
+    __syncthreads();  // K slot 0 is refilled by the first iteration
+  }
 
-    // online softmax (log2 domain), guarded against all -inf tiles and rows
+  // ---- main loop over live tiles; iteration i holds K(t_{i+1}) in K slot (i+1)%2 and
+  // V(t_i) in V slot i%2, and fills K slot i%2 with K(t_{i+2}), V slot (i+1)%2 with V(t_{i+1})
+  int par = 0;
+  while (t < t_hi) {
+    const int tnn = (tn < t_hi) ? next_live(tn + 1) : t_hi;
+    if (tnn < t_hi) {
+      issue(krs, tnn, kslot0 + par * TL::kBytes);
+      side_load(tnn);
+    }
+    if (tn < t_hi) issue(vrs, tn, vslot0 + (par ^ 1) * TL::vBytes);
+
+    // softmax, first half: row max and the rescale factor (needs only this tile's S^T)
     float mx4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};  // four independent chains
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx4[e & 3] = fmaxf(mx4[e & 3], sacc[kb][e]);
+      for (int e = 0; e < 16; ++e) mx4[e & 3] = fmaxf(mx4[e & 3], scur[kb][e]);
     float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
-    mx = max_halves(mx) * cm;
+    mx = max_halves(mx) * cm_cur;
     const float m_next = (mx > m_run + kRescaleThreshold) ? mx : m_run;
     const float m_use = (m_next == kNegInf) ? 0.f : m_next;
     const float alpha = fast_exp2(m_run - m_use);  // 1 when the max did not move, 0 from -inf
-    float ps4[4] = {0.f, 0.f, 0.f, 0.f};  // four independent chains
+    m_run = m_next;
+    if (!__all(alpha == 1.f)) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+    }
+
+    // phase A: S^T of the next tile on the matrix cores while P of this tile is formed on
+    // the vector ALUs. After the last tile the K slot holds stale data; the product is
+    // computed anyway (keeping phase A one basic block) and then discarded.
+    f32x16_t snext[NKB];
+    qk(kslot0 + (par ^ 1) * TL::kBytes, snext);
+    float ps4[4] = {0.f, 0.f, 0.f, 0.f};
     u32x4_t preg[BN / 16];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
@@ -358,7 +271,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
         float pv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          pv[e] = fast_exp2(fmaf(sacc[kb][half * 8 + e], cm, -m_use));
+          pv[e] = fast_exp2(fmaf(scur[kb][half * 8 + e], cm_cur, -m_use));
           ps4[e & 3] += pv[e];
         }
         u32x4_t pk;
@@ -370,16 +283,21 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
       }
     }
     l_run = fmaf(l_run, alpha, (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]));
-    m_run = m_next;
-    if (!__all(alpha == 1.f)) {
+    // interleave: operand reads two matrix instructions ahead, and between consecutive
+    // matrix instructions a few vector ALU / transcendental ops of this tile's softmax
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);    // DS read
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+    for (int i = 0; i < NKB * (D / 16); ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);  // VALU + TRANS
     }
 
-    // O^T += V^T P^T. The V^T operand comes from two transposed reads: lane (16 * g + i)
-    // reads 8 bytes of key row R0 + i / 4 at dims D0 + 4 * (i % 4) and receives keys
-    // R0..R0+3 of dim D0 + i. Keys 4*hf+0..3 and 8+4*hf+0..3 of the 16-key chunk are what
-    // its P registers hold.
+    // phase B: O^T += V^T P^T. The V^T operand comes from two transposed reads: lane
+    // (16 * g + i) reads 8 bytes of key row R0 + i / 4 at dims D0 + 4 * (i % 4) and receives
+    // keys R0..R0+3 of dim D0 + i. Keys 4*hf+0..3 and 8+4*hf+0..3 of the 16-key chunk are
+    // what its P registers hold.
+    const unsigned char* vs = vslot0 + par * TL::vBytes;
     const int tr_row = 4 * hf + (lane & 15) / 4;
     const int tr_dim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
@@ -388,17 +306,26 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
       for (int kc = 0; kc < BN / 16; ++kc) {
         const int d0 = db * 32 + tr_dim;
         const int r0 = kc * 16 + tr_row;
-        const u32x2_t lo = lds_read_tr16(vs + tile_off<D>(r0, d0 >> 3) + ((d0 & 7) << 1));
+        const u32x2_t lo2 = lds_read_tr16(vs + tile_off<D>(r0, d0 >> 3) + ((d0 & 7) << 1));
         const u32x2_t hi2 = lds_read_tr16(vs + tile_off<D>(r0 + 8, d0 >> 3) + ((d0 & 7) << 1));
-        const u32x4_t a = {lo.x, lo.y, hi2.x, hi2.y};
+        const u32x4_t a = {lo2.x, lo2.y, hi2.x, hi2.y};
         oacc[db] = mfma32(T{}, a, preg[kc], oacc[db]);
       }
     }
 
-    if (tn < t_hi) finish_tile(stage ^ 1);
+    // mask the next tile (after phase B, so phases A and B stay one basic block)
+    float cm_next = cexp;
+    if (tn < t_hi) cm_next = apply_mask(tn, xslot0 + (par ^ 1) * TL::xBytes, snext);
+
+    if (tnn < t_hi) side_store(par);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
     __syncthreads();
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) scur[kb] = snext[kb];
+    cm_cur = cm_next;
     t = tn;
-    stage ^= 1;
+    tn = tnn;
+    par ^= 1;
   }
 
   // ---- epilogue: combine the two lane halves' partial sums, normalise, store
@@ -470,6 +397,13 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(AttnParams p) {
 }
 
 template <typename T>
+hipError_t launch_lse_merge_t(const AttnParams& p, hipStream_t s) {
+  const long n = static_cast<long>(p.B) * p.Hq * p.Lq * (p.d / 4);
+  hipLaunchKernelGGL(lse_merge_kernel<T>, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+template <typename T>
 hipError_t launch_prefill_t(const AttnParams& p, hipStream_t s) {
   const int nqb = (p.Lq + p.q_per_block - 1) / p.q_per_block;
   const long blocks = static_cast<long>(p.B) * p.Hkv * nqb;
@@ -485,24 +419,28 @@ hipError_t launch_prefill_t(const AttnParams& p, hipStream_t s) {
     }
   } else {
     switch (p.mask_kind) {
-      case MI_ATTN_MASK_NONE: hipLaunchKernelGGL((prefill_kernel<T, 64, 128, 0>), grid, block, 0, s, p); break;
-      case MI_ATTN_MASK_CAUSAL: hipLaunchKernelGGL((prefill_kernel<T, 64, 128, 1>), grid, block, 0, s, p); break;
-      case MI_ATTN_MASK_WINDOW: hipLaunchKernelGGL((prefill_kernel<T, 64, 128, 2>), grid, block, 0, s, p); break;
-      case MI_ATTN_MASK_DENSE: hipLaunchKernelGGL((prefill_kernel<T, 64, 128, 3>), grid, block, 0, s, p); break;
-      default: hipLaunchKernelGGL((prefill_kernel<T, 64, 128, 4>), grid, block, 0, s, p); break;
+      case MI_ATTN_MASK_NONE: hipLaunchKernelGGL((prefill_kernel<T, 64, 64, 0>), grid, block, 0, s, p); break;
+      case MI_ATTN_MASK_CAUSAL: hipLaunchKernelGGL((prefill_kernel<T, 64, 64, 1>), grid, block, 0, s, p); break;
+      case MI_ATTN_MASK_WINDOW: hipLaunchKernelGGL((prefill_kernel<T, 64, 64, 2>), grid, block, 0, s, p); break;
+      case MI_ATTN_MASK_DENSE: hipLaunchKernelGGL((prefill_kernel<T, 64, 64, 3>), grid, block, 0, s, p); break;
+      default: hipLaunchKernelGGL((prefill_kernel<T, 64, 64, 4>), grid, block, 0, s, p); break;
     }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits <= 1) return e;
-  const long n = static_cast<long>(p.B) * p.Hq * p.Lq * (p.d / 4);
-  hipLaunchKernelGGL(lse_merge_kernel<T>, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, p);
-  return hipGetLastError();
+  return launch_lse_merge_t<T>(p, s);
 }
 
 }  // namespace
 
-int prefill_block_n(int d) { return d == 128 ? 64 : 128; }
+int prefill_block_n(int) { return 64; }
 int prefill_block_m() { return kBlockM; }
+
+hipError_t launch_lse_merge(const AttnParams& p, int dtype, hipStream_t s) {
+  if (dtype == MI_ATTN_BF16) return launch_lse_merge_t<bf16_t>(p, s);
+  if (dtype == MI_ATTN_F16) return launch_lse_merge_t<f16_t>(p, s);
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_prefill(const AttnParams& p, int dtype, hipStream_t s) {
   if (dtype == MI_ATTN_BF16) return launch_prefill_t<bf16_t>(p, s);

@@ -1,0 +1,143 @@
+// Device helpers shared by the MFMA attention kernels (prefill and split-KV decode).
+#pragma once
+
+#include "common.hpp"
+
+namespace mi_attn {
+namespace mfma {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x16_t mfma32(bf16_t, const u32x4_t& a, const u32x4_t& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+__device__ __forceinline__ f32x16_t mfma32(f16_t, const u32x4_t& a, const u32x4_t& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c, 0,
+                                                0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack2(bf16_t, float a, float b) {
+  f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+__device__ __forceinline__ uint32_t pack2(f16_t, float a, float b) {
+  f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
+
+// max over lanes l and l ^ 32 (v_permlane32_swap, no LDS round trip)
+__device__ __forceinline__ float max_halves(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+// Buffer resource over `bytes` bytes at `base`: loads past the end return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, int byte_offset) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, 0));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// 16-byte slot swizzle of a tile row. Rows are stored unpadded; slot s of row r lives at
+// slot s ^ swz(r). With 64 banks (16 lanes per cycle for 128-bit reads, 32 lanes for
+// 64-bit reads) it makes both operand reads conflict-free: the K read (16 consecutive
+// rows, one slot each) and the transposed V read (4 consecutive rows x 4 aligned slots).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int slot) {
+  return r * (D * 2) + ((slot ^ swz<D>(r)) << 4);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+// Transposed 64-bit LDS read: within each 16-lane group, lane j receives element j % 4 of
+// the 8-byte rows read by lanes j / 4, 4 + j / 4, 8 + j / 4 and 12 + j / 4.
+__device__ __forceinline__ u32x2_t lds_read_tr16(const unsigned char* p) {
+  const bf16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)(p));
+  return __builtin_bit_cast(u32x2_t, v);
+}
+
+// The running max only moves when a row's maximum grows by more than 2^8 (log2 units).
+// Between moves, p = exp2(s - m) stays below 2^8, which fp32 sums and 16-bit P hold
+// without loss of relative precision; l and the output use the same m, so the result is
+// unchanged up to rounding, and most tiles skip rescaling the output accumulator.
+constexpr float kRescaleThreshold = 8.0f;
+
+// Workgroup -> (KV group, query block). Workgroups are handed to the 8 XCDs round-robin;
+// the remap gives each XCD a contiguous run of KV groups (their K/V stays in that XCD's
+// L2), and inside a KV group the query blocks with the most tiles start first.
+__device__ __forceinline__ unsigned logical_block(unsigned bid, unsigned nblk) {
+  const unsigned per = nblk / 8u;
+  if (bid < per * 8u) return (bid % 8u) * per + bid / 8u;
+  return bid;
+}
+
+// Per-element mask of one tile's S^T registers (32x32 MFMA layout: lane holds query column
+// l % 32 and, per 32-key block kb, keys kb*32 + 8*(i/4) + 4*hf + i%4 in register i).
+// Visible logits move to the log2 domain (s * cexp + bias * log2 e); hidden ones become
+// -inf. `xr`/`xz` are the tile's top-k ranks and zero_hold values (index = key - j0).
+template <int MK, int NKB>
+__device__ __forceinline__ void mask_tile(f32x16_t* sacc, const AttnParams& p, int j0, int hf, int pos, int i_row,
+                                          int32_t tau_row, float cexp, const int32_t* xr, const float* xz) {
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int kk = kb * 32 + r4 * 8 + hf * 4;  // first of 4 consecutive keys in the tile
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = j0 + kk + e;
+        float s = sacc[kb][r4 * 4 + e] * cexp;
+        bool vis = j < p.Lk;
+        if constexpr (MK == MI_ATTN_MASK_CAUSAL) vis = vis && j <= pos;
+        if constexpr (MK == MI_ATTN_MASK_WINDOW) vis = vis && j <= pos && j >= pos - p.window_left;
+        // side reads use key j0 (always < Lk in a visited tile) in place of keys past Lk
+        if constexpr (MK == MI_ATTN_MASK_DENSE) {
+          const float mv = p.mask[static_cast<long>(i_row) * p.Lk + (vis ? j : j0)];
+          s = fmaf(vis ? mv : 0.f, kLog2e, s);
+        }
+        if constexpr (MK == MI_ATTN_MASK_TOPK) {
+          const int idx = vis ? kk + e : 0;
+          vis = vis && j <= pos && xr[idx] <= tau_row;
+          s = fmaf(xz[idx], kLog2e, s);
+        }
+        sacc[kb][r4 * 4 + e] = vis ? s : kNegInf;
+      }
+    }
+  }
+}
+
+// Whether a tile [j0, j0 + BN) needs per-element masking for a block whose query rows sit
+// at positions P0..P1: tiles every row sees entirely (and inside Lk) skip it.
+template <int MK, int BN>
+__device__ __forceinline__ bool tile_needs_mask(const AttnParams& p, int j0, int P0, int P1) {
+  const int j_end = j0 + BN - 1;
+  bool need = p.no_skip || j_end >= p.Lk || MK == MI_ATTN_MASK_DENSE || MK == MI_ATTN_MASK_TOPK;
+  if constexpr (MK == MI_ATTN_MASK_CAUSAL || MK == MI_ATTN_MASK_WINDOW) need = need || j_end > P0;
+  if constexpr (MK == MI_ATTN_MASK_WINDOW) need = need || j0 < P1 - p.window_left;
+  return need;
+}
+
+}  // namespace mfma
+}  // namespace mi_attn

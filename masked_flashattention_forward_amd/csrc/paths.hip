@@ -1,17 +1,24 @@
-// Path choice for fp16/bf16 inputs: the MFMA kernel over the whole key range (path 1) or
-// split into key ranges whose partial results are merged by log-sum-exp (path 2).
+// Path choice for fp16/bf16 inputs:
+//   1  MFMA prefill kernel over the whole key range, or split into key ranges whose
+//      partial results are merged by log-sum-exp when there are too few workgroups;
+//   2  split-KV decode kernel, for at most 32 query rows per KV head (G * Lq).
 #include "kernels.hpp"
 
 namespace mi_attn {
 
 int prefill_block_n(int d);
 int prefill_block_m();
+int decode_block_n();
+int decode_max_rows();
 hipError_t launch_prefill(const AttnParams& p, int dtype, hipStream_t s);
+hipError_t launch_decode(const AttnParams& p, int dtype, hipStream_t s);
 
 namespace {
 
-constexpr int kTargetBlocks = 2048;   // ~8 workgroups per CU over 256 CUs
+constexpr int kTargetBlocks = 2048;      // prefill: ~8 workgroups per CU over 256 CUs
 constexpr int kMinTilesPerSplit = 8;
+constexpr int kDecodeTargetBlocks = 512;  // decode: 2 resident workgroups per CU
+constexpr int kDecodeMinKeysPerSplit = 512;  // 4 tiles of 32 keys per wavefront
 
 int q_per_block_for(int G) { return prefill_block_m() / G; }
 
@@ -23,32 +30,52 @@ int auto_splits(int blocks, int Lk, int bn) {
   return s < 1 ? 1 : s;
 }
 
+int decode_splits(int groups, int Lk) {
+  int s = (kDecodeTargetBlocks + groups - 1) / groups;
+  const int max_by_len = (Lk + kDecodeMinKeysPerSplit - 1) / kDecodeMinKeysPerSplit;
+  if (s > max_by_len) s = max_by_len;
+  return s < 1 ? 1 : s;
+}
+
+long prefill_blocks(int B, int Hkv, int G, int Lq) {
+  const int qpb = q_per_block_for(G);
+  return static_cast<long>(B) * Hkv * ((Lq + qpb - 1) / qpb);
+}
+
 }  // namespace
 
-bool half_path_available(int path, int d, int G, int /*Lq*/) {
-  if (path != 1 && path != 2) return false;
-  return (d == 64 || d == 128) && G <= prefill_block_m();
+bool half_path_available(int path, int d, int G, int Lq) {
+  if (d != 64 && d != 128) return false;
+  if (path == 1) return G <= prefill_block_m();
+  if (path == 2) return static_cast<long>(G) * Lq <= decode_max_rows();
+  return false;
 }
 
 int choose_half_path(int B, int Hkv, int G, int Lq, int Lk, int d, int /*mask_kind*/) {
-  if (!half_path_available(1, d, G, Lq)) return 0;
-  const int qpb = q_per_block_for(G);
-  const long blocks = static_cast<long>(B) * Hkv * ((Lq + qpb - 1) / qpb);
-  return auto_splits(static_cast<int>(blocks < 0x7fffffff ? blocks : 0x7fffffff), Lk, prefill_block_n(d)) > 1 ? 2 : 1;
+  if (!half_path_available(1, d, G, Lq)) return half_path_available(2, d, G, Lq) ? 2 : 0;
+  const long blocks = prefill_blocks(B, Hkv, G, Lq);
+  // few query rows per KV head and a long key range: stream it with the decode kernel
+  if (half_path_available(2, d, G, Lq) && blocks < kTargetBlocks / 2 && Lk >= 2 * kDecodeMinKeysPerSplit) return 2;
+  return 1;
 }
 
 HalfPlan plan_half_path(int path, int B, int Hkv, int G, int Lq, int Lk, int d, int /*mask_kind*/,
                         int /*window_left*/, int force_splits) {
   HalfPlan h{};
-  h.block_m = prefill_block_m();
-  h.block_n = prefill_block_n(d);
-  h.q_per_block = q_per_block_for(G);
-  const long blocks = static_cast<long>(B) * Hkv * ((Lq + h.q_per_block - 1) / h.q_per_block);
-  h.grid = static_cast<int>(blocks < 0x7fffffff ? blocks : 0x7fffffff);
   int splits = 1;
   if (path == 2) {
+    h.block_m = decode_max_rows();
+    h.block_n = decode_block_n();
+    h.q_per_block = Lq;  // all query rows of a KV head in one workgroup
+    h.grid = B * Hkv;
+    splits = force_splits > 0 ? force_splits : decode_splits(h.grid, Lk);
+  } else {
+    h.block_m = prefill_block_m();
+    h.block_n = prefill_block_n(d);
+    h.q_per_block = q_per_block_for(G);
+    const long blocks = prefill_blocks(B, Hkv, G, Lq);
+    h.grid = static_cast<int>(blocks < 0x7fffffff ? blocks : 0x7fffffff);
     splits = force_splits > 0 ? force_splits : auto_splits(h.grid, Lk, h.block_n);
-    if (splits < 2) splits = 2;
   }
   // split boundaries fall on tile boundaries
   const int tiles = (Lk + h.block_n - 1) / h.block_n;
@@ -59,8 +86,8 @@ HalfPlan plan_half_path(int path, int B, int Hkv, int G, int Lq, int Lk, int d, 
   return h;
 }
 
-hipError_t launch_half_path(int /*path*/, const AttnParams& p, int dtype, hipStream_t s) {
-  return launch_prefill(p, dtype, s);
+hipError_t launch_half_path(int path, const AttnParams& p, int dtype, hipStream_t s) {
+  return path == 2 ? launch_decode(p, dtype, s) : launch_prefill(p, dtype, s);
 }
 
 }  // namespace mi_attn

@@ -118,18 +118,21 @@ def test_runs_are_bitwise_deterministic():
 
 
 @pytest.mark.parametrize("kind", ["causal", "window", "dense", "topk", "none"])
-@pytest.mark.parametrize("splits", [2, 3, 7])
-def test_forced_split_kv_merge(kind, splits):
-    """Split-KV with the LSE merge, including splits whose key range is empty or fully
-    masked (window), against the oracle."""
+@pytest.mark.parametrize("splits", [1, 2, 3, 7])
+@pytest.mark.parametrize("path", [1, 2])
+@pytest.mark.parametrize("d", [128, 64])
+def test_forced_split_kv_merge(kind, splits, path, d):
+    """Split-KV with the LSE merge on the prefill kernel (path 1) and the decode kernel
+    (path 2), including splits whose key range is empty or fully masked (window), against
+    the oracle."""
     import masked_flashattention_forward_amd as mfa
     Lq, Lk = 5, 1111
-    p = synth.make_problem(f"split{splits} {kind}", 2, 8, 2, Lq, Lk, 128, "bf16", kind, 400 + splits,
-                           window_left=70, keep_k=50, with_zero_hold=kind == "topk",
+    p = synth.make_problem(f"path{path} split{splits} d{d} {kind}", 2, 8, 2, Lq, Lk, d, "bf16", kind,
+                           400 + splits, window_left=70, keep_k=50, with_zero_hold=kind == "topk",
                            mask=synth.window_dense_mask(Lq, Lk, 900, 100) if kind == "dense" else None)
     say(p.name)
     try:
-        mfa.set_debug(force_path=2, force_splits=splits)
+        mfa.set_debug(force_path=path, force_splits=splits)
         out, lse = run_gpu(p, out_fill=float("nan"))
     finally:
         mfa.set_debug()
@@ -150,3 +153,15 @@ def test_row_kernel_and_mfma_agree(dtype):
         mfa.set_debug()
     np.testing.assert_allclose(a[0], b[0], rtol=0, atol=2e-2)
     np.testing.assert_allclose(a[1], b[1], rtol=0, atol=1e-3)
+
+
+@pytest.mark.parametrize("G,Lq", [(4, 1), (8, 4), (32, 1), (1, 32), (6, 5)])
+def test_decode_path_shapes(G, Lq):
+    """Shapes the planner sends to the split-KV decode kernel (G * Lq <= 32)."""
+    import masked_flashattention_forward_amd as mfa
+    p = synth.make_problem(f"decode G{G} Lq{Lq}", 2, 2 * G, 2, Lq, 3000, 128, "fp16", "causal", 600 + G)
+    assert mfa.plan(p.B, p.Hq, p.Hkv, p.Lq, p.Lk, p.d, "causal", dtype=mfa.F16)["path"] == "splitkv_decode"
+    say(p.name)
+    out, lse = run_gpu(p, out_fill=float("nan"))
+    ref_o, ref_l = run_oracle(p)
+    compare(p, out, lse, ref_o, ref_l, label=p.name)
