@@ -28,9 +28,6 @@ constexpr int kDecWaves = 4;
 constexpr int kDecThreads = kDecWaves * kWave;
 constexpr int kDecBN = 32;  // keys per wavefront tile
 
-// s_waitcnt immediate for "at most n vector-memory operations outstanding" (gfx9
-// encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their maximum).
-constexpr int vmcnt_imm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
 
 template <int D>
 struct DecTile {
@@ -133,7 +130,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(AttnParams p) {
       const int r = c * (1024 / (D * 2)) + lane / (D / 8);
       const int ps = lane % (D / 8);
       const int gofs = ((j0 + r) * D + ((ps ^ swz<D>(r)) << 3)) * 2;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(dst + c * 1024), 16, gofs, 0, 0, 0);
+      lds_dma16(vrs, dst + c * 1024, gofs);
     }
   };
   constexpr int kLoadsPerTile = TL::kLoads + TL::vLoads;

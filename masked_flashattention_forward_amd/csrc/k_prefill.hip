@@ -39,6 +39,7 @@ struct Tile {
   static constexpr int kBytes = BN * rowBytes;          // K tile, [key][d], no padding
   static constexpr int vBytes = BN * rowBytes;          // V tile, [key][d], no padding
   static constexpr int xBytes = 8 * BN;                 // top-k side data: BN int32 ranks + BN fp32 values
+  static constexpr int stage = kBytes + vBytes + xBytes;
   static constexpr int rowsPerWaveLoad = 1024 / rowBytes;  // one wave's 64 x 16 B direct load
   static constexpr int loadRounds = kBytes / (kThreads * 16);
   static_assert(loadRounds * kThreads * 16 == kBytes, "tile split evenly across direct loads");
@@ -48,11 +49,7 @@ struct Tile {
 template <typename T, int D, int BN, int MK>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
   using TL = Tile<D, BN>;
-  // LDS: two K slots, two V slots, two top-k side-data slots. K runs one tile ahead of V.
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * TL::kBytes + 2 * TL::vBytes + 2 * TL::xBytes];
-  unsigned char* const kslot0 = smem;
-  unsigned char* const vslot0 = smem + 2 * TL::kBytes;
-  unsigned char* const xslot0 = vslot0 + 2 * TL::vBytes;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * TL::stage];
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
@@ -139,44 +136,67 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
   // of the swizzled layout. Rows at or past Lk read as zeros (buffer range check).
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(K, p.Lk * D * 2);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V, p.Lk * D * 2);
-  auto issue = [&](__amdgpu_buffer_rsrc_t rs, int t, unsigned char* dst) {
-    const int j0 = t * BN;
-#pragma unroll
-    for (int c = 0; c < TL::loadRounds; ++c) {
-      const int blk = c * kWaves + wave;  // 1 KB block of the tile
-      const int r = blk * TL::rowsPerWaveLoad + lane / (D / 8);
-      const int ps = lane % (D / 8);      // physical slot this lane fills
-      const int gofs = ((j0 + r) * D + ((ps ^ swz<D>(r)) << 3)) * 2;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + blk * 1024), 16, gofs, 0, 0, 0);
-    }
-  };
-  // top-k side data (rank, zero_hold of the tile's keys) travels with K, through registers
   int32_t xrank = 0;
   float xzh = 0.f;
-  auto side_load = [&](int t) {
+  auto issue_tile = [&](int t, int stg) {
+    const int j0 = t * BN;
+    unsigned char* kst = smem + stg * TL::stage;
+    unsigned char* vst = kst + TL::kBytes;
+#pragma unroll
+    for (int c = 0; c < TL::loadRounds; ++c) {
+      const int blk = c * kWaves + wave;             // 1 KB block of the tile
+      const int r = blk * TL::rowsPerWaveLoad + lane / (D / 8);
+      const int ps = lane % (D / 8);                 // physical slot this lane fills
+      const int gofs = ((j0 + r) * D + ((ps ^ swz<D>(r)) << 3)) * 2;
+      lds_dma16(krs, kst + blk * 1024, gofs);
+      lds_dma16(vrs, vst + blk * 1024, gofs);
+    }
     if constexpr (MK == MI_ATTN_MASK_TOPK) {
       if (tid < BN) {
-        const int key = t * BN + tid;
+        const int key = j0 + tid;
         xrank = key < p.Lk ? p.rank[bgk + key] : 0x7fffffff;
         xzh = key < p.Lk ? p.zero_hold[bgk + key] : 0.f;
       }
     }
   };
-  auto side_store = [&](int slot) {
+  auto finish_tile = [&](int stg) {
     if constexpr (MK == MI_ATTN_MASK_TOPK) {
       if (tid < BN) {
-        int32_t* xr = reinterpret_cast<int32_t*>(xslot0 + slot * TL::xBytes);
+        int32_t* xr = reinterpret_cast<int32_t*>(smem + stg * TL::stage + TL::kBytes + TL::vBytes);
         xr[tid] = xrank;
         reinterpret_cast<float*>(xr + BN)[tid] = xzh;
       }
     }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
   };
 
+  // ---- running state
   constexpr int NKB = BN / 32;  // 32-key blocks per tile
   constexpr int NDB = D / 32;   // 32-dim blocks of O^T
+  f32x16_t oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16_t{};
+  float m_run = kNegInf;  // running max, log2 domain (may lag the true max by < 2^8)
+  float l_run = 0.f;      // this lane's partial running sum
 
-  // S^T = K Q^T for one tile held in `ks`
-  auto qk = [&](const unsigned char* ks, f32x16_t* sacc) {
+  int t = next_live(t_lo);
+  int stage = 0;
+  if (t < t_hi) {
+    issue_tile(t, 0);
+    finish_tile(0);
+  }
+  __syncthreads();
+
+  while (t < t_hi) {
+    const int tn = next_live(t + 1);
+    if (tn < t_hi) issue_tile(tn, stage ^ 1);  // lands in the other stage while this tile computes
+
+    const unsigned char* ks = smem + stage * TL::stage;
+    const unsigned char* vs = ks + TL::kBytes;
+    const int j0 = t * BN;
+
+    // S^T = K Q^T
+    f32x16_t sacc[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       f32x16_t acc = f32x16_t{};
@@ -187,82 +207,28 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
       }
       sacc[kb] = acc;
     }
-  };
 
-  // Mask one tile's S^T in place where the mask does not cover the whole tile; such a
-  // tile moves to the log2 domain here and the returned exponent scale is 1, otherwise
-  // the raw dot products stay and the scale is cexp.
-  auto apply_mask = [&](int t, const unsigned char* xs, f32x16_t* sacc) -> float {
-    const int j0 = t * BN;
-    if (!tile_needs_mask<MK, BN>(p, j0, P0, P1)) return cexp;
-    const int32_t* xr = reinterpret_cast<const int32_t*>(xs);
-    mask_tile<MK, NKB>(sacc, p, j0, hf, pos, i_row, tau_row, cexp, xr, reinterpret_cast<const float*>(xr + BN));
-    return 1.f;
-  };
-
-  // ---- running state
-  f32x16_t oacc[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16_t{};
-  float m_run = kNegInf;  // running max, log2 domain (may lag the true max by < 2^8)
-  float l_run = 0.f;      // this lane's partial running sum
-
-  // ---- prologue: K and V of the first live tile, K of the second
-  int t = next_live(t_lo);
-  int tn = (t < t_hi) ? next_live(t + 1) : t_hi;
-  f32x16_t scur[NKB];
-  float cm_cur = cexp;
-  if (t < t_hi) {
-    issue(krs, t, kslot0);
-    issue(vrs, t, vslot0);
-    side_load(t);
-    side_store(0);
-    if (tn < t_hi) {
-      issue(krs, tn, kslot0 + TL::kBytes);
-      side_load(tn);
-      side_store(1);
+    // mask (tiles the mask does not cover entirely); masked tiles move to the log2
+    // domain here (cm = 1), unmasked ones are scaled inside the exponent (cm = cexp)
+    float cm = cexp;
+    if (tile_needs_mask<MK, BN>(p, j0, P0, P1)) {
+      const int32_t* xr = reinterpret_cast<const int32_t*>(vs + TL::vBytes);
+      mask_tile<MK, NKB>(sacc, p, j0, hf, pos, i_row, tau_row, cexp, xr, reinterpret_cast<const float*>(xr + BN));
+      cm = 1.f;
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    qk(kslot0, scur);
-    cm_cur = apply_mask(t, xslot0, scur);
-    __syncthreads();  // K slot 0 is refilled by the first iteration
-  }
 
-  // ---- main loop over live tiles; iteration i holds K(t_{i+1}) in K slot (i+1)%2 and
-  // V(t_i) in V slot i%2, and fills K slot i%2 with K(t_{i+2}), V slot (i+1)%2 with V(t_{i+1})
-  int par = 0;
-  while (t < t_hi) {
-    const int tnn = (tn < t_hi) ? next_live(tn + 1) : t_hi;
-    if (tnn < t_hi) {
-      issue(krs, tnn, kslot0 + par * TL::kBytes);
-      side_load(tnn);
-    }
-    if (tn < t_hi) issue(vrs, tn, vslot0 + (par ^ 1) * TL::vBytes);
-
-    // softmax, first half: row max and the rescale factor (needs only this tile's S^T)
+    // online softmax (log2 domain), guarded against all -inf tiles and rows
     float mx4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};  // four independent chains
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx4[e & 3] = fmaxf(mx4[e & 3], scur[kb][e]);
+      for (int e = 0; e < 16; ++e) mx4[e & 3] = fmaxf(mx4[e & 3], sacc[kb][e]);
     float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
-    mx = max_halves(mx) * cm_cur;
+    mx = max_halves(mx) * cm;
     const float m_next = (mx > m_run + kRescaleThreshold) ? mx : m_run;
     const float m_use = (m_next == kNegInf) ? 0.f : m_next;
     const float alpha = fast_exp2(m_run - m_use);  // 1 when the max did not move, 0 from -inf
-    m_run = m_next;
-    if (!__all(alpha == 1.f)) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
-    }
-
-    // phase A: S^T of the next tile on the matrix cores while P of this tile is formed on
-    // the vector ALUs. After the last tile the K slot holds stale data; the product is
-    // computed anyway (keeping phase A one basic block) and then discarded.
-    f32x16_t snext[NKB];
-    qk(kslot0 + (par ^ 1) * TL::kBytes, snext);
-    float ps4[4] = {0.f, 0.f, 0.f, 0.f};
+    float ps4[4] = {0.f, 0.f, 0.f, 0.f};  // four independent chains
     u32x4_t preg[BN / 16];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
@@ -271,7 +237,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
         float pv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          pv[e] = fast_exp2(fmaf(scur[kb][half * 8 + e], cm_cur, -m_use));
+          pv[e] = fast_exp2(fmaf(sacc[kb][half * 8 + e], cm, -m_use));
           ps4[e & 3] += pv[e];
         }
         u32x4_t pk;
@@ -283,21 +249,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
       }
     }
     l_run = fmaf(l_run, alpha, (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]));
-    // interleave: operand reads two matrix instructions ahead, and between consecutive
-    // matrix instructions a few vector ALU / transcendental ops of this tile's softmax
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);    // DS read
+    m_run = m_next;
+    if (!__all(alpha == 1.f)) {
 #pragma unroll
-    for (int i = 0; i < NKB * (D / 16); ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-      __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);  // VALU + TRANS
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
     }
 
-    // phase B: O^T += V^T P^T. The V^T operand comes from two transposed reads: lane
-    // (16 * g + i) reads 8 bytes of key row R0 + i / 4 at dims D0 + 4 * (i % 4) and receives
-    // keys R0..R0+3 of dim D0 + i. Keys 4*hf+0..3 and 8+4*hf+0..3 of the 16-key chunk are
-    // what its P registers hold.
-    const unsigned char* vs = vslot0 + par * TL::vBytes;
+    // O^T += V^T P^T. The V^T operand comes from two transposed reads: lane (16 * g + i)
+    // reads 8 bytes of key row R0 + i / 4 at dims D0 + 4 * (i % 4) and receives keys
+    // R0..R0+3 of dim D0 + i. Keys 4*hf+0..3 and 8+4*hf+0..3 of the 16-key chunk are what
+    // its P registers hold.
     const int tr_row = 4 * hf + (lane & 15) / 4;
     const int tr_dim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
@@ -306,26 +267,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
       for (int kc = 0; kc < BN / 16; ++kc) {
         const int d0 = db * 32 + tr_dim;
         const int r0 = kc * 16 + tr_row;
-        const u32x2_t lo2 = lds_read_tr16(vs + tile_off<D>(r0, d0 >> 3) + ((d0 & 7) << 1));
+        const u32x2_t lo = lds_read_tr16(vs + tile_off<D>(r0, d0 >> 3) + ((d0 & 7) << 1));
         const u32x2_t hi2 = lds_read_tr16(vs + tile_off<D>(r0 + 8, d0 >> 3) + ((d0 & 7) << 1));
-        const u32x4_t a = {lo2.x, lo2.y, hi2.x, hi2.y};
+        const u32x4_t a = {lo.x, lo.y, hi2.x, hi2.y};
         oacc[db] = mfma32(T{}, a, preg[kc], oacc[db]);
       }
     }
 
-    // mask the next tile (after phase B, so phases A and B stay one basic block)
-    float cm_next = cexp;
-    if (tn < t_hi) cm_next = apply_mask(tn, xslot0 + (par ^ 1) * TL::xBytes, snext);
-
-    if (tnn < t_hi) side_store(par);
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
+    if (tn < t_hi) finish_tile(stage ^ 1);
     __syncthreads();
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) scur[kb] = snext[kb];
-    cm_cur = cm_next;
     t = tn;
-    tn = tnn;
-    par ^= 1;
+    stage ^= 1;
   }
 
   // ---- epilogue: combine the two lane halves' partial sums, normalise, store

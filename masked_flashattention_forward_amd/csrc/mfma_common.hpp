@@ -93,6 +93,35 @@ __device__ __forceinline__ unsigned logical_block(unsigned bid, unsigned nblk) {
   return bid;
 }
 
+// 32-bit LDS address of a pointer into __shared__ memory
+__device__ __forceinline__ unsigned lds_address(const void* p) {
+  return static_cast<unsigned>(reinterpret_cast<size_t>((__attribute__((address_space(3))) const void*)p));
+}
+
+// 16-byte (or 4-byte) buffer load of each lane written straight to LDS at lds_base +
+// lane * size (buffer_load ... lds, base in M0). Issued through inline assembly so that
+// the compiler does not tie later LDS reads of OTHER ring stages to these loads with a
+// conservative vmcnt(0) wait; the kernels order them with explicit vmcnt waits and
+// workgroup barriers instead.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, const void* lds_base, int voffset) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_address(lds_base));  // wave-uniform
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m0), "v"(voffset), "s"(rs)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t rs, const void* lds_base, int voffset) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_address(lds_base));  // wave-uniform
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(m0), "v"(voffset), "s"(rs)
+               : "memory", "m0");
+}
+
+// s_waitcnt immediate for "at most n vector-memory operations outstanding" (gfx9
+// encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their maximum).
+constexpr int vmcnt_imm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
+
 // Per-element mask of one tile's S^T registers (32x32 MFMA layout: lane holds query column
 // l % 32 and, per 32-key block kb, keys kb*32 + 8*(i/4) + 4*hf + i%4 in register i).
 // Visible logits move to the log2 domain (s * cexp + bias * log2 e); hidden ones become
