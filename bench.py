@@ -222,6 +222,20 @@ def bench_config(name, iters=20):
     return res
 
 
+def measured_traffic(kernel_key: str):
+    """HBM bytes per dispatch from the committed counter runs (profiles/traffic.json), or
+    None when the kernel sources changed since those counters were taken."""
+    import hashlib
+    try:
+        rec = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))["kernels"][kernel_key]
+    except (OSError, KeyError, ValueError):
+        return None
+    m = hashlib.sha256()
+    for f in rec["sources"]:
+        m.update(open(os.path.join(ROOT, "masked_flashattention_forward_amd", "csrc", f), "rb").read())
+    return rec["traffic_bytes"] if m.hexdigest() == rec["source_sha256"] else None
+
+
 def copy_calibration(nbytes: int, iters: int):
     """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
     import torch
@@ -237,8 +251,8 @@ def copy_calibration(nbytes: int, iters: int):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--only", default="c3p", help="headline workload name (see synth.CONFIG_NAMES)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true")
@@ -290,7 +304,9 @@ def main():
                    "plan": plan},
         "roofline": {"bound": "mfma", "kernel": "prefill_kernel<bf16,128,64>", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "avg_kernel_us": round(kern_ms * 1e3, 2)},
+                     "traffic": measured_traffic("prefill_kernel<bf16,128,64,causal> c3 prefill")
+                     if args.only == "c3p" else None,
+                     "algorithmic_bytes": algorithmic_bytes(p), "avg_kernel_us": round(kern_ms * 1e3, 2)},
         "parity_sampled": {"max_out_err": eo, "max_lse_err": el},
     }
     del r
@@ -304,7 +320,11 @@ def main():
         line["configs"] = configs
         d = configs["c3d"]
         line["decode"] = {"workload": d["workload"], "value": d["gbs"], "unit": "GB/s",
-                          "frac_hbm_peak": round(d["gbs"] / PEAK_HBM_GBS, 4)}
+                          "frac_hbm_peak": round(d["gbs"] / PEAK_HBM_GBS, 4),
+                          "roofline": {"bound": "hbm", "kernel": "decode_kernel<bf16,128> + lse_merge_kernel",
+                                       "achieved": d["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                       "frac": round(d["gbs"] / PEAK_HBM_GBS, 4),
+                                       "traffic": measured_traffic("decode_kernel<bf16,128,causal> c3 decode")}}
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle)")
         line["cpu_baseline"] = cpu_baseline(p)
