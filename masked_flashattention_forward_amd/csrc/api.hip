@@ -205,8 +205,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
     int32_t* tau = reinterpret_cast<int32_t*>(ws + pl.off_tau);
     int32_t* tmin = reinterpret_cast<int32_t*>(ws + pl.off_tmin);
     what = "top-k selection";
-    e = launch_topk(zero_hold, B * Hkv, Lq, Lk, keep_k, 1, rank, tau, nullptr, st);
-    if (e == hipSuccess) e = launch_tile_min_rank(rank, B * Hkv, Lk, pl.pub.block_n, tmin, st);
+    e = launch_topk(zero_hold, B * Hkv, Lq, Lk, keep_k, 1, rank, tau, nullptr, tmin, pl.pub.block_n, st);
     p.rank = rank; p.tau = tau; p.tile_min_rank = tmin;
   }
   if (e == hipSuccess && pl.pub.mask_summary) {
@@ -241,7 +240,7 @@ int dynamic_mask_topk(const float* zero_hold, int B, int H, int Lq, int Lk, int 
     return fail(MI_ATTN_EINVAL, "zero_hold, rank and tau must not be NULL");
   if (Lk > 65536) return fail(MI_ATTN_EUNSUPPORTED, "Lk must be <= 65536 (got %d)", Lk);
   if (static_cast<double>(B) * H * Lq * ((Lk + 31) / 32) > 2.0e9) return fail(MI_ATTN_EINVAL, "tensor too large");
-  const hipError_t e = launch_topk(zero_hold, B * H, Lq, Lk, keep_k, causal ? 1 : 0, rank, tau, keep_bits,
+  const hipError_t e = launch_topk(zero_hold, B * H, Lq, Lk, keep_k, causal ? 1 : 0, rank, tau, keep_bits, nullptr, 0,
                                    static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "dynamic_mask_topk");
   return MI_ATTN_OK;

@@ -113,10 +113,11 @@ __host__ __device__ inline void key_range(int mask_kind, int window_left, int Lk
 
 // ------------------------------------------------------------------ launchers
 hipError_t launch_row_kernel(const AttnParams& p, int dtype, hipStream_t s);
+// tile_min (optional, [BH, ceil(Lk / block_n)]) receives the smallest rank of each
+// block_n-key tile; block_n must divide 256 and be at most 64.
 hipError_t launch_topk(const float* zh, int BH, int Lq, int Lk, int keep_k, int causal,
-                       int32_t* rank, int32_t* tau, uint32_t* keep_bits, hipStream_t s);
-hipError_t launch_tile_min_rank(const int32_t* rank, int BH, int Lk, int block_n, int32_t* out,
-                                hipStream_t s);
+                       int32_t* rank, int32_t* tau, uint32_t* keep_bits, int32_t* tile_min, int block_n,
+                       hipStream_t s);
 hipError_t launch_mask_summary(const float* mask, int Lq, int Lk, int q_per_block, int block_n,
                                uint8_t* flags, hipStream_t s);
 

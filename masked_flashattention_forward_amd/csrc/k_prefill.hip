@@ -155,7 +155,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
       if (tid < BN) {
         const int key = j0 + tid;
         xrank = key < p.Lk ? p.rank[bgk + key] : 0x7fffffff;
-        xzh = key < p.Lk ? p.zero_hold[bgk + key] : 0.f;
+        xzh = key < p.Lk ? p.zero_hold[bgk + key] * kLog2e : 0.f;
       }
     }
   };
@@ -211,9 +211,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
     // mask (tiles the mask does not cover entirely); masked tiles move to the log2
     // domain here (cm = 1), unmasked ones are scaled inside the exponent (cm = cexp)
     float cm = cexp;
-    if (tile_needs_mask<MK, BN>(p, j0, P0, P1)) {
+    if constexpr (MK == MI_ATTN_MASK_TOPK) {
       const int32_t* xr = reinterpret_cast<const int32_t*>(vs + TL::vBytes);
-      mask_tile<MK, NKB>(sacc, p, j0, hf, pos, i_row, tau_row, cexp, xr, reinterpret_cast<const float*>(xr + BN));
+      const float* xzl = reinterpret_cast<const float*>(xr + BN);
+      if (j0 + BN - 1 > P0)
+        mask_tile_topk<NKB, true>(sacc, j0, hf, pos, tau_row, cexp, xr, xzl);
+      else
+        mask_tile_topk<NKB, false>(sacc, j0, hf, pos, tau_row, cexp, xr, xzl);
+      cm = 1.f;
+    } else if (tile_needs_mask<MK, BN>(p, j0, P0, P1)) {
+      mask_tile<MK, NKB>(sacc, p, j0, hf, pos, i_row, tau_row, cexp, nullptr, nullptr);
       cm = 1.f;
     }
 

@@ -4,11 +4,17 @@
 //
 // Per (batch, KV head):
 //   1. rank: each key's place in the total order (value descending, index ascending).
-//      Keys are packed into 64-bit words (order-preserving value bits << 32 | index) and
-//      sorted in LDS with a bitonic network; an O(Lk^2) counting kernel covers long caches.
+//      Keys are packed into 64-bit words (order-preserving value bits << 32 | index).
+//      Caches of up to 8192 keys: every 512-key chunk is bitonic-sorted by one workgroup
+//      (in registers and wavefront shuffles, LDS only for the cross-wavefront stages),
+//      then each key's rank is the sum over chunks of the number of smaller words, found
+//      by a binary search in the sorted chunks staged in LDS. Longer caches use an
+//      O(Lk^2) counting kernel.
 //   2. tau: per query row, the keep_k-th smallest rank among the row's allowed keys. One
-//      wavefront sweeps a run of consecutive rows holding a bitmap of the ranks seen so
-//      far in registers; the keep_k-th set bit is found with a wavefront prefix count.
+//      wavefront sweeps 32 consecutive rows, holding a bitmap of the ranks seen so far in
+//      registers. Under the causal mask a row allows one key more than the row before,
+//      so tau can only fall: it is found once by a wavefront prefix count and afterwards
+//      moves, when the new key ranks below it, to the largest set rank below the old tau.
 //   3. optional keep bitmask and per-tile minimum rank (tile skipping in attention).
 #include "common.hpp"
 
@@ -16,8 +22,14 @@ namespace mi_attn {
 
 namespace {
 
-constexpr int kSortMax = 8192;       // keys per (b,h) sorted in LDS (64 KiB of u64)
-constexpr int kSortThreads = 1024;
+using u64 = unsigned long long;
+
+constexpr int kChunk = 512;               // keys bitonic-sorted per workgroup
+constexpr int kChunkThreads = kChunk / 2; // two keys per thread
+constexpr int kMergeMaxKeys = 8192;       // sorted chunks of one (b,h) staged in 64 KiB of LDS
+constexpr int kRankThreads = 256;
+constexpr u64 kPadKey = ~0ull;            // above every real key
+constexpr int32_t kAllKept = 0x7fffffff;  // "no threshold" and the rank past the last key
 
 // Ascending order of the returned word == descending order of x; -0.0 ties +0.0.
 __device__ __forceinline__ uint32_t desc_bits(float x) {
@@ -27,134 +39,279 @@ __device__ __forceinline__ uint32_t desc_bits(float x) {
   return ~asc;
 }
 
-__global__ __launch_bounds__(kSortThreads) void rank_sort_kernel(const float* zh, int Lk, int N,
-                                                                   int32_t* rank, int32_t* order) {
-  extern __shared__ unsigned long long skey[];
+// Strictly increasing in the total order; never equal to kPadKey (NaN is excluded).
+__device__ __forceinline__ u64 order_key(const float* z, int j) {
+  return (static_cast<u64>(desc_bits(z[j])) << 32) | static_cast<unsigned>(j);
+}
+
+__device__ __forceinline__ u64 shfl_xor_u64(u64 x, int m) {
+  const int lo = __shfl_xor(static_cast<int>(static_cast<uint32_t>(x)), m, kWave);
+  const int hi = __shfl_xor(static_cast<int>(static_cast<uint32_t>(x >> 32)), m, kWave);
+  return (static_cast<u64>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+}
+
+__device__ __forceinline__ u64 min_u64(u64 a, u64 b) { return a < b ? a : b; }
+__device__ __forceinline__ u64 max_u64(u64 a, u64 b) { return a < b ? b : a; }
+
+// Sorts chunk blockIdx.y of (b,h) = blockIdx.x ascending into sorted[bh][chunk][0..511].
+// Thread t holds elements 2t and 2t+1. In the stage comparing elements i and i^j, pairs
+// with j <= 64 sit in one wavefront (thread distance j/2 <= 32): shuffles. Larger j go
+// through LDS.
+__global__ __launch_bounds__(kChunkThreads) void chunk_sort_kernel(const float* zh, int Lk, int nchunks,
+                                                                     u64* sorted) {
+  __shared__ u64 xch[kChunk];
   const int bh = blockIdx.x;
+  const int c0 = blockIdx.y * kChunk;
   const float* z = zh + static_cast<long>(bh) * Lk;
-  for (int t = threadIdx.x; t < N; t += blockDim.x)
-    skey[t] = (t < Lk) ? ((static_cast<unsigned long long>(desc_bits(z[t])) << 32) | static_cast<unsigned>(t))
-                       : ~0ull;
-  __syncthreads();
-  for (int kk = 2; kk <= N; kk <<= 1) {
-    for (int j = kk >> 1; j > 0; j >>= 1) {
-      for (int t = threadIdx.x; t < N; t += blockDim.x) {
-        const int u = t ^ j;
-        if (u > t) {
-          const unsigned long long a = skey[t], b = skey[u];
-          const bool up = (t & kk) == 0;
-          if ((a > b) == up) { skey[t] = b; skey[u] = a; }
+  const int e0 = 2 * static_cast<int>(threadIdx.x);
+  u64 a = (c0 + e0 < Lk) ? order_key(z, c0 + e0) : kPadKey;
+  u64 b = (c0 + e0 + 1 < Lk) ? order_key(z, c0 + e0 + 1) : kPadKey;
+#pragma unroll
+  for (int k = 2; k <= kChunk; k <<= 1) {
+    const bool up = (e0 & k) == 0;  // this run of k elements sorts ascending
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j == 1) {
+        const u64 lo = min_u64(a, b), hi = max_u64(a, b);
+        a = up ? lo : hi;
+        b = up ? hi : lo;
+      } else {
+        u64 pa, pb;
+        if (j <= 64) {
+          pa = shfl_xor_u64(a, j >> 1);
+          pb = shfl_xor_u64(b, j >> 1);
+        } else {
+          __syncthreads();
+          xch[e0] = a;
+          xch[e0 + 1] = b;
+          __syncthreads();
+          pa = xch[e0 ^ j];
+          pb = xch[(e0 + 1) ^ j];
         }
+        const bool keep_min = ((e0 & j) == 0) == up;
+        a = keep_min ? min_u64(a, pa) : max_u64(a, pa);
+        b = keep_min ? min_u64(b, pb) : max_u64(b, pb);
       }
-      __syncthreads();
     }
   }
-  for (int t = threadIdx.x; t < Lk; t += blockDim.x) {
-    const int idx = static_cast<int>(skey[t] & 0xffffffffu);
-    rank[static_cast<long>(bh) * Lk + idx] = t;
-    order[static_cast<long>(bh) * Lk + t] = idx;
+  u64* dst = sorted + (static_cast<long>(bh) * nchunks + blockIdx.y) * kChunk;
+  dst[e0] = a;
+  dst[e0 + 1] = b;
+}
+
+// rank_j = number of keys before j in the total order = sum over the sorted chunks of the
+// count of words below key_j (branch-free lower bound over 512 entries). When tile_min is
+// given, also the smallest rank of each block_n-key tile (block_n divides kRankThreads).
+__global__ __launch_bounds__(kRankThreads) void rank_merge_kernel(const float* zh, const u64* sorted, int Lk,
+                                                                    int nchunks, int32_t* rank, int32_t* tile_min,
+                                                                    int block_n) {
+  extern __shared__ u64 srt[];
+  __shared__ int32_t rk_s[kRankThreads];
+  const int bh = blockIdx.x;
+  const int n = nchunks * kChunk;
+  const uint4* src = reinterpret_cast<const uint4*>(sorted + static_cast<long>(bh) * n);
+  uint4* dst = reinterpret_cast<uint4*>(srt);
+  for (int t = threadIdx.x; t < n / 2; t += kRankThreads) dst[t] = src[t];
+  __syncthreads();
+  const int j = blockIdx.y * kRankThreads + threadIdx.x;
+  int cnt = kAllKept;
+  if (j < Lk) {
+    const u64 key = order_key(zh + static_cast<long>(bh) * Lk, j);
+    cnt = 0;
+    // four independent searches at a time, so their LDS latencies overlap; chunks past
+    // nchunks are searched in chunk 0 and not counted
+    for (int c = 0; c < nchunks; c += 4) {
+      const u64* s[4];
+      int pos[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        s[u] = srt + (c + u < nchunks ? c + u : 0) * kChunk;
+        pos[u] = 0;
+      }
+#pragma unroll
+      for (int step = kChunk / 2; step > 0; step >>= 1)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (s[u][pos[u] + step - 1] < key) pos[u] += step;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (c + u < nchunks) cnt += pos[u] + (s[u][pos[u]] < key ? 1 : 0);
+    }
+    rank[static_cast<long>(bh) * Lk + j] = cnt;
+  }
+  if (tile_min == nullptr) return;
+  rk_s[threadIdx.x] = cnt;
+  __syncthreads();
+  const int ntiles = (Lk + block_n - 1) / block_n;
+  const int tile = blockIdx.y * (kRankThreads / block_n) + static_cast<int>(threadIdx.x);
+  if (static_cast<int>(threadIdx.x) < kRankThreads / block_n && tile < ntiles) {
+    int32_t mn = kAllKept;
+    for (int e = 0; e < block_n; ++e) {
+      const int32_t r = rk_s[threadIdx.x * block_n + e];
+      mn = r < mn ? r : mn;
+    }
+    tile_min[static_cast<long>(bh) * ntiles + tile] = mn;
   }
 }
 
-// O(Lk^2) rank for caches longer than the LDS sort: rank_j = #keys ordered before j.
-__global__ __launch_bounds__(256) void rank_count_kernel(const float* zh, int Lk, int32_t* rank,
-                                                           int32_t* order) {
-  __shared__ unsigned long long tile[256];
+// O(Lk^2) rank for caches longer than the merge path: rank_j = #keys ordered before j.
+__global__ __launch_bounds__(256) void rank_count_kernel(const float* zh, int Lk, int32_t* rank) {
+  __shared__ u64 tile[256];
   const int bh = blockIdx.x;
   const float* z = zh + static_cast<long>(bh) * Lk;
   const int j = blockIdx.y * 256 + threadIdx.x;
-  const unsigned long long mine =
-      (j < Lk) ? ((static_cast<unsigned long long>(desc_bits(z[j])) << 32) | static_cast<unsigned>(j)) : ~0ull;
+  const u64 mine = (j < Lk) ? order_key(z, j) : kPadKey;
   int cnt = 0;
   for (int m0 = 0; m0 < Lk; m0 += 256) {
     const int m = m0 + threadIdx.x;
-    tile[threadIdx.x] =
-        (m < Lk) ? ((static_cast<unsigned long long>(desc_bits(z[m])) << 32) | static_cast<unsigned>(m)) : ~0ull;
+    tile[threadIdx.x] = (m < Lk) ? order_key(z, m) : kPadKey;
     __syncthreads();
     const int n = (Lk - m0) < 256 ? (Lk - m0) : 256;
     for (int t = 0; t < n; ++t) cnt += (tile[t] < mine) ? 1 : 0;
     __syncthreads();
   }
-  if (j < Lk) {
-    rank[static_cast<long>(bh) * Lk + j] = cnt;
-    order[static_cast<long>(bh) * Lk + cnt] = j;
-  }
+  if (j < Lk) rank[static_cast<long>(bh) * Lk + j] = cnt;
 }
 
-constexpr int kTauRowsPerWave = 64;
+constexpr int kTauRowsPerWave = 32;
+constexpr int kTauWaves = 4;
 
-// WPL = 32-bit bitmap words per lane; one wavefront covers 64 * 32 * WPL ranks.
+// keep_k-th smallest set rank of the wavefront's bitmap (lane l owns ranks
+// [32 * WPL * l, 32 * WPL * (l + 1)) in words[]); the bitmap holds at least keep_k bits.
 template <int WPL>
-__global__ __launch_bounds__(256) void tau_kernel(const int32_t* rank, const int32_t* order, int Lq,
-                                                    int Lk, int keep_k, int32_t* tau) {
-  const int bh = blockIdx.x;
-  const int wave = threadIdx.x / kWave;
-  const int lane = threadIdx.x % kWave;
-  const int r0 = (blockIdx.y * 4 + wave) * kTauRowsPerWave;
-  if (r0 >= Lq) return;
-  const int r1 = (r0 + kTauRowsPerWave) < Lq ? (r0 + kTauRowsPerWave) : Lq;
-  const int32_t* rk = rank + static_cast<long>(bh) * Lk;
-  const int32_t* od = order + static_cast<long>(bh) * Lk;
-  const int base = lane * 32 * WPL;  // first rank owned by this lane
+__device__ __forceinline__ int kth_set_rank(const uint32_t (&words)[WPL], int keep_k, int lane) {
+  int c = 0;
+#pragma unroll
+  for (int w = 0; w < WPL; ++w) c += __popc(words[w]);
+  int incl = c;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += y;
+  }
+  const int excl = incl - c;
+  const bool here = excl < keep_k && keep_k <= incl;
+  int found = 0;
+  if (here) {
+    int need = keep_k - excl;
+#pragma unroll
+    for (int w = 0; w < WPL; ++w) {
+      const int pc = __popc(words[w]);
+      if (need > 0 && need <= pc) {
+        uint32_t x = words[w];
+        for (int t = 1; t < need; ++t) x &= x - 1;
+        found = (lane * WPL + w) * 32 + (__ffs(x) - 1);
+      }
+      need -= pc;
+    }
+  }
+  const int src = __ffsll(static_cast<unsigned long long>(__ballot(here))) - 1;
+  return __builtin_amdgcn_readlane(found, src);
+}
 
-  // bitmap of the ranks of keys 0 .. pos(r0) - 1
-  const int pos0 = Lk - Lq + r0;
-  uint32_t words[WPL];
+// Largest set rank below t; the bitmap holds at least one.
+template <int WPL>
+__device__ __forceinline__ int set_rank_below(const uint32_t (&words)[WPL], int t, int lane) {
+  int cand = -1;
 #pragma unroll
   for (int w = 0; w < WPL; ++w) {
-    uint32_t x = 0;
-    for (int bit = 0; bit < 32; ++bit) {
-      const int r = base + w * 32 + bit;
-      if (r < Lk && od[r] < pos0) x |= 1u << bit;
-    }
-    words[w] = x;
+    const int base = (lane * WPL + w) * 32;
+    const int lim = t - base;
+    const uint32_t keep = lim >= 32 ? ~0u : (lim <= 0 ? 0u : ((1u << lim) - 1u));
+    const uint32_t x = words[w] & keep;
+    if (x != 0) cand = base + 31 - __clz(x);
   }
+  const unsigned long long b = __ballot(cand >= 0);
+  const int src = 63 - __clzll(b);
+  return __builtin_amdgcn_readlane(cand, src);
+}
 
-  for (int i = r0; i < r1; ++i) {
-    const int pos = Lk - Lq + i;
-    if (pos >= 0) {
-      const int r = rk[pos];
-      if (r >= base && r < base + 32 * WPL) {
-        const int w = (r - base) >> 5;
+// Causal tau. WPL = 32-bit bitmap words per lane; one wavefront covers 64 * 32 * WPL ranks.
+// Workgroup = 4 wavefronts = 128 consecutive rows of one (b,h). Every global load of the
+// kernel is issued before the first barrier, so their latencies overlap.
+template <int WPL>
+__global__ __launch_bounds__(kTauWaves * kWave) void tau_kernel(const int32_t* rank, int Lq, int Lk, int keep_k,
+                                                                  int32_t* tau) {
+  constexpr int NW = kWave * WPL;
+  constexpr int kThreads = kTauWaves * kWave;
+  constexpr int kBuild = (8 * WPL) < 16 ? (8 * WPL) : 16;  // keys per thread per pass of the shared bitmap
+  __shared__ uint32_t block_bm[NW];
+  __shared__ uint32_t wave_bm[kTauWaves][NW];
+  const int bh = blockIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: scalar branches below
+  const int lane = threadIdx.x % kWave;
+  const int32_t* rk = rank + static_cast<long>(bh) * Lk;
+  const int rb = blockIdx.y * kTauWaves * kTauRowsPerWave;  // first row of the workgroup (< Lq)
+  const int pos_b = Lk - Lq + rb;                            // keys [0, pos_b) precede it (pos_b < Lk)
+  const int r0 = rb + wave * kTauRowsPerWave;
+  const int pos_w = pos_b + wave * kTauRowsPerWave;          // keys [0, pos_w) precede row r0
+  const int n = r0 < Lq ? ((Lq - r0) < kTauRowsPerWave ? (Lq - r0) : kTauRowsPerWave) : 0;
+
+  for (int w = threadIdx.x; w < NW; w += kThreads) block_bm[w] = 0;
+  // shared part: keys [0, pos_b), kBuild * kThreads of them per pass
+  int br[kBuild];
 #pragma unroll
-        for (int t = 0; t < WPL; ++t)
-          if (t == w) words[t] |= 1u << (r & 31);
-      }
-    }
-    const int n_allowed = pos + 1;  // pos <= Lk - 1 always
-    if (n_allowed <= keep_k) {
-      if (lane == 0) tau[static_cast<long>(bh) * Lq + i] = 0x7fffffff;
-      continue;
-    }
-    int c = 0;
+  for (int u = 0; u < kBuild; ++u) {
+    const int t = u * kThreads + static_cast<int>(threadIdx.x);
+    br[u] = t < pos_b ? rk[t] : -1;
+  }
+  // this wavefront's part: keys [max(pos_b, 0), pos_w), at most (kTauWaves - 1) * kTauRowsPerWave
+  constexpr int kExtra = ((kTauWaves - 1) * kTauRowsPerWave + kWave - 1) / kWave;
+  int xr[kExtra];
+  const int x0 = pos_b > 0 ? pos_b : 0;
+  const int x_end = n > 0 ? pos_w : 0;
 #pragma unroll
-    for (int w = 0; w < WPL; ++w) c += __popc(words[w]);
-    int incl = c;
+  for (int u = 0; u < kExtra; ++u) {
+    const int t = x0 + u * kWave + lane;
+    xr[u] = t < x_end ? rk[t] : -1;
+  }
+  // the key each row adds: lane i holds the rank of key p_{r0 + i}
+  const int my_pos = pos_w + lane;
+  const int my_rank = (lane < n && my_pos >= 0) ? rk[my_pos] : -1;
+  __syncthreads();
+  for (int t0 = 0;;) {
 #pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int y = __shfl_up(incl, o, kWave);
-      if (lane >= o) incl += y;
-    }
-    const int excl = incl - c;
-    if (excl < keep_k && keep_k <= incl) {
-      int need = keep_k - excl;
-      int found = -1;
+    for (int u = 0; u < kBuild; ++u)
+      if (br[u] >= 0) atomicOr(&block_bm[br[u] >> 5], 1u << (br[u] & 31));
+    t0 += kBuild * kThreads;
+    if (t0 >= pos_b) break;
 #pragma unroll
-      for (int w = 0; w < WPL; ++w) {
-        const int pc = __popc(words[w]);
-        if (found < 0) {
-          if (need <= pc) {
-            uint32_t x = words[w];
-            for (int t = 1; t < need; ++t) x &= x - 1;
-            found = base + w * 32 + (__ffs(x) - 1);
-          } else {
-            need -= pc;
-          }
-        }
-      }
-      tau[static_cast<long>(bh) * Lq + i] = found;
+    for (int u = 0; u < kBuild; ++u) {
+      const int t = t0 + u * kThreads + static_cast<int>(threadIdx.x);
+      br[u] = t < pos_b ? rk[t] : -1;
     }
   }
+  __syncthreads();
+  for (int w = lane; w < NW; w += kWave) wave_bm[wave][w] = block_bm[w];
+#pragma unroll
+  for (int u = 0; u < kExtra; ++u)
+    if (xr[u] >= 0) atomicOr(&wave_bm[wave][xr[u] >> 5], 1u << (xr[u] & 31));
+  __syncthreads();
+  if (n == 0) return;
+
+  uint32_t words[WPL];
+#pragma unroll
+  for (int w = 0; w < WPL; ++w) words[w] = wave_bm[wave][lane * WPL + w];
+  int my_tau = kAllKept;
+  int cur = kAllKept;  // kAllKept until the rows allow more than keep_k keys
+  for (int i = 0; i < n; ++i) {
+    const int r = __builtin_amdgcn_readlane(my_rank, i);
+    if (r >= 0) {
+      const int owner = r / (32 * WPL);
+      const int wi = (r >> 5) - owner * WPL;
+      if (lane == owner) {
+#pragma unroll
+        for (int w = 0; w < WPL; ++w)
+          if (w == wi) words[w] |= 1u << (r & 31);
+      }
+    }
+    const int allowed = pos_w + i + 1;  // keys 0 .. p_i
+    if (allowed <= keep_k) cur = kAllKept;
+    else if (cur == kAllKept) cur = kth_set_rank<WPL>(words, keep_k, lane);
+    else if (r < cur) cur = set_rank_below<WPL>(words, cur, lane);
+    if (lane == i) my_tau = cur;
+  }
+  if (lane < n) tau[static_cast<long>(bh) * Lq + r0 + lane] = my_tau;
 }
 
 __global__ void tau_const_kernel(int n, int32_t value, int32_t* tau) {
@@ -183,19 +340,22 @@ __global__ void keep_bits_kernel(const int32_t* rank, const int32_t* tau, int BH
   bits[t] = x;
 }
 
-__global__ void tile_min_rank_kernel(const int32_t* rank, int BH, int Lk, int block_n, int32_t* out) {
+// One wavefront per tile of block_n <= 64 keys: the smallest rank in it.
+__global__ __launch_bounds__(256) void tile_min_rank_kernel(const int32_t* rank, int BH, int Lk, int block_n,
+                                                              int32_t* out) {
   const int nt = (Lk + block_n - 1) / block_n;
-  const long t = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const long t = static_cast<long>(blockIdx.x) * 4 + threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
   if (t >= static_cast<long>(BH) * nt) return;
   const long bh = t / nt;
-  const int j0 = static_cast<int>(t % nt) * block_n;
-  const int j1 = (j0 + block_n) < Lk ? (j0 + block_n) : Lk;
-  int32_t mn = 0x7fffffff;
-  for (int j = j0; j < j1; ++j) {
-    const int32_t r = rank[bh * Lk + j];
-    mn = r < mn ? r : mn;
+  const int j = static_cast<int>(t % nt) * block_n + lane;
+  int32_t mn = (lane < block_n && j < Lk) ? rank[bh * Lk + j] : kAllKept;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const int32_t y = __shfl_xor(mn, o, kWave);
+    mn = y < mn ? y : mn;
   }
-  out[t] = mn;
+  if (lane == 0) out[t] = mn;
 }
 
 // One wavefront per (query block, key tile): flag = 1 iff some entry is above -inf.
@@ -225,36 +385,48 @@ __global__ __launch_bounds__(256) void mask_summary_kernel(const float* mask, in
 }  // namespace
 
 hipError_t launch_topk(const float* zh, int BH, int Lq, int Lk, int keep_k, int causal, int32_t* rank,
-                       int32_t* tau, uint32_t* keep_bits, hipStream_t s) {
-  // `order` (the inverse permutation) lives in a stream-ordered scratch buffer.
-  int32_t* order = nullptr;
-  hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&order), sizeof(int32_t) * static_cast<size_t>(BH) * Lk, s);
-  if (e != hipSuccess) return e;
-  if (Lk <= kSortMax) {
-    int N = 1;
-    while (N < Lk) N <<= 1;
-    const int threads = N < kSortThreads ? (N < 64 ? 64 : N) : kSortThreads;
-    hipLaunchKernelGGL(rank_sort_kernel, dim3(BH), dim3(threads), sizeof(unsigned long long) * N, s, zh, Lk, N,
-                       rank, order);
+                       int32_t* tau, uint32_t* keep_bits, int32_t* tile_min, int block_n, hipStream_t s) {
+  if (tile_min != nullptr && (block_n <= 0 || block_n > kWave || kRankThreads % block_n != 0))
+    return hipErrorInvalidValue;
+  hipError_t e = hipSuccess;
+  if (Lk <= kMergeMaxKeys) {
+    // sorted chunks live in a stream-ordered scratch buffer
+    const int nchunks = (Lk + kChunk - 1) / kChunk;
+    u64* sorted = nullptr;
+    e = hipMallocAsync(reinterpret_cast<void**>(&sorted), sizeof(u64) * static_cast<size_t>(BH) * nchunks * kChunk, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(chunk_sort_kernel, dim3(BH, nchunks), dim3(kChunkThreads), 0, s, zh, Lk, nchunks, sorted);
+    hipLaunchKernelGGL(rank_merge_kernel, dim3(BH, (Lk + kRankThreads - 1) / kRankThreads), dim3(kRankThreads),
+                       sizeof(u64) * nchunks * kChunk, s, zh, sorted, Lk, nchunks, rank, tile_min, block_n);
+    e = hipGetLastError();
+    const hipError_t ef = hipFreeAsync(sorted, s);
+    if (e == hipSuccess) e = ef;
   } else {
-    hipLaunchKernelGGL(rank_count_kernel, dim3(BH, (Lk + 255) / 256), dim3(256), 0, s, zh, Lk, rank, order);
+    hipLaunchKernelGGL(rank_count_kernel, dim3(BH, (Lk + 255) / 256), dim3(256), 0, s, zh, Lk, rank);
+    e = hipGetLastError();
+    if (e == hipSuccess && tile_min != nullptr) {
+      const long n = static_cast<long>(BH) * ((Lk + block_n - 1) / block_n);
+      hipLaunchKernelGGL(tile_min_rank_kernel, dim3(static_cast<unsigned>((n + 3) / 4)), dim3(256), 0, s, rank, BH,
+                         Lk, block_n, tile_min);
+      e = hipGetLastError();
+    }
   }
-  e = hipGetLastError();
   if (e == hipSuccess) {
     if (!causal) {
-      const int32_t v = (Lk > keep_k) ? keep_k - 1 : 0x7fffffff;
+      const int32_t v = (Lk > keep_k) ? keep_k - 1 : kAllKept;
       const long n = static_cast<long>(BH) * Lq;
       hipLaunchKernelGGL(tau_const_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
                          static_cast<int>(n), v, tau);
     } else {
-      dim3 grid(BH, (Lq + 4 * kTauRowsPerWave - 1) / (4 * kTauRowsPerWave));
+      const dim3 grid(BH, (Lq + kTauWaves * kTauRowsPerWave - 1) / (kTauWaves * kTauRowsPerWave));
+      const dim3 block(kTauWaves * kWave);
       const int wpl = (Lk + 64 * 32 - 1) / (64 * 32);
-      if (wpl <= 1) hipLaunchKernelGGL(tau_kernel<1>, grid, dim3(256), 0, s, rank, order, Lq, Lk, keep_k, tau);
-      else if (wpl <= 2) hipLaunchKernelGGL(tau_kernel<2>, grid, dim3(256), 0, s, rank, order, Lq, Lk, keep_k, tau);
-      else if (wpl <= 4) hipLaunchKernelGGL(tau_kernel<4>, grid, dim3(256), 0, s, rank, order, Lq, Lk, keep_k, tau);
-      else if (wpl <= 8) hipLaunchKernelGGL(tau_kernel<8>, grid, dim3(256), 0, s, rank, order, Lq, Lk, keep_k, tau);
-      else if (wpl <= 16) hipLaunchKernelGGL(tau_kernel<16>, grid, dim3(256), 0, s, rank, order, Lq, Lk, keep_k, tau);
-      else hipLaunchKernelGGL(tau_kernel<32>, grid, dim3(256), 0, s, rank, order, Lq, Lk, keep_k, tau);
+      if (wpl <= 1) hipLaunchKernelGGL(tau_kernel<1>, grid, block, 0, s, rank, Lq, Lk, keep_k, tau);
+      else if (wpl <= 2) hipLaunchKernelGGL(tau_kernel<2>, grid, block, 0, s, rank, Lq, Lk, keep_k, tau);
+      else if (wpl <= 4) hipLaunchKernelGGL(tau_kernel<4>, grid, block, 0, s, rank, Lq, Lk, keep_k, tau);
+      else if (wpl <= 8) hipLaunchKernelGGL(tau_kernel<8>, grid, block, 0, s, rank, Lq, Lk, keep_k, tau);
+      else if (wpl <= 16) hipLaunchKernelGGL(tau_kernel<16>, grid, block, 0, s, rank, Lq, Lk, keep_k, tau);
+      else hipLaunchKernelGGL(tau_kernel<32>, grid, block, 0, s, rank, Lq, Lk, keep_k, tau);
     }
     e = hipGetLastError();
   }
@@ -264,15 +436,7 @@ hipError_t launch_topk(const float* zh, int BH, int Lq, int Lk, int keep_k, int 
                        tau, BH, Lq, Lk, causal, keep_bits);
     e = hipGetLastError();
   }
-  const hipError_t ef = hipFreeAsync(order, s);
-  return e != hipSuccess ? e : ef;
-}
-
-hipError_t launch_tile_min_rank(const int32_t* rank, int BH, int Lk, int block_n, int32_t* out, hipStream_t s) {
-  const long n = static_cast<long>(BH) * ((Lk + block_n - 1) / block_n);
-  hipLaunchKernelGGL(tile_min_rank_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, rank, BH,
-                     Lk, block_n, out);
-  return hipGetLastError();
+  return e;
 }
 
 hipError_t launch_mask_summary(const float* mask, int Lq, int Lk, int q_per_block, int block_n, uint8_t* flags,

@@ -157,6 +157,35 @@ __device__ __forceinline__ void mask_tile(f32x16_t* sacc, const AttnParams& p, i
   }
 }
 
+// Top-k mask of one tile whose side data sits in LDS, padded to the full tile:
+// xr[k] = rank of key j0 + k (INT32_MAX past Lk) and xzl[k] = its zero_hold times log2(e)
+// (0 past Lk). A key stays when its rank is at most the row's threshold; kDiag tiles
+// (reaching past the block's first query position) also hide keys after the row's own
+// position, which covers every key past Lk. Results are in the log2 domain.
+template <int NKB, bool kDiag>
+__device__ __forceinline__ void mask_tile_topk(f32x16_t* sacc, int j0, int hf, int pos, int32_t tau_row,
+                                               float cexp, const int32_t* xr, const float* xzl) {
+  const int lim = pos - j0;  // keys kk <= lim are at or before the row's position
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int kk = kb * 32 + r4 * 8 + hf * 4;  // first of 4 consecutive keys in the tile
+      const int4 rk = *reinterpret_cast<const int4*>(xr + kk);
+      const float4 zl = *reinterpret_cast<const float4*>(xzl + kk);
+      const int rks[4] = {rk.x, rk.y, rk.z, rk.w};
+      const float zs[4] = {zl.x, zl.y, zl.z, zl.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        bool vis = rks[e] <= tau_row;
+        if constexpr (kDiag) vis = vis && kk + e <= lim;
+        const float s = fmaf(sacc[kb][r4 * 4 + e], cexp, zs[e]);
+        sacc[kb][r4 * 4 + e] = vis ? s : kNegInf;
+      }
+    }
+  }
+}
+
 // Whether a tile [j0, j0 + BN) needs per-element masking for a block whose query rows sit
 // at positions P0..P1: tiles every row sees entirely (and inside Lk) skip it.
 template <int MK, int BN>
