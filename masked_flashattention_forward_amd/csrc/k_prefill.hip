@@ -195,17 +195,31 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
     const unsigned char* vs = ks + TL::kBytes;
     const int j0 = t * BN;
 
-    // S^T = K Q^T
+    // S^T = K Q^T. The first 32-key block's K fragments are read before its first MFMA;
+    // afterwards each MFMA overlaps the read of one fragment of the next block.
     f32x16_t sacc[NKB];
+    {
+      constexpr int NDC = D / 16;
+      u32x4_t kf[NKB][NDC];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      f32x16_t acc = f32x16_t{};
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int dc = 0; dc < D / 16; ++dc) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(ks + tile_off<D>(kb * 32 + l32, dc * 2 + hf));
-        acc = mfma32(T{}, a, qreg[dc], acc);
+        for (int dc = 0; dc < NDC; ++dc)
+          kf[kb][dc] = *reinterpret_cast<const u32x4_t*>(ks + tile_off<D>(kb * 32 + l32, dc * 2 + hf));
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        f32x16_t acc = f32x16_t{};
+#pragma unroll
+        for (int dc = 0; dc < NDC; ++dc) acc = mfma32(T{}, kf[kb][dc], qreg[dc], acc);
+        sacc[kb] = acc;
       }
-      sacc[kb] = acc;
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NDC, 0);
+#pragma unroll
+      for (int i = 0; i < (NKB - 1) * NDC; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, NDC, 0);
     }
 
     // mask (tiles the mask does not cover entirely); masked tiles move to the log2
@@ -265,20 +279,35 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
     // O^T += V^T P^T. The V^T operand comes from two transposed reads: lane (16 * g + i)
     // reads 8 bytes of key row R0 + i / 4 at dims D0 + 4 * (i % 4) and receives keys
     // R0..R0+3 of dim D0 + i. Keys 4*hf+0..3 and 8+4*hf+0..3 of the 16-key chunk are what
-    // its P registers hold.
-    const int tr_row = 4 * hf + (lane & 15) / 4;
-    const int tr_dim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    // its P registers hold. Key chunks run outermost, so the NDB accumulators are
+    // independent chains, and the next chunk's V fragments are read during this chunk's
+    // MFMAs.
+    {
+      const int tr_row = 4 * hf + (lane & 15) / 4;
+      const int tr_dim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      constexpr int NKC = BN / 16;
+      u32x4_t vf[NKC][NDB];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+      for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
-      for (int kc = 0; kc < BN / 16; ++kc) {
-        const int d0 = db * 32 + tr_dim;
-        const int r0 = kc * 16 + tr_row;
-        const u32x2_t lo = lds_read_tr16(vs + tile_off<D>(r0, d0 >> 3) + ((d0 & 7) << 1));
-        const u32x2_t hi2 = lds_read_tr16(vs + tile_off<D>(r0 + 8, d0 >> 3) + ((d0 & 7) << 1));
-        const u32x4_t a = {lo.x, lo.y, hi2.x, hi2.y};
-        oacc[db] = mfma32(T{}, a, preg[kc], oacc[db]);
+        for (int db = 0; db < NDB; ++db) {
+          const int d0 = db * 32 + tr_dim;
+          const int r0 = kc * 16 + tr_row;
+          const u32x2_t lo = lds_read_tr16(vs + tile_off<D>(r0, d0 >> 3) + ((d0 & 7) << 1));
+          const u32x2_t hi2 = lds_read_tr16(vs + tile_off<D>(r0 + 8, d0 >> 3) + ((d0 & 7) << 1));
+          vf[kc][db] = u32x4_t{lo.x, lo.y, hi2.x, hi2.y};
+        }
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(T{}, vf[kc][db], preg[kc], oacc[db]);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * NDB, 0);
+#pragma unroll
+      for (int i = 0; i < (NKC - 1) * NDB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, NDB, 0);
     }
 
     if (tn < t_hi) finish_tile(stage ^ 1);

@@ -78,6 +78,11 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const unsigned char* p) {
   return __builtin_bit_cast(u32x2_t, v);
 }
 
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
 // The running max only moves when a row's maximum grows by more than 2^8 (log2 units).
 // Between moves, p = exp2(s - m) stays below 2^8, which fp32 sums and 16-bit P hold
 // without loss of relative precision; l and the output use the same m, so the result is
