@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * TL::stage];
 
   const int tid = threadIdx.x;
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform, so wave-derived values stay scalar
   const int lane = tid % kWave;
   const int l32 = lane & 31;
   const int hf = lane >> 5;  // lane half
@@ -133,23 +133,29 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
 
   // ---- tile loads straight into LDS (buffer_load ... lds): each wave instruction fills
   // 1 KB of the tile; lane i of it takes the global 16-byte chunk that belongs in slot i
-  // of the swizzled layout. Rows at or past Lk read as zeros (buffer range check).
+  // of the swizzled layout. Rows at or past Lk read as zeros (buffer range check). A
+  // lane's swizzle does not depend on the load round, so its global offset is one
+  // loop-invariant register plus a wave-uniform (scalar) offset for the tile and round.
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(K, p.Lk * D * 2);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V, p.Lk * D * 2);
+  int dma_lane;
+  {
+    const int r = wave * TL::rowsPerWaveLoad + lane / (D / 8);
+    const int ps = lane % (D / 8);                   // physical slot this lane fills
+    dma_lane = (r * D + ((ps ^ swz<D>(r)) << 3)) * 2;
+  }
+  const unsigned smem_addr = __builtin_amdgcn_readfirstlane(lds_address(smem));
   int32_t xrank = 0;
   float xzh = 0.f;
   auto issue_tile = [&](int t, int stg) {
     const int j0 = t * BN;
-    unsigned char* kst = smem + stg * TL::stage;
-    unsigned char* vst = kst + TL::kBytes;
+    const unsigned kst = smem_addr + stg * TL::stage;
 #pragma unroll
     for (int c = 0; c < TL::loadRounds; ++c) {
-      const int blk = c * kWaves + wave;             // 1 KB block of the tile
-      const int r = blk * TL::rowsPerWaveLoad + lane / (D / 8);
-      const int ps = lane % (D / 8);                 // physical slot this lane fills
-      const int gofs = ((j0 + r) * D + ((ps ^ swz<D>(r)) << 3)) * 2;
-      lds_dma16(krs, kst + blk * 1024, gofs);
-      lds_dma16(vrs, vst + blk * 1024, gofs);
+      const unsigned blk = (c * kWaves + wave) * 1024;  // 1 KB block of the tile
+      const int so = (j0 + c * kWaves * TL::rowsPerWaveLoad) * D * 2;
+      lds_dma16_at(krs, kst + blk, dma_lane, so);
+      lds_dma16_at(vrs, kst + TL::kBytes + blk, dma_lane, so);
     }
     if constexpr (MK == MI_ATTN_MASK_TOPK) {
       if (tid < BN) {
@@ -169,6 +175,22 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
   };
+
+  // ---- LDS operand addresses. Slot s of row r sits at ((s ^ swz(r)) << 4) in the row;
+  // the swizzle bits of the rows a lane reads do not change with the 32-key block (K) or
+  // the 16-key chunk (V), and the dim chunk enters as a plain XOR: a K fragment is at
+  // kb * 32 * rowBytes + (k_base ^ (dc << 5)), a V^T fragment at
+  // kc * 16 * rowBytes + (v_base[h] ^ (db << 6)). Stage offsets are multiples of 512
+  // bytes and leave the XOR-ed address bits alone.
+  int k_base, v_base0, v_base1;
+  {
+    k_base = l32 * TL::rowBytes | ((hf ^ swz<D>(l32)) << 4);
+    const int tr_row = 4 * hf + (lane & 15) / 4;
+    const int sl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    v_base0 = tr_row * TL::rowBytes | ((sl ^ swz<D>(tr_row)) << 4) | (8 * (lane & 1));
+    v_base1 = (tr_row + 8) * TL::rowBytes | ((sl ^ swz<D>(tr_row + 8)) << 4) | (8 * (lane & 1));
+  }
+  static_assert(TL::stage % 512 == 0 && TL::kBytes % 512 == 0, "stage offsets keep the XOR-ed address bits");
 
   // ---- running state
   constexpr int NKB = BN / 32;  // 32-key blocks per tile
@@ -191,8 +213,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
     const int tn = next_live(t + 1);
     if (tn < t_hi) issue_tile(tn, stage ^ 1);  // lands in the other stage while this tile computes
 
-    const unsigned char* ks = smem + stage * TL::stage;
-    const unsigned char* vs = ks + TL::kBytes;
+    const int ks_ofs = stage * TL::stage;
+    const int vs_ofs = ks_ofs + TL::kBytes;
+    const unsigned char* vs = smem + vs_ofs;
     const int j0 = t * BN;
 
     // S^T = K Q^T. The first 32-key block's K fragments are read before its first MFMA;
@@ -205,7 +228,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int dc = 0; dc < NDC; ++dc)
-          kf[kb][dc] = *reinterpret_cast<const u32x4_t*>(ks + tile_off<D>(kb * 32 + l32, dc * 2 + hf));
+          kf[kb][dc] = *reinterpret_cast<const u32x4_t*>(smem + kb * 32 * TL::rowBytes +
+                                                         ((k_base + ks_ofs) ^ (dc << 5)));
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         f32x16_t acc = f32x16_t{};
@@ -283,18 +307,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
     // independent chains, and the next chunk's V fragments are read during this chunk's
     // MFMAs.
     {
-      const int tr_row = 4 * hf + (lane & 15) / 4;
-      const int tr_dim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
       constexpr int NKC = BN / 16;
+      const int vb0 = v_base0 + vs_ofs, vb1 = v_base1 + vs_ofs;
       u32x4_t vf[NKC][NDB];
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const int d0 = db * 32 + tr_dim;
-          const int r0 = kc * 16 + tr_row;
-          const u32x2_t lo = lds_read_tr16(vs + tile_off<D>(r0, d0 >> 3) + ((d0 & 7) << 1));
-          const u32x2_t hi2 = lds_read_tr16(vs + tile_off<D>(r0 + 8, d0 >> 3) + ((d0 & 7) << 1));
+          const unsigned char* row = smem + kc * 16 * TL::rowBytes;
+          const u32x2_t lo = lds_read_tr16(row + (vb0 ^ (db << 6)));
+          const u32x2_t hi2 = lds_read_tr16(row + (vb1 ^ (db << 6)));
           vf[kc][db] = u32x4_t{lo.x, lo.y, hi2.x, hi2.y};
         }
 #pragma unroll

@@ -115,11 +115,15 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, const void*
                : "s"(m0), "v"(voffset), "s"(rs)
                : "memory", "m0");
 }
-__device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t rs, const void* lds_base, int voffset) {
-  const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_address(lds_base));  // wave-uniform
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+// The same with the LDS destination given as a 32-bit LDS byte address and a
+// wave-uniform byte offset added to every lane's voffset (soffset).
+__device__ __forceinline__ void lds_dma16_at(__amdgpu_buffer_rsrc_t rs, unsigned lds_addr, int voffset,
+                                             int soffset) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_addr);
+  const int so = __builtin_amdgcn_readfirstlane(soffset);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
-               : "s"(m0), "v"(voffset), "s"(rs)
+               : "s"(m0), "v"(voffset), "s"(rs), "s"(so)
                : "memory", "m0");
 }
 
