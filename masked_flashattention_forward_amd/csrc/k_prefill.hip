@@ -46,8 +46,13 @@ struct Tile {
   static_assert(BN <= kThreads, "one top-k side entry per thread");
 };
 
+// resident workgroups per CU: LDS allows 2 for d = 128 and 4 for d = 64; the top-k
+// variant's extra state keeps d = 64 at 2 (4 would cap it at 128 VGPRs)
+template <int D, int MK>
+constexpr int kMinBlocks = (D == 64 && MK != MI_ATTN_MASK_TOPK) ? 4 : 2;
+
 template <typename T, int D, int BN, int MK>
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
+__global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK>)) void prefill_kernel(AttnParams p) {
   using TL = Tile<D, BN>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * TL::stage];
 
