@@ -73,7 +73,17 @@ struct Plan {
   attn_plan_t pub;
   int q_per_block;     // query positions per workgroup (dense-mask summary granularity)
   size_t off_rank, off_tau, off_tmin, off_flags, off_pout, off_plse;
+  int list_cap;        // top-k gathered form: entries per kept-key list (0 when not used)
+  size_t off_lidx, off_lrank, off_lzh, off_lcnt;
 };
+
+// Top-k on the prefill path: attend over per-block kept-key lists (at most keep_k +
+// q_per_block - 1 keys each) instead of every causal tile, when the lists are clearly
+// shorter than the key range.
+int topk_list_cap(int keep_k, int q_per_block, int Lk) {
+  const long cap = ((static_cast<long>(keep_k) + q_per_block + 63) / 64) * 64;
+  return (cap * 4 <= static_cast<long>(Lk) * 3) ? static_cast<int>(cap) : 0;
+}
 
 int make_plan(const Shape& s, Plan* pl) {
   *pl = Plan{};
@@ -115,6 +125,14 @@ int make_plan(const Shape& s, Plan* pl) {
     pl->off_rank = off; off = align256(off + sizeof(int32_t) * bh * s.Lk);
     pl->off_tau = off;  off = align256(off + sizeof(int32_t) * bh * s.Lq);
     pl->off_tmin = off; off = align256(off + sizeof(int32_t) * bh * ((s.Lk + p.block_n - 1) / p.block_n));
+    if (path == 1 && !g_no_skip) pl->list_cap = topk_list_cap(s.keep_k, pl->q_per_block, s.Lk);
+    if (pl->list_cap > 0) {
+      const size_t nl = static_cast<size_t>(bh) * ((s.Lq + pl->q_per_block - 1) / pl->q_per_block);
+      pl->off_lidx = off;  off = align256(off + sizeof(int32_t) * nl * pl->list_cap);
+      pl->off_lrank = off; off = align256(off + sizeof(int32_t) * nl * pl->list_cap);
+      pl->off_lzh = off;   off = align256(off + sizeof(float) * nl * pl->list_cap);
+      pl->off_lcnt = off;  off = align256(off + sizeof(int32_t) * nl);
+    }
   }
   if (s.mask_kind == MI_ATTN_MASK_DENSE && path != 0) {
     p.mask_summary = 1;
@@ -192,8 +210,10 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
   p.no_skip = g_no_skip;
   p.splits = pl.pub.splits;
   {
-    const int tiles = (Lk + pl.pub.block_n - 1) / pl.pub.block_n;
-    p.keys_per_split = ((tiles + pl.pub.splits - 1) / pl.pub.splits) * pl.pub.block_n;
+    // split boundaries fall on tiles of the key range (or of the kept-key list)
+    const int tiles = pl.list_cap > 0 ? pl.list_cap / 64 : (Lk + pl.pub.block_n - 1) / pl.pub.block_n;
+    const int unit = pl.list_cap > 0 ? 64 : pl.pub.block_n;
+    p.keys_per_split = ((tiles + pl.pub.splits - 1) / pl.pub.splits) * unit;
   }
   p.block_n = pl.pub.block_n;
   p.q_per_block = pl.q_per_block;
@@ -207,6 +227,17 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
     what = "top-k selection";
     e = launch_topk(zero_hold, B * Hkv, Lq, Lk, keep_k, 1, rank, tau, nullptr, tmin, pl.pub.block_n, st);
     p.rank = rank; p.tau = tau; p.tile_min_rank = tmin;
+    if (e == hipSuccess && pl.list_cap > 0) {
+      int32_t* lidx = reinterpret_cast<int32_t*>(ws + pl.off_lidx);
+      int32_t* lrank = reinterpret_cast<int32_t*>(ws + pl.off_lrank);
+      float* lzh = reinterpret_cast<float*>(ws + pl.off_lzh);
+      int32_t* lcnt = reinterpret_cast<int32_t*>(ws + pl.off_lcnt);
+      what = "top-k kept-key lists";
+      e = launch_topk_lists(rank, tau, zero_hold, B * Hkv, Lq, Lk, pl.q_per_block, pl.list_cap, lidx, lrank, lzh,
+                            lcnt, st);
+      p.list_idx = lidx; p.list_rank = lrank; p.list_zh = lzh; p.list_count = lcnt;
+      p.list_cap = pl.list_cap;
+    }
   }
   if (e == hipSuccess && pl.pub.mask_summary) {
     uint8_t* flags = reinterpret_cast<uint8_t*>(ws + pl.off_flags);

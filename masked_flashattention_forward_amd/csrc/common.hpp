@@ -76,6 +76,13 @@ struct AttnParams {
   const int32_t* tau;      // top-k: [B, Hkv, Lq]
   const int32_t* tile_min_rank;  // top-k: [B, Hkv, ceil(Lk / block_n)]
   const uint8_t* tile_live;      // dense: [ceil(Lq / q_per_block), ceil(Lk / block_n)]
+  // top-k, gathered form (prefill): per (b, KV head, query block) the keys any row of the
+  // block keeps, ascending, padded to whole 64-key tiles; list_idx == nullptr when unused
+  const int32_t* list_idx;       // [B * Hkv, nqb, list_cap] key index (Lk in the padding)
+  const int32_t* list_rank;      // same layout, the key's rank (INT32_MAX in the padding)
+  const float* list_zh;          // same layout, zero_hold * log2(e) (0 in the padding)
+  const int32_t* list_count;     // [B * Hkv, nqb] keys listed
+  int list_cap;                  // entries per list (a multiple of 64)
   float* part_out;         // split-KV partials [splits, B, Hq, Lq, d] fp32
   float* part_lse;         // split-KV partials [splits, B, Hq, Lq] fp32 (natural log)
   int B, Hq, Hkv, Lq, Lk, d;
@@ -118,6 +125,10 @@ hipError_t launch_row_kernel(const AttnParams& p, int dtype, hipStream_t s);
 hipError_t launch_topk(const float* zh, int BH, int Lq, int Lk, int keep_k, int causal,
                        int32_t* rank, int32_t* tau, uint32_t* keep_bits, int32_t* tile_min, int block_n,
                        hipStream_t s);
+// Kept-key lists of the gathered top-k attention (see AttnParams::list_*).
+hipError_t launch_topk_lists(const int32_t* rank, const int32_t* tau, const float* zh, int BH, int Lq, int Lk,
+                             int q_per_block, int cap, int32_t* list_idx, int32_t* list_rank, float* list_zh,
+                             int32_t* list_count, hipStream_t s);
 hipError_t launch_mask_summary(const float* mask, int Lq, int Lk, int q_per_block, int block_n,
                                uint8_t* flags, hipStream_t s);
 

@@ -38,7 +38,9 @@ struct Tile {
   static constexpr int rowBytes = D * 2;
   static constexpr int kBytes = BN * rowBytes;          // K tile, [key][d], no padding
   static constexpr int vBytes = BN * rowBytes;          // V tile, [key][d], no padding
-  static constexpr int xBytes = 8 * BN;                 // top-k side data: BN int32 ranks + BN fp32 values
+  // top-k side data: BN int32 ranks, BN fp32 values (zero_hold * log2 e), BN int32 key
+  // indices (gathered form), padded to keep the stage a multiple of 512 bytes
+  static constexpr int xBytes = 16 * BN;
   static constexpr int stage = kBytes + vBytes + xBytes;
   static constexpr int rowsPerWaveLoad = 1024 / rowBytes;  // one wave's 64 x 16 B direct load
   static constexpr int loadRounds = kBytes / (kThreads * 16);
@@ -51,8 +53,12 @@ struct Tile {
 template <int D, int MK>
 constexpr int kMinBlocks = (D == 64 && MK != MI_ATTN_MASK_TOPK) ? 4 : 2;
 
-template <typename T, int D, int BN, int MK>
+// GATHER (top-k only): tiles are consecutive 64-key runs of the block's kept-key list
+// (AttnParams::list_*) instead of consecutive keys, so only keys some row of the block
+// keeps are loaded and multiplied.
+template <typename T, int D, int BN, int MK, bool GATHER = false>
 __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK>)) void prefill_kernel(AttnParams p) {
+  static_assert(!GATHER || (MK == MI_ATTN_MASK_TOPK && BN == 64), "gathered tiles are top-k lists of 64 keys");
   using TL = Tile<D, BN>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * TL::stage];
 
@@ -109,9 +115,19 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK>)) void prefill_kernel(
     if (hi < lo) hi = lo;
   }
   const int ntiles_all = (p.Lk + BN - 1) / BN;
-  const int t_lo = lo / BN;
+  int t_lo = lo / BN;
   // an empty range visits no tile (a rounded-up end would reach into the next split)
-  const int t_hi = (hi > lo) ? (hi + BN - 1) / BN : t_lo;
+  int t_hi = (hi > lo) ? (hi + BN - 1) / BN : t_lo;
+  long list_base = 0;  // GATHER: this block's kept-key list; tile t = entries [t*BN, t*BN + BN)
+  if constexpr (GATHER) {
+    const long li = static_cast<long>(bg) * nqb + qb;
+    list_base = li * p.list_cap;
+    const int ntl = (p.list_count[li] + BN - 1) / BN;
+    const int per = p.keys_per_split / BN;  // list tiles per split
+    t_lo = split * per;
+    t_hi = min(ntl, t_lo + per);
+    if (t_hi < t_lo) t_hi = t_lo;
+  }
 
   const long kv_base = static_cast<long>(bg) * p.Lk * D;
   const T* K = static_cast<const T*>(p.k) + kv_base;
@@ -125,7 +141,7 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK>)) void prefill_kernel(
     tau_blk = p.tau[static_cast<long>(bg) * p.Lq + i_first];
   }
   auto tile_live = [&](int t) -> bool {
-    if (p.no_skip) return true;
+    if (GATHER || p.no_skip) return true;
     if constexpr (MK == MI_ATTN_MASK_DENSE) return p.tile_live[static_cast<long>(qb) * ntiles_all + t] != 0;
     if constexpr (MK == MI_ATTN_MASK_TOPK)
       return p.tile_min_rank[static_cast<long>(bg) * ntiles_all + t] <= tau_blk;
@@ -150,7 +166,26 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK>)) void prefill_kernel(
     dma_lane = (r * D + ((ps ^ swz<D>(r)) << 3)) * 2;
   }
   const unsigned smem_addr = __builtin_amdgcn_readfirstlane(lds_address(smem));
-  int32_t xrank = 0;
+  // GATHER: row r of a tile comes from key list[t*BN + r]; a lane's rows in load round c
+  // are r_c = (c * kWaves + wave) * rowsPerWaveLoad + lane / (D / 8), whose swizzle does not
+  // depend on c. Their key indices are loaded one tile ahead into gidx[], so the waits for
+  // them fall on loads that have long completed.
+  int dma_slot = 0;
+  int gidx[TL::loadRounds];
+  if constexpr (GATHER) {
+    const int r = wave * TL::rowsPerWaveLoad + lane / (D / 8);
+    dma_slot = ((lane % (D / 8)) ^ swz<D>(r)) << 4;
+  }
+  auto load_gidx = [&](int t) {
+    if constexpr (GATHER) {
+#pragma unroll
+      for (int c = 0; c < TL::loadRounds; ++c) {
+        const int r = (c * kWaves + wave) * TL::rowsPerWaveLoad + lane / (D / 8);
+        gidx[c] = p.list_idx[list_base + t * BN + r];
+      }
+    }
+  };
+  int32_t xrank = 0, xidx = 0;
   float xzh = 0.f;
   auto issue_tile = [&](int t, int stg) {
     const int j0 = t * BN;
@@ -158,11 +193,26 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK>)) void prefill_kernel(
 #pragma unroll
     for (int c = 0; c < TL::loadRounds; ++c) {
       const unsigned blk = (c * kWaves + wave) * 1024;  // 1 KB block of the tile
-      const int so = (j0 + c * kWaves * TL::rowsPerWaveLoad) * D * 2;
-      lds_dma16_at(krs, kst + blk, dma_lane, so);
-      lds_dma16_at(vrs, kst + TL::kBytes + blk, dma_lane, so);
+      if constexpr (GATHER) {
+        // padding entries (key Lk) lie past the buffer range and read as zeros
+        const int vo = gidx[c] * (D * 2) + dma_slot;
+        lds_dma16_at(krs, kst + blk, vo, 0);
+        lds_dma16_at(vrs, kst + TL::kBytes + blk, vo, 0);
+      } else {
+        const int so = (j0 + c * kWaves * TL::rowsPerWaveLoad) * D * 2;
+        lds_dma16_at(krs, kst + blk, dma_lane, so);
+        lds_dma16_at(vrs, kst + TL::kBytes + blk, dma_lane, so);
+      }
     }
-    if constexpr (MK == MI_ATTN_MASK_TOPK) {
+    if constexpr (GATHER) {
+      if (tid < BN) {
+        const long e = list_base + j0 + tid;
+        xrank = p.list_rank[e];
+        xzh = p.list_zh[e];
+        xidx = p.list_idx[e];
+      }
+      if (t + 1 < t_hi) load_gidx(t + 1);
+    } else if constexpr (MK == MI_ATTN_MASK_TOPK) {
       if (tid < BN) {
         const int key = j0 + tid;
         xrank = key < p.Lk ? p.rank[bgk + key] : 0x7fffffff;
@@ -176,6 +226,7 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK>)) void prefill_kernel(
         int32_t* xr = reinterpret_cast<int32_t*>(smem + stg * TL::stage + TL::kBytes + TL::vBytes);
         xr[tid] = xrank;
         reinterpret_cast<float*>(xr + BN)[tid] = xzh;
+        if constexpr (GATHER) xr[2 * BN + tid] = xidx;
       }
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
@@ -209,6 +260,7 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK>)) void prefill_kernel(
   int t = next_live(t_lo);
   int stage = 0;
   if (t < t_hi) {
+    load_gidx(t);
     issue_tile(t, 0);
     finish_tile(0);
   }
@@ -254,7 +306,16 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK>)) void prefill_kernel(
     // mask (tiles the mask does not cover entirely); masked tiles move to the log2
     // domain here (cm = 1), unmasked ones are scaled inside the exponent (cm = cexp)
     float cm = cexp;
-    if constexpr (MK == MI_ATTN_MASK_TOPK) {
+    if constexpr (GATHER) {
+      const int32_t* xr = reinterpret_cast<const int32_t*>(vs + TL::vBytes);
+      const float* xzl = reinterpret_cast<const float*>(xr + BN);
+      const int32_t* xi = xr + 2 * BN;
+      if (xi[BN - 1] > P0)  // the list ascends: its last key decides whether positions matter
+        mask_tile_topk_list<NKB, true>(sacc, hf, pos, tau_row, cexp, xr, xzl, xi);
+      else
+        mask_tile_topk_list<NKB, false>(sacc, hf, pos, tau_row, cexp, xr, xzl, xi);
+      cm = 1.f;
+    } else if constexpr (MK == MI_ATTN_MASK_TOPK) {
       const int32_t* xr = reinterpret_cast<const int32_t*>(vs + TL::vBytes);
       const float* xzl = reinterpret_cast<const float*>(xr + BN);
       if (j0 + BN - 1 > P0)
@@ -430,7 +491,10 @@ hipError_t launch_prefill_t(const AttnParams& p, hipStream_t s) {
       case MI_ATTN_MASK_CAUSAL: hipLaunchKernelGGL((prefill_kernel<T, 128, 64, 1>), grid, block, 0, s, p); break;
       case MI_ATTN_MASK_WINDOW: hipLaunchKernelGGL((prefill_kernel<T, 128, 64, 2>), grid, block, 0, s, p); break;
       case MI_ATTN_MASK_DENSE: hipLaunchKernelGGL((prefill_kernel<T, 128, 64, 3>), grid, block, 0, s, p); break;
-      default: hipLaunchKernelGGL((prefill_kernel<T, 128, 64, 4>), grid, block, 0, s, p); break;
+      default:
+        if (p.list_idx != nullptr) hipLaunchKernelGGL((prefill_kernel<T, 128, 64, 4, true>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((prefill_kernel<T, 128, 64, 4>), grid, block, 0, s, p);
+        break;
     }
   } else {
     switch (p.mask_kind) {
@@ -438,7 +502,10 @@ hipError_t launch_prefill_t(const AttnParams& p, hipStream_t s) {
       case MI_ATTN_MASK_CAUSAL: hipLaunchKernelGGL((prefill_kernel<T, 64, 64, 1>), grid, block, 0, s, p); break;
       case MI_ATTN_MASK_WINDOW: hipLaunchKernelGGL((prefill_kernel<T, 64, 64, 2>), grid, block, 0, s, p); break;
       case MI_ATTN_MASK_DENSE: hipLaunchKernelGGL((prefill_kernel<T, 64, 64, 3>), grid, block, 0, s, p); break;
-      default: hipLaunchKernelGGL((prefill_kernel<T, 64, 64, 4>), grid, block, 0, s, p); break;
+      default:
+        if (p.list_idx != nullptr) hipLaunchKernelGGL((prefill_kernel<T, 64, 64, 4, true>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((prefill_kernel<T, 64, 64, 4>), grid, block, 0, s, p);
+        break;
     }
   }
   hipError_t e = hipGetLastError();

@@ -358,6 +358,66 @@ __global__ __launch_bounds__(256) void tile_min_rank_kernel(const int32_t* rank,
   if (lane == 0) out[t] = mn;
 }
 
+// Kept-key list of one (b, KV head, query block): the keys j <= p of the block's last row
+// whose rank is at most the threshold of its first row (thresholds do not grow with the
+// row position, so every row of the block keeps a subset), ascending, padded to a whole
+// number of 64-key tiles with key Lk. Exactly keep_k keys up to the first row's position
+// pass the test when its threshold is finite, and every key when it is not (then that
+// position is below keep_k), so a list never holds more than keep_k + q_per_block - 1
+// keys.
+constexpr int kListThreads = 256;
+__global__ __launch_bounds__(kListThreads) void topk_list_kernel(const int32_t* rank, const int32_t* tau,
+                                                                   const float* zh, int Lq, int Lk, int q_per_block,
+                                                                   int nqb, int cap, int32_t* lidx, int32_t* lrank,
+                                                                   float* lzh, int32_t* lcount) {
+  __shared__ int wave_cnt[kListThreads / kWave];
+  const int qb = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid % kWave;
+  const int i_first = qb * q_per_block;
+  const int i_last = min(Lq, i_first + q_per_block) - 1;
+  const int n = Lk - Lq + i_last + 1;  // keys 0 .. p of the last row (may be <= 0)
+  const int32_t tf = tau[static_cast<long>(bh) * Lq + i_first];
+  const int32_t* rk = rank + static_cast<long>(bh) * Lk;
+  const float* z = zh + static_cast<long>(bh) * Lk;
+  const long base = (static_cast<long>(bh) * nqb + qb) * cap;
+  int cnt = 0;
+  for (int j0 = 0; j0 < n; j0 += kListThreads) {
+    const int j = j0 + tid;
+    const int32_t r = j < n ? rk[j] : kAllKept;
+    const bool keep = j < n && r <= tf;
+    const unsigned long long ball = __ballot(keep);
+    const int before = __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(ball >> 32),
+                                                 __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(ball), 0));
+    if (lane == 0) wave_cnt[wave] = __popcll(ball);
+    __syncthreads();
+    int off = cnt, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kListThreads / kWave; ++w) {
+      off += w < wave ? wave_cnt[w] : 0;
+      tot += wave_cnt[w];
+    }
+    const int e = off + before;
+    if (keep && e < cap) {
+      lidx[base + e] = j;
+      lrank[base + e] = r;
+      lzh[base + e] = z[j] * kLog2e;
+    }
+    cnt += tot;
+    __syncthreads();  // wave_cnt is rewritten by the next pass
+  }
+  cnt = cnt < cap ? cnt : cap;  // the bound above makes this a no-op
+  const int padded = ((cnt + 63) / 64) * 64;
+  for (int e = cnt + tid; e < padded; e += kListThreads) {
+    lidx[base + e] = Lk;
+    lrank[base + e] = kAllKept;
+    lzh[base + e] = 0.f;
+  }
+  if (tid == 0) lcount[static_cast<long>(bh) * nqb + qb] = cnt;
+}
+
 // One wavefront per (query block, key tile): flag = 1 iff some entry is above -inf.
 __global__ __launch_bounds__(256) void mask_summary_kernel(const float* mask, int Lq, int Lk,
                                                              int q_per_block, int block_n, int ntiles,
@@ -437,6 +497,16 @@ hipError_t launch_topk(const float* zh, int BH, int Lq, int Lk, int keep_k, int 
     e = hipGetLastError();
   }
   return e;
+}
+
+hipError_t launch_topk_lists(const int32_t* rank, const int32_t* tau, const float* zh, int BH, int Lq, int Lk,
+                             int q_per_block, int cap, int32_t* list_idx, int32_t* list_rank, float* list_zh,
+                             int32_t* list_count, hipStream_t s) {
+  const int nqb = (Lq + q_per_block - 1) / q_per_block;
+  if (cap % 64 != 0 || BH > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(topk_list_kernel, dim3(nqb, BH), dim3(kListThreads), 0, s, rank, tau, zh, Lq, Lk, q_per_block,
+                     nqb, cap, list_idx, list_rank, list_zh, list_count);
+  return hipGetLastError();
 }
 
 hipError_t launch_mask_summary(const float* mask, int Lq, int Lk, int q_per_block, int block_n, uint8_t* flags,

@@ -195,6 +195,33 @@ __device__ __forceinline__ void mask_tile_topk(f32x16_t* sacc, int j0, int hf, i
   }
 }
 
+// The same for a gathered tile: key k of the tile is key xi[k] of the cache (ascending;
+// padding entries carry key Lk, rank INT32_MAX and value 0, so kDiag tiles hide them).
+template <int NKB, bool kDiag>
+__device__ __forceinline__ void mask_tile_topk_list(f32x16_t* sacc, int hf, int pos, int32_t tau_row, float cexp,
+                                                    const int32_t* xr, const float* xzl, const int32_t* xi) {
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int kk = kb * 32 + r4 * 8 + hf * 4;  // first of 4 consecutive keys in the tile
+      const int4 rk = *reinterpret_cast<const int4*>(xr + kk);
+      const float4 zl = *reinterpret_cast<const float4*>(xzl + kk);
+      const int4 ji = *reinterpret_cast<const int4*>(xi + kk);
+      const int rks[4] = {rk.x, rk.y, rk.z, rk.w};
+      const float zs[4] = {zl.x, zl.y, zl.z, zl.w};
+      const int js[4] = {ji.x, ji.y, ji.z, ji.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        bool vis = rks[e] <= tau_row;
+        if constexpr (kDiag) vis = vis && js[e] <= pos;
+        const float s = fmaf(sacc[kb][r4 * 4 + e], cexp, zs[e]);
+        sacc[kb][r4 * 4 + e] = vis ? s : kNegInf;
+      }
+    }
+  }
+}
+
 // Whether a tile [j0, j0 + BN) needs per-element masking for a block whose query rows sit
 // at positions P0..P1: tiles every row sees entirely (and inside Lk) skip it.
 template <int MK, int BN>

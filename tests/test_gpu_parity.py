@@ -101,10 +101,16 @@ def test_no_skip_switch_changes_nothing():
             b = run_gpu(p)
         finally:
             mfa.set_debug()
-        # Skipping only drops keys that are -inf for every row of a tile, but it can move
-        # the chunk boundaries, so fp32 summation order (and a bf16 rounding) may change.
+        # Skipping only drops keys that are -inf for every row of a tile, but it moves the
+        # chunk boundaries, so the fp32 summation order changes and an output may round to
+        # the neighbouring bf16 value (one ulp, 2^-7 relative). Top-k with skipping runs over
+        # each block's kept-key list, so its tiles hold other keys and its running maxima
+        # move at other tiles: P is rounded to bf16 against another reference, and each
+        # weight may differ by 2^-8 relative between the routes, bounding the output
+        # difference by 2^-8 * max|v|.
         np.testing.assert_array_equal(a[1] == -np.inf, b[1] == -np.inf)
-        np.testing.assert_allclose(a[0], b[0], rtol=0, atol=1e-3)
+        atol = 2.0**-8 * float(np.abs(p.f64("v")).max()) if kind == "topk" else 1e-3
+        np.testing.assert_allclose(a[0], b[0], rtol=2.0**-7, atol=atol)
         fin = np.isfinite(a[1])
         np.testing.assert_allclose(a[1][fin], b[1][fin], rtol=0, atol=1e-4)
 
