@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define MI_ATTN_ABI_VERSION 1
+#define MI_ATTN_ABI_VERSION 2
 
 /* element types of q, k, v, out */
 #define MI_ATTN_F32 0
@@ -126,6 +126,9 @@ typedef struct {
   int grid;          /* workgroups of the main kernel                                    */
   int mask_summary;  /* 1 when a per-tile dense-mask summary kernel runs first            */
   size_t workspace_bytes; /* temporary device memory the call takes                     */
+  int topk_list_cap; /* top-k on path 1: keys per query block's kept-key list (the block's
+                        tiles are runs of that list); 0 when every tile of the causal range
+                        is visited and masked per element                                  */
 } attn_plan_t;
 
 /*

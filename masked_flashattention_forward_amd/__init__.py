@@ -26,10 +26,13 @@ class MiAttnError(RuntimeError):
         self.code = code
 
 
+ABI_VERSION = 2  # MI_ATTN_ABI_VERSION of include/mi_attn.h that this binding matches
+
+
 class AttnPlan(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int), ("block_m", ctypes.c_int), ("block_n", ctypes.c_int),
                 ("splits", ctypes.c_int), ("grid", ctypes.c_int), ("mask_summary", ctypes.c_int),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("topk_list_cap", ctypes.c_int)]
 
 
 _lib = None
@@ -60,6 +63,9 @@ def lib() -> ctypes.CDLL:
             fn = getattr(l, name)
             fn.restype = res
             fn.argtypes = args
+        if l.attn_abi_version() != ABI_VERSION:
+            raise MiAttnError(EHIP, f"{LIB_PATH} has ABI version {l.attn_abi_version()}, "
+                                    f"this binding expects {ABI_VERSION}: rebuild it")
         _lib = l
     return _lib
 
@@ -91,7 +97,8 @@ def plan(B, Hq, Hkv, Lq, Lk, d, mask_kind="causal", window_left=0, keep_k=0, dty
     mk = MASK_KINDS[mask_kind] if isinstance(mask_kind, str) else int(mask_kind)
     _check(lib().attn_fwd_plan(B, Hq, Hkv, Lq, Lk, d, mk, window_left, keep_k, dtype, ctypes.byref(p)))
     return {"path": PATH_NAMES[p.path], "block_m": p.block_m, "block_n": p.block_n, "splits": p.splits,
-            "grid": p.grid, "mask_summary": bool(p.mask_summary), "workspace_bytes": p.workspace_bytes}
+            "grid": p.grid, "mask_summary": bool(p.mask_summary), "workspace_bytes": p.workspace_bytes,
+            "topk_list_cap": p.topk_list_cap}
 
 
 def _ptr(t):

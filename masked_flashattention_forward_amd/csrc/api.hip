@@ -146,6 +146,7 @@ int make_plan(const Shape& s, Plan* pl) {
     pl->off_plse = off; off = align256(off + sizeof(float) * p.splits * rows);
   }
   p.workspace_bytes = off;
+  p.topk_list_cap = pl->list_cap;
   return MI_ATTN_OK;
 }
 

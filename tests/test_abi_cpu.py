@@ -88,6 +88,24 @@ def test_fp32_takes_the_row_kernel(lib):
     assert mfa.plan(1, 2, 2, 128, 128, 64, "causal", dtype=mfa.F32)["path"] == "row"
 
 
+def test_topk_prefill_uses_kept_key_lists_when_they_are_short(lib):
+    # c5: each 128-row block keeps at most keep_k + 127 keys -> lists of 1152 of 4096 keys
+    c5 = mfa.plan(2, 16, 16, 4096, 4096, 128, "topk", keep_k=1024)
+    assert c5["path"] == "mfma_prefill" and c5["topk_list_cap"] == 1152
+    # a list as long as most of the key range: every causal tile is visited instead
+    assert mfa.plan(2, 16, 16, 4096, 4096, 128, "topk", keep_k=3500)["topk_list_cap"] == 0
+    # GQA: 128 / G query positions per block
+    assert mfa.plan(2, 8, 2, 300, 1500, 128, "topk", keep_k=200)["topk_list_cap"] == 256
+    # other mask kinds, the decode path and the no-skip switch never use lists
+    assert mfa.plan(2, 16, 16, 4096, 4096, 128, "causal")["topk_list_cap"] == 0
+    assert mfa.plan(16, 32, 8, 1, 32768, 128, "topk", keep_k=1024)["topk_list_cap"] == 0
+    try:
+        mfa.set_debug(no_skip=True)
+        assert mfa.plan(2, 16, 16, 4096, 4096, 128, "topk", keep_k=1024)["topk_list_cap"] == 0
+    finally:
+        mfa.set_debug()
+
+
 def test_forced_path_errors_are_reported(lib):
     try:
         mfa.set_debug(force_path=1)

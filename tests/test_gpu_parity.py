@@ -171,3 +171,17 @@ def test_decode_path_shapes(G, Lq):
     out, lse = run_gpu(p, out_fill=float("nan"))
     ref_o, ref_l = run_oracle(p)
     compare(p, out, lse, ref_o, ref_l, label=p.name)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Lq,Lk,keep", [(1, 2, 2, 1024, 1024, 128), (2, 8, 2, 300, 1500, 200)])
+def test_topk_kept_key_lists(B, Hq, Hkv, Lq, Lk, keep):
+    """Top-k attention over each query block's kept-key list (the gathered tiles), square
+    and with past keys under GQA, against the oracle."""
+    import masked_flashattention_forward_amd as mfa
+    p = synth.make_problem(f"topk lists {B}x{Hq}/{Hkv} {Lq}x{Lk} keep {keep}", B, Hq, Hkv, Lq, Lk, 128, "bf16",
+                           "topk", 700 + keep, keep_k=keep, with_zero_hold=True)
+    assert mfa.plan(B, Hq, Hkv, Lq, Lk, 128, "topk", keep_k=keep)["topk_list_cap"] > 0
+    say(p.name)
+    out, lse = run_gpu(p, out_fill=float("nan"))
+    ref_o, ref_l = run_oracle(p)
+    compare(p, out, lse, ref_o, ref_l, label=p.name)
