@@ -366,11 +366,13 @@ __global__ __launch_bounds__(256) void tile_min_rank_kernel(const int32_t* rank,
 // position is below keep_k), so a list never holds more than keep_k + q_per_block - 1
 // keys.
 constexpr int kListThreads = 256;
+constexpr int kListWaves = kListThreads / kWave;
+constexpr int kListSub = 16;  // 256-key sub-passes per pass (4096 keys per pass)
 __global__ __launch_bounds__(kListThreads) void topk_list_kernel(const int32_t* rank, const int32_t* tau,
                                                                    const float* zh, int Lq, int Lk, int q_per_block,
                                                                    int nqb, int cap, int32_t* lidx, int32_t* lrank,
                                                                    float* lzh, int32_t* lcount) {
-  __shared__ int wave_cnt[kListThreads / kWave];
+  __shared__ int sub_cnt[kListSub][kListWaves];
   const int qb = blockIdx.x;
   const int bh = blockIdx.y;
   const int tid = threadIdx.x;
@@ -384,29 +386,48 @@ __global__ __launch_bounds__(kListThreads) void topk_list_kernel(const int32_t* 
   const float* z = zh + static_cast<long>(bh) * Lk;
   const long base = (static_cast<long>(bh) * nqb + qb) * cap;
   int cnt = 0;
-  for (int j0 = 0; j0 < n; j0 += kListThreads) {
-    const int j = j0 + tid;
-    const int32_t r = j < n ? rk[j] : kAllKept;
-    const bool keep = j < n && r <= tf;
-    const unsigned long long ball = __ballot(keep);
-    const int before = __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(ball >> 32),
-                                                 __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(ball), 0));
-    if (lane == 0) wave_cnt[wave] = __popcll(ball);
-    __syncthreads();
-    int off = cnt, tot = 0;
+  // a pass covers 4096 keys: sub-pass u holds keys j0 + 256 u + (0..255), so the loads are
+  // coalesced and all 16 are in flight together; per-wavefront ballot counts of every
+  // sub-pass go to LDS and one barrier later each lane knows where its keys go
+  for (int j0 = 0; j0 < n; j0 += kListThreads * kListSub) {
+    int32_t r[kListSub];
 #pragma unroll
-    for (int w = 0; w < kListThreads / kWave; ++w) {
-      off += w < wave ? wave_cnt[w] : 0;
-      tot += wave_cnt[w];
+    for (int u = 0; u < kListSub; ++u) {
+      const int j = j0 + u * kListThreads + tid;
+      r[u] = j < n ? rk[j] : kAllKept;
     }
-    const int e = off + before;
-    if (keep && e < cap) {
-      lidx[base + e] = j;
-      lrank[base + e] = r;
-      lzh[base + e] = z[j] * kLog2e;
+    unsigned long long ball[kListSub];
+#pragma unroll
+    for (int u = 0; u < kListSub; ++u) {
+      const int j = j0 + u * kListThreads + tid;
+      ball[u] = __ballot(j < n && r[u] <= tf);
+      if (lane == 0) sub_cnt[u][wave] = __popcll(ball[u]);
     }
-    cnt += tot;
-    __syncthreads();  // wave_cnt is rewritten by the next pass
+    __syncthreads();
+    int run = cnt;  // kept keys before sub-pass u
+#pragma unroll
+    for (int u = 0; u < kListSub; ++u) {
+      int before = run;
+#pragma unroll
+      for (int w = 0; w < kListWaves; ++w) {
+        const int c = sub_cnt[u][w];
+        before += w < wave ? c : 0;
+        run += c;
+      }
+      const unsigned long long b_u = ball[u];
+      if ((b_u >> lane) & 1ull) {
+        const int e = before + __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(b_u >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(b_u), 0));
+        const int j = j0 + u * kListThreads + tid;
+        if (e < cap) {
+          lidx[base + e] = j;
+          lrank[base + e] = r[u];
+          lzh[base + e] = z[j] * kLog2e;
+        }
+      }
+    }
+    cnt = run;
+    __syncthreads();  // sub_cnt is rewritten by the next pass
   }
   cnt = cnt < cap ? cnt : cap;  // the bound above makes this a no-op
   const int padded = ((cnt + 63) / 64) * 64;
