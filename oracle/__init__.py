@@ -14,7 +14,8 @@ rounding order, because its online softmax only rescales partial sums
 softmax, is kept here only to cross-check the first one.
 
 Parity status of each function is stated in its docstring; every function
-here is pinned by ``tests/test_oracle_pins.py``.
+here is pinned by ``tests/test_oracle_pins.py`` (the varlen / paged-cache
+functions by ``tests/test_oracle_paged_pins.py``).
 """
 from .attention import (  # noqa: F401
     NEG_INF,
@@ -32,3 +33,4 @@ from .topk import (  # noqa: F401
     kept_from_rank_tau,
     pack_keep_bits,
 )
+from .paged import gather_sequence_kv, paged_attention_ref  # noqa: F401

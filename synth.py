@@ -153,6 +153,158 @@ def window_dense_mask(Lq: int, Lk: int, first_pos: int, window: int) -> np.ndarr
     return m
 
 
+# ------------------------------------------------------------ varlen / paged problems
+@dataclass
+class PagedProblem:
+    """One attention call over a batch of sequences of different lengths.
+
+    Queries are packed token-major ``[total_q, Hq, d]`` with ``cu_seqlens_q``; sequence
+    ``s`` has ``cu_seqlens_k[s+1] - cu_seqlens_k[s]`` keys. With ``page_size > 0`` K/V are
+    a paged cache ``[num_pages, page_size, Hkv, d]`` addressed through ``block_table``
+    ``[S, max_pages]`` (int32, unused entries 0); with ``page_size == 0`` they are packed
+    ``[total_k, Hkv, d]`` at the ``cu_seqlens_k`` offsets. ``k_new``/``v_new``
+    ``[total_q, Hkv, d]`` (two-source form) hold each sequence's last ``Lq`` keys, and the
+    cache then holds only the first ``Lk - Lq``.
+    """
+    name: str
+    Hq: int
+    Hkv: int
+    d: int
+    dtype: str
+    mask_kind: str
+    scale: float
+    page_size: int
+    window_left: int = 0
+    cu_seqlens_q: np.ndarray = None
+    cu_seqlens_k: np.ndarray = None
+    block_table: np.ndarray | None = None
+    q: np.ndarray = None
+    k: np.ndarray = None
+    v: np.ndarray = None
+    k_new: np.ndarray | None = None
+    v_new: np.ndarray | None = None
+    meta: dict = field(default_factory=dict)
+
+    def f64(self, name: str):
+        a = getattr(self, name)
+        return None if a is None else storage_to_f64(a, self.dtype)
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.cu_seqlens_q.size - 1)
+
+    @property
+    def total_q(self) -> int:
+        return int(self.cu_seqlens_q[-1])
+
+    @property
+    def q_lens(self) -> np.ndarray:
+        return np.diff(self.cu_seqlens_q)
+
+    @property
+    def k_lens(self) -> np.ndarray:
+        return np.diff(self.cu_seqlens_k)
+
+    @property
+    def max_seqlen_q(self) -> int:
+        return int(self.q_lens.max(initial=0))
+
+    @property
+    def max_seqlen_k(self) -> int:
+        return int(self.k_lens.max(initial=0))
+
+    @property
+    def kv_rows(self) -> int:
+        """Leading extent of K/V: pages when paged, rows when packed."""
+        return int(self.k.shape[0])
+
+    @property
+    def two_source(self) -> bool:
+        return self.k_new is not None
+
+
+def make_paged_problem(name, q_lens, k_lens, Hq, Hkv, d, dtype, mask_kind, seed, *, page_size=16,
+                       two_source=False, window_left=0, spare_pages=2, mult=1.0, scale=None) -> PagedProblem:
+    """Draw q, K/V storage, (k_new, v_new), then the page permutation, from ``seed``.
+
+    Physical pages are a random permutation of the pool (plus ``spare_pages`` pages no
+    sequence uses), so logically consecutive pages are scattered as in a serving cache.
+    """
+    q_lens = np.asarray(q_lens, dtype=np.int64)
+    k_lens = np.asarray(k_lens, dtype=np.int64)
+    S = q_lens.size
+    cu_q = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(k_lens)]).astype(np.int32)
+    total_q, total_k = int(cu_q[-1]), int(cu_k[-1])
+    cached = np.maximum(k_lens - q_lens, 0) if two_source else k_lens
+    rng = np.random.default_rng(seed)
+
+    def normal(shape):
+        x = rng.standard_normal(shape, dtype=np.float32)
+        if mult != 1.0:
+            x *= np.float32(mult)
+        return x
+
+    q32 = normal((total_q, Hq, d))
+    if page_size > 0:
+        pages = (cached + page_size - 1) // page_size
+        num_pages = int(pages.sum()) + spare_pages
+        kv_shape = (num_pages, page_size, Hkv, d)
+    else:
+        kv_shape = (total_k, Hkv, d)
+    k32, v32 = normal(kv_shape), normal(kv_shape)
+    kn32 = vn32 = None
+    if two_source:
+        kn32, vn32 = normal((total_q, Hkv, d)), normal((total_q, Hkv, d))
+    table = None
+    if page_size > 0:
+        perm = rng.permutation(num_pages).astype(np.int32)
+        table = np.zeros((S, max(1, int(pages.max(initial=0)))), dtype=np.int32)
+        nxt = 0
+        for s in range(S):
+            table[s, :pages[s]] = perm[nxt:nxt + pages[s]]
+            nxt += int(pages[s])
+    p = PagedProblem(name=name, Hq=Hq, Hkv=Hkv, d=d, dtype=dtype, mask_kind=mask_kind,
+                     scale=default_scale(d) if scale is None else float(np.float32(scale)),
+                     page_size=page_size, window_left=window_left, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k,
+                     block_table=table, q=to_storage(q32, dtype), k=to_storage(k32, dtype),
+                     v=to_storage(v32, dtype),
+                     k_new=None if kn32 is None else to_storage(kn32, dtype),
+                     v_new=None if vn32 is None else to_storage(vn32, dtype))
+    p.meta["seed"] = seed
+    return p
+
+
+def serving_lengths(seed, n_prefill, prefill_q, prefill_ctx, n_decode, decode_ctx):
+    """A mixed serving batch: ``n_prefill`` chunks of ``prefill_q`` new tokens on top of
+    contexts drawn uniformly from ``prefill_ctx = (lo, hi)``, then ``n_decode`` single-token
+    steps with contexts drawn log-uniformly from ``decode_ctx = (lo, hi)``. Returns
+    (q_lens, k_lens); key counts include the new tokens."""
+    rng = np.random.default_rng(seed)
+    pc = rng.integers(prefill_ctx[0], prefill_ctx[1] + 1, size=n_prefill)
+    lo, hi = np.log(decode_ctx[0]), np.log(decode_ctx[1])
+    dc = np.exp(rng.uniform(lo, hi, size=n_decode)).astype(np.int64)
+    q_lens = np.concatenate([np.full(n_prefill, prefill_q), np.ones(n_decode, dtype=np.int64)])
+    k_lens = np.concatenate([pc + prefill_q, dc + 1])
+    return q_lens.astype(np.int64), k_lens.astype(np.int64)
+
+
+def paged_config(name: str) -> PagedProblem:
+    """Varlen / paged workloads: a small mixed batch with the edge cases, and a serving batch."""
+    if name == "v1":
+        # decode step, prefill chunk over a context, a one-key sequence, a plain prefill,
+        # a sequence with no queries, more queries than keys, and one with no keys at all
+        q_lens = [1, 37, 1, 130, 0, 5, 3]
+        k_lens = [300, 200, 1, 130, 50, 3, 0]
+        return make_paged_problem("v1 small mixed varlen, paged 16", q_lens, k_lens, 8, 2, 128, "bf16",
+                                  "causal", 61, page_size=16)
+    if name == "serve":
+        q_lens, k_lens = serving_lengths(62, 4, 512, (1024, 4096), 60, (1024, 16384))
+        return make_paged_problem("serving batch: 4 prefill chunks of 512 + 60 decode steps, paged 16",
+                                  q_lens, k_lens, 32, 8, 128, "bf16", "causal", 63, page_size=16)
+    raise KeyError(name)
+
+
 # ------------------------------------------------------------ named configs
 def config(name: str) -> Problem:
     """The five workloads (and their variants) at full size."""

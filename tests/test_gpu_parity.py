@@ -173,10 +173,12 @@ def test_decode_path_shapes(G, Lq):
     compare(p, out, lse, ref_o, ref_l, label=p.name)
 
 
-@pytest.mark.parametrize("B,Hq,Hkv,Lq,Lk,keep", [(1, 2, 2, 1024, 1024, 128), (2, 8, 2, 300, 1500, 200)])
+@pytest.mark.parametrize("B,Hq,Hkv,Lq,Lk,keep", [(1, 2, 2, 1024, 1024, 128), (2, 8, 2, 300, 1500, 200),
+                                                   (1, 8, 2, 300, 200, 20)])
 def test_topk_kept_key_lists(B, Hq, Hkv, Lq, Lk, keep):
-    """Top-k attention over each query block's kept-key list (the gathered tiles), square
-    and with past keys under GQA, against the oracle."""
+    """Top-k attention over each query block's kept-key list (the gathered tiles): square,
+    with past keys under GQA, and with more queries than keys (the first blocks' rows see
+    no key, so their lists are empty), against the oracle."""
     import masked_flashattention_forward_amd as mfa
     p = synth.make_problem(f"topk lists {B}x{Hq}/{Hkv} {Lq}x{Lk} keep {keep}", B, Hq, Hkv, Lq, Lk, 128, "bf16",
                            "topk", 700 + keep, keep_k=keep, with_zero_hold=True)

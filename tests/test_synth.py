@@ -41,3 +41,30 @@ def test_config_shapes():
     np.testing.assert_array_equal(p.q, c2.q)
     m = synth.window_dense_mask(16, 700, 560, 60)
     assert np.isfinite(m[15]).sum() == 61 and np.isfinite(m[15, 515:576]).all()
+
+
+def test_paged_problem_pages_are_disjoint_and_cover_the_cache():
+    p = synth.paged_config("v1")
+    assert p.total_q == sum([1, 37, 1, 130, 0, 5, 3]) and p.num_seqs == 7
+    used = []
+    for s in range(p.num_seqs):
+        n = (int(p.k_lens[s]) + p.page_size - 1) // p.page_size
+        used.extend(p.block_table[s, :n].tolist())
+    assert len(used) == len(set(used))
+    assert p.kv_rows == len(used) + 2          # two spare pages nobody uses
+    assert all(0 <= x < p.kv_rows for x in used)
+    a = synth.paged_config("v1")
+    np.testing.assert_array_equal(a.k, p.k)
+    np.testing.assert_array_equal(a.block_table, p.block_table)
+
+
+def test_two_source_problem_caches_only_the_context():
+    p = synth.make_paged_problem("t", [3, 1], [10, 4], 4, 2, 8, "bf16", "causal", 5, page_size=4,
+                                 two_source=True, spare_pages=0)
+    assert p.k_new.shape == (4, 2, 8) and p.k.shape == (2 + 1, 4, 2, 8)   # ceil(7/4) + ceil(3/4) pages
+
+
+def test_serving_lengths_mix():
+    q, k = synth.serving_lengths(62, 4, 512, (1024, 4096), 60, (1024, 16384))
+    assert (q[:4] == 512).all() and (q[4:] == 1).all()
+    assert (k[:4] >= 1024 + 512).all() and (k[4:] >= 1024).all() and (k[4:] <= 16385).all()
