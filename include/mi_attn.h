@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define MI_ATTN_ABI_VERSION 2
+#define MI_ATTN_ABI_VERSION 3
 
 /* element types of q, k, v, out */
 #define MI_ATTN_F32 0
@@ -115,6 +115,62 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
 int dynamic_mask_topk(const float* zero_hold, int B, int H, int Lq, int Lk, int keep_k,
                       int causal, int32_t* rank, int32_t* tau, uint32_t* keep_bits,
                       void* stream);
+
+/*
+ * attn_fwd_varlen: the same forward for a batch of sequences of different lengths whose
+ * keys and values sit in a paged cache or packed back to back. It is the varlen call the
+ * vLLM pull request #11277 page asks to align with (queries packed with cu_seqlens_q, key
+ * counts from cu_seqlens_k, max_seqlen_q/k, a block table, causal and window masks) and,
+ * with k_new/v_new, the form the same page's reply describes for its own backend: the
+ * cached keys and the new tokens' keys are passed separately, so the new ones need not
+ * be written into the cache before attention reads them.
+ *
+ *   Sequence s has Lq_s = cu_seqlens_q[s+1] - cu_seqlens_q[s] queries and
+ *   Lk_s = cu_seqlens_k[s+1] - cu_seqlens_k[s] keys; its query i sits at position
+ *   Lk_s - Lq_s + i (bottom-right, as in attn_fwd), and GQA maps heads as in attn_fwd.
+ *
+ *   q, out        [total_q, Hq, d] token-major; sequence s owns rows cu_seqlens_q[s] ...
+ *   lse           fp32 [total_q, Hq] (token-major), or NULL.
+ *   k, v          block_table != NULL: paged cache [kv_rows, page_size, Hkv, d]; key j of
+ *                 sequence s is slot j % page_size of page
+ *                 block_table[s * max_pages + j / page_size].
+ *                 block_table == NULL: packed [kv_rows, Hkv, d]; key j of sequence s is
+ *                 row cu_seqlens_k[s] + j.
+ *   k_new, v_new  both NULL (single source), or both [total_q, Hkv, d]: then the last Lq_s
+ *                 keys of sequence s are its own rows of k_new/v_new (row
+ *                 cu_seqlens_q[s] + i is key Lk_s - Lq_s + i) and k/v supply only the
+ *                 first Lk_s - Lq_s keys. A sequence with Lk_s < Lq_s then has no valid
+ *                 split; its rows come back fully masked (out 0, lse -inf).
+ *   cu_seqlens_q, cu_seqlens_k  device int32 [num_seqs + 1], nondecreasing, cu_seqlens_q
+ *                 from 0 to total_q.
+ *   max_seqlen_q, max_seqlen_k  the largest Lq_s and Lk_s (host values, >= 0); they only
+ *                 steer how the key range is split across workgroups.
+ *   block_table   device int32 [num_seqs, max_pages], or NULL (packed form).
+ *   max_pages     columns of block_table (>= 1 when it is given).
+ *   page_size     keys per page, a power of two (paged form; ignored when packed).
+ *   kv_rows       pages (paged) or rows (packed) held by k and v, >= 1.
+ *   mask_kind     MI_ATTN_MASK_NONE, _CAUSAL or _WINDOW (window_left >= 0).
+ *   dtype         MI_ATTN_F16 or MI_ATTN_BF16, d 64 or 128; fp32 accumulation.
+ *
+ *   The int32 device arrays are not read on the host. If they break the rules above,
+ *   the affected rows hold unspecified values, but every read stays inside the arrays
+ *   described here (indices are clamped) and nothing is written outside out and lse.
+ *   total_q == 0 enqueues nothing. Temporary device memory, taken and released on the
+ *   stream like attn_fwd's: the work-unit schedule (8 bytes per (sequence, query block))
+ *   and, when the key range is split, fp32 partials of splits * total_q * Hq * (d + 1)
+ *   values.
+ *   Returns MI_ATTN_OK, MI_ATTN_EINVAL (negative sizes, Hq % Hkv != 0, a required pointer
+ *   NULL, exactly one of k_new/v_new given, page_size not a power of two, non-finite
+ *   scale, window_left < 0, unknown dtype or mask_kind), MI_ATTN_EUNSUPPORTED (fp32, the
+ *   dense or top-k mask, head dim other than 64/128) or MI_ATTN_EHIP.
+ */
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                    const int32_t* cu_seqlens_q, int max_seqlen_q,
+                    const int32_t* cu_seqlens_k, int max_seqlen_k,
+                    int num_seqs, int total_q, int Hq, int Hkv, int d, float scale,
+                    int mask_kind, int window_left,
+                    const int32_t* block_table, int max_pages, int page_size, int kv_rows,
+                    const void* k_new, const void* v_new, int dtype, void* stream);
 
 /* which kernels attn_fwd would run for a shape (host-only query, no GPU work) */
 typedef struct {

@@ -26,7 +26,7 @@ class MiAttnError(RuntimeError):
         self.code = code
 
 
-ABI_VERSION = 2  # MI_ATTN_ABI_VERSION of include/mi_attn.h that this binding matches
+ABI_VERSION = 3  # MI_ATTN_ABI_VERSION of include/mi_attn.h that this binding matches
 
 
 class AttnPlan(ctypes.Structure):
@@ -43,6 +43,10 @@ _SIGS = {
                     ctypes.c_void_p]),
     "dynamic_mask_topk": (ctypes.c_int, [ctypes.c_void_p] + [ctypes.c_int] * 6
                           + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "attn_fwd_varlen": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_void_p, ctypes.c_int] * 2
+                        + [ctypes.c_int] * 5 + [ctypes.c_float] + [ctypes.c_int] * 2
+                        + [ctypes.c_void_p] + [ctypes.c_int] * 3 + [ctypes.c_void_p] * 2
+                        + [ctypes.c_int, ctypes.c_void_p]),
     "attn_fwd_plan": (ctypes.c_int, [ctypes.c_int] * 10 + [ctypes.POINTER(AttnPlan)]),
     "attn_set_debug": (None, [ctypes.c_int] * 3),
     "attn_last_error": (ctypes.c_char_p, []),
@@ -155,6 +159,79 @@ def attn_fwd(q, k, v, *, scale=None, mask_kind="causal", window_left=0, mask=Non
     rc = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Lq, Lk, d,
                         float(scale), mk, int(window_left), _ptr(mask), _ptr(zero_hold), int(keep_k),
                         _dtype_code(q), _stream_handle(q.device, stream))
+    _check(rc)
+    return out, lse
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, *, max_seqlen_q=None, max_seqlen_k=None,
+                    block_table=None, k_new=None, v_new=None, scale=None, mask_kind="causal", window_left=0,
+                    out=None, lse=None, return_lse=True, stream=None):
+    """Masked attention over a batch of sequences of different lengths (attn_fwd_varlen).
+
+    q ``[total_q, Hq, d]`` token-major; cu_seqlens_q/k int32 ``[num_seqs + 1]`` on q's
+    device. With ``block_table`` (int32 ``[num_seqs, max_pages]``) k/v are a paged cache
+    ``[num_pages, page_size, Hkv, d]``; without it they are packed ``[total_k, Hkv, d]``.
+    ``k_new``/``v_new`` ``[total_q, Hkv, d]`` select the two-source form (the last Lq keys
+    of each sequence). ``max_seqlen_q/k`` are host ints; when None they are read from the
+    cu_seqlens tensors, which synchronises with the device. Returns ``(out, lse)``, lse
+    fp32 ``[total_q, Hq]``.
+    """
+    import torch
+
+    def dev_tensor(name, t, dims, dtype=None):
+        if not t.is_cuda or t.dim() != dims or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous {dims}-D tensor on q's device")
+        if dtype is not None and t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype}")
+
+    if not q.is_cuda or q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous 3-D GPU tensor [total_q, Hq, d]")
+    total_q, Hq, d = q.shape
+    paged = block_table is not None
+    for name, t in (("k", k), ("v", v)):
+        dev_tensor(name, t, 4 if paged else 3, q.dtype)
+    if tuple(v.shape) != tuple(k.shape) or k.shape[-1] != d:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    Hkv = k.shape[-2]
+    kv_rows = k.shape[0]
+    page_size = k.shape[1] if paged else 0
+    max_pages = 0
+    if paged:
+        dev_tensor("block_table", block_table, 2, torch.int32)
+        max_pages = block_table.shape[1]
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        dev_tensor(name, t, 1, torch.int32)
+    num_seqs = cu_seqlens_q.numel() - 1
+    if cu_seqlens_k.numel() != num_seqs + 1 or (paged and block_table.shape[0] != num_seqs):
+        raise ValueError("cu_seqlens_q, cu_seqlens_k and block_table disagree on the number of sequences")
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new, or neither")
+    if k_new is not None:
+        for name, t in (("k_new", k_new), ("v_new", v_new)):
+            dev_tensor(name, t, 3, q.dtype)
+            if tuple(t.shape) != (total_q, Hkv, d):
+                raise ValueError(f"{name} must be [total_q, Hkv, d]")
+    if max_seqlen_q is None:
+        max_seqlen_q = int((cu_seqlens_q[1:] - cu_seqlens_q[:-1]).max().item()) if num_seqs else 0
+    if max_seqlen_k is None:
+        max_seqlen_k = int((cu_seqlens_k[1:] - cu_seqlens_k[:-1]).max().item()) if num_seqs else 0
+    mk = MASK_KINDS[mask_kind] if isinstance(mask_kind, str) else int(mask_kind)
+    if out is None:
+        out = torch.empty_like(q)
+    elif tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must match q")
+    if lse is None and return_lse:
+        lse = torch.empty((total_q, Hq), dtype=torch.float32, device=q.device)
+    if lse is not None and (tuple(lse.shape) != (total_q, Hq) or lse.dtype != torch.float32
+                            or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous fp32 [total_q, Hq] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    rc = lib().attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
+                               int(max_seqlen_q), _ptr(cu_seqlens_k), int(max_seqlen_k), num_seqs, total_q, Hq,
+                               Hkv, d, float(scale), mk, int(window_left), _ptr(block_table), int(max_pages),
+                               int(page_size), int(kv_rows), _ptr(k_new), _ptr(v_new), _dtype_code(q),
+                               _stream_handle(q.device, stream))
     _check(rc)
     return out, lse
 

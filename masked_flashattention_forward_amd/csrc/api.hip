@@ -262,6 +262,94 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
   return MI_ATTN_OK;
 }
 
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                    const int32_t* cu_seqlens_q, int max_seqlen_q, const int32_t* cu_seqlens_k, int max_seqlen_k,
+                    int num_seqs, int total_q, int Hq, int Hkv, int d, float scale, int mask_kind, int window_left,
+                    const int32_t* block_table, int max_pages, int page_size, int kv_rows, const void* k_new,
+                    const void* v_new, int dtype, void* stream) {
+  g_err.clear();
+  if (num_seqs < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+    return fail(MI_ATTN_EINVAL, "num_seqs, total_q and max_seqlen_q/k must be >= 0");
+  if (Hq <= 0 || Hkv <= 0 || d <= 0) return fail(MI_ATTN_EINVAL, "Hq, Hkv and d must be positive");
+  if (Hq % Hkv != 0) return fail(MI_ATTN_EINVAL, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  if (mask_kind < MI_ATTN_MASK_NONE || mask_kind > MI_ATTN_MASK_TOPK)
+    return fail(MI_ATTN_EINVAL, "unknown mask_kind %d", mask_kind);
+  if (dtype < MI_ATTN_F32 || dtype > MI_ATTN_BF16) return fail(MI_ATTN_EINVAL, "unknown dtype %d", dtype);
+  if (mask_kind == MI_ATTN_MASK_WINDOW && window_left < 0)
+    return fail(MI_ATTN_EINVAL, "window_left must be >= 0 (got %d)", window_left);
+  if (!std::isfinite(scale)) return fail(MI_ATTN_EINVAL, "scale must be finite");
+  if ((k_new == nullptr) != (v_new == nullptr)) return fail(MI_ATTN_EINVAL, "give both k_new and v_new, or neither");
+  if (kv_rows < 1) return fail(MI_ATTN_EINVAL, "kv_rows must be >= 1 (got %d)", kv_rows);
+  int page_shift = 0;
+  if (block_table != nullptr) {
+    if (page_size < 1 || (page_size & (page_size - 1)) != 0)
+      return fail(MI_ATTN_EINVAL, "page_size must be a power of two (got %d)", page_size);
+    if (max_pages < 1) return fail(MI_ATTN_EINVAL, "max_pages must be >= 1 (got %d)", max_pages);
+    while ((1 << page_shift) < page_size) ++page_shift;
+    if (static_cast<double>(kv_rows) * page_size > 2147483647.0)
+      return fail(MI_ATTN_EINVAL, "kv_rows * page_size must stay below 2^31 keys");
+  }
+  if (dtype == MI_ATTN_F32) return fail(MI_ATTN_EUNSUPPORTED, "varlen attention takes fp16/bf16 inputs");
+  if (d != 64 && d != 128) return fail(MI_ATTN_EUNSUPPORTED, "head dim must be 64 or 128 (got %d)", d);
+  if (mask_kind == MI_ATTN_MASK_DENSE || mask_kind == MI_ATTN_MASK_TOPK)
+    return fail(MI_ATTN_EUNSUPPORTED, "varlen attention takes the none, causal and window masks");
+  const int G = Hq / Hkv;
+  if (G > prefill_block_m())
+    return fail(MI_ATTN_EUNSUPPORTED, "at most %d query heads per KV head", prefill_block_m());
+  if (static_cast<double>(total_q) * Hq * d > 9.0e15) return fail(MI_ATTN_EINVAL, "tensor too large");
+  if (total_q == 0 || num_seqs == 0) return MI_ATTN_OK;
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || cu_seqlens_q == nullptr ||
+      cu_seqlens_k == nullptr)
+    return fail(MI_ATTN_EINVAL, "q, k, v, out, cu_seqlens_q and cu_seqlens_k must not be NULL");
+
+  // work units: sum over sequences of ceil(Lq_s / qpb) <= (total_q + num_seqs * (qpb - 1)) / qpb
+  const int qpb = varlen_q_per_block(G);
+  const long cap = (static_cast<long>(total_q) + static_cast<long>(num_seqs) * (qpb - 1)) / qpb;
+  if (cap * Hkv > 0x7fffffffL) return fail(MI_ATTN_EUNSUPPORTED, "too many work units (%ld)", cap * Hkv);
+  const int splits = varlen_splits(cap * Hkv, max_seqlen_k, g_force_splits);
+  size_t off = 0;
+  const size_t off_sched = off;
+  off = align256(off + sizeof(int2) * cap);
+  const size_t off_cnt = off;
+  off = align256(off + sizeof(int32_t));
+  size_t off_pout = 0, off_plse = 0;
+  if (splits > 1) {
+    const size_t rows = static_cast<size_t>(total_q) * Hq;
+    off_pout = off; off = align256(off + sizeof(float) * splits * rows * d);
+    off_plse = off; off = align256(off + sizeof(float) * splits * rows);
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = nullptr;
+  hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&ws), off, st);
+  if (e != hipSuccess) return hip_fail(e, "hipMallocAsync(workspace)");
+
+  AttnParams p{};
+  p.q = q; p.k = k; p.v = v; p.out = out; p.lse = lse;
+  p.B = 1; p.Hq = Hq; p.Hkv = Hkv; p.Lq = 0; p.Lk = 0; p.d = d; p.G = G;
+  p.scale = scale; p.mask_kind = mask_kind; p.window_left = window_left;
+  p.no_skip = g_no_skip;
+  p.splits = splits;
+  p.block_n = prefill_block_n(d);
+  p.q_per_block = qpb;
+  p.cu_q = cu_seqlens_q; p.cu_k = cu_seqlens_k;
+  p.block_table = block_table; p.k_new = k_new; p.v_new = v_new;
+  p.sched_cap = static_cast<int>(cap);
+  p.num_seqs = num_seqs; p.total_q = total_q;
+  p.max_pages = block_table != nullptr ? max_pages : 1;
+  p.page_shift = page_shift;
+  p.kv_rows = kv_rows;
+  if (splits > 1) {
+    p.part_out = reinterpret_cast<float*>(ws + off_pout);
+    p.part_lse = reinterpret_cast<float*>(ws + off_plse);
+  }
+  e = launch_prefill_varlen(p, dtype, reinterpret_cast<int2*>(ws + off_sched),
+                            reinterpret_cast<int32_t*>(ws + off_cnt), st);
+  const hipError_t ef = hipFreeAsync(ws, st);
+  if (e != hipSuccess) return hip_fail(e, "varlen attention kernel");
+  if (ef != hipSuccess) return hip_fail(ef, "hipFreeAsync(workspace)");
+  return MI_ATTN_OK;
+}
+
 int dynamic_mask_topk(const float* zero_hold, int B, int H, int Lq, int Lk, int keep_k, int causal, int32_t* rank,
                       int32_t* tau, uint32_t* keep_bits, void* stream) {
   g_err.clear();

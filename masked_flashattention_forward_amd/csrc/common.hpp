@@ -83,8 +83,20 @@ struct AttnParams {
   const float* list_zh;          // same layout, zero_hold * log2(e) (0 in the padding)
   const int32_t* list_count;     // [B * Hkv, nqb] keys listed
   int list_cap;                  // entries per list (a multiple of 64)
-  float* part_out;         // split-KV partials [splits, B, Hq, Lq, d] fp32
-  float* part_lse;         // split-KV partials [splits, B, Hq, Lq] fp32 (natural log)
+  // varlen (attn_fwd_varlen): q/out token-major [total_q, Hq, d], lse [total_q, Hq];
+  // K/V paged [kv_rows pages, 1 << page_shift, Hkv, d] through block_table, or packed
+  // [kv_rows, Hkv, d] at the cu_k offsets when block_table == nullptr
+  const int32_t* cu_q;          // [num_seqs + 1]
+  const int32_t* cu_k;          // [num_seqs + 1]
+  const int32_t* block_table;   // [num_seqs, max_pages]
+  const void* k_new;            // two-source form: [total_q, Hkv, d], the last Lq keys
+  const void* v_new;
+  const int2* sched;            // work units (sequence, query block), sched_count valid
+  const int32_t* sched_count;
+  int sched_cap;                // units the grid provides for (upper bound)
+  int num_seqs, total_q, max_pages, page_shift, kv_rows;
+  float* part_out;         // split-KV partials [splits, rows, d] fp32 (rows: B*Hq*Lq or total_q*Hq)
+  float* part_lse;         // split-KV partials [splits, rows] fp32 (natural log)
   int B, Hq, Hkv, Lq, Lk, d;
   int G;                   // Hq / Hkv
   float scale;

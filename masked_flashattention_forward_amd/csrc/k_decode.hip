@@ -167,14 +167,14 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(AttnParams p) {
       sacc[0] = acc;
     }
     float cm = cexp;
-    if (tile_needs_mask<MK, kDecBN>(p, j0, P0, P1)) {
+    if (tile_needs_mask<MK, kDecBN>(p, p.Lk, j0, P0, P1)) {
       const int32_t* xr = nullptr;
       const float* xz = nullptr;
       if constexpr (MK == MI_ATTN_MASK_TOPK) {
         xr = p.rank + bgk + j0;
         xz = p.zero_hold + bgk + j0;
       }
-      mask_tile<MK, 1>(sacc, p, j0, hf, pos, i_row, tau_row, cexp, xr, xz);
+      mask_tile<MK, 1>(sacc, p, p.Lk, j0, hf, pos, i_row, tau_row, cexp, xr, xz);
       cm = 1.f;
     }
 

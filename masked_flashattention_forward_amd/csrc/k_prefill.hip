@@ -56,9 +56,15 @@ constexpr int kMinBlocks = (D == 64 && MK != MI_ATTN_MASK_TOPK) ? 4 : 2;
 // GATHER (top-k only): tiles are consecutive 64-key runs of the block's kept-key list
 // (AttnParams::list_*) instead of consecutive keys, so only keys some row of the block
 // keeps are loaded and multiplied.
-template <typename T, int D, int BN, int MK, bool GATHER = false>
+// VARLEN: a batch of sequences of different lengths (vLLM pull request #11277 page, the
+// varlen call with cu_seqlens and a block table): queries token-major, a work unit is
+// (sequence, query block) from a device-built schedule, and each K/V row is fetched from
+// its own cache page (or packed row, or the new-token array of the two-source form)
+// with a per-lane 64-bit address.
+template <typename T, int D, int BN, int MK, bool GATHER = false, bool VARLEN = false>
 __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK>)) void prefill_kernel(AttnParams p) {
   static_assert(!GATHER || (MK == MI_ATTN_MASK_TOPK && BN == 64), "gathered tiles are top-k lists of 64 keys");
+  static_assert(!VARLEN || (!GATHER && MK <= MI_ATTN_MASK_WINDOW), "varlen takes the key-position masks");
   using TL = Tile<D, BN>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * TL::stage];
 
@@ -68,27 +74,55 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK>)) void prefill_kernel(
   const int l32 = lane & 31;
   const int hf = lane >> 5;  // lane half
 
-  // ---- work unit: (b, g, query block, split)
-  const int nqb = (p.Lq + p.q_per_block - 1) / p.q_per_block;
-  const unsigned lb = logical_block(blockIdx.x, gridDim.x);
-  const int qb = nqb - 1 - static_cast<int>(lb % nqb);
-  const int bg = static_cast<int>(lb / nqb);
-  const int b = bg / p.Hkv;
-  const int g = bg % p.Hkv;
+  // ---- work unit: (b, g, query block, split), or (sequence, g, query block, split)
   const int split = blockIdx.y;
+  const unsigned lb = logical_block(blockIdx.x, gridDim.x);
+  int nqb = 1, qb, bg, b, g, Lq, Lk;
+  int seq = 0, q_start = 0, ctx = 0;  // VARLEN: sequence, its first token, cached keys
+  if constexpr (VARLEN) {
+    // consecutive logical blocks: consecutive units of one KV head, so the query blocks
+    // of a sequence that share its K/V run on the same XCD
+    const int u = static_cast<int>(lb % static_cast<unsigned>(p.sched_cap));
+    g = static_cast<int>(lb / static_cast<unsigned>(p.sched_cap));
+    if (u >= *p.sched_count) return;  // the whole workgroup, before any barrier
+    const int2 su = p.sched[u];
+    seq = su.x;
+    qb = su.y;
+    // every offset is clamped, so inconsistent lengths cannot move an access out of bounds
+    q_start = min(max(p.cu_q[seq], 0), p.total_q);
+    Lq = min(max(p.cu_q[seq + 1], q_start), p.total_q) - q_start;
+    Lk = max(p.cu_k[seq + 1] - p.cu_k[seq], 0);
+    ctx = p.k_new != nullptr ? Lk - Lq : Lk;
+    b = 0;
+    bg = 0;
+  } else {
+    Lq = p.Lq;
+    Lk = p.Lk;
+    nqb = (Lq + p.q_per_block - 1) / p.q_per_block;
+    qb = nqb - 1 - static_cast<int>(lb % nqb);
+    bg = static_cast<int>(lb / nqb);
+    b = bg / p.Hkv;
+    g = bg % p.Hkv;
+  }
   const int i_first = qb * p.q_per_block;
-  const int i_last = min(p.Lq, i_first + p.q_per_block) - 1;
+  const int i_last = min(Lq, i_first + p.q_per_block) - 1;
   const int rows_blk = (i_last - i_first + 1) * p.G;
-  const int P0 = p.Lk - p.Lq + i_first;
-  const int P1 = p.Lk - p.Lq + i_last;
+  const int P0 = Lk - Lq + i_first;
+  const int P1 = Lk - Lq + i_last;
 
   // ---- this lane's query row (the S^T column it owns)
   const int rloc = wave * 32 + l32;
   const bool row_ok = rloc < rows_blk;
   const int i_row = i_first + (row_ok ? rloc / p.G : 0);
   const int h_row = g * p.G + (row_ok ? rloc % p.G : 0);
-  const int pos = p.Lk - p.Lq + i_row;
-  const long row_index = (static_cast<long>(b) * p.Hq + h_row) * p.Lq + i_row;
+  const int pos = Lk - Lq + i_row;
+  // output row: [B, Hq, Lq] order, or token-major [total_q, Hq] for VARLEN
+  const long row_index = VARLEN ? static_cast<long>(q_start + i_row) * p.Hq + h_row
+                                : (static_cast<long>(b) * p.Hq + h_row) * Lq + i_row;
+  const long rows_all = VARLEN ? static_cast<long>(p.total_q) * p.Hq : static_cast<long>(p.B) * p.Hq * Lq;
+  // VARLEN: a wavefront whose 32 rows are all past the block's rows (short query runs,
+  // decode steps) only helps load tiles
+  const bool wave_live = !VARLEN || wave * 32 < rows_blk;
 
   // ---- Q^T operand in registers: lane holds 8 dims (dc*16 + hf*8 ..) of its row
   const T* Q = static_cast<const T*>(p.q);
@@ -105,16 +139,19 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK>)) void prefill_kernel(
 
   // ---- key range of this block (and split)
   int lo, hi;
-  key_range(MK, p.window_left, p.Lk, P0, P1, &lo, &hi);
-  if (p.no_skip) { lo = 0; hi = p.Lk; }
+  key_range(MK, p.window_left, Lk, P0, P1, &lo, &hi);
+  if (p.no_skip) { lo = 0; hi = Lk; }
+  if (VARLEN && ctx < 0) hi = lo;  // two-source with fewer keys than queries: rows stay masked
   if (p.splits > 1) {
-    const int s0 = split * p.keys_per_split;
-    const int s1 = min(p.Lk, s0 + p.keys_per_split);
+    // VARLEN: each sequence's own key range is cut into p.splits runs of whole tiles
+    const int kps = VARLEN ? ((Lk + BN - 1) / BN + p.splits - 1) / p.splits * BN : p.keys_per_split;
+    const int s0 = split * kps;
+    const int s1 = min(Lk, s0 + kps);
     lo = max(lo, s0);
     hi = min(hi, s1);
     if (hi < lo) hi = lo;
   }
-  const int ntiles_all = (p.Lk + BN - 1) / BN;
+  const int ntiles_all = (Lk + BN - 1) / BN;
   int t_lo = lo / BN;
   // an empty range visits no tile (a rounded-up end would reach into the next split)
   int t_hi = (hi > lo) ? (hi + BN - 1) / BN : t_lo;
@@ -129,10 +166,10 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK>)) void prefill_kernel(
     if (t_hi < t_lo) t_hi = t_lo;
   }
 
-  const long kv_base = static_cast<long>(bg) * p.Lk * D;
+  const long kv_base = VARLEN ? 0 : static_cast<long>(bg) * Lk * D;
   const T* K = static_cast<const T*>(p.k) + kv_base;
   const T* V = static_cast<const T*>(p.v) + kv_base;
-  const long bgk = static_cast<long>(bg) * p.Lk;
+  const long bgk = static_cast<long>(bg) * Lk;
 
   // top-k: the block's largest threshold (thresholds do not grow with the row position)
   int32_t tau_row = 0, tau_blk = 0;
@@ -157,8 +194,8 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK>)) void prefill_kernel(
   // of the swizzled layout. Rows at or past Lk read as zeros (buffer range check). A
   // lane's swizzle does not depend on the load round, so its global offset is one
   // loop-invariant register plus a wave-uniform (scalar) offset for the tile and round.
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K, p.Lk * D * 2);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V, p.Lk * D * 2);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K, VARLEN ? 0 : Lk * D * 2);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V, VARLEN ? 0 : Lk * D * 2);
   int dma_lane;
   {
     const int r = wave * TL::rowsPerWaveLoad + lane / (D / 8);
@@ -172,10 +209,15 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK>)) void prefill_kernel(
   // them fall on loads that have long completed.
   int dma_slot = 0;
   int gidx[TL::loadRounds];
-  if constexpr (GATHER) {
+  if constexpr (GATHER || VARLEN) {
     const int r = wave * TL::rowsPerWaveLoad + lane / (D / 8);
     dma_slot = ((lane % (D / 8)) ^ swz<D>(r)) << 4;
   }
+  // VARLEN: gidx[c] is the cache page of the lane's row in round c (paged form), loaded
+  // one tile ahead like the gathered key indices. Rows past the sequence's last key
+  // repeat that key (it is masked); the clamps keep every index inside the table and cache.
+  const long table_row = VARLEN ? static_cast<long>(seq) * p.max_pages : 0;
+  const int page_mask = VARLEN ? (1 << p.page_shift) - 1 : 0;
   auto load_gidx = [&](int t) {
     if constexpr (GATHER) {
 #pragma unroll
@@ -184,6 +226,33 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK>)) void prefill_kernel(
         gidx[c] = p.list_idx[list_base + t * BN + r];
       }
     }
+    if constexpr (VARLEN) {
+      if (p.block_table != nullptr) {
+#pragma unroll
+        for (int c = 0; c < TL::loadRounds; ++c) {
+          const int r = (c * kWaves + wave) * TL::rowsPerWaveLoad + lane / (D / 8);
+          const int j = min(t * BN + r, Lk - 1);
+          gidx[c] = p.block_table[table_row + min(j >> p.page_shift, p.max_pages - 1)];
+        }
+      }
+    }
+  };
+  // VARLEN: element offset of key j's row (head g, this lane's 16-byte slot) and whether
+  // it comes from the new-token array
+  const long slot_elems = dma_slot >> 1;
+  auto varlen_row = [&](int j, int page, bool* is_new) -> long {
+    j = min(j, Lk - 1);
+    long row;
+    *is_new = j >= ctx;
+    if (*is_new) {
+      row = q_start + (j - ctx);
+    } else if (p.block_table != nullptr) {
+      const int pg = min(max(page, 0), p.kv_rows - 1);
+      row = (static_cast<long>(pg) << p.page_shift) | (j & page_mask);
+    } else {
+      row = min(max(static_cast<long>(p.cu_k[seq]) + j, 0L), static_cast<long>(p.kv_rows) - 1);
+    }
+    return (row * p.Hkv + g) * D + slot_elems;
   };
   int32_t xrank = 0, xidx = 0;
   float xzh = 0.f;
@@ -198,6 +267,14 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK>)) void prefill_kernel(
         const int vo = gidx[c] * (D * 2) + dma_slot;
         lds_dma16_at(krs, kst + blk, vo, 0);
         lds_dma16_at(vrs, kst + TL::kBytes + blk, vo, 0);
+      } else if constexpr (VARLEN) {
+        const int r = (c * kWaves + wave) * TL::rowsPerWaveLoad + lane / (D / 8);
+        bool is_new;
+        const long e = varlen_row(j0 + r, gidx[c], &is_new);
+        const T* kb = static_cast<const T*>(is_new ? p.k_new : p.k);
+        const T* vb = static_cast<const T*>(is_new ? p.v_new : p.v);
+        lds_dma16_global(kst + blk, kb + e);
+        lds_dma16_global(kst + TL::kBytes + blk, vb + e);
       } else {
         const int so = (j0 + c * kWaves * TL::rowsPerWaveLoad) * D * 2;
         lds_dma16_at(krs, kst + blk, dma_lane, so);
@@ -212,11 +289,13 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK>)) void prefill_kernel(
         xidx = p.list_idx[e];
       }
       if (t + 1 < t_hi) load_gidx(t + 1);
+    } else if constexpr (VARLEN) {
+      load_gidx(t + 1);  // clamped, so past the last tile it reads a valid entry
     } else if constexpr (MK == MI_ATTN_MASK_TOPK) {
       if (tid < BN) {
         const int key = j0 + tid;
-        xrank = key < p.Lk ? p.rank[bgk + key] : 0x7fffffff;
-        xzh = key < p.Lk ? p.zero_hold[bgk + key] * kLog2e : 0.f;
+        xrank = key < Lk ? p.rank[bgk + key] : 0x7fffffff;
+        xzh = key < Lk ? p.zero_hold[bgk + key] * kLog2e : 0.f;
       }
     }
   };
@@ -270,138 +349,140 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK>)) void prefill_kernel(
     const int tn = next_live(t + 1);
     if (tn < t_hi) issue_tile(tn, stage ^ 1);  // lands in the other stage while this tile computes
 
-    const int ks_ofs = stage * TL::stage;
-    const int vs_ofs = ks_ofs + TL::kBytes;
-    const unsigned char* vs = smem + vs_ofs;
-    const int j0 = t * BN;
+    if (wave_live) {
+      const int ks_ofs = stage * TL::stage;
+      const int vs_ofs = ks_ofs + TL::kBytes;
+      const unsigned char* vs = smem + vs_ofs;
+      const int j0 = t * BN;
 
-    // S^T = K Q^T. The first 32-key block's K fragments are read before its first MFMA;
-    // afterwards each MFMA overlaps the read of one fragment of the next block.
-    f32x16_t sacc[NKB];
-    {
-      constexpr int NDC = D / 16;
-      u32x4_t kf[NKB][NDC];
+      // S^T = K Q^T. The first 32-key block's K fragments are read before its first MFMA;
+      // afterwards each MFMA overlaps the read of one fragment of the next block.
+      f32x16_t sacc[NKB];
+      {
+        constexpr int NDC = D / 16;
+        u32x4_t kf[NKB][NDC];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int dc = 0; dc < NDC; ++dc)
+            kf[kb][dc] = *reinterpret_cast<const u32x4_t*>(smem + kb * 32 * TL::rowBytes +
+                                                           ((k_base + ks_ofs) ^ (dc << 5)));
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          f32x16_t acc = f32x16_t{};
+#pragma unroll
+          for (int dc = 0; dc < NDC; ++dc) acc = mfma32(T{}, kf[kb][dc], qreg[dc], acc);
+          sacc[kb] = acc;
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NDC, 0);
+#pragma unroll
+        for (int i = 0; i < (NKB - 1) * NDC; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, NDC, 0);
+      }
+
+      // mask (tiles the mask does not cover entirely); masked tiles move to the log2
+      // domain here (cm = 1), unmasked ones are scaled inside the exponent (cm = cexp)
+      float cm = cexp;
+      if constexpr (GATHER) {
+        const int32_t* xr = reinterpret_cast<const int32_t*>(vs + TL::vBytes);
+        const float* xzl = reinterpret_cast<const float*>(xr + BN);
+        const int32_t* xi = xr + 2 * BN;
+        if (xi[BN - 1] > P0)  // the list ascends: its last key decides whether positions matter
+          mask_tile_topk_list<NKB, true>(sacc, hf, pos, tau_row, cexp, xr, xzl, xi);
+        else
+          mask_tile_topk_list<NKB, false>(sacc, hf, pos, tau_row, cexp, xr, xzl, xi);
+        cm = 1.f;
+      } else if constexpr (MK == MI_ATTN_MASK_TOPK) {
+        const int32_t* xr = reinterpret_cast<const int32_t*>(vs + TL::vBytes);
+        const float* xzl = reinterpret_cast<const float*>(xr + BN);
+        if (j0 + BN - 1 > P0)
+          mask_tile_topk<NKB, true>(sacc, j0, hf, pos, tau_row, cexp, xr, xzl);
+        else
+          mask_tile_topk<NKB, false>(sacc, j0, hf, pos, tau_row, cexp, xr, xzl);
+        cm = 1.f;
+      } else if (tile_needs_mask<MK, BN>(p, Lk, j0, P0, P1)) {
+        mask_tile<MK, NKB>(sacc, p, Lk, j0, hf, pos, i_row, tau_row, cexp, nullptr, nullptr);
+        cm = 1.f;
+      }
+
+      // online softmax (log2 domain), guarded against all -inf tiles and rows
+      float mx4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};  // four independent chains
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int dc = 0; dc < NDC; ++dc)
-          kf[kb][dc] = *reinterpret_cast<const u32x4_t*>(smem + kb * 32 * TL::rowBytes +
-                                                         ((k_base + ks_ofs) ^ (dc << 5)));
+        for (int e = 0; e < 16; ++e) mx4[e & 3] = fmaxf(mx4[e & 3], sacc[kb][e]);
+      float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
+      mx = max_halves(mx) * cm;
+      const float m_next = (mx > m_run + kRescaleThreshold) ? mx : m_run;
+      const float m_use = (m_next == kNegInf) ? 0.f : m_next;
+      const float alpha = fast_exp2(m_run - m_use);  // 1 when the max did not move, 0 from -inf
+      float ps4[4] = {0.f, 0.f, 0.f, 0.f};  // four independent chains
+      u32x4_t preg[BN / 16];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        f32x16_t acc = f32x16_t{};
 #pragma unroll
-        for (int dc = 0; dc < NDC; ++dc) acc = mfma32(T{}, kf[kb][dc], qreg[dc], acc);
-        sacc[kb] = acc;
-      }
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NDC, 0);
+        for (int half = 0; half < 2; ++half) {
+          float pv[8];
 #pragma unroll
-      for (int i = 0; i < (NKB - 1) * NDC; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, NDC, 0);
-    }
-
-    // mask (tiles the mask does not cover entirely); masked tiles move to the log2
-    // domain here (cm = 1), unmasked ones are scaled inside the exponent (cm = cexp)
-    float cm = cexp;
-    if constexpr (GATHER) {
-      const int32_t* xr = reinterpret_cast<const int32_t*>(vs + TL::vBytes);
-      const float* xzl = reinterpret_cast<const float*>(xr + BN);
-      const int32_t* xi = xr + 2 * BN;
-      if (xi[BN - 1] > P0)  // the list ascends: its last key decides whether positions matter
-        mask_tile_topk_list<NKB, true>(sacc, hf, pos, tau_row, cexp, xr, xzl, xi);
-      else
-        mask_tile_topk_list<NKB, false>(sacc, hf, pos, tau_row, cexp, xr, xzl, xi);
-      cm = 1.f;
-    } else if constexpr (MK == MI_ATTN_MASK_TOPK) {
-      const int32_t* xr = reinterpret_cast<const int32_t*>(vs + TL::vBytes);
-      const float* xzl = reinterpret_cast<const float*>(xr + BN);
-      if (j0 + BN - 1 > P0)
-        mask_tile_topk<NKB, true>(sacc, j0, hf, pos, tau_row, cexp, xr, xzl);
-      else
-        mask_tile_topk<NKB, false>(sacc, j0, hf, pos, tau_row, cexp, xr, xzl);
-      cm = 1.f;
-    } else if (tile_needs_mask<MK, BN>(p, j0, P0, P1)) {
-      mask_tile<MK, NKB>(sacc, p, j0, hf, pos, i_row, tau_row, cexp, nullptr, nullptr);
-      cm = 1.f;
-    }
-
-    // online softmax (log2 domain), guarded against all -inf tiles and rows
-    float mx4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};  // four independent chains
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx4[e & 3] = fmaxf(mx4[e & 3], sacc[kb][e]);
-    float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
-    mx = max_halves(mx) * cm;
-    const float m_next = (mx > m_run + kRescaleThreshold) ? mx : m_run;
-    const float m_use = (m_next == kNegInf) ? 0.f : m_next;
-    const float alpha = fast_exp2(m_run - m_use);  // 1 when the max did not move, 0 from -inf
-    float ps4[4] = {0.f, 0.f, 0.f, 0.f};  // four independent chains
-    u32x4_t preg[BN / 16];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        float pv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pv[e] = fast_exp2(fmaf(sacc[kb][half * 8 + e], cm, -m_use));
-          ps4[e & 3] += pv[e];
+          for (int e = 0; e < 8; ++e) {
+            pv[e] = fast_exp2(fmaf(sacc[kb][half * 8 + e], cm, -m_use));
+            ps4[e & 3] += pv[e];
+          }
+          u32x4_t pk;
+          pk.x = pack2(T{}, pv[0], pv[1]);
+          pk.y = pack2(T{}, pv[2], pv[3]);
+          pk.z = pack2(T{}, pv[4], pv[5]);
+          pk.w = pack2(T{}, pv[6], pv[7]);
+          preg[kb * 2 + half] = pk;
         }
-        u32x4_t pk;
-        pk.x = pack2(T{}, pv[0], pv[1]);
-        pk.y = pack2(T{}, pv[2], pv[3]);
-        pk.z = pack2(T{}, pv[4], pv[5]);
-        pk.w = pack2(T{}, pv[6], pv[7]);
-        preg[kb * 2 + half] = pk;
       }
-    }
-    l_run = fmaf(l_run, alpha, (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]));
-    m_run = m_next;
-    if (!__all(alpha == 1.f)) {
+      l_run = fmaf(l_run, alpha, (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]));
+      m_run = m_next;
+      if (!__all(alpha == 1.f)) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
-    }
+        for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+      }
 
-    // O^T += V^T P^T. The V^T operand comes from two transposed reads: lane (16 * g + i)
-    // reads 8 bytes of key row R0 + i / 4 at dims D0 + 4 * (i % 4) and receives keys
-    // R0..R0+3 of dim D0 + i. Keys 4*hf+0..3 and 8+4*hf+0..3 of the 16-key chunk are what
-    // its P registers hold. Key chunks run outermost, so the NDB accumulators are
-    // independent chains, and the next chunk's V fragments are read during this chunk's
-    // MFMAs.
-    // The PV MFMAs issue at raised wavefront priority: when the other wavefront on the SIMD
-    // has vector work ready at the same time, the matrix core is kept fed first (measured
-    // +4% on c3 prefill; raising it for the QK MFMAs as well gains nothing).
-    __builtin_amdgcn_s_setprio(1);
-    {
-      constexpr int NKC = BN / 16;
-      const int vb0 = v_base0 + vs_ofs, vb1 = v_base1 + vs_ofs;
-      u32x4_t vf[NKC][NDB];
+      // O^T += V^T P^T. The V^T operand comes from two transposed reads: lane (16 * g + i)
+      // reads 8 bytes of key row R0 + i / 4 at dims D0 + 4 * (i % 4) and receives keys
+      // R0..R0+3 of dim D0 + i. Keys 4*hf+0..3 and 8+4*hf+0..3 of the 16-key chunk are what
+      // its P registers hold. Key chunks run outermost, so the NDB accumulators are
+      // independent chains, and the next chunk's V fragments are read during this chunk's
+      // MFMAs.
+      // The PV MFMAs issue at raised wavefront priority: when the other wavefront on the SIMD
+      // has vector work ready at the same time, the matrix core is kept fed first (measured
+      // +4% on c3 prefill; raising it for the QK MFMAs as well gains nothing).
+      __builtin_amdgcn_s_setprio(1);
+      {
+        constexpr int NKC = BN / 16;
+        const int vb0 = v_base0 + vs_ofs, vb1 = v_base1 + vs_ofs;
+        u32x4_t vf[NKC][NDB];
 #pragma unroll
-      for (int kc = 0; kc < NKC; ++kc)
+        for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const unsigned char* row = smem + kc * 16 * TL::rowBytes;
-          const u32x2_t lo = lds_read_tr16(row + (vb0 ^ (db << 6)));
-          const u32x2_t hi2 = lds_read_tr16(row + (vb1 ^ (db << 6)));
-          vf[kc][db] = u32x4_t{lo.x, lo.y, hi2.x, hi2.y};
+          for (int db = 0; db < NDB; ++db) {
+            const unsigned char* row = smem + kc * 16 * TL::rowBytes;
+            const u32x2_t lo = lds_read_tr16(row + (vb0 ^ (db << 6)));
+            const u32x2_t hi2 = lds_read_tr16(row + (vb1 ^ (db << 6)));
+            vf[kc][db] = u32x4_t{lo.x, lo.y, hi2.x, hi2.y};
+          }
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(T{}, vf[kc][db], preg[kc], oacc[db]);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * NDB, 0);
+#pragma unroll
+        for (int i = 0; i < (NKC - 1) * NDB; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
         }
-#pragma unroll
-      for (int kc = 0; kc < NKC; ++kc)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(T{}, vf[kc][db], preg[kc], oacc[db]);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * NDB, 0);
-#pragma unroll
-      for (int i = 0; i < (NKC - 1) * NDB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, NDB, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, NDB, 0);
-    }
-    __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_s_setprio(0);
+    }  // wave_live
 
     if (tn < t_hi) finish_tile(stage ^ 1);
     __syncthreads();
@@ -416,7 +497,6 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK>)) void prefill_kernel(
   const float inv = dead ? 0.f : 1.f / l_tot;
   const float lse = dead ? kNegInf : (m_run + fast_log2(l_tot)) * kLn2;
   if (p.splits > 1) {
-    const long rows_all = static_cast<long>(p.B) * p.Hq * p.Lq;
     float* po = p.part_out + (static_cast<long>(split) * rows_all + row_index) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -518,7 +598,102 @@ hipError_t launch_prefill_t(const AttnParams& p, hipStream_t s) {
   return launch_lse_merge_t<T>(p, s);
 }
 
+// Work units of a varlen call: each sequence's query blocks (the last, longest causal
+// range first), sequences in order. One workgroup scans the per-sequence block counts
+// 1024 sequences at a time; units past `cap` (possible only when cu_q is inconsistent)
+// are dropped.
+constexpr int kSchedThreads = 1024;
+
+__global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(const int32_t* cu_q, int S, int total_q,
+                                                                        int qpb, int cap, int2* sched,
+                                                                        int32_t* count) {
+  __shared__ long long wsum[kSchedThreads / kWave];
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = tid / kWave;
+  long long carry = 0;  // units before this pass (same value in every thread)
+  for (int base = 0; base < S; base += kSchedThreads) {
+    const int s = base + tid;
+    int n = 0;
+    if (s < S) {
+      const int a = min(max(cu_q[s], 0), total_q);
+      const int b = min(max(cu_q[s + 1], a), total_q);
+      n = (b - a + qpb - 1) / qpb;
+    }
+    long long x = n;  // inclusive scan inside the wavefront
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const long long y = __shfl_up(x, o, kWave);
+      if (lane >= o) x += y;
+    }
+    if (lane == kWave - 1) wsum[wave] = x;
+    __syncthreads();
+    long long before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kSchedThreads / kWave; ++w) {
+      if (w < wave) before += wsum[w];
+      total += wsum[w];
+    }
+    const long long start = carry + before + x - n;
+    for (int k = 0; k < n; ++k) {
+      const long long u = start + k;
+      if (u >= cap) break;
+      sched[u] = make_int2(s, n - 1 - k);
+    }
+    carry += total;
+    __syncthreads();  // wsum is rewritten by the next pass
+  }
+  if (tid == 0) *count = static_cast<int32_t>(carry < cap ? carry : cap);
+}
+
+template <typename T>
+hipError_t launch_prefill_varlen_t(const AttnParams& p, hipStream_t s) {
+  const long blocks = static_cast<long>(p.sched_cap) * p.Hkv;
+  if (blocks > 0x7fffffffL || p.splits > 65535) return hipErrorInvalidValue;
+  dim3 grid(static_cast<unsigned>(blocks), p.splits), block(kThreads);
+  if (p.d == 128) {
+    switch (p.mask_kind) {
+      case MI_ATTN_MASK_NONE:
+        hipLaunchKernelGGL((prefill_kernel<T, 128, 64, 0, false, true>), grid, block, 0, s, p);
+        break;
+      case MI_ATTN_MASK_CAUSAL:
+        hipLaunchKernelGGL((prefill_kernel<T, 128, 64, 1, false, true>), grid, block, 0, s, p);
+        break;
+      default: hipLaunchKernelGGL((prefill_kernel<T, 128, 64, 2, false, true>), grid, block, 0, s, p); break;
+    }
+  } else {
+    switch (p.mask_kind) {
+      case MI_ATTN_MASK_NONE:
+        hipLaunchKernelGGL((prefill_kernel<T, 64, 64, 0, false, true>), grid, block, 0, s, p);
+        break;
+      case MI_ATTN_MASK_CAUSAL:
+        hipLaunchKernelGGL((prefill_kernel<T, 64, 64, 1, false, true>), grid, block, 0, s, p);
+        break;
+      default: hipLaunchKernelGGL((prefill_kernel<T, 64, 64, 2, false, true>), grid, block, 0, s, p); break;
+    }
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.splits <= 1) return e;
+  AttnParams m = p;  // partial rows are the token-major output rows
+  m.B = 1;
+  m.Lq = p.total_q;
+  return launch_lse_merge_t<T>(m, s);
+}
+
 }  // namespace
+
+hipError_t launch_prefill_varlen(const AttnParams& p, int dtype, int2* sched, int32_t* sched_count,
+                                 hipStream_t s) {
+  if (dtype != MI_ATTN_BF16 && dtype != MI_ATTN_F16) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(varlen_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, s, p.cu_q, p.num_seqs, p.total_q,
+                     p.q_per_block, p.sched_cap, sched, sched_count);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  AttnParams pv = p;
+  pv.sched = sched;
+  pv.sched_count = sched_count;
+  return dtype == MI_ATTN_BF16 ? launch_prefill_varlen_t<bf16_t>(pv, s) : launch_prefill_varlen_t<f16_t>(pv, s);
+}
 
 int prefill_block_n(int) { return 64; }
 int prefill_block_m() { return kBlockM; }

@@ -21,4 +21,15 @@ HalfPlan plan_half_path(int path, int B, int Hkv, int G, int Lq, int Lk, int d, 
                         int force_splits);
 hipError_t launch_half_path(int path, const AttnParams& p, int dtype, hipStream_t s);
 
+// MFMA prefill tile shape: query rows and keys per workgroup tile.
+int prefill_block_m();
+int prefill_block_n(int d);
+
+// Varlen / paged forward (attn_fwd_varlen): query positions per workgroup for G heads
+// per KV head, the key-range split count, and the launch (schedule kernel, MFMA kernel,
+// and the LSE merge when split). sched must hold p.sched_cap entries.
+int varlen_q_per_block(int G);
+int varlen_splits(long blocks, int max_seqlen_k, int force_splits);
+hipError_t launch_prefill_varlen(const AttnParams& p, int dtype, int2* sched, int32_t* sched_count, hipStream_t s);
+
 }  // namespace mi_attn

@@ -127,6 +127,17 @@ __device__ __forceinline__ void lds_dma16_at(__amdgpu_buffer_rsrc_t rs, unsigned
                : "memory", "m0");
 }
 
+// The same from a per-lane 64-bit global address (global_load_lds_dwordx4): lane i's 16
+// bytes from src land at lds_addr + 16 * i. Used where the rows of one tile come from
+// unrelated places (cache pages), which a 32-bit buffer offset cannot always reach.
+__device__ __forceinline__ void lds_dma16_global(unsigned lds_addr, const void* src) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(m0), "v"(src)
+               : "memory", "m0");
+}
+
 // s_waitcnt immediate for "at most n vector-memory operations outstanding" (gfx9
 // encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their maximum).
 constexpr int vmcnt_imm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
@@ -135,9 +146,11 @@ constexpr int vmcnt_imm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4
 // l % 32 and, per 32-key block kb, keys kb*32 + 8*(i/4) + 4*hf + i%4 in register i).
 // Visible logits move to the log2 domain (s * cexp + bias * log2 e); hidden ones become
 // -inf. `xr`/`xz` are the tile's top-k ranks and zero_hold values (index = key - j0).
+// Lk is the key count of the (batch or sequence) the tile belongs to.
 template <int MK, int NKB>
-__device__ __forceinline__ void mask_tile(f32x16_t* sacc, const AttnParams& p, int j0, int hf, int pos, int i_row,
-                                          int32_t tau_row, float cexp, const int32_t* xr, const float* xz) {
+__device__ __forceinline__ void mask_tile(f32x16_t* sacc, const AttnParams& p, int Lk, int j0, int hf, int pos,
+                                          int i_row, int32_t tau_row, float cexp, const int32_t* xr,
+                                          const float* xz) {
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -147,7 +160,7 @@ __device__ __forceinline__ void mask_tile(f32x16_t* sacc, const AttnParams& p, i
       for (int e = 0; e < 4; ++e) {
         const int j = j0 + kk + e;
         float s = sacc[kb][r4 * 4 + e] * cexp;
-        bool vis = j < p.Lk;
+        bool vis = j < Lk;
         if constexpr (MK == MI_ATTN_MASK_CAUSAL) vis = vis && j <= pos;
         if constexpr (MK == MI_ATTN_MASK_WINDOW) vis = vis && j <= pos && j >= pos - p.window_left;
         // side reads use key j0 (always < Lk in a visited tile) in place of keys past Lk
@@ -225,9 +238,9 @@ __device__ __forceinline__ void mask_tile_topk_list(f32x16_t* sacc, int hf, int 
 // Whether a tile [j0, j0 + BN) needs per-element masking for a block whose query rows sit
 // at positions P0..P1: tiles every row sees entirely (and inside Lk) skip it.
 template <int MK, int BN>
-__device__ __forceinline__ bool tile_needs_mask(const AttnParams& p, int j0, int P0, int P1) {
+__device__ __forceinline__ bool tile_needs_mask(const AttnParams& p, int Lk, int j0, int P0, int P1) {
   const int j_end = j0 + BN - 1;
-  bool need = p.no_skip || j_end >= p.Lk || MK == MI_ATTN_MASK_DENSE || MK == MI_ATTN_MASK_TOPK;
+  bool need = p.no_skip || j_end >= Lk || MK == MI_ATTN_MASK_DENSE || MK == MI_ATTN_MASK_TOPK;
   if constexpr (MK == MI_ATTN_MASK_CAUSAL || MK == MI_ATTN_MASK_WINDOW) need = need || j_end > P0;
   if constexpr (MK == MI_ATTN_MASK_WINDOW) need = need || j0 < P1 - p.window_left;
   return need;

@@ -6,8 +6,6 @@
 
 namespace mi_attn {
 
-int prefill_block_n(int d);
-int prefill_block_m();
 int decode_block_n();
 int decode_max_rows();
 hipError_t launch_prefill(const AttnParams& p, int dtype, hipStream_t s);
@@ -84,6 +82,17 @@ HalfPlan plan_half_path(int path, int B, int Hkv, int G, int Lq, int Lk, int d, 
   const int tiles_per_split = (tiles + splits - 1) / splits;
   h.splits = (tiles + tiles_per_split - 1) / tiles_per_split;
   return h;
+}
+
+int varlen_q_per_block(int G) { return q_per_block_for(G); }
+
+int varlen_splits(long blocks, int max_seqlen_k, int force_splits) {
+  const int bn = prefill_block_n(128);
+  const int tiles = (max_seqlen_k + bn - 1) / bn;
+  int s = force_splits > 0 ? force_splits
+                           : auto_splits(static_cast<int>(blocks < 0x7fffffff ? blocks : 0x7fffffff), max_seqlen_k, bn);
+  if (s > tiles) s = tiles;
+  return s < 1 ? 1 : s;
 }
 
 hipError_t launch_half_path(int path, const AttnParams& p, int dtype, hipStream_t s) {

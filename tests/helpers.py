@@ -80,3 +80,61 @@ def compare(p: synth.Problem, out, lse, ref_out, ref_lse, rows=None, heads=None,
     assert err_o <= tol_o, f"{label}: output error {err_o} > {tol_o}"
     assert err_l <= tol_l, f"{label}: LSE error {err_l} > {tol_l}"
     return err_o, err_l
+
+
+# ---------------------------------------------------------------- varlen / paged problems
+def run_gpu_paged(p: synth.PagedProblem, *, out_fill=None, max_seqlen_k=None):
+    import torch
+    import masked_flashattention_forward_amd as mfa
+    q, k, v = (to_device(getattr(p, n), p.dtype) for n in ("q", "k", "v"))
+    kn = vn = None
+    if p.two_source:
+        kn, vn = to_device(p.k_new, p.dtype), to_device(p.v_new, p.dtype)
+    cu_q = torch.from_numpy(p.cu_seqlens_q).cuda()
+    cu_k = torch.from_numpy(p.cu_seqlens_k).cuda()
+    bt = None if p.block_table is None else torch.from_numpy(p.block_table).cuda()
+    out = torch.empty_like(q)
+    lse = torch.empty((p.total_q, p.Hq), dtype=torch.float32, device=q.device)
+    if out_fill is not None:
+        out.fill_(out_fill)
+        lse.fill_(out_fill)
+    mfa.attn_fwd_varlen(q, k, v, cu_q, cu_k, max_seqlen_q=p.max_seqlen_q,
+                        max_seqlen_k=p.max_seqlen_k if max_seqlen_k is None else max_seqlen_k,
+                        block_table=bt, k_new=kn, v_new=vn, scale=p.scale, mask_kind=p.mask_kind,
+                        window_left=p.window_left, out=out, lse=lse)
+    torch.cuda.synchronize()
+    return out_to_f64(out, p.dtype), lse.cpu().numpy().astype(np.float64)
+
+
+def run_oracle_paged(p: synth.PagedProblem, seqs=None):
+    """fp64 oracle; with ``seqs`` only those sequences are computed (their K/V rows are
+    gathered from the cache in storage form first) and the other rows are NaN."""
+    if seqs is None:
+        return oracle.paged_attention_ref(p.f64("q"), p.f64("k"), p.f64("v"), p.cu_seqlens_q, p.cu_seqlens_k,
+                                          p.block_table, p.page_size, p.scale, p.mask_kind,
+                                          window_left=p.window_left, k_new=p.f64("k_new"), v_new=p.f64("v_new"))
+    out = np.full((p.total_q, p.Hq, p.d), np.nan)
+    lse = np.full((p.total_q, p.Hq), np.nan)
+    for s in seqs:
+        q0, q1 = int(p.cu_seqlens_q[s]), int(p.cu_seqlens_q[s + 1])
+        Lk = int(p.k_lens[s])
+        ctx = max(Lk - (q1 - q0), 0) if p.two_source else Lk
+        j = np.arange(ctx)
+        if p.block_table is None:
+            rows_k = p.k[int(p.cu_seqlens_k[s]) + j]
+            rows_v = p.v[int(p.cu_seqlens_k[s]) + j]
+        else:
+            pg = p.block_table[s][j // p.page_size]
+            rows_k, rows_v = p.k[pg, j % p.page_size], p.v[pg, j % p.page_size]
+        # a one-sequence packed problem holding all Lk rows (the new-token rows unused)
+        kk = np.zeros((Lk,) + rows_k.shape[1:], dtype=rows_k.dtype)
+        vv = np.zeros_like(kk)
+        kk[:ctx], vv[:ctx] = rows_k, rows_v
+        f = lambda a: synth.storage_to_f64(a, p.dtype)  # noqa: E731
+        o, l = oracle.paged_attention_ref(
+            f(p.q[q0:q1]), f(kk), f(vv), [0, q1 - q0], [0, Lk], None, 0, p.scale, p.mask_kind,
+            window_left=p.window_left,
+            k_new=None if not p.two_source else f(p.k_new[q0:q1]),
+            v_new=None if not p.two_source else f(p.v_new[q0:q1]))
+        out[q0:q1], lse[q0:q1] = o, l
+    return out, lse

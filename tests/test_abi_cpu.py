@@ -151,3 +151,37 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(mfa, "_lib", None)
     with pytest.raises(mfa.MiAttnError):
         mfa.lib()
+
+
+def varlen_rc(lib, **kw):
+    """attn_fwd_varlen with NULL device pointers: only host validation can run."""
+    a = dict(q=None, k=None, v=None, out=None, lse=None, cu_q=None, max_q=1, cu_k=None, max_k=8, num_seqs=2,
+             total_q=0, Hq=4, Hkv=2, d=128, scale=0.1, mask_kind=1, window_left=0, block_table=None,
+             max_pages=4, page_size=16, kv_rows=8, k_new=None, v_new=None, dtype=2, stream=None)
+    a.update(kw)
+    return lib.attn_fwd_varlen(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(total_q=-1), -1), (dict(num_seqs=-1), -1), (dict(max_k=-1), -1),
+    (dict(Hq=3), -1), (dict(Hkv=0), -1), (dict(mask_kind=9), -1), (dict(dtype=7), -1),
+    (dict(mask_kind=2, window_left=-2), -1), (dict(scale=float("inf")), -1),
+    (dict(k_new=ctypes.c_void_p(16)), -1),                                  # k_new without v_new
+    (dict(block_table=ctypes.c_void_p(16), page_size=12), -1),              # not a power of two
+    (dict(block_table=ctypes.c_void_p(16), page_size=0), -1),
+    (dict(block_table=ctypes.c_void_p(16), max_pages=0), -1),
+    (dict(kv_rows=0), -1),
+    (dict(dtype=0), -2), (dict(d=96), -2), (dict(mask_kind=3), -2), (dict(mask_kind=4), -2),
+    (dict(Hq=256, Hkv=1), -2),                                              # more heads per KV head than rows
+    (dict(total_q=5), -1),                                                  # NULL tensors with work to do
+])
+def test_varlen_rejects_invalid_arguments(lib, kw, code):
+    assert varlen_rc(lib, **kw) == code
+    assert lib.attn_last_error().decode() != ""
+
+
+def test_varlen_with_no_queries_enqueues_nothing(lib):
+    # total_q == 0 returns before any device pointer or stream is used
+    assert varlen_rc(lib, total_q=0) == 0
+    assert varlen_rc(lib, total_q=0, block_table=ctypes.c_void_p(16), page_size=32) == 0
+    assert varlen_rc(lib, num_seqs=0, total_q=0) == 0
