@@ -59,6 +59,11 @@ def lib() -> ctypes.CDLL:
     """The loaded library; raises if it has not been built."""
     global _lib
     if _lib is None:
+        # torch first: it ships its own HIP runtime under the same soname
+        # (libamdhip64.so.7); loading the library before torch would bring the system
+        # copy into the process as well, and two HIP runtimes do not share devices,
+        # allocations or streams.
+        import torch  # noqa: F401
         if not os.path.exists(LIB_PATH):
             raise MiAttnError(EHIP, f"{LIB_PATH} is missing: build it with "
                                     "`python -m masked_flashattention_forward_amd.build`")

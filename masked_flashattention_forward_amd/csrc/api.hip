@@ -287,8 +287,13 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, floa
     if (max_pages < 1) return fail(MI_ATTN_EINVAL, "max_pages must be >= 1 (got %d)", max_pages);
     while ((1 << page_shift) < page_size) ++page_shift;
     if (static_cast<double>(kv_rows) * page_size > 2147483647.0)
-      return fail(MI_ATTN_EINVAL, "kv_rows * page_size must stay below 2^31 keys");
+      return fail(MI_ATTN_EUNSUPPORTED, "kv_rows * page_size must stay below 2^31 keys");
+    if (static_cast<double>(max_pages) * page_size > 1073741824.0)
+      return fail(MI_ATTN_EUNSUPPORTED, "max_pages * page_size must stay at or below 2^30 keys");
+  } else if (kv_rows > (1 << 30)) {
+    return fail(MI_ATTN_EUNSUPPORTED, "packed K/V must have at most 2^30 rows");
   }
+  if (total_q > (1 << 30)) return fail(MI_ATTN_EUNSUPPORTED, "total_q must be at most 2^30");
   if (dtype == MI_ATTN_F32) return fail(MI_ATTN_EUNSUPPORTED, "varlen attention takes fp16/bf16 inputs");
   if (d != 64 && d != 128) return fail(MI_ATTN_EUNSUPPORTED, "head dim must be 64 or 128 (got %d)", d);
   if (mask_kind == MI_ATTN_MASK_DENSE || mask_kind == MI_ATTN_MASK_TOPK)
@@ -303,49 +308,60 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, floa
     return fail(MI_ATTN_EINVAL, "q, k, v, out, cu_seqlens_q and cu_seqlens_k must not be NULL");
 
   // work units: sum over sequences of ceil(Lq_s / qpb) <= (total_q + num_seqs * (qpb - 1)) / qpb
+  // (a decode-type sequence is one unit, which that bound also covers)
   const int qpb = varlen_q_per_block(G);
-  const long cap = (static_cast<long>(total_q) + static_cast<long>(num_seqs) * (qpb - 1)) / qpb;
-  if (cap * Hkv > 0x7fffffffL) return fail(MI_ATTN_EUNSUPPORTED, "too many work units (%ld)", cap * Hkv);
-  const int splits = varlen_splits(cap * Hkv, max_seqlen_k, g_force_splits);
+  const long units_cap = (static_cast<long>(total_q) + static_cast<long>(num_seqs) * (qpb - 1)) / qpb;
+  if (units_cap > 0x3fffffffL) return fail(MI_ATTN_EUNSUPPORTED, "too many work units (%ld)", units_cap);
+  VarlenBuffers b{};
+  b.units_cap = static_cast<int>(units_cap);
+  b.target_items = varlen_target_items(Hkv);
+  b.force_items = g_force_splits;
+  b.items_cap = varlen_items_cap(b.units_cap, b.target_items, b.force_items);
+  if (static_cast<long>(b.items_cap) * Hkv > 0x7fffffffL)
+    return fail(MI_ATTN_EUNSUPPORTED, "too many workgroups (%ld items x %d KV heads)", static_cast<long>(b.items_cap),
+                Hkv);
+  const size_t ic = static_cast<size_t>(b.items_cap) * Hkv;
   size_t off = 0;
-  const size_t off_sched = off;
-  off = align256(off + sizeof(int2) * cap);
-  const size_t off_cnt = off;
-  off = align256(off + sizeof(int32_t));
-  size_t off_pout = 0, off_plse = 0;
-  if (splits > 1) {
-    const size_t rows = static_cast<size_t>(total_q) * Hq;
-    off_pout = off; off = align256(off + sizeof(float) * splits * rows * d);
-    off_plse = off; off = align256(off + sizeof(float) * splits * rows);
-  }
+  const size_t off_units = off; off = align256(off + sizeof(int4) * b.units_cap);
+  const size_t off_ip = off;    off = align256(off + sizeof(int4) * b.items_cap);
+  const size_t off_id = off;    off = align256(off + sizeof(int4) * b.items_cap);
+  const size_t off_cnt = off;   off = align256(off + sizeof(int32_t) * 3);
+  const size_t off_ppo = off;   off = align256(off + sizeof(float) * ic * kVarlenPrefillRows * d);
+  const size_t off_ppl = off;   off = align256(off + sizeof(float) * ic * kVarlenPrefillRows);
+  const size_t off_pdo = off;   off = align256(off + sizeof(float) * ic * 32 * d);
+  const size_t off_pdl = off;   off = align256(off + sizeof(float) * ic * 32);
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* ws = nullptr;
   hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&ws), off, st);
   if (e != hipSuccess) return hip_fail(e, "hipMallocAsync(workspace)");
+  b.units = reinterpret_cast<int4*>(ws + off_units);
+  b.items_p = reinterpret_cast<int4*>(ws + off_ip);
+  b.items_d = reinterpret_cast<int4*>(ws + off_id);
+  b.counts = reinterpret_cast<int32_t*>(ws + off_cnt);
+  b.pp_out = reinterpret_cast<float*>(ws + off_ppo);
+  b.pp_lse = reinterpret_cast<float*>(ws + off_ppl);
+  b.pd_out = reinterpret_cast<float*>(ws + off_pdo);
+  b.pd_lse = reinterpret_cast<float*>(ws + off_pdl);
 
   AttnParams p{};
   p.q = q; p.k = k; p.v = v; p.out = out; p.lse = lse;
   p.B = 1; p.Hq = Hq; p.Hkv = Hkv; p.Lq = 0; p.Lk = 0; p.d = d; p.G = G;
   p.scale = scale; p.mask_kind = mask_kind; p.window_left = window_left;
   p.no_skip = g_no_skip;
-  p.splits = splits;
+  p.splits = 1;
   p.block_n = prefill_block_n(d);
   p.q_per_block = qpb;
   p.cu_q = cu_seqlens_q; p.cu_k = cu_seqlens_k;
   p.block_table = block_table; p.k_new = k_new; p.v_new = v_new;
-  p.sched_cap = static_cast<int>(cap);
   p.num_seqs = num_seqs; p.total_q = total_q;
   p.max_pages = block_table != nullptr ? max_pages : 1;
   p.page_shift = page_shift;
   p.kv_rows = kv_rows;
-  if (splits > 1) {
-    p.part_out = reinterpret_cast<float*>(ws + off_pout);
-    p.part_lse = reinterpret_cast<float*>(ws + off_plse);
-  }
-  e = launch_prefill_varlen(p, dtype, reinterpret_cast<int2*>(ws + off_sched),
-                            reinterpret_cast<int32_t*>(ws + off_cnt), st);
+  (void)max_seqlen_q;
+  (void)max_seqlen_k;
+  e = launch_varlen(p, dtype, b, st);
   const hipError_t ef = hipFreeAsync(ws, st);
-  if (e != hipSuccess) return hip_fail(e, "varlen attention kernel");
+  if (e != hipSuccess) return hip_fail(e, "varlen attention kernels");
   if (ef != hipSuccess) return hip_fail(ef, "hipFreeAsync(workspace)");
   return MI_ATTN_OK;
 }

@@ -91,12 +91,18 @@ struct AttnParams {
   const int32_t* block_table;   // [num_seqs, max_pages]
   const void* k_new;            // two-source form: [total_q, Hkv, d], the last Lq keys
   const void* v_new;
-  const int2* sched;            // work units (sequence, query block), sched_count valid
-  const int32_t* sched_count;
-  int sched_cap;                // units the grid provides for (upper bound)
+  // work lists built on the device (varlen_plan_kernel): a unit is (sequence, query
+  // block), split into items, each a key range [k0, k1) handled by one workgroup per KV
+  // head. Units with one item write the output; the others write partials that
+  // varlen_merge_kernel combines.
+  const int4* vl_units;         // {sequence, query block, first item, items | decode-type << 30}
+  const int4* vl_items;         // the launching kernel's list: {unit, k0, k1, 0}
+  const int32_t* vl_counts;     // {units, prefill-type items, decode-type items}
+  int vl_items_cap;             // entries of each item list (grid x = vl_items_cap * Hkv)
   int num_seqs, total_q, max_pages, page_shift, kv_rows;
-  float* part_out;         // split-KV partials [splits, rows, d] fp32 (rows: B*Hq*Lq or total_q*Hq)
-  float* part_lse;         // split-KV partials [splits, rows] fp32 (natural log)
+  float* part_out;         // split-KV partials [splits, B*Hq*Lq, d] fp32, or per varlen item
+                           // [items_cap, Hkv, rows per workgroup, d]
+  float* part_lse;         // the matching LSE partials (natural log)
   int B, Hq, Hkv, Lq, Lk, d;
   int G;                   // Hq / Hkv
   float scale;

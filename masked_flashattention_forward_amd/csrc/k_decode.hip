@@ -42,8 +42,12 @@ struct DecTile {
   static_assert((kDecWaves - 1) * mergeFloats * 4 <= lds, "merge area fits in the rings");
 };
 
-template <typename T, int D, int MK>
+// VARLEN: one item of the varlen work list (a key range of a sequence with at most 32
+// query rows per KV head); K/V rows come from cache pages, packed rows or the new-token
+// arrays through per-lane 64-bit addresses, and the output is token-major.
+template <typename T, int D, int MK, bool VARLEN = false>
 __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(AttnParams p) {
+  static_assert(!VARLEN || MK <= MI_ATTN_MASK_WINDOW, "varlen takes the key-position masks");
   using TL = DecTile<D>;
   constexpr int NDB = TL::NDB;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[TL::lds];
@@ -54,20 +58,45 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(AttnParams p) {
   const int l32 = lane & 31;
   const int hf = lane >> 5;
 
-  const int bg = blockIdx.x;
-  const int b = bg / p.Hkv;
-  const int g = bg % p.Hkv;
+  int bg, b, g, Lq, Lk;
   const int split = blockIdx.y;
-  const int rows = p.G * p.Lq;
-  const int P0 = p.Lk - p.Lq;      // position of the first query row
-  const int P1 = p.Lk - 1;         // position of the last
+  VarlenSeq vs{};
+  int item = 0;
+  bool item_partial = false;
+  int lo, hi;
+  if constexpr (VARLEN) {
+    // the KV heads of one item are consecutive workgroups (they read the same cache rows)
+    g = static_cast<int>(blockIdx.x % static_cast<unsigned>(p.Hkv));
+    item = static_cast<int>(blockIdx.x / static_cast<unsigned>(p.Hkv));
+    if (item >= p.vl_counts[2]) return;  // the whole workgroup, before any barrier
+    const int4 it = p.vl_items[item];
+    const int4 un = p.vl_units[it.x];
+    vs = varlen_seq(p, un.x);
+    item_partial = (un.w & 0x3fffffff) > 1;
+    lo = it.y;  // the item's key range, cut on 64-key boundaries by the work-list kernel
+    hi = it.z;
+    Lq = vs.Lq;
+    Lk = vs.Lk;
+    bg = 0;
+    b = 0;
+  } else {
+    bg = blockIdx.x;
+    b = bg / p.Hkv;
+    g = bg % p.Hkv;
+    Lq = p.Lq;
+    Lk = p.Lk;
+  }
+  const int rows = p.G * Lq;
+  const int P0 = Lk - Lq;      // position of the first query row
+  const int P1 = Lk - 1;       // position of the last
 
   // this lane's row (query-major: row r -> query r / G, head g*G + r % G)
   const bool row_ok = l32 < rows;
   const int i_row = row_ok ? l32 / p.G : 0;
   const int h_row = g * p.G + (row_ok ? l32 % p.G : 0);
-  const int pos = p.Lk - p.Lq + i_row;
-  const long row_index = (static_cast<long>(b) * p.Hq + h_row) * p.Lq + i_row;
+  const int pos = Lk - Lq + i_row;
+  const long row_index = VARLEN ? static_cast<long>(vs.q_start + i_row) * p.Hq + h_row
+                                : (static_cast<long>(b) * p.Hq + h_row) * Lq + i_row;
 
   const T* Q = static_cast<const T*>(p.q);
   const bool negate = p.scale < 0.f;
@@ -82,23 +111,22 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(AttnParams p) {
   }
 
   // key range of this split
-  int lo, hi;
-  key_range(MK, p.window_left, p.Lk, P0, P1, &lo, &hi);
-  if (p.no_skip) { lo = 0; hi = p.Lk; }
-  {
+  if constexpr (!VARLEN) {
+    key_range(MK, p.window_left, Lk, P0, P1, &lo, &hi);
+    if (p.no_skip) { lo = 0; hi = Lk; }
     const int s0 = split * p.keys_per_split;
-    const int s1 = min(p.Lk, s0 + p.keys_per_split);
+    const int s1 = min(Lk, s0 + p.keys_per_split);
     lo = max(lo, s0);
     hi = min(hi, s1);
   }
   const int t_lo = lo / kDecBN;
   const int t_hi = (hi > lo) ? (hi + kDecBN - 1) / kDecBN : t_lo;
-  const int ntiles_all = (p.Lk + kDecBN - 1) / kDecBN;
+  const int ntiles_all = (Lk + kDecBN - 1) / kDecBN;
 
-  const long kv_base = static_cast<long>(bg) * p.Lk * D;
-  const long bgk = static_cast<long>(bg) * p.Lk;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(static_cast<const T*>(p.k) + kv_base, p.Lk * D * 2);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(static_cast<const T*>(p.v) + kv_base, p.Lk * D * 2);
+  const long kv_base = VARLEN ? 0 : static_cast<long>(bg) * Lk * D;
+  const long bgk = static_cast<long>(bg) * Lk;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(static_cast<const T*>(p.k) + kv_base, VARLEN ? 0 : Lk * D * 2);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(static_cast<const T*>(p.v) + kv_base, VARLEN ? 0 : Lk * D * 2);
 
   int32_t tau_row = 0, tau_blk = 0;
   if constexpr (MK == MI_ATTN_MASK_TOPK) {
@@ -118,13 +146,39 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(AttnParams p) {
   };
 
   unsigned char* const ring = smem + wave * TL::waveBytes;
+  // VARLEN base pointers in registers (the per-lane cache / new-token choice selects values)
+  const T* const k_cache = static_cast<const T*>(p.k);
+  const T* const v_cache = static_cast<const T*>(p.v);
+  const T* const k_fresh = static_cast<const T*>(p.k_new);
+  const T* const v_fresh = static_cast<const T*>(p.v_new);
+  // VARLEN (paged form): block-table entry of key j0 + l32 of the next tile to issue,
+  // loaded one tile ahead; the V rows' entries come from the lanes holding those keys.
+  int page_next = 0;
   auto issue = [&](int t, u32x4_t* kr, int stg) {
     const int j0 = t * kDecBN;
+    unsigned char* dst = ring + stg * TL::vBytes;
+    if constexpr (VARLEN) {
+      const int page = page_next;
+      bool nk;
+      const long ek = varlen_row<D>(p, vs, g, j0 + l32, page, hf * 8, &nk);
+      const T* kb = pick(nk, k_fresh, k_cache) + ek;
+#pragma unroll
+      for (int dc = 0; dc < TL::kLoads; ++dc) kr[dc] = *reinterpret_cast<const u32x4_t*>(kb + dc * 16);
+#pragma unroll
+      for (int c = 0; c < TL::vLoads; ++c) {
+        const int r = c * (1024 / (D * 2)) + lane / (D / 8);
+        const int ps = lane % (D / 8);
+        bool nv;
+        const long ev = varlen_row<D>(p, vs, g, j0 + r, __shfl(page, r, kWave), (ps ^ swz<D>(r)) << 3, &nv);
+        lds_dma16_global(lds_address(dst + c * 1024), pick(nv, v_fresh, v_cache) + ev);
+      }
+      if (p.block_table != nullptr) page_next = varlen_page(p, vs, j0 + kDecWaves * kDecBN + l32);
+      return;
+    }
     // K: lane holds key j0 + l32, dims dc*16 + hf*8 .. +8 (the A operand of S^T = K Q^T)
 #pragma unroll
     for (int dc = 0; dc < TL::kLoads; ++dc) kr[dc] = buffer_load16(krs, ((j0 + l32) * D + dc * 16 + hf * 8) * 2);
     // V: 1 KB direct loads into the swizzled [key][d] tile
-    unsigned char* dst = ring + stg * TL::vBytes;
 #pragma unroll
     for (int c = 0; c < TL::vLoads; ++c) {
       const int r = c * (1024 / (D * 2)) + lane / (D / 8);
@@ -144,6 +198,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(AttnParams p) {
   u32x4_t kcur[TL::kLoads], knext[TL::kLoads];
   int t = next_tile(t_lo + wave);
   int stg = 0;
+  if (VARLEN && t < t_hi && p.block_table != nullptr) page_next = varlen_page(p, vs, t * kDecBN + l32);
   if (t < t_hi) issue(t, kcur, 0);
   const int tr_row = 4 * hf + (lane & 15) / 4;
   const int tr_dim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
@@ -152,7 +207,11 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(AttnParams p) {
     const int tn = next_tile(t + kDecWaves);
     if (tn < t_hi) {
       issue(tn, knext, stg ^ 1);
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerTile));  // tile t has landed
+      // tile t has landed (tn's loads, and the varlen block-table load behind them, may not)
+      if (VARLEN && p.block_table != nullptr)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerTile + 1));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerTile));
     } else {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
@@ -167,14 +226,14 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(AttnParams p) {
       sacc[0] = acc;
     }
     float cm = cexp;
-    if (tile_needs_mask<MK, kDecBN>(p, p.Lk, j0, P0, P1)) {
+    if (tile_needs_mask<MK, kDecBN>(p, Lk, j0, P0, P1)) {
       const int32_t* xr = nullptr;
       const float* xz = nullptr;
       if constexpr (MK == MI_ATTN_MASK_TOPK) {
         xr = p.rank + bgk + j0;
         xz = p.zero_hold + bgk + j0;
       }
-      mask_tile<MK, 1>(sacc, p, p.Lk, j0, hf, pos, i_row, tau_row, cexp, xr, xz);
+      mask_tile<MK, 1>(sacc, p, Lk, j0, hf, pos, i_row, tau_row, cexp, xr, xz);
       cm = 1.f;
     }
 
@@ -262,9 +321,11 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(AttnParams p) {
   const bool dead = !(l_tot > 0.f);
   const float inv = dead ? 0.f : 1.f / l_tot;
   const float lse = dead ? kNegInf : (m_all + fast_log2(l_tot)) * kLn2;
-  if (p.splits > 1) {
-    const long rows_all = static_cast<long>(p.B) * p.Hq * p.Lq;
-    float* po = p.part_out + (static_cast<long>(split) * rows_all + row_index) * D;
+  if (VARLEN ? item_partial : p.splits > 1) {
+    // partial slot: split-major rows, or the item's own [Hkv, 32] rows
+    const long slot = VARLEN ? (static_cast<long>(item) * p.Hkv + g) * 32 + l32
+                             : static_cast<long>(split) * p.B * p.Hq * Lq + row_index;
+    float* po = p.part_out + slot * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -273,7 +334,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(AttnParams p) {
         *reinterpret_cast<float4*>(po + d0) = float4{oacc[db][r4 * 4] * inv, oacc[db][r4 * 4 + 1] * inv,
                                                      oacc[db][r4 * 4 + 2] * inv, oacc[db][r4 * 4 + 3] * inv};
       }
-    if (hf == 0) p.part_lse[split * rows_all + row_index] = lse;
+    if (hf == 0) p.part_lse[slot] = lse;
     return;
   }
   T* O = static_cast<T*>(p.out) + row_index * D;
@@ -301,9 +362,33 @@ void launch_decode_d(const AttnParams& p, hipStream_t s) {
   }
 }
 
+// varlen items of decode type: grid = items x KV heads, no split dimension
+template <typename T, int D>
+void launch_decode_varlen_d(const AttnParams& p, hipStream_t s) {
+  dim3 grid(static_cast<unsigned>(static_cast<long>(p.vl_items_cap) * p.Hkv)), block(kDecThreads);
+  switch (p.mask_kind) {
+    case MI_ATTN_MASK_NONE: hipLaunchKernelGGL((decode_kernel<T, D, 0, true>), grid, block, 0, s, p); break;
+    case MI_ATTN_MASK_CAUSAL: hipLaunchKernelGGL((decode_kernel<T, D, 1, true>), grid, block, 0, s, p); break;
+    default: hipLaunchKernelGGL((decode_kernel<T, D, 2, true>), grid, block, 0, s, p); break;
+  }
+}
+
 }  // namespace
 
 int decode_block_n() { return kDecBN; }
+
+hipError_t launch_decode_varlen(const AttnParams& p, int dtype, hipStream_t s) {
+  if (static_cast<long>(p.vl_items_cap) * p.Hkv > 0x7fffffffL) return hipErrorInvalidValue;
+  if (dtype == MI_ATTN_BF16) {
+    if (p.d == 128) launch_decode_varlen_d<bf16_t, 128>(p, s); else launch_decode_varlen_d<bf16_t, 64>(p, s);
+  } else if (dtype == MI_ATTN_F16) {
+    if (p.d == 128) launch_decode_varlen_d<f16_t, 128>(p, s); else launch_decode_varlen_d<f16_t, 64>(p, s);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 int decode_max_rows() { return 32; }
 
 hipError_t launch_decode(const AttnParams& p, int dtype, hipStream_t s) {

@@ -32,6 +32,7 @@ using namespace mfma;
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kBlockM = 32 * kWaves;  // query rows per workgroup
+static_assert(kBlockM == kVarlenPrefillRows, "varlen partial slots hold one workgroup's rows");
 
 template <int D, int BN>
 struct Tile {
@@ -48,6 +49,11 @@ struct Tile {
   static_assert(BN <= kThreads, "one top-k side entry per thread");
 };
 
+// log2 of the keys one round of direct loads covers (4 waves x 1 KB of 2*D-byte rows)
+template <int D>
+constexpr int kLog2RoundKeys = (D == 128) ? 4 : 5;
+constexpr int kLog2BN = 6;  // 64-key tiles
+
 // resident workgroups per CU: LDS allows 2 for d = 128 and 4 for d = 64; the top-k
 // variant's extra state keeps d = 64 at 2 (4 would cap it at 128 VGPRs)
 template <int D, int MK>
@@ -57,10 +63,10 @@ constexpr int kMinBlocks = (D == 64 && MK != MI_ATTN_MASK_TOPK) ? 4 : 2;
 // (AttnParams::list_*) instead of consecutive keys, so only keys some row of the block
 // keeps are loaded and multiplied.
 // VARLEN: a batch of sequences of different lengths (vLLM pull request #11277 page, the
-// varlen call with cu_seqlens and a block table): queries token-major, a work unit is
-// (sequence, query block) from a device-built schedule, and each K/V row is fetched from
-// its own cache page (or packed row, or the new-token array of the two-source form)
-// with a per-lane 64-bit address.
+// varlen call with cu_seqlens and a block table): queries token-major, a workgroup takes
+// one item of the device-built work list (a key range of one (sequence, query block)),
+// and each K/V row is fetched from its own cache page (or packed row, or the new-token
+// array of the two-source form) with a per-lane 64-bit address.
 template <typename T, int D, int BN, int MK, bool GATHER = false, bool VARLEN = false>
 __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK>)) void prefill_kernel(AttnParams p) {
   static_assert(!GATHER || (MK == MI_ATTN_MASK_TOPK && BN == 64), "gathered tiles are top-k lists of 64 keys");
@@ -74,25 +80,41 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK>)) void prefill_kernel(
   const int l32 = lane & 31;
   const int hf = lane >> 5;  // lane half
 
-  // ---- work unit: (b, g, query block, split), or (sequence, g, query block, split)
+  // ---- work unit: (b, g, query block, split), or a varlen item and g
   const int split = blockIdx.y;
   const unsigned lb = logical_block(blockIdx.x, gridDim.x);
   int nqb = 1, qb, bg, b, g, Lq, Lk;
-  int seq = 0, q_start = 0, ctx = 0;  // VARLEN: sequence, its first token, cached keys
+  VarlenSeq sq{};
+  int item = 0, k0 = 0, k1 = 0;  // VARLEN: item, its key range
+  bool item_partial = false;     // VARLEN: the unit has several items (partials + merge)
   if constexpr (VARLEN) {
-    // consecutive logical blocks: consecutive units of one KV head, so the query blocks
-    // of a sequence that share its K/V run on the same XCD
-    const int u = static_cast<int>(lb % static_cast<unsigned>(p.sched_cap));
-    g = static_cast<int>(lb / static_cast<unsigned>(p.sched_cap));
-    if (u >= *p.sched_count) return;  // the whole workgroup, before any barrier
-    const int2 su = p.sched[u];
-    seq = su.x;
-    qb = su.y;
-    // every offset is clamped, so inconsistent lengths cannot move an access out of bounds
-    q_start = min(max(p.cu_q[seq], 0), p.total_q);
-    Lq = min(max(p.cu_q[seq + 1], q_start), p.total_q) - q_start;
-    Lk = max(p.cu_k[seq + 1] - p.cu_k[seq], 0);
-    ctx = p.k_new != nullptr ? Lk - Lq : Lk;
+    // The grid is sized for the most items possible; the valid (item, KV head) pairs
+    // are spread evenly over the 8 XCDs (workgroups go to XCDs round-robin), each XCD
+    // taking a contiguous run of items of one KV head, so the query blocks of a
+    // sequence, which share its K/V, run together on one XCD and its L2.
+    (void)lb;
+    const int n_items = p.vl_counts[1];
+    const int n_work = n_items * p.Hkv;
+    const int per_xcd = (n_work + 7) / 8;
+    const int k_in_xcd = static_cast<int>(blockIdx.x / 8u);
+    const int w = static_cast<int>(blockIdx.x % 8u) * per_xcd + k_in_xcd;
+    if (k_in_xcd >= per_xcd || w >= n_work) return;  // the whole workgroup, before any barrier
+    g = w / n_items;
+    item = w % n_items;
+    const int4 it = p.vl_items[item];
+    const int4 un = p.vl_units[it.x];
+    sq = varlen_seq(p, un.x);
+    sq.q_start = __builtin_amdgcn_readfirstlane(sq.q_start);  // uniform: keep them scalar
+    sq.Lq = __builtin_amdgcn_readfirstlane(sq.Lq);
+    sq.Lk = __builtin_amdgcn_readfirstlane(sq.Lk);
+    sq.ctx = __builtin_amdgcn_readfirstlane(sq.ctx);
+    sq.k_start = __builtin_amdgcn_readfirstlane(sq.k_start);
+    qb = un.y;
+    item_partial = (un.w & 0x3fffffff) > 1;
+    k0 = it.y;
+    k1 = it.z;
+    Lq = sq.Lq;
+    Lk = sq.Lk;
     b = 0;
     bg = 0;
   } else {
@@ -117,12 +139,9 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK>)) void prefill_kernel(
   const int h_row = g * p.G + (row_ok ? rloc % p.G : 0);
   const int pos = Lk - Lq + i_row;
   // output row: [B, Hq, Lq] order, or token-major [total_q, Hq] for VARLEN
-  const long row_index = VARLEN ? static_cast<long>(q_start + i_row) * p.Hq + h_row
+  const long row_index = VARLEN ? static_cast<long>(sq.q_start + i_row) * p.Hq + h_row
                                 : (static_cast<long>(b) * p.Hq + h_row) * Lq + i_row;
   const long rows_all = VARLEN ? static_cast<long>(p.total_q) * p.Hq : static_cast<long>(p.B) * p.Hq * Lq;
-  // VARLEN: a wavefront whose 32 rows are all past the block's rows (short query runs,
-  // decode steps) only helps load tiles
-  const bool wave_live = !VARLEN || wave * 32 < rows_blk;
 
   // ---- Q^T operand in registers: lane holds 8 dims (dc*16 + hf*8 ..) of its row
   const T* Q = static_cast<const T*>(p.q);
@@ -141,12 +160,14 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK>)) void prefill_kernel(
   int lo, hi;
   key_range(MK, p.window_left, Lk, P0, P1, &lo, &hi);
   if (p.no_skip) { lo = 0; hi = Lk; }
-  if (VARLEN && ctx < 0) hi = lo;  // two-source with fewer keys than queries: rows stay masked
-  if (p.splits > 1) {
-    // VARLEN: each sequence's own key range is cut into p.splits runs of whole tiles
-    const int kps = VARLEN ? ((Lk + BN - 1) / BN + p.splits - 1) / p.splits * BN : p.keys_per_split;
-    const int s0 = split * kps;
-    const int s1 = min(Lk, s0 + kps);
+  if (VARLEN) {
+    // the item's range: part of [lo, hi) cut on tile boundaries by the work-list kernel
+    // (empty for a two-source sequence with fewer keys than queries)
+    lo = k0;
+    hi = k1;
+  } else if (p.splits > 1) {
+    const int s0 = split * p.keys_per_split;
+    const int s1 = min(Lk, s0 + p.keys_per_split);
     lo = max(lo, s0);
     hi = min(hi, s1);
     if (hi < lo) hi = lo;
@@ -166,6 +187,12 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK>)) void prefill_kernel(
     if (t_hi < t_lo) t_hi = t_lo;
   }
 
+  // VARLEN base pointers, held in registers so that the per-lane choice between the cache
+  // and the new-token arrays selects values, not kernel-argument addresses
+  const T* const k_cache = static_cast<const T*>(p.k);
+  const T* const v_cache = static_cast<const T*>(p.v);
+  const T* const k_fresh = static_cast<const T*>(p.k_new);
+  const T* const v_fresh = static_cast<const T*>(p.v_new);
   const long kv_base = VARLEN ? 0 : static_cast<long>(bg) * Lk * D;
   const T* K = static_cast<const T*>(p.k) + kv_base;
   const T* V = static_cast<const T*>(p.v) + kv_base;
@@ -213,11 +240,41 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK>)) void prefill_kernel(
     const int r = wave * TL::rowsPerWaveLoad + lane / (D / 8);
     dma_slot = ((lane % (D / 8)) ^ swz<D>(r)) << 4;
   }
-  // VARLEN: gidx[c] is the cache page of the lane's row in round c (paged form), loaded
-  // one tile ahead like the gathered key indices. Rows past the sequence's last key
-  // repeat that key (it is masked); the clamps keep every index inside the table and cache.
-  const long table_row = VARLEN ? static_cast<long>(seq) * p.max_pages : 0;
+  // VARLEN addressing. A load round covers kRoundKeys consecutive keys; the lane fills row
+  // rl of the round at 16-byte slot dma_slot. A tile inside one source whose rounds each
+  // lie in one page (or are consecutive packed or new-token rows) is loaded from per-lane
+  // 64-bit addresses lane_base + row * row_bytes, one multiply-add per round, with the
+  // pages of the tile's rounds read from one block-table entry per lane loaded a tile
+  // ahead (lane i & 3 holds the tile's (i & 3)-th page). Other tiles (the last one, one
+  // across the cached / new boundary, pages shorter than a round) address every row on
+  // its own.
+  constexpr int kRoundKeys = kWaves * TL::rowsPerWaveLoad;
+  static_assert((1 << kLog2RoundKeys<D>) == kRoundKeys, "round keys");
+  static_assert(!VARLEN || (1 << kLog2BN) == BN, "varlen tiles of 64 keys");
+  static_assert(BN / kRoundKeys <= 4, "a tile of direct rounds spans at most 4 pages");
   const int page_mask = VARLEN ? (1 << p.page_shift) - 1 : 0;
+  const unsigned row_bytes = static_cast<unsigned>(p.Hkv) * D * 2;  // one key's row of all KV heads
+  const uint64_t lane_part = VARLEN ? static_cast<uint64_t>(g) * D * 2 +
+                                          static_cast<uint64_t>(wave * TL::rowsPerWaveLoad + lane / (D / 8)) * row_bytes +
+                                          dma_slot
+                                    : 0;
+  const uint64_t kc_lane = reinterpret_cast<uint64_t>(p.k) + lane_part;
+  const uint64_t vc_lane = reinterpret_cast<uint64_t>(p.v) + lane_part;
+  const uint64_t kf_lane = reinterpret_cast<uint64_t>(p.k_new) + lane_part;
+  const uint64_t vf_lane = reinterpret_cast<uint64_t>(p.v_new) + lane_part;
+  int pg_lane = 0;
+  auto load_pages = [&](int t) {
+    if (VARLEN && p.block_table != nullptr) {
+      const int last = (max(sq.Lk, 1) - 1) >> p.page_shift;
+      const int idx = min(min(((t * BN) >> p.page_shift) + (lane & 3), last), p.max_pages - 1);
+      pg_lane = p.block_table[static_cast<long>(sq.seq) * p.max_pages + idx];
+    }
+  };
+  auto tile_direct = [&](int j0) -> bool {
+    if (j0 + BN > sq.Lk) return false;
+    if (j0 >= sq.ctx) return true;  // new-token rows (two-source form)
+    return j0 + BN <= sq.ctx && (p.block_table == nullptr || p.page_shift >= kLog2RoundKeys<D>);
+  };
   auto load_gidx = [&](int t) {
     if constexpr (GATHER) {
 #pragma unroll
@@ -226,55 +283,68 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK>)) void prefill_kernel(
         gidx[c] = p.list_idx[list_base + t * BN + r];
       }
     }
-    if constexpr (VARLEN) {
-      if (p.block_table != nullptr) {
-#pragma unroll
-        for (int c = 0; c < TL::loadRounds; ++c) {
-          const int r = (c * kWaves + wave) * TL::rowsPerWaveLoad + lane / (D / 8);
-          const int j = min(t * BN + r, Lk - 1);
-          gidx[c] = p.block_table[table_row + min(j >> p.page_shift, p.max_pages - 1)];
-        }
-      }
-    }
-  };
-  // VARLEN: element offset of key j's row (head g, this lane's 16-byte slot) and whether
-  // it comes from the new-token array
-  const long slot_elems = dma_slot >> 1;
-  auto varlen_row = [&](int j, int page, bool* is_new) -> long {
-    j = min(j, Lk - 1);
-    long row;
-    *is_new = j >= ctx;
-    if (*is_new) {
-      row = q_start + (j - ctx);
-    } else if (p.block_table != nullptr) {
-      const int pg = min(max(page, 0), p.kv_rows - 1);
-      row = (static_cast<long>(pg) << p.page_shift) | (j & page_mask);
-    } else {
-      row = min(max(static_cast<long>(p.cu_k[seq]) + j, 0L), static_cast<long>(p.kv_rows) - 1);
-    }
-    return (row * p.Hkv + g) * D + slot_elems;
   };
   int32_t xrank = 0, xidx = 0;
   float xzh = 0.f;
   auto issue_tile = [&](int t, int stg) {
     const int j0 = t * BN;
     const unsigned kst = smem_addr + stg * TL::stage;
+    if constexpr (VARLEN) {
+      if (tile_direct(j0)) {
+        const bool fresh = j0 >= sq.ctx;
+        const uint64_t kl = fresh ? kf_lane : kc_lane;
+        const uint64_t vl = fresh ? vf_lane : vc_lane;
+        // first row of each round (every index below 2^31), all formed before the first
+        // load is issued: reading the page register waits for outstanding vector memory
+        // operations, which must not include this tile's own loads
+        unsigned row[TL::loadRounds];
 #pragma unroll
-    for (int c = 0; c < TL::loadRounds; ++c) {
+        for (int c = 0; c < TL::loadRounds; ++c) {
+          const int jc = j0 + c * kRoundKeys;
+          if (fresh) {
+            row[c] = static_cast<unsigned>(sq.q_start + (jc - sq.ctx));
+          } else if (p.block_table != nullptr) {
+            const int pg = min(max(__builtin_amdgcn_readlane(pg_lane, (c * kRoundKeys) >> p.page_shift), 0),
+                               p.kv_rows - 1);
+            row[c] = (static_cast<unsigned>(pg) << p.page_shift) | static_cast<unsigned>(jc & page_mask);
+          } else {
+            row[c] = static_cast<unsigned>(sq.k_start + jc);
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < TL::loadRounds; ++c) {
+          const unsigned blk = (c * kWaves + wave) * 1024;
+          const uint64_t off = static_cast<uint64_t>(row[c]) * row_bytes;
+          lds_dma16_global(kst + blk, reinterpret_cast<const void*>(kl + off));
+          lds_dma16_global(kst + TL::kBytes + blk, reinterpret_cast<const void*>(vl + off));
+        }
+      } else {
+        // every row on its own (clamped to the last key), its page read here
+        int page[TL::loadRounds];
+#pragma unroll
+        for (int c = 0; c < TL::loadRounds; ++c) {
+          const int j = j0 + (c * kWaves + wave) * TL::rowsPerWaveLoad + lane / (D / 8);
+          page[c] = p.block_table != nullptr ? varlen_page(p, sq, j) : 0;
+        }
+#pragma unroll
+        for (int c = 0; c < TL::loadRounds; ++c) {
+          const unsigned blk = (c * kWaves + wave) * 1024;
+          const int j = j0 + (c * kWaves + wave) * TL::rowsPerWaveLoad + lane / (D / 8);
+          bool is_new;
+          const long e = varlen_row<D>(p, sq, g, j, page[c], dma_slot >> 1, &is_new);
+          lds_dma16_global(kst + blk, pick(is_new, k_fresh, k_cache) + e);
+          lds_dma16_global(kst + TL::kBytes + blk, pick(is_new, v_fresh, v_cache) + e);
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < TL::loadRounds && !VARLEN; ++c) {
       const unsigned blk = (c * kWaves + wave) * 1024;  // 1 KB block of the tile
       if constexpr (GATHER) {
         // padding entries (key Lk) lie past the buffer range and read as zeros
         const int vo = gidx[c] * (D * 2) + dma_slot;
         lds_dma16_at(krs, kst + blk, vo, 0);
         lds_dma16_at(vrs, kst + TL::kBytes + blk, vo, 0);
-      } else if constexpr (VARLEN) {
-        const int r = (c * kWaves + wave) * TL::rowsPerWaveLoad + lane / (D / 8);
-        bool is_new;
-        const long e = varlen_row(j0 + r, gidx[c], &is_new);
-        const T* kb = static_cast<const T*>(is_new ? p.k_new : p.k);
-        const T* vb = static_cast<const T*>(is_new ? p.v_new : p.v);
-        lds_dma16_global(kst + blk, kb + e);
-        lds_dma16_global(kst + TL::kBytes + blk, vb + e);
       } else {
         const int so = (j0 + c * kWaves * TL::rowsPerWaveLoad) * D * 2;
         lds_dma16_at(krs, kst + blk, dma_lane, so);
@@ -290,7 +360,7 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK>)) void prefill_kernel(
       }
       if (t + 1 < t_hi) load_gidx(t + 1);
     } else if constexpr (VARLEN) {
-      load_gidx(t + 1);  // clamped, so past the last tile it reads a valid entry
+      load_pages(t + 1);  // clamped, so past the last tile it reads a valid entry
     } else if constexpr (MK == MI_ATTN_MASK_TOPK) {
       if (tid < BN) {
         const int key = j0 + tid;
@@ -340,6 +410,7 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK>)) void prefill_kernel(
   int stage = 0;
   if (t < t_hi) {
     load_gidx(t);
+    load_pages(t);
     issue_tile(t, 0);
     finish_tile(0);
   }
@@ -349,140 +420,138 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK>)) void prefill_kernel(
     const int tn = next_live(t + 1);
     if (tn < t_hi) issue_tile(tn, stage ^ 1);  // lands in the other stage while this tile computes
 
-    if (wave_live) {
-      const int ks_ofs = stage * TL::stage;
-      const int vs_ofs = ks_ofs + TL::kBytes;
-      const unsigned char* vs = smem + vs_ofs;
-      const int j0 = t * BN;
+    const int ks_ofs = stage * TL::stage;
+    const int vs_ofs = ks_ofs + TL::kBytes;
+    const unsigned char* vs = smem + vs_ofs;
+    const int j0 = t * BN;
 
-      // S^T = K Q^T. The first 32-key block's K fragments are read before its first MFMA;
-      // afterwards each MFMA overlaps the read of one fragment of the next block.
-      f32x16_t sacc[NKB];
-      {
-        constexpr int NDC = D / 16;
-        u32x4_t kf[NKB][NDC];
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int dc = 0; dc < NDC; ++dc)
-            kf[kb][dc] = *reinterpret_cast<const u32x4_t*>(smem + kb * 32 * TL::rowBytes +
-                                                           ((k_base + ks_ofs) ^ (dc << 5)));
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          f32x16_t acc = f32x16_t{};
-#pragma unroll
-          for (int dc = 0; dc < NDC; ++dc) acc = mfma32(T{}, kf[kb][dc], qreg[dc], acc);
-          sacc[kb] = acc;
-        }
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NDC, 0);
-#pragma unroll
-        for (int i = 0; i < (NKB - 1) * NDC; ++i) {
-          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, NDC, 0);
-      }
-
-      // mask (tiles the mask does not cover entirely); masked tiles move to the log2
-      // domain here (cm = 1), unmasked ones are scaled inside the exponent (cm = cexp)
-      float cm = cexp;
-      if constexpr (GATHER) {
-        const int32_t* xr = reinterpret_cast<const int32_t*>(vs + TL::vBytes);
-        const float* xzl = reinterpret_cast<const float*>(xr + BN);
-        const int32_t* xi = xr + 2 * BN;
-        if (xi[BN - 1] > P0)  // the list ascends: its last key decides whether positions matter
-          mask_tile_topk_list<NKB, true>(sacc, hf, pos, tau_row, cexp, xr, xzl, xi);
-        else
-          mask_tile_topk_list<NKB, false>(sacc, hf, pos, tau_row, cexp, xr, xzl, xi);
-        cm = 1.f;
-      } else if constexpr (MK == MI_ATTN_MASK_TOPK) {
-        const int32_t* xr = reinterpret_cast<const int32_t*>(vs + TL::vBytes);
-        const float* xzl = reinterpret_cast<const float*>(xr + BN);
-        if (j0 + BN - 1 > P0)
-          mask_tile_topk<NKB, true>(sacc, j0, hf, pos, tau_row, cexp, xr, xzl);
-        else
-          mask_tile_topk<NKB, false>(sacc, j0, hf, pos, tau_row, cexp, xr, xzl);
-        cm = 1.f;
-      } else if (tile_needs_mask<MK, BN>(p, Lk, j0, P0, P1)) {
-        mask_tile<MK, NKB>(sacc, p, Lk, j0, hf, pos, i_row, tau_row, cexp, nullptr, nullptr);
-        cm = 1.f;
-      }
-
-      // online softmax (log2 domain), guarded against all -inf tiles and rows
-      float mx4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};  // four independent chains
+    // S^T = K Q^T. The first 32-key block's K fragments are read before its first MFMA;
+    // afterwards each MFMA overlaps the read of one fragment of the next block.
+    f32x16_t sacc[NKB];
+    {
+      constexpr int NDC = D / 16;
+      u32x4_t kf[NKB][NDC];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mx4[e & 3] = fmaxf(mx4[e & 3], sacc[kb][e]);
-      float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
-      mx = max_halves(mx) * cm;
-      const float m_next = (mx > m_run + kRescaleThreshold) ? mx : m_run;
-      const float m_use = (m_next == kNegInf) ? 0.f : m_next;
-      const float alpha = fast_exp2(m_run - m_use);  // 1 when the max did not move, 0 from -inf
-      float ps4[4] = {0.f, 0.f, 0.f, 0.f};  // four independent chains
-      u32x4_t preg[BN / 16];
+        for (int dc = 0; dc < NDC; ++dc)
+          kf[kb][dc] = *reinterpret_cast<const u32x4_t*>(smem + kb * 32 * TL::rowBytes +
+                                                         ((k_base + ks_ofs) ^ (dc << 5)));
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
+        f32x16_t acc = f32x16_t{};
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          float pv[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            pv[e] = fast_exp2(fmaf(sacc[kb][half * 8 + e], cm, -m_use));
-            ps4[e & 3] += pv[e];
-          }
-          u32x4_t pk;
-          pk.x = pack2(T{}, pv[0], pv[1]);
-          pk.y = pack2(T{}, pv[2], pv[3]);
-          pk.z = pack2(T{}, pv[4], pv[5]);
-          pk.w = pack2(T{}, pv[6], pv[7]);
-          preg[kb * 2 + half] = pk;
-        }
+        for (int dc = 0; dc < NDC; ++dc) acc = mfma32(T{}, kf[kb][dc], qreg[dc], acc);
+        sacc[kb] = acc;
       }
-      l_run = fmaf(l_run, alpha, (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]));
-      m_run = m_next;
-      if (!__all(alpha == 1.f)) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NDC, 0);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+      for (int i = 0; i < (NKB - 1) * NDC; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, NDC, 0);
+    }
 
-      // O^T += V^T P^T. The V^T operand comes from two transposed reads: lane (16 * g + i)
-      // reads 8 bytes of key row R0 + i / 4 at dims D0 + 4 * (i % 4) and receives keys
-      // R0..R0+3 of dim D0 + i. Keys 4*hf+0..3 and 8+4*hf+0..3 of the 16-key chunk are what
-      // its P registers hold. Key chunks run outermost, so the NDB accumulators are
-      // independent chains, and the next chunk's V fragments are read during this chunk's
-      // MFMAs.
-      // The PV MFMAs issue at raised wavefront priority: when the other wavefront on the SIMD
-      // has vector work ready at the same time, the matrix core is kept fed first (measured
-      // +4% on c3 prefill; raising it for the QK MFMAs as well gains nothing).
-      __builtin_amdgcn_s_setprio(1);
-      {
-        constexpr int NKC = BN / 16;
-        const int vb0 = v_base0 + vs_ofs, vb1 = v_base1 + vs_ofs;
-        u32x4_t vf[NKC][NDB];
+    // mask (tiles the mask does not cover entirely); masked tiles move to the log2
+    // domain here (cm = 1), unmasked ones are scaled inside the exponent (cm = cexp)
+    float cm = cexp;
+    if constexpr (GATHER) {
+      const int32_t* xr = reinterpret_cast<const int32_t*>(vs + TL::vBytes);
+      const float* xzl = reinterpret_cast<const float*>(xr + BN);
+      const int32_t* xi = xr + 2 * BN;
+      if (xi[BN - 1] > P0)  // the list ascends: its last key decides whether positions matter
+        mask_tile_topk_list<NKB, true>(sacc, hf, pos, tau_row, cexp, xr, xzl, xi);
+      else
+        mask_tile_topk_list<NKB, false>(sacc, hf, pos, tau_row, cexp, xr, xzl, xi);
+      cm = 1.f;
+    } else if constexpr (MK == MI_ATTN_MASK_TOPK) {
+      const int32_t* xr = reinterpret_cast<const int32_t*>(vs + TL::vBytes);
+      const float* xzl = reinterpret_cast<const float*>(xr + BN);
+      if (j0 + BN - 1 > P0)
+        mask_tile_topk<NKB, true>(sacc, j0, hf, pos, tau_row, cexp, xr, xzl);
+      else
+        mask_tile_topk<NKB, false>(sacc, j0, hf, pos, tau_row, cexp, xr, xzl);
+      cm = 1.f;
+    } else if (tile_needs_mask<MK, BN>(p, Lk, j0, P0, P1)) {
+      mask_tile<MK, NKB>(sacc, p, Lk, j0, hf, pos, i_row, tau_row, cexp, nullptr, nullptr);
+      cm = 1.f;
+    }
+
+    // online softmax (log2 domain), guarded against all -inf tiles and rows
+    float mx4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};  // four independent chains
 #pragma unroll
-        for (int kc = 0; kc < NKC; ++kc)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const unsigned char* row = smem + kc * 16 * TL::rowBytes;
-            const u32x2_t lo = lds_read_tr16(row + (vb0 ^ (db << 6)));
-            const u32x2_t hi2 = lds_read_tr16(row + (vb1 ^ (db << 6)));
-            vf[kc][db] = u32x4_t{lo.x, lo.y, hi2.x, hi2.y};
-          }
+      for (int e = 0; e < 16; ++e) mx4[e & 3] = fmaxf(mx4[e & 3], sacc[kb][e]);
+    float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
+    mx = max_halves(mx) * cm;
+    const float m_next = (mx > m_run + kRescaleThreshold) ? mx : m_run;
+    const float m_use = (m_next == kNegInf) ? 0.f : m_next;
+    const float alpha = fast_exp2(m_run - m_use);  // 1 when the max did not move, 0 from -inf
+    float ps4[4] = {0.f, 0.f, 0.f, 0.f};  // four independent chains
+    u32x4_t preg[BN / 16];
 #pragma unroll
-        for (int kc = 0; kc < NKC; ++kc)
+    for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-          for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(T{}, vf[kc][db], preg[kc], oacc[db]);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * NDB, 0);
+      for (int half = 0; half < 2; ++half) {
+        float pv[8];
 #pragma unroll
-        for (int i = 0; i < (NKC - 1) * NDB; ++i) {
-          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        for (int e = 0; e < 8; ++e) {
+          pv[e] = fast_exp2(fmaf(sacc[kb][half * 8 + e], cm, -m_use));
+          ps4[e & 3] += pv[e];
         }
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, NDB, 0);
+        u32x4_t pk;
+        pk.x = pack2(T{}, pv[0], pv[1]);
+        pk.y = pack2(T{}, pv[2], pv[3]);
+        pk.z = pack2(T{}, pv[4], pv[5]);
+        pk.w = pack2(T{}, pv[6], pv[7]);
+        preg[kb * 2 + half] = pk;
       }
-      __builtin_amdgcn_s_setprio(0);
-    }  // wave_live
+    }
+    l_run = fmaf(l_run, alpha, (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]));
+    m_run = m_next;
+    if (!__all(alpha == 1.f)) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+    }
+
+    // O^T += V^T P^T. The V^T operand comes from two transposed reads: lane (16 * g + i)
+    // reads 8 bytes of key row R0 + i / 4 at dims D0 + 4 * (i % 4) and receives keys
+    // R0..R0+3 of dim D0 + i. Keys 4*hf+0..3 and 8+4*hf+0..3 of the 16-key chunk are what
+    // its P registers hold. Key chunks run outermost, so the NDB accumulators are
+    // independent chains, and the next chunk's V fragments are read during this chunk's
+    // MFMAs.
+    // The PV MFMAs issue at raised wavefront priority: when the other wavefront on the SIMD
+    // has vector work ready at the same time, the matrix core is kept fed first (measured
+    // +4% on c3 prefill; raising it for the QK MFMAs as well gains nothing).
+    __builtin_amdgcn_s_setprio(1);
+    {
+      constexpr int NKC = BN / 16;
+      const int vb0 = v_base0 + vs_ofs, vb1 = v_base1 + vs_ofs;
+      u32x4_t vf[NKC][NDB];
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const unsigned char* row = smem + kc * 16 * TL::rowBytes;
+          const u32x2_t lo = lds_read_tr16(row + (vb0 ^ (db << 6)));
+          const u32x2_t hi2 = lds_read_tr16(row + (vb1 ^ (db << 6)));
+          vf[kc][db] = u32x4_t{lo.x, lo.y, hi2.x, hi2.y};
+        }
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(T{}, vf[kc][db], preg[kc], oacc[db]);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * NDB, 0);
+#pragma unroll
+      for (int i = 0; i < (NKC - 1) * NDB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, NDB, 0);
+    }
+    __builtin_amdgcn_s_setprio(0);
 
     if (tn < t_hi) finish_tile(stage ^ 1);
     __syncthreads();
@@ -496,8 +565,11 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK>)) void prefill_kernel(
   const bool dead = !(l_tot > 0.f);
   const float inv = dead ? 0.f : 1.f / l_tot;
   const float lse = dead ? kNegInf : (m_run + fast_log2(l_tot)) * kLn2;
-  if (p.splits > 1) {
-    float* po = p.part_out + (static_cast<long>(split) * rows_all + row_index) * D;
+  if (VARLEN ? item_partial : p.splits > 1) {
+    // partial slot: split-major rows, or the item's own [Hkv, kBlockM] rows
+    const long slot = VARLEN ? (static_cast<long>(item) * p.Hkv + g) * kBlockM + rloc
+                             : static_cast<long>(split) * rows_all + row_index;
+    float* po = p.part_out + slot * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -507,7 +579,7 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK>)) void prefill_kernel(
                     oacc[db][r4 * 4 + 3] * inv};
         *reinterpret_cast<float4*>(po + d0) = v;
       }
-    if (hf == 0) p.part_lse[split * rows_all + row_index] = lse;
+    if (hf == 0) p.part_lse[slot] = lse;
     return;
   }
   T* O = static_cast<T*>(p.out) + row_index * D;
@@ -598,59 +670,13 @@ hipError_t launch_prefill_t(const AttnParams& p, hipStream_t s) {
   return launch_lse_merge_t<T>(p, s);
 }
 
-// Work units of a varlen call: each sequence's query blocks (the last, longest causal
-// range first), sequences in order. One workgroup scans the per-sequence block counts
-// 1024 sequences at a time; units past `cap` (possible only when cu_q is inconsistent)
-// are dropped.
-constexpr int kSchedThreads = 1024;
-
-__global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(const int32_t* cu_q, int S, int total_q,
-                                                                        int qpb, int cap, int2* sched,
-                                                                        int32_t* count) {
-  __shared__ long long wsum[kSchedThreads / kWave];
-  const int tid = threadIdx.x;
-  const int lane = tid % kWave;
-  const int wave = tid / kWave;
-  long long carry = 0;  // units before this pass (same value in every thread)
-  for (int base = 0; base < S; base += kSchedThreads) {
-    const int s = base + tid;
-    int n = 0;
-    if (s < S) {
-      const int a = min(max(cu_q[s], 0), total_q);
-      const int b = min(max(cu_q[s + 1], a), total_q);
-      n = (b - a + qpb - 1) / qpb;
-    }
-    long long x = n;  // inclusive scan inside the wavefront
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const long long y = __shfl_up(x, o, kWave);
-      if (lane >= o) x += y;
-    }
-    if (lane == kWave - 1) wsum[wave] = x;
-    __syncthreads();
-    long long before = 0, total = 0;
-#pragma unroll
-    for (int w = 0; w < kSchedThreads / kWave; ++w) {
-      if (w < wave) before += wsum[w];
-      total += wsum[w];
-    }
-    const long long start = carry + before + x - n;
-    for (int k = 0; k < n; ++k) {
-      const long long u = start + k;
-      if (u >= cap) break;
-      sched[u] = make_int2(s, n - 1 - k);
-    }
-    carry += total;
-    __syncthreads();  // wsum is rewritten by the next pass
-  }
-  if (tid == 0) *count = static_cast<int32_t>(carry < cap ? carry : cap);
-}
-
+// Varlen items of prefill type (query runs longer than 32 rows per KV head); the LSE
+// merge of split units runs separately.
 template <typename T>
 hipError_t launch_prefill_varlen_t(const AttnParams& p, hipStream_t s) {
-  const long blocks = static_cast<long>(p.sched_cap) * p.Hkv;
-  if (blocks > 0x7fffffffL || p.splits > 65535) return hipErrorInvalidValue;
-  dim3 grid(static_cast<unsigned>(blocks), p.splits), block(kThreads);
+  const long blocks = (static_cast<long>(p.vl_items_cap) * p.Hkv + 7) / 8 * 8;  // whole rounds of 8 XCDs
+  if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
+  dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
   if (p.d == 128) {
     switch (p.mask_kind) {
       case MI_ATTN_MASK_NONE:
@@ -672,27 +698,15 @@ hipError_t launch_prefill_varlen_t(const AttnParams& p, hipStream_t s) {
       default: hipLaunchKernelGGL((prefill_kernel<T, 64, 64, 2, false, true>), grid, block, 0, s, p); break;
     }
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.splits <= 1) return e;
-  AttnParams m = p;  // partial rows are the token-major output rows
-  m.B = 1;
-  m.Lq = p.total_q;
-  return launch_lse_merge_t<T>(m, s);
+  return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_prefill_varlen(const AttnParams& p, int dtype, int2* sched, int32_t* sched_count,
-                                 hipStream_t s) {
-  if (dtype != MI_ATTN_BF16 && dtype != MI_ATTN_F16) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(varlen_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, s, p.cu_q, p.num_seqs, p.total_q,
-                     p.q_per_block, p.sched_cap, sched, sched_count);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  AttnParams pv = p;
-  pv.sched = sched;
-  pv.sched_count = sched_count;
-  return dtype == MI_ATTN_BF16 ? launch_prefill_varlen_t<bf16_t>(pv, s) : launch_prefill_varlen_t<f16_t>(pv, s);
+hipError_t launch_prefill_varlen(const AttnParams& p, int dtype, hipStream_t s) {
+  if (dtype == MI_ATTN_BF16) return launch_prefill_varlen_t<bf16_t>(p, s);
+  if (dtype == MI_ATTN_F16) return launch_prefill_varlen_t<f16_t>(p, s);
+  return hipErrorInvalidValue;
 }
 
 int prefill_block_n(int) { return 64; }

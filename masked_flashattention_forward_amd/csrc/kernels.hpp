@@ -25,11 +25,30 @@ hipError_t launch_half_path(int path, const AttnParams& p, int dtype, hipStream_
 int prefill_block_m();
 int prefill_block_n(int d);
 
-// Varlen / paged forward (attn_fwd_varlen): query positions per workgroup for G heads
-// per KV head, the key-range split count, and the launch (schedule kernel, MFMA kernel,
-// and the LSE merge when split). sched must hold p.sched_cap entries.
+// Varlen / paged forward (attn_fwd_varlen): device-built work lists (units and items, see
+// k_varlen.hip), the MFMA prefill and split-KV decode kernels over them, and the LSE
+// merge of units split into several items. Buffers are sized by the host:
+//   units    int4 [units_cap]        items_p, items_d  int4 [items_cap]     counts int32 [3]
+//   pp_out   fp32 [items_cap, Hkv, 128, d]   pp_lse  [items_cap, Hkv, 128]
+//   pd_out   fp32 [items_cap, Hkv, 32, d]    pd_lse  [items_cap, Hkv, 32]
+constexpr int kVarlenPrefillRows = 128;  // = prefill_block_m(): partial rows per prefill-type item
+struct VarlenBuffers {
+  int4* units;
+  int4* items_p;
+  int4* items_d;
+  int32_t* counts;
+  float* pp_out;
+  float* pp_lse;
+  float* pd_out;
+  float* pd_lse;
+  int units_cap;     // >= the number of (sequence, query block) units
+  int items_cap;     // varlen_items_cap(units_cap, target_items, force_items)
+  int target_items;  // items per type the plan aims for
+  int force_items;   // > 0: exactly this many items per unit (fewer for short units)
+};
 int varlen_q_per_block(int G);
-int varlen_splits(long blocks, int max_seqlen_k, int force_splits);
-hipError_t launch_prefill_varlen(const AttnParams& p, int dtype, int2* sched, int32_t* sched_count, hipStream_t s);
+int varlen_target_items(int Hkv);
+int varlen_items_cap(int units_cap, int target_items, int force);
+hipError_t launch_varlen(const AttnParams& p, int dtype, const VarlenBuffers& b, hipStream_t s);
 
 }  // namespace mi_attn

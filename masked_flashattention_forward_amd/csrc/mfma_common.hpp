@@ -138,6 +138,60 @@ __device__ __forceinline__ void lds_dma16_global(unsigned lds_addr, const void* 
                : "memory", "m0");
 }
 
+// Varlen K/V addressing. A sequence's keys 0 .. Lk-1: the first ctx come from the cache
+// (paged through the block table, or packed at cu_k[seq]), the rest (two-source form)
+// from the new-token arrays at row q_start + j - ctx. Every index is clamped into its
+// array, so no value of the caller's int32 arrays can move an access out of bounds.
+struct VarlenSeq {
+  int seq, q_start, Lq, Lk, ctx, k_start;
+};
+
+__device__ __forceinline__ VarlenSeq varlen_seq(const AttnParams& p, int seq) {
+  VarlenSeq v;
+  v.seq = seq;
+  v.q_start = min(max(p.cu_q[seq], 0), p.total_q);
+  v.Lq = min(max(p.cu_q[seq + 1], v.q_start), p.total_q) - v.q_start;
+  // at most the keys the cache can hold for one sequence (plus its new ones), so loop
+  // bounds stay small whatever the lengths say
+  const int cache_keys = p.block_table != nullptr ? (p.max_pages << p.page_shift) : p.kv_rows;
+  v.k_start = p.cu_k[seq];
+  v.Lk = min(max(p.cu_k[seq + 1] - v.k_start, 0), cache_keys + (p.k_new != nullptr ? v.Lq : 0));
+  v.ctx = p.k_new != nullptr ? v.Lk - v.Lq : v.Lk;
+  return v;
+}
+
+// Block-table entry for key j (clamped to the last key, which the mask hides when j is
+// past it); only meaningful for the paged form.
+__device__ __forceinline__ int varlen_page(const AttnParams& p, const VarlenSeq& v, int j) {
+  j = min(j, v.Lk - 1);
+  return p.block_table[static_cast<long>(v.seq) * p.max_pages + min(max(j, 0) >> p.page_shift, p.max_pages - 1)];
+}
+
+// Element offset of key j's row of KV head g (plus `col` elements), and whether it lies
+// in the new-token arrays; `page` is varlen_page(p, v, j) for the paged form. Branch
+// free: both candidate rows are formed and one is selected per lane (callers select the
+// base pointer the same way, from values held in registers).
+template <int D>
+__device__ __forceinline__ long varlen_row(const AttnParams& p, const VarlenSeq& v, int g, int j, int page, int col,
+                                           bool* is_new) {
+  j = min(j, v.Lk - 1);
+  const bool nw = j >= v.ctx;
+  const int pg = min(max(page, 0), p.kv_rows - 1);
+  const long paged_row = (static_cast<long>(pg) << p.page_shift) | (j & ((1 << p.page_shift) - 1));
+  const long packed_row = min(max(static_cast<long>(v.k_start) + j, 0L), static_cast<long>(p.kv_rows) - 1);
+  const long cache_row = p.block_table != nullptr ? paged_row : packed_row;
+  const long row = nw ? static_cast<long>(v.q_start) + (j - v.ctx) : cache_row;
+  *is_new = nw;
+  return (row * p.Hkv + g) * D + col;
+}
+
+// c ? a : b on pointer values (by-value parameters: a select of two variables would
+// otherwise become a select of their addresses and a load)
+template <typename T>
+__device__ __forceinline__ const T* pick(bool c, const T* a, const T* b) {
+  return c ? a : b;
+}
+
 // s_waitcnt immediate for "at most n vector-memory operations outstanding" (gfx9
 // encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their maximum).
 constexpr int vmcnt_imm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }

@@ -86,13 +86,9 @@ HalfPlan plan_half_path(int path, int B, int Hkv, int G, int Lq, int Lk, int d, 
 
 int varlen_q_per_block(int G) { return q_per_block_for(G); }
 
-int varlen_splits(long blocks, int max_seqlen_k, int force_splits) {
-  const int bn = prefill_block_n(128);
-  const int tiles = (max_seqlen_k + bn - 1) / bn;
-  int s = force_splits > 0 ? force_splits
-                           : auto_splits(static_cast<int>(blocks < 0x7fffffff ? blocks : 0x7fffffff), max_seqlen_k, bn);
-  if (s > tiles) s = tiles;
-  return s < 1 ? 1 : s;
+int varlen_target_items(int Hkv) {
+  const int t = kTargetBlocks / (Hkv > 0 ? Hkv : 1);
+  return t < 1 ? 1 : t;
 }
 
 hipError_t launch_half_path(int path, const AttnParams& p, int dtype, hipStream_t s) {

@@ -185,3 +185,14 @@ def test_varlen_with_no_queries_enqueues_nothing(lib):
     assert varlen_rc(lib, total_q=0) == 0
     assert varlen_rc(lib, total_q=0, block_table=ctypes.c_void_p(16), page_size=32) == 0
     assert varlen_rc(lib, num_seqs=0, total_q=0) == 0
+
+
+def test_binding_shares_torchs_hip_runtime():
+    """Loading the library through the binding before the caller imports torch still puts
+    one HIP runtime in the process (torch's), not the system copy next to it."""
+    code = ("import masked_flashattention_forward_amd as m; m.lib(); import torch; "
+            "maps = open('/proc/self/maps').read(); "
+            "print(len({l.split()[-1] for l in maps.splitlines() if 'libamdhip64' in l}))")
+    r = subprocess.run(["python", "-c", code], capture_output=True, text=True, cwd=ROOT, timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip().splitlines()[-1] == "1"

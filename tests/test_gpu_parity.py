@@ -187,3 +187,23 @@ def test_topk_kept_key_lists(B, Hq, Hkv, Lq, Lk, keep):
     out, lse = run_gpu(p, out_fill=float("nan"))
     ref_o, ref_l = run_oracle(p)
     compare(p, out, lse, ref_o, ref_l, label=p.name)
+
+
+FULL_SIZE = ["c3p", "c3d", "c4_d128_bf16", "c4_d64_bf16", "c4_d128_fp16", "c4_d64_fp16", "c5"]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", FULL_SIZE)
+def test_full_size_sampled(name):
+    """The timed workloads at full size, in the launch configuration the benchmark uses
+    (the plan depends on the shape only): every output is checked for NaN, and sampled
+    (batch, head) pairs on sampled rows, first and last row included, against the oracle."""
+    p = synth.config(name)
+    say(f"config {name}: {p.name}")
+    out, lse = run_gpu(p, out_fill=float("nan"))
+    assert not np.isnan(out).any() and not np.isnan(lse).any()
+    rng = np.random.default_rng(123)
+    heads = sorted({(int(rng.integers(p.B)), int(rng.integers(p.Hq))) for _ in range(3)} | {(p.B - 1, p.Hq - 1)})
+    rows = np.unique(np.concatenate([[0, p.Lq - 1], rng.integers(0, p.Lq, size=8)]))
+    ref_o, ref_l = run_oracle(p, rows=rows, heads=heads)
+    compare(p, out, lse, ref_o, ref_l, rows=rows, heads=heads, label=f"{name} sampled")

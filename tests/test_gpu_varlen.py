@@ -127,3 +127,15 @@ def test_serving_batch_sampled_sequences():
     ref_o, ref_l = run_oracle_paged(p, seqs=seqs)
     compare(p, out, lse, ref_o, ref_l, label=p.name + " (sampled sequences)")
     assert not np.isnan(out).any() and not np.isnan(lse).any()
+
+
+@pytest.mark.parametrize("G", [1, 8, 32])
+def test_decode_type_boundary(G):
+    """Sequences with exactly 32 query rows per KV head run on the decode kernel, one row
+    more on the prefill kernel; both next to each other in one call."""
+    Hkv = 2
+    q_lens = [32 // G, 32 // G + 1, 1, 32 // G]
+    k_lens = [900, 900, 2000, 70]
+    p = synth.make_paged_problem(f"varlen decode/prefill boundary G{G}", q_lens, k_lens, G * Hkv, Hkv, 128, "bf16",
+                                 "causal", 800 + G, page_size=16)
+    check(p)
