@@ -54,10 +54,11 @@ template <int D>
 constexpr int kLog2RoundKeys = (D == 128) ? 4 : 5;
 constexpr int kLog2BN = 6;  // 64-key tiles
 
-// resident workgroups per CU: LDS allows 2 for d = 128 and 4 for d = 64; the top-k
-// variant's extra state keeps d = 64 at 2 (4 would cap it at 128 VGPRs)
-template <int D, int MK>
-constexpr int kMinBlocks = (D == 64 && MK != MI_ATTN_MASK_TOPK) ? 4 : 2;
+// resident workgroups per CU: LDS allows 2 for d = 128 and 4 for d = 64. At d = 64 the
+// top-k variant's extra state keeps it at 2 and the varlen variant's per-row addressing
+// at 3 (4 would cap them at 128 VGPRs and spill).
+template <int D, int MK, bool VARLEN>
+constexpr int kMinBlocks = D == 128 ? 2 : MK == MI_ATTN_MASK_TOPK ? 2 : VARLEN ? 3 : 4;
 
 // GATHER (top-k only): tiles are consecutive 64-key runs of the block's kept-key list
 // (AttnParams::list_*) instead of consecutive keys, so only keys some row of the block
@@ -68,7 +69,7 @@ constexpr int kMinBlocks = (D == 64 && MK != MI_ATTN_MASK_TOPK) ? 4 : 2;
 // and each K/V row is fetched from its own cache page (or packed row, or the new-token
 // array of the two-source form) with a per-lane 64-bit address.
 template <typename T, int D, int BN, int MK, bool GATHER = false, bool VARLEN = false>
-__global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK>)) void prefill_kernel(AttnParams p) {
+__global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN>)) void prefill_kernel(AttnParams p) {
   static_assert(!GATHER || (MK == MI_ATTN_MASK_TOPK && BN == 64), "gathered tiles are top-k lists of 64 keys");
   static_assert(!VARLEN || (!GATHER && MK <= MI_ATTN_MASK_WINDOW), "varlen takes the key-position masks");
   using TL = Tile<D, BN>;
