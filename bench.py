@@ -10,8 +10,11 @@ The same line carries:
                 timed with events on the stream the library launches on;
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload;
   configs       every other workload (decode GB/s, long causal, top-k, dense window,
-                tiny fp32) and the paged serving batch of attn_fwd_varlen. Parity at these
-                sizes is the GPU tests' job (tests/test_gpu_parity.py, test_gpu_varlen.py);
+                tiny fp32), the paged serving batch of attn_fwd_varlen and the attn_fwd_ex
+                workloads (transposed KV cache, ALiBi + softcap, non-causal top-k, per-head
+                mask; each with the plain call's time on the same data). Parity at these
+                sizes is the GPU tests' job (tests/test_gpu_parity.py, test_gpu_varlen.py,
+                test_gpu_ex.py);
                 the benchmark only times.
 
 Usage: python bench.py [--steps K] [--warmup W] [--only NAME] [--no-cpu-baseline]
@@ -192,6 +195,60 @@ def bench_config(name, iters=20):
     return res
 
 
+def bench_ex_config(name, iters=20):
+    """One attn_fwd_ex workload (synth.ex_config): a general layout, score modifiers, a
+    top-k variant or a per-head mask on one of the five configurations. Reports the time
+    next to that of the plain call on the same data, so the line shows what the option
+    costs."""
+    import torch
+    import masked_flashattention_forward_amd as mfa
+    import synth
+    p, o = synth.ex_config(name)
+    r = Runner(p)
+
+    def lay(t):
+        return t.transpose(1, 2).contiguous().transpose(1, 2) if o["layout"] == "blhd" else t
+
+    q, k, v = lay(r.q), lay(r.k), lay(r.v)
+    out = lay(torch.empty_like(r.q))
+    mask = None
+    if o["mask"] is not None:
+        mask = torch.from_numpy(o["mask"]).cuda()
+    elif p.mask_kind == "dense":
+        mask = r.mask
+    sl = None if o["alibi"] is None else torch.from_numpy(o["alibi"]).cuda()
+
+    def call():
+        mfa.attn_fwd_ex(q, k, v, scale=p.scale, mask_kind=p.mask_kind, window_left=p.window_left, mask=mask,
+                        zero_hold=r.zh, keep_k=p.keep_k, topk_causal=o["topk_causal"], alibi_slopes=sl,
+                        softcap=o["softcap"], out=out, lse=r.lse)
+
+    for _ in range(3):
+        call()
+        r()
+    torch.cuda.synchronize()
+    ms = r.event_time_ms(iters, call)
+    ms_plain = r.event_time_ms(iters)
+    if o["mask"] is not None:
+        pairs = int(np.isfinite(np.broadcast_to(o["mask"], (p.B, p.Hq, p.Lq, p.Lk))).sum())
+    elif p.mask_kind == "topk" and not o["topk_causal"]:
+        pairs = p.B * p.Hq * p.Lq * min(p.keep_k, p.Lk)
+    else:
+        pairs = visible_pairs(p)
+    flops = 4.0 * p.d * pairs
+    byts = algorithmic_bytes(p) + (0 if o["mask"] is None else o["mask"].nbytes)
+    res = {"workload": p.name, "B": p.B, "Hq": p.Hq, "Hkv": p.Hkv, "Lq": p.Lq, "Lk": p.Lk, "d": p.d,
+           "dtype": p.dtype, "mask": p.mask_kind, "layout": o["layout"], "alibi": o["alibi"] is not None,
+           "softcap": o["softcap"], "topk_causal": o["topk_causal"], "per_head_mask": o["mask"] is not None,
+           "us": round(ms * 1e3, 2), "us_plain_call": round(ms_plain * 1e3, 2),
+           "tflops": round(flops / ms / 1e9, 2), "pct_mfma_peak": round(100 * flops / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+           "gbs": round(byts / ms / 1e6, 1), "pct_hbm_peak": round(100 * byts / ms / 1e6 / PEAK_HBM_GBS, 2)}
+    del r, q, k, v, out, mask
+    torch.cuda.empty_cache()
+    log(f"{name}: {json.dumps(res)}")
+    return res
+
+
 def paged_pairs_and_keys(p):
     """Visible (row, key) pairs over all query heads, and distinct visible keys per KV
     head, of a varlen problem (each sequence bottom-right aligned)."""
@@ -356,6 +413,9 @@ def main():
             configs[name] = bench_config(name)
         log("config serve (paged varlen)")
         configs["serve"] = bench_paged_config("serve")
+        for name in synth.EX_NAMES:
+            log(f"config {name} (attn_fwd_ex)")
+            configs[name] = bench_ex_config(name)
         line["configs"] = configs
         d = configs["c3d"]
         line["decode"] = {"workload": d["workload"], "value": d["gbs"], "unit": "GB/s",

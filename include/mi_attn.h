@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define MI_ATTN_ABI_VERSION 3
+#define MI_ATTN_ABI_VERSION 4
 
 /* element types of q, k, v, out */
 #define MI_ATTN_F32 0
@@ -171,6 +171,74 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, floa
                     int mask_kind, int window_left,
                     const int32_t* block_table, int max_pages, int page_size, int kv_rows,
                     const void* k_new, const void* v_new, int dtype, void* stream);
+
+/*
+ * attn_fwd_ex: attn_fwd with general layouts, per-head masks and score modifiers.
+ *
+ * The vLLM pull request #11277 page lists, in the varlen call its reviewers ask backends
+ * to align with ("API alignment" request), two score modifiers beside the mask:
+ * alibi_slopes and softcap; the InfiniTrain pull request #193 page names the same two
+ * among its unsupported features ("TODO"), next to an external custom mask. Neither page
+ * defines them; this library takes the convention of the varlen API the vLLM page
+ * quotes, in this order:
+ *   t     = scale * q.k                                   (the scaled score)
+ *   t     = softcap * tanh(t / softcap)                  when softcap > 0
+ *   t    -= alibi_slopes[h] * |p_i - j|                  when alibi_slopes != NULL
+ *   logit = t + M[b, h, i, j]                            (the mask of mask_kind)
+ * with p_i = Lk - Lq + i as in attn_fwd, then the guarded softmax of attn_fwd (out 0 and
+ * lse -inf for a row with no visible key).
+ *
+ *   q, k, v, out      device pointers; element (b, h, row, c) of q sits at
+ *                     q + b*q_stride[0] + h*q_stride[1] + row*q_stride[2] + c (elements,
+ *                     the head dimension contiguous), likewise k/v (over KV heads) and
+ *                     out. A transposed KV cache [B, Lk, Hkv, d] is k_stride =
+ *                     {Lk*Hkv*d, d, Hkv*d}. Strides are >= 0; out must not overlap itself
+ *                     or the inputs. For fp16/bf16 the pointers are 16-byte aligned and
+ *                     every stride a multiple of 8 elements, and (Lk - 1) * k_stride[2] + d
+ *                     (likewise for v) must stay below 2^30 elements.
+ *   lse               fp32 [B, Hq, Lq] contiguous, or NULL.
+ *   mask              fp32 device; element (b, h, i, j) at mask + b*mask_stride[0] +
+ *                     h*mask_stride[1] + i*mask_stride[2] + j*mask_stride[3]; a zero stride
+ *                     shares the mask over that dimension ({0, 0, Lk, 1} is the single
+ *                     [Lq, Lk] mask of attn_fwd). Required by MI_ATTN_MASK_DENSE. With
+ *                     MI_ATTN_MASK_TOPK it is optional and, when given, added to the kept
+ *                     keys' logits together with their zero_hold values. Ignored otherwise.
+ *   zero_hold, keep_k as in attn_fwd ([B, Hkv, Lk] contiguous).
+ *   topk_causal       MI_ATTN_MASK_TOPK: 1 selects among the keys j <= p_i (attn_fwd's
+ *                     rule), 0 among all keys (every row keeps the same keep_k keys), as
+ *                     dynamic_mask_topk's causal argument.
+ *   alibi_slopes      fp32 device [Hq] or NULL.
+ *   softcap           >= 0 and finite; 0 turns it off.
+ *   Returns attn_fwd's codes; MI_ATTN_EINVAL also for args == NULL, a negative stride,
+ *   a zero out stride over a dimension longer than 1, a misaligned pointer or stride, a
+ *   negative or non-finite softcap, or topk_causal other than 0/1; MI_ATTN_EUNSUPPORTED
+ *   for K/V rows too far apart.
+ */
+typedef struct {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;
+  int64_t q_stride[3];    /* batch, head, row (elements) */
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int64_t out_stride[3];
+  int B, Hq, Hkv, Lq, Lk, d;
+  float scale;
+  int mask_kind;
+  int window_left;
+  const float* mask;
+  int64_t mask_stride[4]; /* batch, head, query row, key (elements) */
+  const float* zero_hold;
+  int keep_k;
+  int topk_causal;
+  const float* alibi_slopes;
+  float softcap;
+  int dtype;
+} attn_fwd_args_t;
+
+int attn_fwd_ex(const attn_fwd_args_t* args, void* stream);
 
 /* which kernels attn_fwd would run for a shape (host-only query, no GPU work) */
 typedef struct {

@@ -26,13 +26,26 @@ class MiAttnError(RuntimeError):
         self.code = code
 
 
-ABI_VERSION = 3  # MI_ATTN_ABI_VERSION of include/mi_attn.h that this binding matches
+ABI_VERSION = 4  # MI_ATTN_ABI_VERSION of include/mi_attn.h that this binding matches
 
 
 class AttnPlan(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int), ("block_m", ctypes.c_int), ("block_n", ctypes.c_int),
                 ("splits", ctypes.c_int), ("grid", ctypes.c_int), ("mask_summary", ctypes.c_int),
                 ("workspace_bytes", ctypes.c_size_t), ("topk_list_cap", ctypes.c_int)]
+
+
+class AttnFwdArgs(ctypes.Structure):
+    """attn_fwd_args_t of include/mi_attn.h (the same field order and types)."""
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("out", ctypes.c_void_p),
+                ("lse", ctypes.c_void_p),
+                ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3), ("v_stride", ctypes.c_int64 * 3),
+                ("out_stride", ctypes.c_int64 * 3),
+                ("B", ctypes.c_int), ("Hq", ctypes.c_int), ("Hkv", ctypes.c_int), ("Lq", ctypes.c_int),
+                ("Lk", ctypes.c_int), ("d", ctypes.c_int), ("scale", ctypes.c_float), ("mask_kind", ctypes.c_int),
+                ("window_left", ctypes.c_int), ("mask", ctypes.c_void_p), ("mask_stride", ctypes.c_int64 * 4),
+                ("zero_hold", ctypes.c_void_p), ("keep_k", ctypes.c_int), ("topk_causal", ctypes.c_int),
+                ("alibi_slopes", ctypes.c_void_p), ("softcap", ctypes.c_float), ("dtype", ctypes.c_int)]
 
 
 _lib = None
@@ -47,6 +60,7 @@ _SIGS = {
                         + [ctypes.c_int] * 5 + [ctypes.c_float] + [ctypes.c_int] * 2
                         + [ctypes.c_void_p] + [ctypes.c_int] * 3 + [ctypes.c_void_p] * 2
                         + [ctypes.c_int, ctypes.c_void_p]),
+    "attn_fwd_ex": (ctypes.c_int, [ctypes.POINTER(AttnFwdArgs), ctypes.c_void_p]),
     "attn_fwd_plan": (ctypes.c_int, [ctypes.c_int] * 10 + [ctypes.POINTER(AttnPlan)]),
     "attn_set_debug": (None, [ctypes.c_int] * 3),
     "attn_last_error": (ctypes.c_char_p, []),
@@ -165,6 +179,75 @@ def attn_fwd(q, k, v, *, scale=None, mask_kind="causal", window_left=0, mask=Non
                         float(scale), mk, int(window_left), _ptr(mask), _ptr(zero_hold), int(keep_k),
                         _dtype_code(q), _stream_handle(q.device, stream))
     _check(rc)
+    return out, lse
+
+
+def attn_fwd_ex(q, k, v, *, scale=None, mask_kind="causal", window_left=0, mask=None, zero_hold=None, keep_k=0,
+                topk_causal=True, alibi_slopes=None, softcap=0.0, out=None, lse=None, return_lse=True, stream=None):
+    """Masked attention forward with general layouts and score modifiers (attn_fwd_ex).
+
+    q ``[B,Hq,Lq,d]`` and k/v ``[B,Hkv,Lk,d]`` may be any strided views whose last
+    dimension is contiguous (a transposed cache ``[B,Lk,Hkv,d]`` passed as
+    ``cache.transpose(1, 2)``). ``mask`` is an fp32 tensor that broadcasts to
+    ``[B,Hq,Lq,Lk]`` (dense kind; with ``"topk"`` it is optional and added to the kept
+    keys). ``topk_causal=False`` selects the top-k among all keys. ``alibi_slopes`` fp32
+    ``[Hq]``; ``softcap`` > 0 caps the scaled scores. ``out`` may be strided too.
+    Returns ``(out, lse)``.
+    """
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or t.dim() != 4 or t.stride(3) != 1:
+            raise ValueError(f"{name} must be a 4-D GPU tensor with a contiguous last dimension")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share a dtype")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k and v must be on one device")
+    B, Hq, Lq, d = q.shape
+    Bk, Hkv, Lk, dk = k.shape
+    if (Bk, dk) != (B, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    mk = MASK_KINDS[mask_kind] if isinstance(mask_kind, str) else int(mask_kind)
+    mask_e = None
+    if mask is not None:
+        if mask.dtype != torch.float32 or mask.device != q.device:
+            raise ValueError("mask must be an fp32 tensor on q's device")
+        mask_e = mask.expand(B, Hq, Lq, Lk)  # broadcast dimensions get stride 0
+    if zero_hold is not None:
+        if zero_hold.dtype != torch.float32 or tuple(zero_hold.shape) != (B, Hkv, Lk) \
+                or not zero_hold.is_contiguous() or zero_hold.device != q.device:
+            raise ValueError("zero_hold must be a contiguous fp32 [B, Hkv, Lk] tensor on q's device")
+    if alibi_slopes is not None:
+        if alibi_slopes.dtype != torch.float32 or tuple(alibi_slopes.shape) != (Hq,) \
+                or not alibi_slopes.is_contiguous() or alibi_slopes.device != q.device:
+            raise ValueError("alibi_slopes must be a contiguous fp32 [Hq] tensor on q's device")
+    if out is None:
+        out = torch.empty((B, Hq, Lq, d), dtype=q.dtype, device=q.device)
+    elif tuple(out.shape) != (B, Hq, Lq, d) or out.dtype != q.dtype or out.stride(3) != 1:
+        raise ValueError("out must match q's shape and dtype with a contiguous last dimension")
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    if lse is not None and (tuple(lse.shape) != (B, Hq, Lq) or lse.dtype != torch.float32
+                            or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous fp32 [B, Hq, Lq] tensor")
+    a = AttnFwdArgs()
+    a.q, a.k, a.v, a.out = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr()
+    a.lse = None if lse is None else lse.data_ptr()
+    for dst, t in ((a.q_stride, q), (a.k_stride, k), (a.v_stride, v), (a.out_stride, out)):
+        for i in range(3):
+            dst[i] = t.stride(i)
+    a.B, a.Hq, a.Hkv, a.Lq, a.Lk, a.d = B, Hq, Hkv, Lq, Lk, d
+    a.scale = float(1.0 / math.sqrt(d) if scale is None else scale)
+    a.mask_kind, a.window_left = mk, int(window_left)
+    if mask_e is not None:
+        a.mask = mask_e.data_ptr()
+        for i in range(4):
+            a.mask_stride[i] = mask_e.stride(i)
+    a.zero_hold = None if zero_hold is None else zero_hold.data_ptr()
+    a.keep_k, a.topk_causal = int(keep_k), int(bool(topk_causal))
+    a.alibi_slopes = None if alibi_slopes is None else alibi_slopes.data_ptr()
+    a.softcap = float(softcap)
+    a.dtype = _dtype_code(q)
+    _check(lib().attn_fwd_ex(ctypes.byref(a), _stream_handle(q.device, stream)))
     return out, lse
 
 

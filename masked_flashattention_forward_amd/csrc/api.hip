@@ -35,6 +35,7 @@ int g_force_splits = 0;
 
 struct Shape {
   int B, Hq, Hkv, Lq, Lk, d, mask_kind, window_left, keep_k, dtype;
+  int flag_b = 1, flag_g = 1;  // dense-mask summary rows per batch / KV head (1: shared)
 };
 
 int validate(const Shape& s) {
@@ -137,8 +138,8 @@ int make_plan(const Shape& s, Plan* pl) {
   if (s.mask_kind == MI_ATTN_MASK_DENSE && path != 0) {
     p.mask_summary = 1;
     pl->off_flags = off;
-    off = align256(off + static_cast<size_t>((s.Lq + pl->q_per_block - 1) / pl->q_per_block) *
-                             ((s.Lk + p.block_n - 1) / p.block_n));
+    off = align256(off + static_cast<size_t>(s.flag_b) * s.flag_g *
+                             ((s.Lq + pl->q_per_block - 1) / pl->q_per_block) * ((s.Lk + p.block_n - 1) / p.block_n));
   }
   if (p.splits > 1) {
     const size_t rows = static_cast<size_t>(s.B) * s.Hq * s.Lq;
@@ -178,36 +179,79 @@ int attn_fwd_plan(int B, int Hq, int Hkv, int Lq, int Lk, int d, int mask_kind, 
   return MI_ATTN_OK;
 }
 
-int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv, int Lq,
-             int Lk, int d, float scale, int mask_kind, int window_left, const float* mask, const float* zero_hold,
-             int keep_k, int dtype, void* stream) {
+int attn_fwd_ex(const attn_fwd_args_t* a, void* stream) {
   g_err.clear();
-  const Shape s{B, Hq, Hkv, Lq, Lk, d, mask_kind, window_left, keep_k, dtype};
+  if (a == nullptr) return fail(MI_ATTN_EINVAL, "args must not be NULL");
+  Shape s{a->B, a->Hq, a->Hkv, a->Lq, a->Lk, a->d, a->mask_kind, a->window_left, a->keep_k, a->dtype};
   int rc = validate(s);
   if (rc != MI_ATTN_OK) return rc;
-  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
+  if (a->q == nullptr || a->k == nullptr || a->v == nullptr || a->out == nullptr)
     return fail(MI_ATTN_EINVAL, "q, k, v and out must not be NULL");
-  if (!std::isfinite(scale)) return fail(MI_ATTN_EINVAL, "scale must be finite");
-  if (mask_kind == MI_ATTN_MASK_DENSE && mask == nullptr)
+  if (!std::isfinite(a->scale)) return fail(MI_ATTN_EINVAL, "scale must be finite");
+  if (a->mask_kind == MI_ATTN_MASK_DENSE && a->mask == nullptr)
     return fail(MI_ATTN_EINVAL, "mask_kind DENSE needs a mask pointer");
-  if (mask_kind == MI_ATTN_MASK_TOPK && zero_hold == nullptr)
+  if (a->mask_kind == MI_ATTN_MASK_TOPK && a->zero_hold == nullptr)
     return fail(MI_ATTN_EINVAL, "mask_kind TOPK needs a zero_hold pointer");
+  if (a->topk_causal != 0 && a->topk_causal != 1) return fail(MI_ATTN_EINVAL, "topk_causal must be 0 or 1");
+  if (!std::isfinite(a->softcap) || a->softcap < 0.f) return fail(MI_ATTN_EINVAL, "softcap must be finite and >= 0");
+  // strides: non-negative; out never written twice; 16-byte rows for the vector loads
+  const int64_t* st[4] = {a->q_stride, a->k_stride, a->v_stride, a->out_stride};
+  const char* nm[4] = {"q", "k", "v", "out"};
+  const int hs[4] = {a->Hq, a->Hkv, a->Hkv, a->Hq};
+  const int ls[4] = {a->Lq, a->Lk, a->Lk, a->Lq};
+  const void* ptr[4] = {a->q, a->k, a->v, a->out};
+  const int es = a->dtype == MI_ATTN_F32 ? 4 : 2;
+  for (int t = 0; t < 4; ++t) {
+    for (int x = 0; x < 3; ++x)
+      if (st[t][x] < 0) return fail(MI_ATTN_EINVAL, "%s stride %d is negative", nm[t], x);
+    if (t == 3 && ((a->B > 1 && st[t][0] == 0) || (a->Hq > 1 && st[t][1] == 0) || (a->Lq > 1 && st[t][2] == 0)))
+      return fail(MI_ATTN_EINVAL, "out strides must be positive over dimensions longer than 1");
+    if (a->dtype != MI_ATTN_F32) {
+      if (reinterpret_cast<uintptr_t>(ptr[t]) % 16 != 0 || st[t][0] % 8 || st[t][1] % 8 || st[t][2] % 8)
+        return fail(MI_ATTN_EINVAL, "%s must be 16-byte aligned with strides in multiples of 8 elements", nm[t]);
+      if (t == 1 || t == 2) {
+        // one (batch, KV head) slice is addressed with 32-bit byte offsets
+        const double span = (static_cast<double>(ls[t]) * st[t][2] + a->d) * es;
+        if (span > 2147483647.0)
+          return fail(MI_ATTN_EUNSUPPORTED, "%s rows too far apart for 32-bit offsets (Lk * row stride)", nm[t]);
+      }
+    }
+    (void)hs;
+  }
+  for (int x = 0; x < 4; ++x)
+    if (a->mask_stride[x] < 0) return fail(MI_ATTN_EINVAL, "mask stride %d is negative", x);
+  const bool use_mask = a->mask_kind == MI_ATTN_MASK_DENSE || (a->mask_kind == MI_ATTN_MASK_TOPK && a->mask != nullptr);
+  if (a->mask_kind == MI_ATTN_MASK_DENSE) {
+    s.flag_b = (a->B > 1 && a->mask_stride[0] != 0) ? a->B : 1;
+    s.flag_g = (a->Hq > 1 && a->mask_stride[1] != 0) ? a->Hkv : 1;
+  }
   Plan pl;
   rc = make_plan(s, &pl);
   if (rc != MI_ATTN_OK) return rc;
 
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipStream_t st_ = static_cast<hipStream_t>(stream);
   char* ws = nullptr;
   if (pl.pub.workspace_bytes > 0) {
-    hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&ws), pl.pub.workspace_bytes, st);
+    hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&ws), pl.pub.workspace_bytes, st_);
     if (e != hipSuccess) return hip_fail(e, "hipMallocAsync(workspace)");
   }
 
+  const int B = a->B, Hq = a->Hq, Hkv = a->Hkv, Lq = a->Lq, Lk = a->Lk;
   AttnParams p{};
-  p.q = q; p.k = k; p.v = v; p.out = out; p.lse = lse;
-  p.mask = mask; p.zero_hold = zero_hold;
-  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Lq = Lq; p.Lk = Lk; p.d = d; p.G = Hq / Hkv;
-  p.scale = scale; p.mask_kind = mask_kind; p.window_left = window_left; p.keep_k = keep_k;
+  p.q = a->q; p.k = a->k; p.v = a->v; p.out = a->out; p.lse = a->lse;
+  p.mask = use_mask ? a->mask : nullptr;
+  p.zero_hold = a->zero_hold;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Lq = Lq; p.Lk = Lk; p.d = a->d; p.G = Hq / Hkv;
+  p.scale = a->scale; p.mask_kind = a->mask_kind; p.window_left = a->window_left; p.keep_k = a->keep_k;
+  for (int x = 0; x < 3; ++x) {
+    p.qs[x] = a->q_stride[x]; p.ks[x] = a->k_stride[x]; p.vs[x] = a->v_stride[x]; p.os[x] = a->out_stride[x];
+  }
+  for (int x = 0; x < 4; ++x) p.ms[x] = a->mask_stride[x];
+  p.flag_b = s.flag_b;
+  p.flag_g = s.flag_g;
+  p.alibi = a->alibi_slopes;
+  p.softcap = a->softcap;
+  p.topk_causal = a->mask_kind == MI_ATTN_MASK_TOPK ? a->topk_causal : 1;
   p.no_skip = g_no_skip;
   p.splits = pl.pub.splits;
   {
@@ -221,12 +265,13 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
 
   hipError_t e = hipSuccess;
   const char* what = "";
-  if (mask_kind == MI_ATTN_MASK_TOPK) {
+  if (a->mask_kind == MI_ATTN_MASK_TOPK) {
     int32_t* rank = reinterpret_cast<int32_t*>(ws + pl.off_rank);
     int32_t* tau = reinterpret_cast<int32_t*>(ws + pl.off_tau);
     int32_t* tmin = reinterpret_cast<int32_t*>(ws + pl.off_tmin);
     what = "top-k selection";
-    e = launch_topk(zero_hold, B * Hkv, Lq, Lk, keep_k, 1, rank, tau, nullptr, tmin, pl.pub.block_n, st);
+    e = launch_topk(a->zero_hold, B * Hkv, Lq, Lk, a->keep_k, p.topk_causal, rank, tau, nullptr, tmin, pl.pub.block_n,
+                    st_);
     p.rank = rank; p.tau = tau; p.tile_min_rank = tmin;
     if (e == hipSuccess && pl.list_cap > 0) {
       int32_t* lidx = reinterpret_cast<int32_t*>(ws + pl.off_lidx);
@@ -234,8 +279,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
       float* lzh = reinterpret_cast<float*>(ws + pl.off_lzh);
       int32_t* lcnt = reinterpret_cast<int32_t*>(ws + pl.off_lcnt);
       what = "top-k kept-key lists";
-      e = launch_topk_lists(rank, tau, zero_hold, B * Hkv, Lq, Lk, pl.q_per_block, pl.list_cap, lidx, lrank, lzh,
-                            lcnt, st);
+      e = launch_topk_lists(rank, tau, a->zero_hold, B * Hkv, Lq, Lk, pl.q_per_block, pl.list_cap, p.topk_causal,
+                            lidx, lrank, lzh, lcnt, st_);
       p.list_idx = lidx; p.list_rank = lrank; p.list_zh = lzh; p.list_count = lcnt;
       p.list_cap = pl.list_cap;
     }
@@ -243,7 +288,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
   if (e == hipSuccess && pl.pub.mask_summary) {
     uint8_t* flags = reinterpret_cast<uint8_t*>(ws + pl.off_flags);
     what = "dense-mask summary";
-    e = launch_mask_summary(mask, Lq, Lk, pl.q_per_block, pl.pub.block_n, flags, st);
+    e = launch_mask_summary(p, pl.pub.block_n, flags, st_);
     p.tile_live = flags;
   }
   if (e == hipSuccess) {
@@ -252,14 +297,37 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
       p.part_lse = reinterpret_cast<float*>(ws + pl.off_plse);
     }
     what = "attention kernel";
-    e = (pl.pub.path == 0) ? launch_row_kernel(p, dtype, st) : launch_half_path(pl.pub.path, p, dtype, st);
+    e = (pl.pub.path == 0) ? launch_row_kernel(p, a->dtype, st_) : launch_half_path(pl.pub.path, p, a->dtype, st_);
   }
   if (ws != nullptr) {
-    const hipError_t ef = hipFreeAsync(ws, st);
+    const hipError_t ef = hipFreeAsync(ws, st_);
     if (e == hipSuccess && ef != hipSuccess) return hip_fail(ef, "hipFreeAsync(workspace)");
   }
   if (e != hipSuccess) return hip_fail(e, what);
   return MI_ATTN_OK;
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv, int Lq,
+             int Lk, int d, float scale, int mask_kind, int window_left, const float* mask, const float* zero_hold,
+             int keep_k, int dtype, void* stream) {
+  // the contiguous layouts, the single [Lq, Lk] mask (dense kind only), causal top-k
+  attn_fwd_args_t a{};
+  a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Lq = Lq; a.Lk = Lk; a.d = d;
+  const int64_t qh = static_cast<int64_t>(Lq) * d, kh = static_cast<int64_t>(Lk) * d;
+  a.q_stride[0] = a.out_stride[0] = qh * Hq;
+  a.q_stride[1] = a.out_stride[1] = qh;
+  a.q_stride[2] = a.out_stride[2] = d;
+  a.k_stride[0] = a.v_stride[0] = kh * Hkv;
+  a.k_stride[1] = a.v_stride[1] = kh;
+  a.k_stride[2] = a.v_stride[2] = d;
+  a.scale = scale; a.mask_kind = mask_kind; a.window_left = window_left;
+  a.mask = mask_kind == MI_ATTN_MASK_DENSE ? mask : nullptr;
+  a.mask_stride[2] = Lk;
+  a.mask_stride[3] = 1;
+  a.zero_hold = zero_hold; a.keep_k = keep_k; a.topk_causal = 1;
+  a.dtype = dtype;
+  return attn_fwd_ex(&a, stream);
 }
 
 int attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,

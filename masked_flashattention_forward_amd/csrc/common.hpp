@@ -114,7 +114,28 @@ struct AttnParams {
   int keys_per_split;
   int block_n;
   int q_per_block;         // query positions per workgroup (summary granularity)
+  // Element strides of q, k, v and out: {batch, head, row}; the head dimension is
+  // contiguous. attn_fwd passes the contiguous ones. (Not used by the varlen kernels.)
+  long qs[3], ks[3], vs[3], os[3];
+  // dense mask element (b, h, i, j) at mask[b*ms[0] + h*ms[1] + i*ms[2] + j*ms[3]]; a
+  // zero stride shares the mask over that dimension
+  long ms[4];
+  // dense-mask summary flags: [flag_b][flag_g][query blocks][tiles], flag_b = B when
+  // the mask varies with the batch (else 1), flag_g = Hkv when it varies with the head
+  int flag_b, flag_g;
+  const float* alibi;      // [Hq] slopes or nullptr: logit -= slope_h * |p_i - j|
+  float softcap;           // > 0: logit -> softcap * tanh(logit / softcap) before the bias
+  int topk_causal;         // top-k among causally allowed keys (1) or among all keys (0)
 };
+
+// Whether a call carries a per-element score modifier (every tile is then modified).
+__host__ __device__ inline bool has_mods(const AttnParams& p) { return p.softcap > 0.f || p.alibi != nullptr; }
+
+// The mask kind whose bounds limit the visited key range: top-k over all keys visits
+// every key, like no mask.
+__host__ __device__ inline int range_kind(const AttnParams& p) {
+  return (p.mask_kind == MI_ATTN_MASK_TOPK && !p.topk_causal) ? MI_ATTN_MASK_NONE : p.mask_kind;
+}
 
 // Visible key range [lo, hi) for a contiguous span of query positions [p0, p1]
 // (positions are bottom-right aligned). Keys outside the range are hidden for every
@@ -144,10 +165,12 @@ hipError_t launch_topk(const float* zh, int BH, int Lq, int Lk, int keep_k, int 
                        int32_t* rank, int32_t* tau, uint32_t* keep_bits, int32_t* tile_min, int block_n,
                        hipStream_t s);
 // Kept-key lists of the gathered top-k attention (see AttnParams::list_*).
+// causal == 0: every row may keep any key (the lists hold the keys of rank <= tau).
 hipError_t launch_topk_lists(const int32_t* rank, const int32_t* tau, const float* zh, int BH, int Lq, int Lk,
-                             int q_per_block, int cap, int32_t* list_idx, int32_t* list_rank, float* list_zh,
-                             int32_t* list_count, hipStream_t s);
-hipError_t launch_mask_summary(const float* mask, int Lq, int Lk, int q_per_block, int block_n,
-                               uint8_t* flags, hipStream_t s);
+                             int q_per_block, int cap, int causal, int32_t* list_idx, int32_t* list_rank,
+                             float* list_zh, int32_t* list_count, hipStream_t s);
+// Dense-mask summary flags (see AttnParams::flag_b): 1 iff some entry of the tile is
+// above -inf for some row of the query block and some query head of the KV head.
+hipError_t launch_mask_summary(const AttnParams& p, int block_n, uint8_t* flags, hipStream_t s);
 
 }  // namespace mi_attn

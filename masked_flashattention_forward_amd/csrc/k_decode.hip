@@ -45,7 +45,7 @@ struct DecTile {
 // VARLEN: one item of the varlen work list (a key range of a sequence with at most 32
 // query rows per KV head); K/V rows come from cache pages, packed rows or the new-token
 // arrays through per-lane 64-bit addresses, and the output is token-major.
-template <typename T, int D, int MK, bool VARLEN = false>
+template <typename T, int D, int MK, bool VARLEN = false, bool EXT = false>
 __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(AttnParams p) {
   static_assert(!VARLEN || MK <= MI_ATTN_MASK_WINDOW, "varlen takes the key-position masks");
   using TL = DecTile<D>;
@@ -98,21 +98,25 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(AttnParams p) {
   const long row_index = VARLEN ? static_cast<long>(vs.q_start + i_row) * p.Hq + h_row
                                 : (static_cast<long>(b) * p.Hq + h_row) * Lq + i_row;
 
+  // element offsets of this lane's q and out rows (strided for the single-batch call)
+  const long q_off = VARLEN ? row_index * D : b * p.qs[0] + h_row * p.qs[1] + i_row * p.qs[2];
+  const long o_off = VARLEN ? row_index * D : b * p.os[0] + h_row * p.os[1] + i_row * p.os[2];
   const T* Q = static_cast<const T*>(p.q);
   const bool negate = p.scale < 0.f;
   const float cexp = fabsf(p.scale) * kLog2e;
+  const Mods md = make_mods<EXT>(p, cexp, b, h_row, i_row, pos, MK == MI_ATTN_MASK_DENSE || MK == MI_ATTN_MASK_TOPK);
   u32x4_t qreg[D / 16];
 #pragma unroll
   for (int dc = 0; dc < D / 16; ++dc) {
     u32x4_t x = {0u, 0u, 0u, 0u};
-    if (row_ok) x = *reinterpret_cast<const u32x4_t*>(Q + row_index * D + dc * 16 + hf * 8);
+    if (row_ok) x = *reinterpret_cast<const u32x4_t*>(Q + q_off + dc * 16 + hf * 8);
     if (negate) x ^= 0x80008000u;
     qreg[dc] = x;
   }
 
   // key range of this split
   if constexpr (!VARLEN) {
-    key_range(MK, p.window_left, Lk, P0, P1, &lo, &hi);
+    key_range(range_kind(p), p.window_left, Lk, P0, P1, &lo, &hi);
     if (p.no_skip) { lo = 0; hi = Lk; }
     const int s0 = split * p.keys_per_split;
     const int s1 = min(Lk, s0 + p.keys_per_split);
@@ -123,19 +127,30 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(AttnParams p) {
   const int t_hi = (hi > lo) ? (hi + kDecBN - 1) / kDecBN : t_lo;
   const int ntiles_all = (Lk + kDecBN - 1) / kDecBN;
 
-  const long kv_base = VARLEN ? 0 : static_cast<long>(bg) * Lk * D;
+  // K / V of this (batch, KV head): rows ks / vs elements apart (D for contiguous K/V);
+  // the ranges cover rows 0 .. Lk-1 (the host keeps them below 2^31 bytes)
+  const long ksr = VARLEN ? D : p.ks[2];
+  const long vsr = VARLEN ? D : p.vs[2];
   const long bgk = static_cast<long>(bg) * Lk;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(static_cast<const T*>(p.k) + kv_base, VARLEN ? 0 : Lk * D * 2);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(static_cast<const T*>(p.v) + kv_base, VARLEN ? 0 : Lk * D * 2);
+  const __amdgpu_buffer_rsrc_t krs =
+      make_rsrc(static_cast<const T*>(p.k) + (VARLEN ? 0 : b * p.ks[0] + g * p.ks[1]),
+                VARLEN ? 0 : static_cast<int>(((Lk - 1) * ksr + D) * 2));
+  const __amdgpu_buffer_rsrc_t vrs =
+      make_rsrc(static_cast<const T*>(p.v) + (VARLEN ? 0 : b * p.vs[0] + g * p.vs[1]),
+                VARLEN ? 0 : static_cast<int>(((Lk - 1) * vsr + D) * 2));
 
   int32_t tau_row = 0, tau_blk = 0;
   if constexpr (MK == MI_ATTN_MASK_TOPK) {
-    tau_row = p.tau[static_cast<long>(bg) * p.Lq + i_row];
-    tau_blk = p.tau[static_cast<long>(bg) * p.Lq];
+    // clamped below Lk: every allowed key when tau says "all kept", never a padding key
+    tau_row = min(p.tau[static_cast<long>(bg) * p.Lq + i_row], Lk - 1);
+    tau_blk = min(p.tau[static_cast<long>(bg) * p.Lq], Lk - 1);
   }
+  // dense-mask summary flags of this (batch, KV head) (one query block)
+  const long flag_base =
+      (static_cast<long>(p.flag_b > 1 ? b : 0) * p.flag_g + (p.flag_g > 1 ? g : 0)) * ntiles_all;
   auto tile_live = [&](int t) -> bool {
     if (p.no_skip) return true;
-    if constexpr (MK == MI_ATTN_MASK_DENSE) return p.tile_live[t] != 0;  // one query block
+    if constexpr (MK == MI_ATTN_MASK_DENSE) return p.tile_live[flag_base + t] != 0;
     if constexpr (MK == MI_ATTN_MASK_TOPK) return p.tile_min_rank[static_cast<long>(bg) * ntiles_all + t] <= tau_blk;
     return true;
   };
@@ -177,13 +192,14 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(AttnParams p) {
     }
     // K: lane holds key j0 + l32, dims dc*16 + hf*8 .. +8 (the A operand of S^T = K Q^T)
 #pragma unroll
-    for (int dc = 0; dc < TL::kLoads; ++dc) kr[dc] = buffer_load16(krs, ((j0 + l32) * D + dc * 16 + hf * 8) * 2);
+    for (int dc = 0; dc < TL::kLoads; ++dc)
+      kr[dc] = buffer_load16(krs, static_cast<int>(((j0 + l32) * ksr + dc * 16 + hf * 8) * 2));
     // V: 1 KB direct loads into the swizzled [key][d] tile
 #pragma unroll
     for (int c = 0; c < TL::vLoads; ++c) {
       const int r = c * (1024 / (D * 2)) + lane / (D / 8);
       const int ps = lane % (D / 8);
-      const int gofs = ((j0 + r) * D + ((ps ^ swz<D>(r)) << 3)) * 2;
+      const int gofs = static_cast<int>(((j0 + r) * vsr + ((ps ^ swz<D>(r)) << 3)) * 2);
       lds_dma16(vrs, dst + c * 1024, gofs);
     }
   };
@@ -226,14 +242,14 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(AttnParams p) {
       sacc[0] = acc;
     }
     float cm = cexp;
-    if (tile_needs_mask<MK, kDecBN>(p, Lk, j0, P0, P1)) {
+    if (tile_needs_mask<MK, kDecBN, EXT>(p, Lk, j0, P0, P1)) {
       const int32_t* xr = nullptr;
       const float* xz = nullptr;
       if constexpr (MK == MI_ATTN_MASK_TOPK) {
         xr = p.rank + bgk + j0;
         xz = p.zero_hold + bgk + j0;
       }
-      mask_tile<MK, 1>(sacc, p, Lk, j0, hf, pos, i_row, tau_row, cexp, xr, xz);
+      mask_tile<MK, 1, EXT>(sacc, p, Lk, j0, hf, pos, tau_row, md, xr, xz);
       cm = 1.f;
     }
 
@@ -337,7 +353,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(AttnParams p) {
     if (hf == 0) p.part_lse[slot] = lse;
     return;
   }
-  T* O = static_cast<T*>(p.out) + row_index * D;
+  T* O = static_cast<T*>(p.out) + o_off;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -350,16 +366,22 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(AttnParams p) {
   if (hf == 0 && p.lse != nullptr) p.lse[row_index] = lse;
 }
 
-template <typename T, int D>
-void launch_decode_d(const AttnParams& p, hipStream_t s) {
+template <typename T, int D, bool EXT>
+void launch_decode_e(const AttnParams& p, hipStream_t s) {
   dim3 grid(p.B * p.Hkv, p.splits), block(kDecThreads);
   switch (p.mask_kind) {
-    case MI_ATTN_MASK_NONE: hipLaunchKernelGGL((decode_kernel<T, D, 0>), grid, block, 0, s, p); break;
-    case MI_ATTN_MASK_CAUSAL: hipLaunchKernelGGL((decode_kernel<T, D, 1>), grid, block, 0, s, p); break;
-    case MI_ATTN_MASK_WINDOW: hipLaunchKernelGGL((decode_kernel<T, D, 2>), grid, block, 0, s, p); break;
-    case MI_ATTN_MASK_DENSE: hipLaunchKernelGGL((decode_kernel<T, D, 3>), grid, block, 0, s, p); break;
-    default: hipLaunchKernelGGL((decode_kernel<T, D, 4>), grid, block, 0, s, p); break;
+    case MI_ATTN_MASK_NONE: hipLaunchKernelGGL((decode_kernel<T, D, 0, false, EXT>), grid, block, 0, s, p); break;
+    case MI_ATTN_MASK_CAUSAL: hipLaunchKernelGGL((decode_kernel<T, D, 1, false, EXT>), grid, block, 0, s, p); break;
+    case MI_ATTN_MASK_WINDOW: hipLaunchKernelGGL((decode_kernel<T, D, 2, false, EXT>), grid, block, 0, s, p); break;
+    case MI_ATTN_MASK_DENSE: hipLaunchKernelGGL((decode_kernel<T, D, 3, false, EXT>), grid, block, 0, s, p); break;
+    default: hipLaunchKernelGGL((decode_kernel<T, D, 4, false, EXT>), grid, block, 0, s, p); break;
   }
+}
+
+template <typename T, int D>
+void launch_decode_d(const AttnParams& p, hipStream_t s) {
+  if (needs_ext(p)) launch_decode_e<T, D, true>(p, s);
+  else launch_decode_e<T, D, false>(p, s);
 }
 
 // varlen items of decode type: grid = items x KV heads, no split dimension

@@ -55,10 +55,10 @@ constexpr int kLog2RoundKeys = (D == 128) ? 4 : 5;
 constexpr int kLog2BN = 6;  // 64-key tiles
 
 // resident workgroups per CU: LDS allows 2 for d = 128 and 4 for d = 64. At d = 64 the
-// top-k variant's extra state keeps it at 2 and the varlen variant's per-row addressing
-// at 3 (4 would cap them at 128 VGPRs and spill).
-template <int D, int MK, bool VARLEN>
-constexpr int kMinBlocks = D == 128 ? 2 : MK == MI_ATTN_MASK_TOPK ? 2 : VARLEN ? 3 : 4;
+// top-k variant's extra state and the score modifiers (EXT) keep it at 2 and the varlen
+// variant's per-row addressing at 3 (4 would cap them at 128 VGPRs and spill).
+template <int D, int MK, bool VARLEN, bool EXT>
+constexpr int kMinBlocks = D == 128 ? 2 : (MK == MI_ATTN_MASK_TOPK || EXT) ? 2 : VARLEN ? 3 : 4;
 
 // GATHER (top-k only): tiles are consecutive 64-key runs of the block's kept-key list
 // (AttnParams::list_*) instead of consecutive keys, so only keys some row of the block
@@ -68,8 +68,8 @@ constexpr int kMinBlocks = D == 128 ? 2 : MK == MI_ATTN_MASK_TOPK ? 2 : VARLEN ?
 // one item of the device-built work list (a key range of one (sequence, query block)),
 // and each K/V row is fetched from its own cache page (or packed row, or the new-token
 // array of the two-source form) with a per-lane 64-bit address.
-template <typename T, int D, int BN, int MK, bool GATHER = false, bool VARLEN = false>
-__global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN>)) void prefill_kernel(AttnParams p) {
+template <typename T, int D, int BN, int MK, bool GATHER = false, bool VARLEN = false, bool EXT = false>
+__global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN, EXT>)) void prefill_kernel(AttnParams p) {
   static_assert(!GATHER || (MK == MI_ATTN_MASK_TOPK && BN == 64), "gathered tiles are top-k lists of 64 keys");
   static_assert(!VARLEN || (!GATHER && MK <= MI_ATTN_MASK_WINDOW), "varlen takes the key-position masks");
   using TL = Tile<D, BN>;
@@ -144,22 +144,28 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN>)) void prefill
                                 : (static_cast<long>(b) * p.Hq + h_row) * Lq + i_row;
   const long rows_all = VARLEN ? static_cast<long>(p.total_q) * p.Hq : static_cast<long>(p.B) * p.Hq * Lq;
 
+  // element offsets of this lane's q and out rows (strided for the single-batch call)
+  const long q_off = VARLEN ? row_index * D : b * p.qs[0] + h_row * p.qs[1] + i_row * p.qs[2];
+  const long o_off = VARLEN ? row_index * D : b * p.os[0] + h_row * p.os[1] + i_row * p.os[2];
+
   // ---- Q^T operand in registers: lane holds 8 dims (dc*16 + hf*8 ..) of its row
   const T* Q = static_cast<const T*>(p.q);
   const bool negate = p.scale < 0.f;  // fold the sign into Q so the log2-domain scale is > 0
   const float cexp = fabsf(p.scale) * kLog2e;
+  // score modifiers and the dense mask row of this lane (rows past the block read row i_first)
+  const Mods md = make_mods<EXT>(p, cexp, b, h_row, i_row, pos, MK == MI_ATTN_MASK_DENSE || MK == MI_ATTN_MASK_TOPK);
   u32x4_t qreg[D / 16];
 #pragma unroll
   for (int dc = 0; dc < D / 16; ++dc) {
     u32x4_t x = {0u, 0u, 0u, 0u};
-    if (row_ok) x = *reinterpret_cast<const u32x4_t*>(Q + row_index * D + dc * 16 + hf * 8);
+    if (row_ok) x = *reinterpret_cast<const u32x4_t*>(Q + q_off + dc * 16 + hf * 8);
     if (negate) x ^= 0x80008000u;
     qreg[dc] = x;
   }
 
   // ---- key range of this block (and split)
   int lo, hi;
-  key_range(MK, p.window_left, Lk, P0, P1, &lo, &hi);
+  key_range(range_kind(p), p.window_left, Lk, P0, P1, &lo, &hi);
   if (p.no_skip) { lo = 0; hi = Lk; }
   if (VARLEN) {
     // the item's range: part of [lo, hi) cut on tile boundaries by the work-list kernel
@@ -194,20 +200,27 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN>)) void prefill
   const T* const v_cache = static_cast<const T*>(p.v);
   const T* const k_fresh = static_cast<const T*>(p.k_new);
   const T* const v_fresh = static_cast<const T*>(p.v_new);
-  const long kv_base = VARLEN ? 0 : static_cast<long>(bg) * Lk * D;
-  const T* K = static_cast<const T*>(p.k) + kv_base;
-  const T* V = static_cast<const T*>(p.v) + kv_base;
+  // K / V of this (batch, KV head): rows ks / vs elements apart (D for contiguous K/V)
+  const long ksr = VARLEN ? D : p.ks[2];
+  const long vsr = VARLEN ? D : p.vs[2];
+  const T* K = static_cast<const T*>(p.k) + (VARLEN ? 0 : b * p.ks[0] + g * p.ks[1]);
+  const T* V = static_cast<const T*>(p.v) + (VARLEN ? 0 : b * p.vs[0] + g * p.vs[1]);
   const long bgk = static_cast<long>(bg) * Lk;
 
   // top-k: the block's largest threshold (thresholds do not grow with the row position)
   int32_t tau_row = 0, tau_blk = 0;
   if constexpr (MK == MI_ATTN_MASK_TOPK) {
-    tau_row = p.tau[static_cast<long>(bg) * p.Lq + i_row];
-    tau_blk = p.tau[static_cast<long>(bg) * p.Lq + i_first];
+    // ranks of real keys are below Lk: the clamp keeps every allowed key when tau says
+    // "all kept" (INT32_MAX) and never keeps padding keys (rank INT32_MAX)
+    tau_row = min(p.tau[static_cast<long>(bg) * p.Lq + i_row], Lk - 1);
+    tau_blk = min(p.tau[static_cast<long>(bg) * p.Lq + i_first], Lk - 1);
   }
+  // dense-mask summary flags of this (batch, KV head), query block
+  const long flag_base = ((static_cast<long>(p.flag_b > 1 ? b : 0) * p.flag_g + (p.flag_g > 1 ? g : 0)) * nqb + qb) *
+                         ntiles_all;
   auto tile_live = [&](int t) -> bool {
     if (GATHER || p.no_skip) return true;
-    if constexpr (MK == MI_ATTN_MASK_DENSE) return p.tile_live[static_cast<long>(qb) * ntiles_all + t] != 0;
+    if constexpr (MK == MI_ATTN_MASK_DENSE) return p.tile_live[flag_base + t] != 0;
     if constexpr (MK == MI_ATTN_MASK_TOPK)
       return p.tile_min_rank[static_cast<long>(bg) * ntiles_all + t] <= tau_blk;
     return true;
@@ -222,13 +235,15 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN>)) void prefill
   // of the swizzled layout. Rows at or past Lk read as zeros (buffer range check). A
   // lane's swizzle does not depend on the load round, so its global offset is one
   // loop-invariant register plus a wave-uniform (scalar) offset for the tile and round.
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K, VARLEN ? 0 : Lk * D * 2);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V, VARLEN ? 0 : Lk * D * 2);
-  int dma_lane;
+  // the range covers rows 0 .. Lk-1 (the host keeps it below 2^31 bytes)
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K, VARLEN ? 0 : static_cast<int>(((Lk - 1) * ksr + D) * 2));
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V, VARLEN ? 0 : static_cast<int>(((Lk - 1) * vsr + D) * 2));
+  int dma_lane_k, dma_lane_v;
   {
     const int r = wave * TL::rowsPerWaveLoad + lane / (D / 8);
     const int ps = lane % (D / 8);                   // physical slot this lane fills
-    dma_lane = (r * D + ((ps ^ swz<D>(r)) << 3)) * 2;
+    dma_lane_k = static_cast<int>((r * ksr + ((ps ^ swz<D>(r)) << 3)) * 2);
+    dma_lane_v = static_cast<int>((r * vsr + ((ps ^ swz<D>(r)) << 3)) * 2);
   }
   const unsigned smem_addr = __builtin_amdgcn_readfirstlane(lds_address(smem));
   // GATHER: row r of a tile comes from key list[t*BN + r]; a lane's rows in load round c
@@ -343,13 +358,12 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN>)) void prefill
       const unsigned blk = (c * kWaves + wave) * 1024;  // 1 KB block of the tile
       if constexpr (GATHER) {
         // padding entries (key Lk) lie past the buffer range and read as zeros
-        const int vo = gidx[c] * (D * 2) + dma_slot;
-        lds_dma16_at(krs, kst + blk, vo, 0);
-        lds_dma16_at(vrs, kst + TL::kBytes + blk, vo, 0);
+        lds_dma16_at(krs, kst + blk, static_cast<int>(gidx[c] * ksr * 2) + dma_slot, 0);
+        lds_dma16_at(vrs, kst + TL::kBytes + blk, static_cast<int>(gidx[c] * vsr * 2) + dma_slot, 0);
       } else {
-        const int so = (j0 + c * kWaves * TL::rowsPerWaveLoad) * D * 2;
-        lds_dma16_at(krs, kst + blk, dma_lane, so);
-        lds_dma16_at(vrs, kst + TL::kBytes + blk, dma_lane, so);
+        const int row0 = j0 + c * kWaves * TL::rowsPerWaveLoad;
+        lds_dma16_at(krs, kst + blk, dma_lane_k, static_cast<int>(row0 * ksr * 2));
+        lds_dma16_at(vrs, kst + TL::kBytes + blk, dma_lane_v, static_cast<int>(row0 * vsr * 2));
       }
     }
     if constexpr (GATHER) {
@@ -461,21 +475,22 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN>)) void prefill
       const int32_t* xr = reinterpret_cast<const int32_t*>(vs + TL::vBytes);
       const float* xzl = reinterpret_cast<const float*>(xr + BN);
       const int32_t* xi = xr + 2 * BN;
-      if (xi[BN - 1] > P0)  // the list ascends: its last key decides whether positions matter
-        mask_tile_topk_list<NKB, true>(sacc, hf, pos, tau_row, cexp, xr, xzl, xi);
+      // the list ascends: its last key decides whether positions matter (causal selection)
+      if (p.topk_causal && xi[BN - 1] > P0)
+        mask_tile_topk_list<NKB, true, EXT>(sacc, hf, pos, tau_row, md, xr, xzl, xi);
       else
-        mask_tile_topk_list<NKB, false>(sacc, hf, pos, tau_row, cexp, xr, xzl, xi);
+        mask_tile_topk_list<NKB, false, EXT>(sacc, hf, pos, tau_row, md, xr, xzl, xi);
       cm = 1.f;
     } else if constexpr (MK == MI_ATTN_MASK_TOPK) {
       const int32_t* xr = reinterpret_cast<const int32_t*>(vs + TL::vBytes);
       const float* xzl = reinterpret_cast<const float*>(xr + BN);
-      if (j0 + BN - 1 > P0)
-        mask_tile_topk<NKB, true>(sacc, j0, hf, pos, tau_row, cexp, xr, xzl);
+      if (p.topk_causal && j0 + BN - 1 > P0)
+        mask_tile_topk<NKB, true, EXT>(sacc, j0, hf, pos, tau_row, md, xr, xzl);
       else
-        mask_tile_topk<NKB, false>(sacc, j0, hf, pos, tau_row, cexp, xr, xzl);
+        mask_tile_topk<NKB, false, EXT>(sacc, j0, hf, pos, tau_row, md, xr, xzl);
       cm = 1.f;
-    } else if (tile_needs_mask<MK, BN>(p, Lk, j0, P0, P1)) {
-      mask_tile<MK, NKB>(sacc, p, Lk, j0, hf, pos, i_row, tau_row, cexp, nullptr, nullptr);
+    } else if (tile_needs_mask<MK, BN, EXT>(p, Lk, j0, P0, P1)) {
+      mask_tile<MK, NKB, EXT>(sacc, p, Lk, j0, hf, pos, tau_row, md, nullptr, nullptr);
       cm = 1.f;
     }
 
@@ -583,7 +598,7 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN>)) void prefill
     if (hf == 0) p.part_lse[slot] = lse;
     return;
   }
-  T* O = static_cast<T*>(p.out) + row_index * D;
+  T* O = static_cast<T*>(p.out) + o_off;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -622,7 +637,8 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(AttnParams p) {
   }
   const bool dead = !(tot > 0.f);
   const float inv = dead ? 0.f : 1.f / tot;
-  T* O = static_cast<T*>(p.out) + row * D + d0;
+  const long i = row % p.Lq, h = (row / p.Lq) % p.Hq, bb = row / (static_cast<long>(p.Lq) * p.Hq);
+  T* O = static_cast<T*>(p.out) + bb * p.os[0] + h * p.os[1] + i * p.os[2] + d0;
   O[0] = from_f32<T>(acc.x * inv);
   O[1] = from_f32<T>(acc.y * inv);
   O[2] = from_f32<T>(acc.z * inv);
@@ -637,34 +653,36 @@ hipError_t launch_lse_merge_t(const AttnParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename T, int D, bool EXT>
+void launch_prefill_d(dim3 grid, const AttnParams& p, hipStream_t s) {
+  const dim3 block(kThreads);
+  switch (p.mask_kind) {
+    case MI_ATTN_MASK_NONE: hipLaunchKernelGGL((prefill_kernel<T, D, 64, 0, false, false, EXT>), grid, block, 0, s, p); break;
+    case MI_ATTN_MASK_CAUSAL: hipLaunchKernelGGL((prefill_kernel<T, D, 64, 1, false, false, EXT>), grid, block, 0, s, p); break;
+    case MI_ATTN_MASK_WINDOW: hipLaunchKernelGGL((prefill_kernel<T, D, 64, 2, false, false, EXT>), grid, block, 0, s, p); break;
+    case MI_ATTN_MASK_DENSE: hipLaunchKernelGGL((prefill_kernel<T, D, 64, 3, false, false, EXT>), grid, block, 0, s, p); break;
+    default:
+      if (p.list_idx != nullptr)
+        hipLaunchKernelGGL((prefill_kernel<T, D, 64, 4, true, false, EXT>), grid, block, 0, s, p);
+      else
+        hipLaunchKernelGGL((prefill_kernel<T, D, 64, 4, false, false, EXT>), grid, block, 0, s, p);
+      break;
+  }
+}
+
 template <typename T>
 hipError_t launch_prefill_t(const AttnParams& p, hipStream_t s) {
   const int nqb = (p.Lq + p.q_per_block - 1) / p.q_per_block;
   const long blocks = static_cast<long>(p.B) * p.Hkv * nqb;
   if (blocks > 0x7fffffffL || p.splits > 65535) return hipErrorInvalidValue;
-  dim3 grid(static_cast<unsigned>(blocks), p.splits), block(kThreads);
+  dim3 grid(static_cast<unsigned>(blocks), p.splits);
+  const bool ext = needs_ext(p);
   if (p.d == 128) {
-    switch (p.mask_kind) {
-      case MI_ATTN_MASK_NONE: hipLaunchKernelGGL((prefill_kernel<T, 128, 64, 0>), grid, block, 0, s, p); break;
-      case MI_ATTN_MASK_CAUSAL: hipLaunchKernelGGL((prefill_kernel<T, 128, 64, 1>), grid, block, 0, s, p); break;
-      case MI_ATTN_MASK_WINDOW: hipLaunchKernelGGL((prefill_kernel<T, 128, 64, 2>), grid, block, 0, s, p); break;
-      case MI_ATTN_MASK_DENSE: hipLaunchKernelGGL((prefill_kernel<T, 128, 64, 3>), grid, block, 0, s, p); break;
-      default:
-        if (p.list_idx != nullptr) hipLaunchKernelGGL((prefill_kernel<T, 128, 64, 4, true>), grid, block, 0, s, p);
-        else hipLaunchKernelGGL((prefill_kernel<T, 128, 64, 4>), grid, block, 0, s, p);
-        break;
-    }
+    if (ext) launch_prefill_d<T, 128, true>(grid, p, s);
+    else launch_prefill_d<T, 128, false>(grid, p, s);
   } else {
-    switch (p.mask_kind) {
-      case MI_ATTN_MASK_NONE: hipLaunchKernelGGL((prefill_kernel<T, 64, 64, 0>), grid, block, 0, s, p); break;
-      case MI_ATTN_MASK_CAUSAL: hipLaunchKernelGGL((prefill_kernel<T, 64, 64, 1>), grid, block, 0, s, p); break;
-      case MI_ATTN_MASK_WINDOW: hipLaunchKernelGGL((prefill_kernel<T, 64, 64, 2>), grid, block, 0, s, p); break;
-      case MI_ATTN_MASK_DENSE: hipLaunchKernelGGL((prefill_kernel<T, 64, 64, 3>), grid, block, 0, s, p); break;
-      default:
-        if (p.list_idx != nullptr) hipLaunchKernelGGL((prefill_kernel<T, 64, 64, 4, true>), grid, block, 0, s, p);
-        else hipLaunchKernelGGL((prefill_kernel<T, 64, 64, 4>), grid, block, 0, s, p);
-        break;
-    }
+    if (ext) launch_prefill_d<T, 64, true>(grid, p, s);
+    else launch_prefill_d<T, 64, false>(grid, p, s);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits <= 1) return e;

@@ -31,20 +31,25 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void row_kernel(AttnParams p
   const int d = p.d;
   const int pos = p.Lk - p.Lq + i;  // bottom-right aligned absolute position
 
-  const T* qrow = static_cast<const T*>(p.q) + row * d;
-  const long kv_off = (static_cast<long>(b) * p.Hkv + g) * p.Lk * d;
-  const T* kb = static_cast<const T*>(p.k) + kv_off;
-  const T* vb = static_cast<const T*>(p.v) + kv_off;
+  // strided rows (element strides {batch, head, row}; the head dimension is contiguous)
+  const T* qrow = static_cast<const T*>(p.q) + b * p.qs[0] + h * p.qs[1] + i * p.qs[2];
+  const T* kb = static_cast<const T*>(p.k) + b * p.ks[0] + g * p.ks[1];
+  const T* vb = static_cast<const T*>(p.v) + b * p.vs[0] + g * p.vs[1];
+  const long ksr = p.ks[2], vsr = p.vs[2];
+  // dense mask row of (b, h, i) (also added to the kept keys of the top-k kind)
+  const float* mrow = p.mask != nullptr ? p.mask + b * p.ms[0] + h * p.ms[1] + i * p.ms[2] : nullptr;
+  const float slope = p.alibi != nullptr ? p.alibi[h] : 0.f;
 
   for (int c = lane; c < d; c += kWave) sq[wave][c] = to_f32(qrow[c]);
   __builtin_amdgcn_wave_barrier();
 
   int lo, hi;
-  key_range(p.mask_kind, p.window_left, p.Lk, pos, pos, &lo, &hi);
+  key_range(range_kind(p), p.window_left, p.Lk, pos, pos, &lo, &hi);
   if (p.no_skip) { lo = 0; hi = p.Lk; }
 
   const long bg = static_cast<long>(b) * p.Hkv + g;
-  const int32_t tau = (p.mask_kind == MI_ATTN_MASK_TOPK) ? p.tau[bg * p.Lq + i] : 0;
+  // clamped below Lk: ranks of real keys are 0 .. Lk-1
+  const int32_t tau = (p.mask_kind == MI_ATTN_MASK_TOPK) ? min(p.tau[bg * p.Lq + i], p.Lk - 1) : 0;
 
   float m = kNegInf, l = 0.f;
   float acc[kMaxD / kWave];
@@ -55,10 +60,13 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void row_kernel(AttnParams p
     const int j = j0 + lane;
     float s = kNegInf;
     if (j < hi) {
-      const T* kr = kb + static_cast<long>(j) * d;
+      const T* kr = kb + static_cast<long>(j) * ksr;
       float dot = 0.f;
       for (int c = 0; c < d; ++c) dot = fmaf(sq[wave][c], to_f32(kr[c]), dot);
       s = dot * p.scale;
+      // score modifiers: softcap of the scaled score, then the ALiBi distance bias
+      if (p.softcap > 0.f) s = p.softcap * tanhf(s / p.softcap);
+      if (slope != 0.f) s -= slope * static_cast<float>(abs(pos - j));
       switch (p.mask_kind) {
         case MI_ATTN_MASK_CAUSAL:
           if (j > pos) s = kNegInf;
@@ -67,11 +75,11 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void row_kernel(AttnParams p
           if (j > pos || j < pos - p.window_left) s = kNegInf;
           break;
         case MI_ATTN_MASK_DENSE:
-          s += p.mask[static_cast<long>(i) * p.Lk + j];
+          s += mrow[j * p.ms[3]];
           break;
         case MI_ATTN_MASK_TOPK:
-          if (j <= pos && p.rank[bg * p.Lk + j] <= tau)
-            s += p.zero_hold[bg * p.Lk + j];
+          if ((!p.topk_causal || j <= pos) && p.rank[bg * p.Lk + j] <= tau)
+            s += p.zero_hold[bg * p.Lk + j] + (mrow != nullptr ? mrow[j * p.ms[3]] : 0.f);
           else
             s = kNegInf;
           break;
@@ -96,14 +104,14 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void row_kernel(AttnParams p
       if (c < d) {
         float a = acc[t] * alpha;
         for (int jj = 0; jj < nk; ++jj)
-          a = fmaf(sp[wave][jj], to_f32(vb[static_cast<long>(j0 + jj) * d + c]), a);
+          a = fmaf(sp[wave][jj], to_f32(vb[static_cast<long>(j0 + jj) * vsr + c]), a);
         acc[t] = a;
       }
     }
     __builtin_amdgcn_wave_barrier();
   }
 
-  T* orow = static_cast<T*>(p.out) + row * d;
+  T* orow = static_cast<T*>(p.out) + b * p.os[0] + h * p.os[1] + i * p.os[2];
   const bool dead = (l == 0.f);
   const float inv = dead ? 0.f : 1.f / l;
 #pragma unroll

@@ -370,8 +370,8 @@ constexpr int kListWaves = kListThreads / kWave;
 constexpr int kListSub = 16;  // 256-key sub-passes per pass (4096 keys per pass)
 __global__ __launch_bounds__(kListThreads) void topk_list_kernel(const int32_t* rank, const int32_t* tau,
                                                                    const float* zh, int Lq, int Lk, int q_per_block,
-                                                                   int nqb, int cap, int32_t* lidx, int32_t* lrank,
-                                                                   float* lzh, int32_t* lcount) {
+                                                                   int nqb, int cap, int causal, int32_t* lidx,
+                                                                   int32_t* lrank, float* lzh, int32_t* lcount) {
   __shared__ int sub_cnt[kListSub][kListWaves];
   const int qb = blockIdx.x;
   const int bh = blockIdx.y;
@@ -380,7 +380,8 @@ __global__ __launch_bounds__(kListThreads) void topk_list_kernel(const int32_t* 
   const int lane = tid % kWave;
   const int i_first = qb * q_per_block;
   const int i_last = min(Lq, i_first + q_per_block) - 1;
-  const int n = Lk - Lq + i_last + 1;  // keys 0 .. p of the last row (may be <= 0)
+  // keys 0 .. p of the last row (may be <= 0), or every key when rows may keep any
+  const int n = causal ? Lk - Lq + i_last + 1 : Lk;
   const int32_t tf = tau[static_cast<long>(bh) * Lq + i_first];
   const int32_t* rk = rank + static_cast<long>(bh) * Lk;
   const float* z = zh + static_cast<long>(bh) * Lk;
@@ -439,25 +440,34 @@ __global__ __launch_bounds__(kListThreads) void topk_list_kernel(const int32_t* 
   if (tid == 0) lcount[static_cast<long>(bh) * nqb + qb] = cnt;
 }
 
-// One wavefront per (query block, key tile): flag = 1 iff some entry is above -inf.
-__global__ __launch_bounds__(256) void mask_summary_kernel(const float* mask, int Lq, int Lk,
-                                                             int q_per_block, int block_n, int ntiles,
+// One wavefront per flag (batch, KV head, query block, key tile) of a dense mask that may
+// differ per batch and head (see AttnParams::flag_b): 1 iff some entry is above -inf for
+// some row of the block and some query head of the KV head. A mask shared over a
+// dimension has one flag row for it.
+__global__ __launch_bounds__(256) void mask_summary_kernel(AttnParams p, int block_n, int nqb, int ntiles,
                                                              long nflags, uint8_t* flags) {
   const long f = static_cast<long>(blockIdx.x) * 4 + threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   if (f >= nflags) return;
-  const int qb = static_cast<int>(f / ntiles);
   const int t = static_cast<int>(f % ntiles);
-  const int i0 = qb * q_per_block;
-  const int i1 = (i0 + q_per_block) < Lq ? (i0 + q_per_block) : Lq;
+  const int qb = static_cast<int>((f / ntiles) % nqb);
+  const int fg = static_cast<int>((f / (static_cast<long>(ntiles) * nqb)) % p.flag_g);
+  const int fb = static_cast<int>(f / (static_cast<long>(ntiles) * nqb * p.flag_g));
+  const int i0 = qb * p.q_per_block;
+  const int i1 = (i0 + p.q_per_block) < p.Lq ? (i0 + p.q_per_block) : p.Lq;
   const int j0 = t * block_n;
-  const int j1 = (j0 + block_n) < Lk ? (j0 + block_n) : Lk;
+  const int j1 = (j0 + block_n) < p.Lk ? (j0 + block_n) : p.Lk;
   const int w = j1 - j0;
+  const int nh = p.flag_g > 1 ? p.G : 1;  // query heads of the KV head (one when shared)
+  const long nrow = static_cast<long>(i1 - i0) * nh;
+  const float* mb = p.mask + fb * p.ms[0] + static_cast<long>(fg) * p.G * p.ms[1];
   bool live = false;
-  for (long e = lane; e < static_cast<long>(i1 - i0) * w; e += kWave) {
-    const int i = i0 + static_cast<int>(e / w);
+  for (long e = lane; e < nrow * w; e += kWave) {
+    const long r = e / w;
     const int j = j0 + static_cast<int>(e % w);
-    live |= mask[static_cast<long>(i) * Lk + j] > kNegInf;
+    const int i = i0 + static_cast<int>(r / nh);
+    const int hh = static_cast<int>(r % nh);
+    live |= mb[hh * p.ms[1] + i * p.ms[2] + j * p.ms[3]] > kNegInf;
   }
   const bool any = __any(live);
   if (lane == 0) flags[f] = any ? 1 : 0;
@@ -521,22 +531,22 @@ hipError_t launch_topk(const float* zh, int BH, int Lq, int Lk, int keep_k, int 
 }
 
 hipError_t launch_topk_lists(const int32_t* rank, const int32_t* tau, const float* zh, int BH, int Lq, int Lk,
-                             int q_per_block, int cap, int32_t* list_idx, int32_t* list_rank, float* list_zh,
-                             int32_t* list_count, hipStream_t s) {
+                             int q_per_block, int cap, int causal, int32_t* list_idx, int32_t* list_rank,
+                             float* list_zh, int32_t* list_count, hipStream_t s) {
   const int nqb = (Lq + q_per_block - 1) / q_per_block;
   if (cap % 64 != 0 || BH > 65535) return hipErrorInvalidValue;
   hipLaunchKernelGGL(topk_list_kernel, dim3(nqb, BH), dim3(kListThreads), 0, s, rank, tau, zh, Lq, Lk, q_per_block,
-                     nqb, cap, list_idx, list_rank, list_zh, list_count);
+                     nqb, cap, causal, list_idx, list_rank, list_zh, list_count);
   return hipGetLastError();
 }
 
-hipError_t launch_mask_summary(const float* mask, int Lq, int Lk, int q_per_block, int block_n, uint8_t* flags,
-                               hipStream_t s) {
-  const int nqb = (Lq + q_per_block - 1) / q_per_block;
-  const int nt = (Lk + block_n - 1) / block_n;
-  const long nflags = static_cast<long>(nqb) * nt;
-  hipLaunchKernelGGL(mask_summary_kernel, dim3(static_cast<unsigned>((nflags + 3) / 4)), dim3(256), 0, s, mask, Lq,
-                     Lk, q_per_block, block_n, nt, nflags, flags);
+hipError_t launch_mask_summary(const AttnParams& p, int block_n, uint8_t* flags, hipStream_t s) {
+  const int nqb = (p.Lq + p.q_per_block - 1) / p.q_per_block;
+  const int nt = (p.Lk + block_n - 1) / block_n;
+  const long nflags = static_cast<long>(p.flag_b) * p.flag_g * nqb * nt;
+  if ((nflags + 3) / 4 > 0x7fffffffL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mask_summary_kernel, dim3(static_cast<unsigned>((nflags + 3) / 4)), dim3(256), 0, s, p, block_n,
+                     nqb, nt, nflags, flags);
   return hipGetLastError();
 }
 

@@ -196,15 +196,69 @@ __device__ __forceinline__ const T* pick(bool c, const T* a, const T* b) {
 // encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their maximum).
 constexpr int vmcnt_imm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
 
+// Per-lane state of the score modifiers and the dense mask (built once per kernel).
+// The MFMA gives s = q.k (the sign of the scale folded into Q); the logit in log2 units
+// is s * cexp with cexp = |scale| * log2(e).
+struct Mods {
+  float cexp;     // |scale| * log2(e)
+  float scale;    // |scale|
+  float cap;      // softcap (0: off)
+  float slope2;   // ALiBi slope of the lane's query head times log2(e) (0: off)
+  int pos;        // the lane's absolute query position
+  const float* mrow;  // dense mask row of the lane's (b, h, i), or nullptr
+  long msj;           // its key stride
+};
+
+// (EXT: the modifier fields; the dense mask row is used by the dense kind, and by EXT
+// instances of the top-k kind)
+template <bool EXT>
+__device__ __forceinline__ Mods make_mods(const AttnParams& p, float cexp, int b, int h_row, int i_row, int pos,
+                                          bool with_mask) {
+  Mods m{};
+  m.cexp = cexp;
+  if constexpr (EXT) {
+    m.scale = fabsf(p.scale);
+    m.cap = p.softcap;
+    m.slope2 = p.alibi != nullptr ? p.alibi[h_row] * kLog2e : 0.f;
+    m.pos = pos;
+  }
+  m.mrow = with_mask && p.mask != nullptr ? p.mask + b * p.ms[0] + h_row * p.ms[1] + i_row * p.ms[2] : nullptr;
+  m.msj = p.ms[3];
+  return m;
+}
+
+// Whether a call needs the EXT kernel instances.
+__host__ __device__ inline bool needs_ext(const AttnParams& p) {
+  return has_mods(p) || (p.mask_kind == MI_ATTN_MASK_TOPK && p.mask != nullptr);
+}
+
+// Logit of key j in log2 units from the raw score s. EXT instances (calls with a score
+// modifier or a top-k mask combined with a dense one) apply softcap (cap * tanh(t / cap)
+// of the scaled score t), then the ALiBi bias -slope * |p_i - j|; tanh(x) = 1 - 2 /
+// (e^{2x} + 1), which saturates to +-1 without overflow. The others only scale.
+template <bool EXT>
+__device__ __forceinline__ float modified_logit(float s, int j, const Mods& m) {
+  float x = s * m.cexp;
+  if constexpr (!EXT) return x;
+  if (m.cap > 0.f) {
+    const float t = s * m.scale / m.cap;
+    const float e = __builtin_amdgcn_exp2f(t * (2.f * kLog2e));
+    x = m.cap * (1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f)) * kLog2e;
+  }
+  if (m.slope2 != 0.f) x -= m.slope2 * static_cast<float>(abs(m.pos - j));
+  return x;
+}
+
 // Per-element mask of one tile's S^T registers (32x32 MFMA layout: lane holds query column
 // l % 32 and, per 32-key block kb, keys kb*32 + 8*(i/4) + 4*hf + i%4 in register i).
-// Visible logits move to the log2 domain (s * cexp + bias * log2 e); hidden ones become
-// -inf. `xr`/`xz` are the tile's top-k ranks and zero_hold values (index = key - j0).
-// Lk is the key count of the (batch or sequence) the tile belongs to.
-template <int MK, int NKB>
+// Visible logits move to the log2 domain (modified_logit, plus the dense mask or the top-k
+// bias, times log2 e); hidden ones become -inf. `xr`/`xz` are the tile's top-k ranks and
+// zero_hold values (index = key - j0); a dense mask given with the top-k kind is added to
+// the kept keys. Lk is the key count of the (batch or sequence) the tile belongs to; tau_row
+// is clamped to Lk - 1 by the caller, so keys past Lk (rank INT32_MAX) are never kept.
+template <int MK, int NKB, bool EXT>
 __device__ __forceinline__ void mask_tile(f32x16_t* sacc, const AttnParams& p, int Lk, int j0, int hf, int pos,
-                                          int i_row, int32_t tau_row, float cexp, const int32_t* xr,
-                                          const float* xz) {
+                                          int32_t tau_row, const Mods& md, const int32_t* xr, const float* xz) {
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -213,19 +267,21 @@ __device__ __forceinline__ void mask_tile(f32x16_t* sacc, const AttnParams& p, i
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int j = j0 + kk + e;
-        float s = sacc[kb][r4 * 4 + e] * cexp;
+        float s = modified_logit<EXT>(sacc[kb][r4 * 4 + e], j, md);
         bool vis = j < Lk;
         if constexpr (MK == MI_ATTN_MASK_CAUSAL) vis = vis && j <= pos;
         if constexpr (MK == MI_ATTN_MASK_WINDOW) vis = vis && j <= pos && j >= pos - p.window_left;
         // side reads use key j0 (always < Lk in a visited tile) in place of keys past Lk
         if constexpr (MK == MI_ATTN_MASK_DENSE) {
-          const float mv = p.mask[static_cast<long>(i_row) * p.Lk + (vis ? j : j0)];
+          const float mv = md.mrow[(vis ? j : j0) * md.msj];
           s = fmaf(vis ? mv : 0.f, kLog2e, s);
         }
         if constexpr (MK == MI_ATTN_MASK_TOPK) {
           const int idx = vis ? kk + e : 0;
-          vis = vis && j <= pos && xr[idx] <= tau_row;
-          s = fmaf(xz[idx], kLog2e, s);
+          vis = vis && (!p.topk_causal || j <= pos) && xr[idx] <= tau_row;
+          float bias = xz[idx];
+          if (EXT && md.mrow != nullptr) bias += md.mrow[(vis ? j : j0) * md.msj];
+          s = fmaf(bias, kLog2e, s);
         }
         sacc[kb][r4 * 4 + e] = vis ? s : kNegInf;
       }
@@ -235,12 +291,13 @@ __device__ __forceinline__ void mask_tile(f32x16_t* sacc, const AttnParams& p, i
 
 // Top-k mask of one tile whose side data sits in LDS, padded to the full tile:
 // xr[k] = rank of key j0 + k (INT32_MAX past Lk) and xzl[k] = its zero_hold times log2(e)
-// (0 past Lk). A key stays when its rank is at most the row's threshold; kDiag tiles
-// (reaching past the block's first query position) also hide keys after the row's own
-// position, which covers every key past Lk. Results are in the log2 domain.
-template <int NKB, bool kDiag>
+// (0 past Lk). A key stays when its rank is at most the row's threshold (clamped below
+// Lk, so keys past Lk never stay); kDiag tiles (reaching past the block's first query
+// position, causal selection only) also hide keys after the row's own position. Results
+// are in the log2 domain.
+template <int NKB, bool kDiag, bool EXT>
 __device__ __forceinline__ void mask_tile_topk(f32x16_t* sacc, int j0, int hf, int pos, int32_t tau_row,
-                                               float cexp, const int32_t* xr, const float* xzl) {
+                                               const Mods& md, const int32_t* xr, const float* xzl) {
   const int lim = pos - j0;  // keys kk <= lim are at or before the row's position
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
@@ -255,7 +312,9 @@ __device__ __forceinline__ void mask_tile_topk(f32x16_t* sacc, int j0, int hf, i
       for (int e = 0; e < 4; ++e) {
         bool vis = rks[e] <= tau_row;
         if constexpr (kDiag) vis = vis && kk + e <= lim;
-        const float s = fmaf(sacc[kb][r4 * 4 + e], cexp, zs[e]);
+        float bias = zs[e];
+        if (EXT && md.mrow != nullptr) bias = fmaf(md.mrow[(vis ? j0 + kk + e : j0) * md.msj], kLog2e, bias);
+        const float s = modified_logit<EXT>(sacc[kb][r4 * 4 + e], j0 + kk + e, md) + bias;
         sacc[kb][r4 * 4 + e] = vis ? s : kNegInf;
       }
     }
@@ -263,10 +322,12 @@ __device__ __forceinline__ void mask_tile_topk(f32x16_t* sacc, int j0, int hf, i
 }
 
 // The same for a gathered tile: key k of the tile is key xi[k] of the cache (ascending;
-// padding entries carry key Lk, rank INT32_MAX and value 0, so kDiag tiles hide them).
-template <int NKB, bool kDiag>
-__device__ __forceinline__ void mask_tile_topk_list(f32x16_t* sacc, int hf, int pos, int32_t tau_row, float cexp,
-                                                    const int32_t* xr, const float* xzl, const int32_t* xi) {
+// padding entries carry key Lk, rank INT32_MAX and value 0, and the clamped threshold
+// hides them).
+template <int NKB, bool kDiag, bool EXT>
+__device__ __forceinline__ void mask_tile_topk_list(f32x16_t* sacc, int hf, int pos, int32_t tau_row,
+                                                    const Mods& md, const int32_t* xr, const float* xzl,
+                                                    const int32_t* xi) {
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -282,19 +343,22 @@ __device__ __forceinline__ void mask_tile_topk_list(f32x16_t* sacc, int hf, int 
       for (int e = 0; e < 4; ++e) {
         bool vis = rks[e] <= tau_row;
         if constexpr (kDiag) vis = vis && js[e] <= pos;
-        const float s = fmaf(sacc[kb][r4 * 4 + e], cexp, zs[e]);
+        float bias = zs[e];
+        if (EXT && md.mrow != nullptr) bias = fmaf(md.mrow[(vis ? js[e] : 0) * md.msj], kLog2e, bias);
+        const float s = modified_logit<EXT>(sacc[kb][r4 * 4 + e], js[e], md) + bias;
         sacc[kb][r4 * 4 + e] = vis ? s : kNegInf;
       }
     }
   }
 }
 
-// Whether a tile [j0, j0 + BN) needs per-element masking for a block whose query rows sit
-// at positions P0..P1: tiles every row sees entirely (and inside Lk) skip it.
-template <int MK, int BN>
+// Whether a tile [j0, j0 + BN) needs per-element work for a block whose query rows sit at
+// positions P0..P1: tiles every row sees entirely (and inside Lk) skip it, unless a score
+// modifier applies to every key.
+template <int MK, int BN, bool EXT>
 __device__ __forceinline__ bool tile_needs_mask(const AttnParams& p, int Lk, int j0, int P0, int P1) {
   const int j_end = j0 + BN - 1;
-  bool need = p.no_skip || j_end >= Lk || MK == MI_ATTN_MASK_DENSE || MK == MI_ATTN_MASK_TOPK;
+  bool need = p.no_skip || j_end >= Lk || MK == MI_ATTN_MASK_DENSE || MK == MI_ATTN_MASK_TOPK || EXT;
   if constexpr (MK == MI_ATTN_MASK_CAUSAL || MK == MI_ATTN_MASK_WINDOW) need = need || j_end > P0;
   if constexpr (MK == MI_ATTN_MASK_WINDOW) need = need || j0 < P1 - p.window_left;
   return need;

@@ -339,3 +339,49 @@ def config(name: str) -> Problem:
 
 CONFIG_NAMES = ["c1", "c2", "c2b", "c2c", "c2w", "c3p", "c3d",
                 "c4_d64_bf16", "c4_d64_fp16", "c4_d128_bf16", "c4_d128_fp16", "c5"]
+
+
+# ------------------------------------------------------------ attn_fwd_ex workloads
+def alibi_slopes(H: int) -> np.ndarray:
+    """fp32 [H]: the geometric slopes 2^(-8 (h+1) / H), the usual ALiBi choice (an input
+    here: the pages name the slopes argument without giving values)."""
+    return (2.0 ** (-8.0 * (np.arange(H) + 1) / H)).astype(np.float32)
+
+
+def per_head_window_mask(B: int, H: int, Lq: int, Lk: int, first_pos: int, base_window: int) -> np.ndarray:
+    """fp32 [1, H, Lq, Lk]: head h sees keys pos-(base_window - h)..pos (a window that
+    narrows with the head), the same for every batch."""
+    m = np.stack([window_dense_mask(Lq, Lk, first_pos, max(base_window - h, 0)) for h in range(H)])
+    return m[None]
+
+
+EX_NAMES = ["c3p_alibi_softcap", "c3p_kv_blhd", "c3d_kv_blhd", "c5_noncausal", "c2_per_head_mask"]
+
+
+def ex_config(name: str):
+    """Workloads of attn_fwd_ex: one of the five configurations with a general layout, a
+    score modifier, a top-k variant or a per-head mask. Returns (problem, options) with
+    options: layout ("bhld" or "blhd" for q, k, v and out), alibi (fp32 [Hq] or None),
+    softcap (float), topk_causal (bool), mask (fp32 array broadcasting to [B,Hq,Lq,Lk]
+    or None)."""
+    opts = {"layout": "bhld", "alibi": None, "softcap": 0.0, "topk_causal": True, "mask": None}
+    if name == "c3p_alibi_softcap":
+        p = config("c3p")
+        opts.update(alibi=alibi_slopes(p.Hq), softcap=30.0)
+    elif name == "c3p_kv_blhd":
+        p = config("c3p")
+        opts.update(layout="blhd")
+    elif name == "c3d_kv_blhd":
+        p = config("c3d")
+        opts.update(layout="blhd")
+    elif name == "c5_noncausal":
+        p = config("c5")
+        opts.update(topk_causal=False)
+    elif name == "c2_per_head_mask":
+        p = config("c2")
+        # the rows sit at positions 560..575 of the 700-key cache, as in c2
+        opts.update(mask=per_head_window_mask(p.B, p.Hq, p.Lq, p.Lk, 560, 60))
+    else:
+        raise KeyError(name)
+    p.name = f"{p.name} + {name.split('_', 1)[1].replace('_', ' ')}"
+    return p, opts

@@ -136,6 +136,66 @@ def test_attn_fwd_rejects_before_any_gpu_work(lib, kw):
     assert lib.attn_last_error().decode() != ""
 
 
+def ex_args(**kw):
+    """attn_fwd_ex arguments for a contiguous bf16 [1,2,8,64] call with fake pointers (never
+    dereferenced: validation fails first), then the overrides in kw."""
+    a = mfa.AttnFwdArgs()
+    a.q = a.k = a.v = a.out = 0x1000
+    B, H, L, d = 1, 2, 8, 64
+    for arr in (a.q_stride, a.k_stride, a.v_stride, a.out_stride):
+        arr[0], arr[1], arr[2] = H * L * d, L * d, d
+    a.B, a.Hq, a.Hkv, a.Lq, a.Lk, a.d = B, H, H, L, L, d
+    a.scale, a.mask_kind, a.dtype, a.topk_causal = 0.125, 1, 2, 1
+    a.mask_stride[2], a.mask_stride[3] = L, 1
+    for name, val in kw.items():
+        if isinstance(val, tuple):
+            arr = getattr(a, name)
+            for i, x in enumerate(val):
+                arr[i] = x
+        else:
+            setattr(a, name, val)
+    return a
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k_stride=(1024, 512, -64)), -1),         # negative stride
+    (dict(out_stride=(1024, 0, 64)), -1),          # two heads written to one place
+    (dict(q=0x1008), -1),                          # not 16-byte aligned
+    (dict(v_stride=(1024, 512, 68)), -1),          # rows not 16-byte aligned
+    (dict(softcap=-1.0), -1),
+    (dict(softcap=float("inf")), -1),
+    (dict(mask_kind=4, zero_hold=0x2000, keep_k=4, topk_causal=2), -1),
+    (dict(mask_kind=3), -1),                       # dense kind without a mask
+    (dict(mask_kind=3, mask=0x2000, mask_stride=(0, 0, -8, 1)), -1),
+    (dict(k_stride=(1 << 40, 1 << 32, 1 << 28)), -2),  # K rows too far apart for 32-bit offsets
+])
+def test_attn_fwd_ex_rejects_before_any_gpu_work(lib, kw, code):
+    assert lib.attn_fwd_ex(ctypes.byref(ex_args(**kw)), None) == code
+    assert lib.attn_last_error().decode() != ""
+
+
+def test_attn_fwd_ex_rejects_a_null_argument_block(lib):
+    assert lib.attn_fwd_ex(None, None) == -1
+
+
+def test_args_struct_matches_the_header_layout():
+    """The ctypes mirror of attn_fwd_args_t has the size and field offsets a C compiler
+    gives the header's struct."""
+    src = ("#include <stddef.h>\n#include <stdio.h>\n#include \"mi_attn.h\"\n"
+           "int main(void){printf(\"%zu %zu %zu %zu %zu\\n\", sizeof(attn_fwd_args_t),"
+           " offsetof(attn_fwd_args_t, B), offsetof(attn_fwd_args_t, mask),"
+           " offsetof(attn_fwd_args_t, alibi_slopes), offsetof(attn_fwd_args_t, dtype));return 0;}")
+    import tempfile
+    with tempfile.TemporaryDirectory() as tmp:
+        c = os.path.join(tmp, "s.c")
+        open(c, "w").write(src)
+        exe = os.path.join(tmp, "s")
+        subprocess.run(["gcc", "-I", os.path.dirname(HEADER), c, "-o", exe], check=True)
+        got = [int(x) for x in subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()]
+    A = mfa.AttnFwdArgs
+    assert got == [ctypes.sizeof(A), A.B.offset, A.mask.offset, A.alibi_slopes.offset, A.dtype.offset]
+
+
 def test_topk_rejects_invalid_arguments(lib):
     fake = ctypes.c_void_p(0x1000)
     f = lib.dynamic_mask_topk
