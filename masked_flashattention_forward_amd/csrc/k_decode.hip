@@ -242,7 +242,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(AttnParams p) {
       sacc[0] = acc;
     }
     float cm = cexp;
-    if (tile_needs_mask<MK, kDecBN, EXT>(p, Lk, j0, P0, P1)) {
+    if (tile_needs_mask<MK, kDecBN>(p, Lk, j0, P0, P1)) {
       const int32_t* xr = nullptr;
       const float* xz = nullptr;
       if constexpr (MK == MI_ATTN_MASK_TOPK) {
@@ -250,6 +250,9 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(AttnParams p) {
         xz = p.zero_hold + bgk + j0;
       }
       mask_tile<MK, 1, EXT>(sacc, p, Lk, j0, hf, pos, tau_row, md, xr, xz);
+      cm = 1.f;
+    } else if constexpr (EXT) {
+      mods_tile<1>(sacc, j0, hf, md);  // a tile every row sees: the score modifiers alone
       cm = 1.f;
     }
 

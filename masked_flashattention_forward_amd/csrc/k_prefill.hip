@@ -489,8 +489,11 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN, EXT>)) void pr
       else
         mask_tile_topk<NKB, false, EXT>(sacc, j0, hf, pos, tau_row, md, xr, xzl);
       cm = 1.f;
-    } else if (tile_needs_mask<MK, BN, EXT>(p, Lk, j0, P0, P1)) {
+    } else if (tile_needs_mask<MK, BN>(p, Lk, j0, P0, P1)) {
       mask_tile<MK, NKB, EXT>(sacc, p, Lk, j0, hf, pos, tau_row, md, nullptr, nullptr);
+      cm = 1.f;
+    } else if constexpr (EXT) {
+      mods_tile<NKB>(sacc, j0, hf, md);  // a tile every row sees: the score modifiers alone
       cm = 1.f;
     }
 

@@ -201,8 +201,9 @@ constexpr int vmcnt_imm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4
 // is s * cexp with cexp = |scale| * log2(e).
 struct Mods {
   float cexp;     // |scale| * log2(e)
-  float scale;    // |scale|
   float cap;      // softcap (0: off)
+  float ct;       // softcap: 2 * |scale| / cap * log2(e), the exponent factor of tanh
+  float k1, k2;   // softcap: cap * log2(e) and -2 * cap * log2(e)
   float slope2;   // ALiBi slope of the lane's query head times log2(e) (0: off)
   int pos;        // the lane's absolute query position
   const float* mrow;  // dense mask row of the lane's (b, h, i), or nullptr
@@ -217,8 +218,12 @@ __device__ __forceinline__ Mods make_mods(const AttnParams& p, float cexp, int b
   Mods m{};
   m.cexp = cexp;
   if constexpr (EXT) {
-    m.scale = fabsf(p.scale);
     m.cap = p.softcap;
+    if (m.cap > 0.f) {
+      m.ct = 2.f * fabsf(p.scale) / m.cap * kLog2e;
+      m.k1 = m.cap * kLog2e;
+      m.k2 = -2.f * m.cap * kLog2e;
+    }
     m.slope2 = p.alibi != nullptr ? p.alibi[h_row] * kLog2e : 0.f;
     m.pos = pos;
   }
@@ -232,21 +237,38 @@ __host__ __device__ inline bool needs_ext(const AttnParams& p) {
   return has_mods(p) || (p.mask_kind == MI_ATTN_MASK_TOPK && p.mask != nullptr);
 }
 
-// Logit of key j in log2 units from the raw score s. EXT instances (calls with a score
-// modifier or a top-k mask combined with a dense one) apply softcap (cap * tanh(t / cap)
-// of the scaled score t), then the ALiBi bias -slope * |p_i - j|; tanh(x) = 1 - 2 /
-// (e^{2x} + 1), which saturates to +-1 without overflow. The others only scale.
+// Logit in log2 units from the raw score s of a key at signed distance dist = j - p_i
+// (a float: exact below 2^24). EXT instances apply softcap, cap * tanh(t / cap) of the
+// scaled score t with tanh(x) = 1 - 2 / (e^{2x} + 1) (saturates to +-1, no overflow),
+// then the ALiBi bias -slope * |dist| (the abs is an operand modifier); the others
+// only scale.
 template <bool EXT>
-__device__ __forceinline__ float modified_logit(float s, int j, const Mods& m) {
-  float x = s * m.cexp;
-  if constexpr (!EXT) return x;
-  if (m.cap > 0.f) {
-    const float t = s * m.scale / m.cap;
-    const float e = __builtin_amdgcn_exp2f(t * (2.f * kLog2e));
-    x = m.cap * (1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f)) * kLog2e;
+__device__ __forceinline__ float modified_logit(float s, float dist, const Mods& m) {
+  if constexpr (!EXT) {
+    return s * m.cexp;
+  } else {
+    float x;
+    if (m.cap > 0.f) {
+      const float r = __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(s * m.ct) + 1.f);
+      x = fmaf(m.k2, r, m.k1);
+    } else {
+      x = s * m.cexp;
+    }
+    if (m.slope2 != 0.f) x = fmaf(-m.slope2, fabsf(dist), x);
+    return x;
   }
-  if (m.slope2 != 0.f) x -= m.slope2 * static_cast<float>(abs(m.pos - j));
-  return x;
+}
+
+// EXT tile that needs no mask (every key visible to every row of the block): the score
+// modifiers only, in the log2 domain.
+template <int NKB>
+__device__ __forceinline__ void mods_tile(f32x16_t* sacc, int j0, int hf, const Mods& md) {
+  const float base = static_cast<float>(j0 + hf * 4 - md.pos);  // distance of the lane's first key
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      sacc[kb][i] = modified_logit<true>(sacc[kb][i], base + static_cast<float>(kb * 32 + (i / 4) * 8 + i % 4), md);
 }
 
 // Per-element mask of one tile's S^T registers (32x32 MFMA layout: lane holds query column
@@ -259,6 +281,7 @@ __device__ __forceinline__ float modified_logit(float s, int j, const Mods& m) {
 template <int MK, int NKB, bool EXT>
 __device__ __forceinline__ void mask_tile(f32x16_t* sacc, const AttnParams& p, int Lk, int j0, int hf, int pos,
                                           int32_t tau_row, const Mods& md, const int32_t* xr, const float* xz) {
+  const float base = EXT ? static_cast<float>(j0 + hf * 4 - pos) : 0.f;  // distance of the lane's first key
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -267,7 +290,7 @@ __device__ __forceinline__ void mask_tile(f32x16_t* sacc, const AttnParams& p, i
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int j = j0 + kk + e;
-        float s = modified_logit<EXT>(sacc[kb][r4 * 4 + e], j, md);
+        float s = modified_logit<EXT>(sacc[kb][r4 * 4 + e], base + static_cast<float>(kk - hf * 4 + e), md);
         bool vis = j < Lk;
         if constexpr (MK == MI_ATTN_MASK_CAUSAL) vis = vis && j <= pos;
         if constexpr (MK == MI_ATTN_MASK_WINDOW) vis = vis && j <= pos && j >= pos - p.window_left;
@@ -314,7 +337,7 @@ __device__ __forceinline__ void mask_tile_topk(f32x16_t* sacc, int j0, int hf, i
         if constexpr (kDiag) vis = vis && kk + e <= lim;
         float bias = zs[e];
         if (EXT && md.mrow != nullptr) bias = fmaf(md.mrow[(vis ? j0 + kk + e : j0) * md.msj], kLog2e, bias);
-        const float s = modified_logit<EXT>(sacc[kb][r4 * 4 + e], j0 + kk + e, md) + bias;
+        const float s = modified_logit<EXT>(sacc[kb][r4 * 4 + e], static_cast<float>(j0 + kk + e - pos), md) + bias;
         sacc[kb][r4 * 4 + e] = vis ? s : kNegInf;
       }
     }
@@ -345,20 +368,20 @@ __device__ __forceinline__ void mask_tile_topk_list(f32x16_t* sacc, int hf, int 
         if constexpr (kDiag) vis = vis && js[e] <= pos;
         float bias = zs[e];
         if (EXT && md.mrow != nullptr) bias = fmaf(md.mrow[(vis ? js[e] : 0) * md.msj], kLog2e, bias);
-        const float s = modified_logit<EXT>(sacc[kb][r4 * 4 + e], js[e], md) + bias;
+        const float s = modified_logit<EXT>(sacc[kb][r4 * 4 + e], static_cast<float>(js[e] - pos), md) + bias;
         sacc[kb][r4 * 4 + e] = vis ? s : kNegInf;
       }
     }
   }
 }
 
-// Whether a tile [j0, j0 + BN) needs per-element work for a block whose query rows sit at
-// positions P0..P1: tiles every row sees entirely (and inside Lk) skip it, unless a score
-// modifier applies to every key.
-template <int MK, int BN, bool EXT>
+// Whether a tile [j0, j0 + BN) needs per-element masking for a block whose query rows sit
+// at positions P0..P1: tiles every row sees entirely (and inside Lk) skip it (EXT
+// instances then apply the score modifiers alone, mods_tile).
+template <int MK, int BN>
 __device__ __forceinline__ bool tile_needs_mask(const AttnParams& p, int Lk, int j0, int P0, int P1) {
   const int j_end = j0 + BN - 1;
-  bool need = p.no_skip || j_end >= Lk || MK == MI_ATTN_MASK_DENSE || MK == MI_ATTN_MASK_TOPK || EXT;
+  bool need = p.no_skip || j_end >= Lk || MK == MI_ATTN_MASK_DENSE || MK == MI_ATTN_MASK_TOPK;
   if constexpr (MK == MI_ATTN_MASK_CAUSAL || MK == MI_ATTN_MASK_WINDOW) need = need || j_end > P0;
   if constexpr (MK == MI_ATTN_MASK_WINDOW) need = need || j0 < P1 - p.window_left;
   return need;
