@@ -16,7 +16,8 @@ softmax, is kept here only to cross-check the first one.
 Parity status of each function is stated in its docstring; every function
 here is pinned by ``tests/test_oracle_pins.py`` (the varlen / paged-cache
 functions by ``tests/test_oracle_paged_pins.py``, the score modifiers, per-head
-masks and top-k variants of ``general.py`` by ``tests/test_oracle_general_pins.py``).
+masks and top-k variants of ``general.py`` by ``tests/test_oracle_general_pins.py``,
+the gradients of ``backward.py`` by ``tests/test_oracle_backward_pins.py``).
 """
 from .attention import (  # noqa: F401
     NEG_INF,
@@ -36,3 +37,4 @@ from .topk import (  # noqa: F401
 )
 from .paged import gather_sequence_kv, paged_attention_ref  # noqa: F401
 from .general import general_attention_ref, general_mask, general_scores  # noqa: F401
+from .backward import attention_backward_ref, attention_backward_rows_ref  # noqa: F401
