@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define MI_ATTN_ABI_VERSION 4
+#define MI_ATTN_ABI_VERSION 5
 
 /* element types of q, k, v, out */
 #define MI_ATTN_F32 0
@@ -239,6 +239,40 @@ typedef struct {
 } attn_fwd_args_t;
 
 int attn_fwd_ex(const attn_fwd_args_t* args, void* stream);
+
+/*
+ * attn_bwd: gradients of attn_fwd, as the InfiniTrain pull request #193 page pairs the
+ * FlashAttention forward with its backward ("main changes": forward and backward for
+ * FP16/BF16 with head dims 64 and 128; the autograd function keeps what the backward
+ * needs, "Framework and autograd"). With Z = scale * q k^T + M (M as in attn_fwd) and
+ * P = softmax(Z) by rows, recomputed from the forward's lse:
+ *     dv = P^T dout                      dP = dout v^T
+ *     dZ = P * (dP - rowsum(dout * out)) (the softmax Jacobian)
+ *     dq = scale * dZ k                  dk = scale * dZ^T q
+ * With GQA a KV head's dk and dv are the sums over the Hq / Hkv query heads that read it.
+ * No gradient flows into mask or zero_hold. A row whose keys are all hidden (lse = -inf)
+ * contributes nothing and gets dq = 0.
+ *
+ *   q, k, v, out, lse   the forward's inputs and results (layouts of attn_fwd; lse must
+ *                       be the one attn_fwd wrote for these inputs, not NULL).
+ *   dout                device, [B, Hq, Lq, d] `dtype`: the gradient of out.
+ *   dq, dk, dv          device, written (not accumulated), layouts of q, k and v. They
+ *                       must not overlap the inputs.
+ *   B .. keep_k, dtype  as in attn_fwd (the top-k kind selects causally, as attn_fwd).
+ *   stream              as in attn_fwd. Temporary device memory: rowsum(dout * out),
+ *                       4 bytes per query row, plus the top-k ranks for that kind.
+ *
+ *   fp16/bf16 only (fp32 returns MI_ATTN_EUNSUPPORTED), head dims 64 and 128, at most
+ *   128 query heads per KV head, Hq * Lq * d * 2 below 2^31 bytes. Products take fp16/bf16
+ *   operands (P and dZ are rounded to the input type before the second products) with
+ *   fp32 accumulation; dq, dk and dv are rounded to nearest-even in the input type.
+ *   Returns attn_fwd's codes.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv,
+             int B, int Hq, int Hkv, int Lq, int Lk, int d, float scale,
+             int mask_kind, int window_left, const float* mask, const float* zero_hold,
+             int keep_k, int dtype, void* stream);
 
 /* which kernels attn_fwd would run for a shape (host-only query, no GPU work) */
 typedef struct {

@@ -26,7 +26,7 @@ class MiAttnError(RuntimeError):
         self.code = code
 
 
-ABI_VERSION = 4  # MI_ATTN_ABI_VERSION of include/mi_attn.h that this binding matches
+ABI_VERSION = 5  # MI_ATTN_ABI_VERSION of include/mi_attn.h that this binding matches
 
 
 class AttnPlan(ctypes.Structure):
@@ -61,6 +61,10 @@ _SIGS = {
                         + [ctypes.c_void_p] + [ctypes.c_int] * 3 + [ctypes.c_void_p] * 2
                         + [ctypes.c_int, ctypes.c_void_p]),
     "attn_fwd_ex": (ctypes.c_int, [ctypes.POINTER(AttnFwdArgs), ctypes.c_void_p]),
+    "attn_bwd": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_void_p] + [ctypes.c_void_p] * 4
+                 + [ctypes.c_int] * 6 + [ctypes.c_float]
+                 + [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                    ctypes.c_void_p]),
     "attn_fwd_plan": (ctypes.c_int, [ctypes.c_int] * 10 + [ctypes.POINTER(AttnPlan)]),
     "attn_set_debug": (None, [ctypes.c_int] * 3),
     "attn_last_error": (ctypes.c_char_p, []),
@@ -249,6 +253,53 @@ def attn_fwd_ex(q, k, v, *, scale=None, mask_kind="causal", window_left=0, mask=
     a.dtype = _dtype_code(q)
     _check(lib().attn_fwd_ex(ctypes.byref(a), _stream_handle(q.device, stream)))
     return out, lse
+
+
+def attn_bwd(q, k, v, out, lse, dout, *, scale=None, mask_kind="causal", window_left=0, mask=None, zero_hold=None,
+             keep_k=0, dq=None, dk=None, dv=None, stream=None):
+    """Gradients of attn_fwd: ``(dq, dk, dv)`` for the output gradient ``dout``.
+
+    q, k, v, mask, zero_hold, keep_k and the mask arguments as given to attn_fwd; out and
+    lse as it returned them (lse is required); dout like out. fp16/bf16, d 64 or 128.
+    dq, dk and dv may be given (contiguous, shapes and dtype of q, k and v); they are
+    overwritten.
+    """
+    import torch
+    B, Hq, Lq, d = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    for name, t, shape in (("q", q, (B, Hq, Lq, d)), ("k", k, (B, Hkv, Lk, d)), ("v", v, (B, Hkv, Lk, d)),
+                           ("out", out, (B, Hq, Lq, d)), ("dout", dout, (B, Hq, Lq, d))):
+        if not t.is_cuda or tuple(t.shape) != shape or not t.is_contiguous() or t.dtype != q.dtype \
+                or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous {shape} {q.dtype} tensor on q's device")
+    if lse is None or tuple(lse.shape) != (B, Hq, Lq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be the contiguous fp32 [B, Hq, Lq] tensor attn_fwd wrote")
+    mk = MASK_KINDS[mask_kind] if isinstance(mask_kind, str) else int(mask_kind)
+    if mask is not None:
+        if mask.dtype != torch.float32 or tuple(mask.shape) != (Lq, Lk) or not mask.is_contiguous() \
+                or mask.device != q.device:
+            raise ValueError("mask must be a contiguous fp32 [Lq, Lk] tensor on q's device")
+    if zero_hold is not None:
+        if zero_hold.dtype != torch.float32 or tuple(zero_hold.shape) != (B, Hkv, Lk) \
+                or not zero_hold.is_contiguous() or zero_hold.device != q.device:
+            raise ValueError("zero_hold must be a contiguous fp32 [B, Hkv, Lk] tensor on q's device")
+    grads = []
+    for name, g, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if g is None:
+            g = torch.empty_like(like)
+        elif tuple(g.shape) != tuple(like.shape) or g.dtype != like.dtype or not g.is_contiguous():
+            raise ValueError(f"{name} must match the shape and dtype of its input")
+        grads.append(g)
+    dq, dk, dv = grads
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    rc = lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                        B, Hq, Hkv, Lq, Lk, d, float(scale), mk, int(window_left),
+                        _ptr(mask if mk == MASK_KINDS["dense"] else None),
+                        _ptr(zero_hold if mk == MASK_KINDS["topk"] else None), int(keep_k), _dtype_code(q),
+                        _stream_handle(q.device, stream))
+    _check(rc)
+    return dq, dk, dv
 
 
 def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, *, max_seqlen_q=None, max_seqlen_k=None,

@@ -330,6 +330,79 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
   return attn_fwd_ex(&a, stream);
 }
 
+int attn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse, const void* dout,
+             void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Lq, int Lk, int d, float scale,
+             int mask_kind, int window_left, const float* mask, const float* zero_hold, int keep_k, int dtype,
+             void* stream) {
+  g_err.clear();
+  const Shape s{B, Hq, Hkv, Lq, Lk, d, mask_kind, window_left, keep_k, dtype};
+  int rc = validate(s);
+  if (rc != MI_ATTN_OK) return rc;
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || lse == nullptr || dout == nullptr ||
+      dq == nullptr || dk == nullptr || dv == nullptr)
+    return fail(MI_ATTN_EINVAL, "q, k, v, out, lse, dout, dq, dk and dv must not be NULL");
+  if (!std::isfinite(scale)) return fail(MI_ATTN_EINVAL, "scale must be finite");
+  if (mask_kind == MI_ATTN_MASK_DENSE && mask == nullptr)
+    return fail(MI_ATTN_EINVAL, "mask_kind DENSE needs a mask pointer");
+  if (mask_kind == MI_ATTN_MASK_TOPK && zero_hold == nullptr)
+    return fail(MI_ATTN_EINVAL, "mask_kind TOPK needs a zero_hold pointer");
+  if (dtype == MI_ATTN_F32) return fail(MI_ATTN_EUNSUPPORTED, "attn_bwd takes fp16/bf16 inputs");
+  const int G = Hq / Hkv;
+  if (G > 128) return fail(MI_ATTN_EUNSUPPORTED, "attn_bwd supports at most 128 query heads per KV head");
+  if (static_cast<double>(Hq) * Lq * d * 2 > 2147483647.0)
+    return fail(MI_ATTN_EUNSUPPORTED, "Hq * Lq * d * 2 must stay below 2^31 bytes");
+  const void* in[6] = {q, k, v, out, dout, lse};
+  const void* gr[3] = {dq, dk, dv};
+  for (const void* x : in)
+    if (reinterpret_cast<uintptr_t>(x) % 16 != 0) return fail(MI_ATTN_EINVAL, "inputs must be 16-byte aligned");
+  for (const void* x : gr)
+    if (reinterpret_cast<uintptr_t>(x) % 16 != 0) return fail(MI_ATTN_EINVAL, "dq, dk and dv must be 16-byte aligned");
+
+  const long rows = static_cast<long>(B) * Hq * Lq;
+  const long bh = static_cast<long>(B) * Hkv;
+  size_t off = 0;
+  const size_t off_dsum = off; off = align256(off + sizeof(float) * rows);
+  size_t off_rank = 0, off_tau = 0;
+  if (mask_kind == MI_ATTN_MASK_TOPK) {
+    off_rank = off; off = align256(off + sizeof(int32_t) * bh * Lk);
+    off_tau = off;  off = align256(off + sizeof(int32_t) * bh * Lq);
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = nullptr;
+  hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&ws), off, st);
+  if (e != hipSuccess) return hip_fail(e, "hipMallocAsync(workspace)");
+
+  AttnParams p{};
+  p.q = q; p.k = k; p.v = v; p.out = const_cast<void*>(out); p.lse = const_cast<float*>(lse);
+  p.dout = dout; p.dq = dq; p.dk = dk; p.dv = dv;
+  p.dsum = reinterpret_cast<float*>(ws + off_dsum);
+  p.mask = mask_kind == MI_ATTN_MASK_DENSE ? mask : nullptr;
+  p.ms[2] = Lk;
+  p.ms[3] = 1;
+  p.zero_hold = zero_hold;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Lq = Lq; p.Lk = Lk; p.d = d; p.G = G;
+  p.scale = scale; p.mask_kind = mask_kind; p.window_left = window_left; p.keep_k = keep_k;
+  p.topk_causal = 1;
+  p.no_skip = g_no_skip;
+  p.splits = 1;
+  p.q_per_block = 128 / G;
+  const char* what = "attention backward kernels";
+  if (mask_kind == MI_ATTN_MASK_TOPK) {
+    int32_t* rank = reinterpret_cast<int32_t*>(ws + off_rank);
+    int32_t* tau = reinterpret_cast<int32_t*>(ws + off_tau);
+    what = "top-k selection";
+    e = launch_topk(zero_hold, B * Hkv, Lq, Lk, keep_k, 1, rank, tau, nullptr, nullptr, 0, st);
+    p.rank = rank;
+    p.tau = tau;
+    if (e == hipSuccess) what = "attention backward kernels";
+  }
+  if (e == hipSuccess) e = launch_backward(p, dtype, st);
+  const hipError_t ef = hipFreeAsync(ws, st);
+  if (e != hipSuccess) return hip_fail(e, what);
+  if (ef != hipSuccess) return hip_fail(ef, "hipFreeAsync(workspace)");
+  return MI_ATTN_OK;
+}
+
 int attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
                     const int32_t* cu_seqlens_q, int max_seqlen_q, const int32_t* cu_seqlens_k, int max_seqlen_k,
                     int num_seqs, int total_q, int Hq, int Hkv, int d, float scale, int mask_kind, int window_left,

@@ -126,6 +126,13 @@ struct AttnParams {
   const float* alibi;      // [Hq] slopes or nullptr: logit -= slope_h * |p_i - j|
   float softcap;           // > 0: logit -> softcap * tanh(logit / softcap) before the bias
   int topk_causal;         // top-k among causally allowed keys (1) or among all keys (0)
+  // backward (attn_bwd): the output gradient and the gradients, laid out like out, q, k, v;
+  // dsum = rowsum(dout * out), fp32 [B, Hq, Lq]
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dsum;
 };
 
 // Whether a call carries a per-element score modifier (every tile is then modified).
@@ -159,6 +166,8 @@ __host__ __device__ inline void key_range(int mask_kind, int window_left, int Lk
 
 // ------------------------------------------------------------------ launchers
 hipError_t launch_row_kernel(const AttnParams& p, int dtype, hipStream_t s);
+// backward: dsum, then dK/dV and dQ (contiguous layouts, fp16/bf16, d 64 or 128)
+hipError_t launch_backward(const AttnParams& p, int dtype, hipStream_t s);
 // tile_min (optional, [BH, ceil(Lk / block_n)]) receives the smallest rank of each
 // block_n-key tile; block_n must divide 256 and be at most 64.
 hipError_t launch_topk(const float* zh, int BH, int Lq, int Lk, int keep_k, int causal,

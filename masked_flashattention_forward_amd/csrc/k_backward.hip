@@ -1,0 +1,488 @@
+// Backward of the masked attention forward: dq, dk, dv from the saved LSE.
+//
+// The InfiniTrain pull request #193 page integrates forward and backward kernels for the
+// same attention ("main changes": fwd/bwd for FP16 and BF16, head dims 64 and 128; the
+// autograd function saves what the backward needs). With P recomputed from q, k and the
+// saved LSE, the chain rule of the forward gives, per (row i, key j):
+//   dv_j += P_ij dO_i                   dP_ij = dO_i . v_j
+//   dS_ij = P_ij (dP_ij - D_i),         D_i  = rowsum(dO_i * O_i)
+//   dq_i += scale dS_ij k_j             dk_j += scale dS_ij q_i
+// (the softmax Jacobian; a fully masked row has P = 0 and contributes nothing).
+//
+// Three kernels, no atomics:
+//   dsum_kernel  D_i for every row.
+//   dkdv_kernel  one workgroup per (batch, KV head, 128 keys); each wavefront owns 32 keys
+//                (K and V as B operands in registers) and loops over 32-row tiles of the
+//                query rows of all G heads that read the KV head (query-major), staged
+//                in LDS:  S = Q K^T, dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS
+//                with dO^T / Q^T from transposed LDS reads and P / dS straight from the
+//                registers (the C layout of S is the B layout these products need).
+//   dq_kernel    the forward's structure: one workgroup per (batch, KV head, 128 rows),
+//                64-key K/V tiles in LDS: S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T.
+#include "common.hpp"
+#include "mfma_common.hpp"
+
+namespace mi_attn {
+
+namespace {
+
+using namespace mfma;
+
+constexpr int kBW = 4;             // wavefronts per workgroup
+constexpr int kBT = kBW * kWave;
+
+// A tile of `ROWS` rows of D 16-bit values in LDS: [row][d], unpadded, 16-byte slots
+// swizzled by swz<D> (the forward's layout, conflict-free for both operand reads).
+template <int D, int ROWS>
+struct BTile {
+  static constexpr int rowBytes = D * 2;
+  static constexpr int bytes = ROWS * rowBytes;
+  static constexpr int rowsPerWaveLoad = 1024 / rowBytes;  // rows one wave's direct load fills
+  static constexpr int rounds = bytes / (kBT * 16);        // direct loads per wave
+  static_assert(rounds * kBT * 16 == bytes, "tile split evenly over the direct loads");
+};
+
+// ------------------------------------------------------------------ D = rowsum(dO * O)
+template <typename T>
+__global__ __launch_bounds__(256) void dsum_kernel(AttnParams p) {
+  const long rows = static_cast<long>(p.B) * p.Hq * p.Lq;
+  const long row = static_cast<long>(blockIdx.x) * 4 + threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  if (row >= rows) return;
+  const T* o = static_cast<const T*>(p.out) + row * p.d;
+  const T* g = static_cast<const T*>(p.dout) + row * p.d;
+  float acc = 0.f;
+  for (int c = lane; c < p.d; c += kWave) acc = fmaf(to_f32(o[c]), to_f32(g[c]), acc);
+  acc = wave_sum(acc);
+  if (lane == 0) p.dsum[row] = acc;
+}
+
+// LDS operand addresses shared by both kernels (see the forward kernel): a row fragment
+// (A operand: lane = row l32, 8 values dc*16 + hf*8) at blk * 32 * rowBytes +
+// (row_base ^ (dc << 5)); a transposed fragment (A operand: lane = column D0 + l32, the 8
+// rows whose values its P / dS registers hold) from two 64-bit transposed reads at
+// chunk * 16 * rowBytes + (tr_base[0|1] ^ (db << 6)).
+template <int D>
+struct Bases {
+  int row_base, tr0, tr1;
+  __device__ Bases(int lane) {
+    const int l32 = lane & 31, hf = lane >> 5;
+    constexpr int rb = D * 2;
+    row_base = l32 * rb | ((hf ^ swz<D>(l32)) << 4);
+    const int tr_row = 4 * hf + (lane & 15) / 4;
+    const int sl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    tr0 = tr_row * rb | ((sl ^ swz<D>(tr_row)) << 4) | (8 * (lane & 1));
+    tr1 = (tr_row + 8) * rb | ((sl ^ swz<D>(tr_row + 8)) << 4) | (8 * (lane & 1));
+  }
+};
+
+__device__ __forceinline__ u32x4_t row_frag(const unsigned char* tile, int row_base, int blk, int dc, int rowBytes) {
+  return *reinterpret_cast<const u32x4_t*>(tile + blk * 32 * rowBytes + (row_base ^ (dc << 5)));
+}
+__device__ __forceinline__ u32x4_t tr_frag(const unsigned char* tile, int tr0, int tr1, int chunk, int db,
+                                           int rowBytes) {
+  const unsigned char* r = tile + chunk * 16 * rowBytes;
+  const u32x2_t lo = lds_read_tr16(r + (tr0 ^ (db << 6)));
+  const u32x2_t hi = lds_read_tr16(r + (tr1 ^ (db << 6)));
+  return u32x4_t{lo.x, lo.y, hi.x, hi.y};
+}
+
+// P (or dS) registers of one 32-column C tile packed to 16 bit: chunk c holds rows
+// 16 c + {4 hf .. 4 hf + 3, 8 + 4 hf .. 8 + 4 hf + 3}, the rows the transposed reads pair
+// them with.
+template <typename T>
+__device__ __forceinline__ u32x4_t pack_half(const f32x16_t& x, int half) {
+  return u32x4_t{pack2(T{}, x[half * 8 + 0], x[half * 8 + 1]), pack2(T{}, x[half * 8 + 2], x[half * 8 + 3]),
+                 pack2(T{}, x[half * 8 + 4], x[half * 8 + 5]), pack2(T{}, x[half * 8 + 6], x[half * 8 + 7])};
+}
+
+// 16 fp32 values of a 32x32 C tile column as 4 groups of 4 consecutive rows, scaled and
+// rounded into a T row at `dst` (dims db * 32 + 8 * r4 + 4 * hf .. + 3).
+template <typename T>
+__device__ __forceinline__ void store_col(T* dst, const f32x16_t& x, int db, int hf, float mul) {
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4) {
+    const int d0 = db * 32 + r4 * 8 + hf * 4;
+    *reinterpret_cast<u32x2_t*>(dst + d0) = u32x2_t{pack2(T{}, x[r4 * 4] * mul, x[r4 * 4 + 1] * mul),
+                                                    pack2(T{}, x[r4 * 4 + 2] * mul, x[r4 * 4 + 3] * mul)};
+  }
+}
+
+// ------------------------------------------------------------------ dK, dV
+// Side data of a 32-row tile: per row the LSE (log2 units, +inf for a dead or absent row,
+// so P = 0), D, the absolute position and the top-k threshold.
+struct RowSide {
+  float lse2;
+  float dsum;
+  int pos;
+  int tau;
+};
+
+template <typename T, int D, int MK>
+__global__ __launch_bounds__(kBT, 1) void dkdv_kernel(AttnParams p) {
+  using QT = BTile<D, 32>;
+  constexpr int NDC = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int kStage = 2 * QT::bytes + 32 * static_cast<int>(sizeof(RowSide));
+  static_assert(kStage % 512 == 0, "stage offsets keep the XOR-ed address bits");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kStage];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave;
+  const int l32 = lane & 31;
+  const int hf = lane >> 5;
+  const int Lq = p.Lq, Lk = p.Lk, G = p.G;
+
+  const int nkb = (Lk + 127) / 128;
+  const unsigned lb = logical_block(blockIdx.x, gridDim.x);
+  const int kblk = static_cast<int>(lb % nkb);
+  const int bg = static_cast<int>(lb / nkb);
+  const int b = bg / p.Hkv, g = bg % p.Hkv;
+  const int j_lane = kblk * 128 + wave * 32 + l32;  // this lane's key (the column it owns)
+  const bool key_ok = j_lane < Lk;
+  const long kv_row = (static_cast<long>(bg) * Lk + (key_ok ? j_lane : 0)) * D;
+
+  // K^T and V^T B operands of the lane's key
+  u32x4_t kreg[NDC], vreg[NDC];
+#pragma unroll
+  for (int dc = 0; dc < NDC; ++dc) {
+    u32x4_t x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+    if (key_ok) {
+      x = *reinterpret_cast<const u32x4_t*>(static_cast<const T*>(p.k) + kv_row + dc * 16 + hf * 8);
+      y = *reinterpret_cast<const u32x4_t*>(static_cast<const T*>(p.v) + kv_row + dc * 16 + hf * 8);
+    }
+    kreg[dc] = x;
+    vreg[dc] = y;
+  }
+  int32_t rank_lane = 0x7fffffff;
+  float zh_lane = 0.f;
+  if constexpr (MK == MI_ATTN_MASK_TOPK) {
+    if (key_ok) {
+      rank_lane = p.rank[static_cast<long>(bg) * Lk + j_lane];
+      zh_lane = p.zero_hold[static_cast<long>(bg) * Lk + j_lane] * kLog2e;
+    }
+  }
+
+  // query rows that can see a key of this block: rows of all G heads, query-major
+  const int k_first = kblk * 128, k_last = min(Lk, k_first + 128) - 1;
+  int i_lo = 0, i_hi = Lq - 1;
+  if (MK == MI_ATTN_MASK_CAUSAL || MK == MI_ATTN_MASK_WINDOW || MK == MI_ATTN_MASK_TOPK)
+    i_lo = max(0, k_first - (Lk - Lq));
+  if (MK == MI_ATTN_MASK_WINDOW) i_hi = min(Lq - 1, k_last + p.window_left - (Lk - Lq));
+  if (p.no_skip) { i_lo = 0; i_hi = Lq - 1; }
+  const int R = G * Lq;
+  const int t_lo = (i_lo * G) / 32;
+  const int t_hi = i_lo <= i_hi ? ((i_hi + 1) * G + 31) / 32 : t_lo;
+
+  // direct loads: lane fills 16-byte slot ps of row rr of its load rounds; rows of the
+  // batch are addressed through a buffer over all its query heads (past the end: zeros)
+  const T* qb_ptr = static_cast<const T*>(p.q) + static_cast<long>(b) * p.Hq * Lq * D;
+  const T* ob_ptr = static_cast<const T*>(p.dout) + static_cast<long>(b) * p.Hq * Lq * D;
+  const int batch_bytes = p.Hq * Lq * D * 2;  // < 2^31 (checked on the host)
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qb_ptr, batch_bytes);
+  const __amdgpu_buffer_rsrc_t ors = make_rsrc(ob_ptr, batch_bytes);
+  const unsigned smem_addr = __builtin_amdgcn_readfirstlane(lds_address(smem));
+  const int ps = lane % (D / 8);
+  RowSide side{};
+  auto issue = [&](int t, int stg) {
+    const int r0 = t * 32;
+#pragma unroll
+    for (int c = 0; c < QT::rounds; ++c) {
+      const int rr = (c * kBW + wave) * QT::rowsPerWaveLoad + lane / (D / 8);
+      const int r = r0 + rr;
+      const int i = r / G;
+      const long row = (static_cast<long>(g) * G + (r - i * G)) * Lq + i;  // within the batch
+      const int off = r < R ? static_cast<int>(row * D * 2) + ((ps ^ swz<D>(rr)) << 4) : batch_bytes;
+      const unsigned dst = smem_addr + stg * kStage + (c * kBW + wave) * 1024;
+      lds_dma16_at(qrs, dst, off, 0);
+      lds_dma16_at(ors, dst + QT::bytes, off, 0);
+    }
+    if (tid < 32) {
+      const int r = r0 + tid;
+      const int i = r / G;
+      side.lse2 = __builtin_inff();
+      side.dsum = 0.f;
+      side.pos = -0x40000000;  // sees no key
+      side.tau = -1;
+      if (r < R) {
+        const long ri = ((static_cast<long>(b) * p.Hq + g * G + (r - i * G)) * Lq) + i;
+        const float l = p.lse[ri];
+        side.lse2 = l == kNegInf ? __builtin_inff() : l * kLog2e;
+        side.dsum = p.dsum[ri];
+        side.pos = Lk - Lq + i;
+        if constexpr (MK == MI_ATTN_MASK_TOPK) side.tau = min(p.tau[static_cast<long>(bg) * Lq + i], Lk - 1);
+      }
+    }
+  };
+  auto finish = [&](int stg) {
+    if (tid < 32) reinterpret_cast<RowSide*>(smem + stg * kStage + 2 * QT::bytes)[tid] = side;
+    __builtin_amdgcn_s_waitcnt(0);
+  };
+
+  const Bases<D> bs(lane);
+  const float cexp = p.scale * kLog2e;  // signed: no sign folded into an operand here
+  f32x16_t dkacc[NDB], dvacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dkacc[db] = f32x16_t{};
+    dvacc[db] = f32x16_t{};
+  }
+
+  int t = t_lo, stg = 0;
+  if (t < t_hi) {
+    issue(t, 0);
+    finish(0);
+  }
+  __syncthreads();
+  while (t < t_hi) {
+    if (t + 1 < t_hi) issue(t + 1, stg ^ 1);
+    const unsigned char* qt = smem + stg * kStage;
+    const unsigned char* ot = qt + QT::bytes;
+    const RowSide* rs = reinterpret_cast<const RowSide*>(qt + 2 * QT::bytes);
+
+    // S = Q K^T and dP = dO V^T (32 rows x 32 keys; lane = key, registers = rows)
+    f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc) s = mfma32(T{}, row_frag(qt, bs.row_base, 0, dc, QT::rowBytes), kreg[dc], s);
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc) dp = mfma32(T{}, row_frag(ot, bs.row_base, 0, dc, QT::rowBytes), vreg[dc], dp);
+
+    // P = exp2(logit - lse) with the mask of the (row, key) pair; dS = P (dP - D)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rr = r4 * 8 + hf * 4 + e;
+        const RowSide sd = rs[rr];
+        float x = s[r4 * 4 + e] * cexp;
+        bool vis = key_ok;
+        if constexpr (MK == MI_ATTN_MASK_CAUSAL) vis = vis && j_lane <= sd.pos;
+        if constexpr (MK == MI_ATTN_MASK_WINDOW) vis = vis && j_lane <= sd.pos && j_lane >= sd.pos - p.window_left;
+        if constexpr (MK == MI_ATTN_MASK_DENSE) {
+          const int i = sd.pos - (Lk - Lq);
+          vis = vis && i >= 0;
+          const float mv = vis ? p.mask[static_cast<long>(i) * Lk + j_lane] : 0.f;
+          x = fmaf(mv, kLog2e, x);
+        }
+        if constexpr (MK == MI_ATTN_MASK_TOPK) {
+          vis = vis && j_lane <= sd.pos && rank_lane <= sd.tau;
+          x += zh_lane;
+        }
+        const float pv = vis ? fast_exp2(x - sd.lse2) : 0.f;
+        s[r4 * 4 + e] = pv;
+        dp[r4 * 4 + e] = pv * (dp[r4 * 4 + e] - sd.dsum);
+      }
+    }
+
+    // dV^T += dO^T P and dK^T += Q^T dS (d x 32 keys; contraction over the 32 rows)
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const u32x4_t pb = pack_half<T>(s, half);
+      const u32x4_t sb = pack_half<T>(dp, half);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        dvacc[db] = mfma32(T{}, tr_frag(ot, bs.tr0, bs.tr1, half, db, QT::rowBytes), pb, dvacc[db]);
+        dkacc[db] = mfma32(T{}, tr_frag(qt, bs.tr0, bs.tr1, half, db, QT::rowBytes), sb, dkacc[db]);
+      }
+    }
+
+    if (t + 1 < t_hi) finish(stg ^ 1);
+    __syncthreads();
+    ++t;
+    stg ^= 1;
+  }
+
+  if (!key_ok) return;
+  T* dk = static_cast<T*>(p.dk) + kv_row;
+  T* dv = static_cast<T*>(p.dv) + kv_row;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    store_col<T>(dk, dkacc[db], db, hf, p.scale);
+    store_col<T>(dv, dvacc[db], db, hf, 1.f);
+  }
+}
+
+// ------------------------------------------------------------------ dQ
+template <typename T, int D, int MK>
+__global__ __launch_bounds__(kBT, 2) void dq_kernel(AttnParams p) {
+  constexpr int BN = 64;
+  using KT = BTile<D, BN>;
+  constexpr int NDC = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int kStage = 2 * KT::bytes;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kStage];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave;
+  const int l32 = lane & 31;
+  const int hf = lane >> 5;
+  const int Lq = p.Lq, Lk = p.Lk, G = p.G;
+
+  const int nqb = (Lq + p.q_per_block - 1) / p.q_per_block;
+  const unsigned lb = logical_block(blockIdx.x, gridDim.x);
+  const int qb = nqb - 1 - static_cast<int>(lb % nqb);
+  const int bg = static_cast<int>(lb / nqb);
+  const int b = bg / p.Hkv, g = bg % p.Hkv;
+  const int i_first = qb * p.q_per_block;
+  const int i_last = min(Lq, i_first + p.q_per_block) - 1;
+  const int rows_blk = (i_last - i_first + 1) * G;
+  const int P0 = Lk - Lq + i_first, P1 = Lk - Lq + i_last;
+
+  // this lane's row (the S^T column it owns), query-major over the G heads
+  const int rloc = wave * 32 + l32;
+  const bool row_ok = rloc < rows_blk;
+  const int i_row = i_first + (row_ok ? rloc / G : 0);
+  const int h_row = g * G + (row_ok ? rloc % G : 0);
+  const int pos = Lk - Lq + i_row;
+  const long row_index = (static_cast<long>(b) * p.Hq + h_row) * Lq + i_row;
+
+  u32x4_t qreg[NDC], oreg[NDC];  // Q^T and dO^T B operands of the lane's row
+#pragma unroll
+  for (int dc = 0; dc < NDC; ++dc) {
+    u32x4_t x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+    if (row_ok) {
+      x = *reinterpret_cast<const u32x4_t*>(static_cast<const T*>(p.q) + row_index * D + dc * 16 + hf * 8);
+      y = *reinterpret_cast<const u32x4_t*>(static_cast<const T*>(p.dout) + row_index * D + dc * 16 + hf * 8);
+    }
+    qreg[dc] = x;
+    oreg[dc] = y;
+  }
+  const float cexp = p.scale * kLog2e;  // signed
+  const float lse = row_ok ? p.lse[row_index] : kNegInf;
+  const float lse2 = lse == kNegInf ? __builtin_inff() : lse * kLog2e;  // dead rows: P = 0
+  const float dsum = row_ok ? p.dsum[row_index] : 0.f;
+  const Mods md = make_mods<false>(p, cexp, b, h_row, i_row, pos, MK == MI_ATTN_MASK_DENSE);
+  int32_t tau_row = 0;
+  if constexpr (MK == MI_ATTN_MASK_TOPK) tau_row = min(p.tau[static_cast<long>(bg) * Lq + i_row], Lk - 1);
+  const long bgk = static_cast<long>(bg) * Lk;
+
+  int lo, hi;
+  key_range(MK, p.window_left, Lk, P0, P1, &lo, &hi);
+  if (p.no_skip) { lo = 0; hi = Lk; }
+  const int t_lo = lo / BN;
+  const int t_hi = hi > lo ? (hi + BN - 1) / BN : t_lo;
+
+  const T* K = static_cast<const T*>(p.k) + bgk * D;
+  const T* V = static_cast<const T*>(p.v) + bgk * D;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K, Lk * D * 2);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V, Lk * D * 2);
+  const unsigned smem_addr = __builtin_amdgcn_readfirstlane(lds_address(smem));
+  int dma_lane;
+  {
+    const int r = wave * KT::rowsPerWaveLoad + lane / (D / 8);
+    dma_lane = (r * D + (((lane % (D / 8)) ^ swz<D>(r)) << 3)) * 2;
+  }
+  auto issue = [&](int t, int stg) {
+#pragma unroll
+    for (int c = 0; c < KT::rounds; ++c) {
+      const int so = (t * BN + c * kBW * KT::rowsPerWaveLoad) * D * 2;
+      const unsigned dst = smem_addr + stg * kStage + (c * kBW + wave) * 1024;
+      lds_dma16_at(krs, dst, dma_lane, so);
+      lds_dma16_at(vrs, dst + KT::bytes, dma_lane, so);
+    }
+  };
+
+  const Bases<D> bs(lane);
+  f32x16_t dqacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) dqacc[db] = f32x16_t{};
+
+  int t = t_lo, stg = 0;
+  if (t < t_hi) {
+    issue(t, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+  __syncthreads();
+  while (t < t_hi) {
+    if (t + 1 < t_hi) issue(t + 1, stg ^ 1);
+    const unsigned char* kt = smem + stg * kStage;
+    const unsigned char* vt = kt + KT::bytes;
+    const int j0 = t * BN;
+
+    // S^T = K Q^T and dP^T = V dO^T (64 keys x 32 rows; lane = row, registers = keys)
+    f32x16_t s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16_t a = f32x16_t{}, c = f32x16_t{};
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc) a = mfma32(T{}, row_frag(kt, bs.row_base, kb, dc, KT::rowBytes), qreg[dc], a);
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc) c = mfma32(T{}, row_frag(vt, bs.row_base, kb, dc, KT::rowBytes), oreg[dc], c);
+      s[kb] = a;
+      dp[kb] = c;
+    }
+    // logits in log2 units (masked where the tile needs it), P, dS = P (dP - D)
+    if (tile_needs_mask<MK, BN>(p, Lk, j0, P0, P1)) {
+      mask_tile<MK, 2, false>(s, p, Lk, j0, hf, pos, tau_row, md,
+                              MK == MI_ATTN_MASK_TOPK ? p.rank + bgk + j0 : nullptr,
+                              MK == MI_ATTN_MASK_TOPK ? p.zero_hold + bgk + j0 : nullptr);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[kb] *= cexp;
+    }
+    u32x4_t dsreg[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float pv = fast_exp2(s[kb][e] - lse2);
+        dp[kb][e] = pv * (dp[kb][e] - dsum);
+      }
+      dsreg[kb * 2] = pack_half<T>(dp[kb], 0);
+      dsreg[kb * 2 + 1] = pack_half<T>(dp[kb], 1);
+    }
+    // dQ^T += K^T dS^T (d x 32 rows; contraction over the 64 keys)
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        dqacc[db] = mfma32(T{}, tr_frag(kt, bs.tr0, bs.tr1, kc, db, KT::rowBytes), dsreg[kc], dqacc[db]);
+
+    if (t + 1 < t_hi) __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    ++t;
+    stg ^= 1;
+  }
+
+  if (!row_ok) return;
+  T* dq = static_cast<T*>(p.dq) + row_index * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) store_col<T>(dq, dqacc[db], db, hf, p.scale);
+}
+
+template <typename T, int D>
+hipError_t launch_bwd_t(const AttnParams& p, hipStream_t s) {
+  const long rows = static_cast<long>(p.B) * p.Hq * p.Lq;
+  hipLaunchKernelGGL(dsum_kernel<T>, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, s, p);
+  const long nkb = (p.Lk + 127) / 128;
+  const dim3 g1(static_cast<unsigned>(static_cast<long>(p.B) * p.Hkv * nkb));
+  const long nqb = (p.Lq + p.q_per_block - 1) / p.q_per_block;
+  const dim3 g2(static_cast<unsigned>(static_cast<long>(p.B) * p.Hkv * nqb));
+  switch (p.mask_kind) {
+#define MI_BWD_CASE(KIND)                                                              \
+  case KIND:                                                                           \
+    hipLaunchKernelGGL((dkdv_kernel<T, D, KIND>), g1, dim3(kBT), 0, s, p);             \
+    hipLaunchKernelGGL((dq_kernel<T, D, KIND>), g2, dim3(kBT), 0, s, p);               \
+    break;
+    MI_BWD_CASE(MI_ATTN_MASK_NONE)
+    MI_BWD_CASE(MI_ATTN_MASK_CAUSAL)
+    MI_BWD_CASE(MI_ATTN_MASK_WINDOW)
+    MI_BWD_CASE(MI_ATTN_MASK_DENSE)
+    MI_BWD_CASE(MI_ATTN_MASK_TOPK)
+#undef MI_BWD_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward(const AttnParams& p, int dtype, hipStream_t s) {
+  if (dtype == MI_ATTN_BF16) return p.d == 128 ? launch_bwd_t<bf16_t, 128>(p, s) : launch_bwd_t<bf16_t, 64>(p, s);
+  if (dtype == MI_ATTN_F16) return p.d == 128 ? launch_bwd_t<f16_t, 128>(p, s) : launch_bwd_t<f16_t, 64>(p, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mi_attn

@@ -27,9 +27,9 @@ import numpy as np
 from .attention import NEG_INF, mask_matrix
 
 
-def attention_backward_rows_ref(q, k, v, dout, scale, A):
-    """One head: q ``[n, d]``, k/v ``[Lk, d]``, dout ``[n, d]``, mask A ``[n, Lk]``.
-    Returns (dq ``[n, d]``, dk ``[Lk, d]``, dv ``[Lk, d]``) in fp64."""
+def softmax_backward_terms(q, k, v, dout, scale, A):
+    """One head's intermediate quantities of the definition above: P ``[n, Lk]`` and
+    dZ ``[n, Lk]`` (fp64)."""
     Z = scale * (q @ k.T) + A
     M = Z.max(axis=1)
     dead = M == NEG_INF
@@ -38,9 +38,16 @@ def attention_backward_rows_ref(q, k, v, dout, scale, A):
     l = W.sum(axis=1)
     P = np.zeros_like(W)
     P[~dead] = W[~dead] / l[~dead, None]
-    dv = P.T @ dout
     dP = dout @ v.T
     dZ = P * (dP - (dP * P).sum(axis=1, keepdims=True))
+    return P, dZ
+
+
+def attention_backward_rows_ref(q, k, v, dout, scale, A):
+    """One head: q ``[n, d]``, k/v ``[Lk, d]``, dout ``[n, d]``, mask A ``[n, Lk]``.
+    Returns (dq ``[n, d]``, dk ``[Lk, d]``, dv ``[Lk, d]``) in fp64."""
+    P, dZ = softmax_backward_terms(q, k, v, dout, scale, A)
+    dv = P.T @ dout
     dq = scale * (dZ @ k)
     dk = scale * (dZ.T @ q)
     return dq, dk, dv

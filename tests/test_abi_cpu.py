@@ -136,6 +136,33 @@ def test_attn_fwd_rejects_before_any_gpu_work(lib, kw):
     assert lib.attn_last_error().decode() != ""
 
 
+def call_bwd(**kw):
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+    args = dict(q=fake, k=fake, v=fake, out=fake, lse=fake, dout=fake, dq=fake, dk=fake, dv=fake, B=1, Hq=2, Hkv=2,
+                Lq=8, Lk=8, d=64, scale=0.125, mask_kind=1, window_left=0, mask=None, zero_hold=None, keep_k=0,
+                dtype=2, stream=None)
+    args.update(kw)
+    return mfa.lib().attn_bwd(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(lse=None), -1), (dict(dout=None), -1), (dict(dk=None), -1), (dict(q=None), -1),
+    (dict(scale=float("nan")), -1),
+    (dict(mask_kind=3, mask=None), -1),
+    (dict(mask_kind=4, zero_hold=None, keep_k=4), -1),
+    (dict(mask_kind=2, window_left=-1), -1),
+    (dict(Hq=3, Hkv=2), -1),
+    (dict(dq=ctypes.c_void_p(0x1008)), -1),        # not 16-byte aligned
+    (dict(dtype=0), -2),                           # fp32 has no backward kernels
+    (dict(d=96), -2),
+    (dict(Hq=258, Hkv=1), -2),                     # more than 128 query heads per KV head
+    (dict(Hq=64, Lq=1 << 17, d=128), -2),          # a batch of q past 2^31 bytes
+])
+def test_attn_bwd_rejects_before_any_gpu_work(lib, kw, code):
+    assert call_bwd(**kw) == code
+    assert lib.attn_last_error().decode() != ""
+
+
 def ex_args(**kw):
     """attn_fwd_ex arguments for a contiguous bf16 [1,2,8,64] call with fake pointers (never
     dereferenced: validation fails first), then the overrides in kw."""
