@@ -12,9 +12,10 @@ The same line carries:
   configs       every other workload (decode GB/s, long causal, top-k, dense window,
                 tiny fp32), the paged serving batch of attn_fwd_varlen and the attn_fwd_ex
                 workloads (transposed KV cache, ALiBi + softcap, non-causal top-k, per-head
-                mask; each with the plain call's time on the same data). Parity at these
+                mask; each with the plain call's time on the same data) and the backward
+                (attn_bwd) on the long causal and prefill workloads. Parity at these
                 sizes is the GPU tests' job (tests/test_gpu_parity.py, test_gpu_varlen.py,
-                test_gpu_ex.py);
+                test_gpu_ex.py, test_gpu_bwd.py);
                 the benchmark only times.
 
 Usage: python bench.py [--steps K] [--warmup W] [--only NAME] [--no-cpu-baseline]
@@ -249,6 +250,44 @@ def bench_ex_config(name, iters=20):
     return res
 
 
+def bench_bwd_config(name, iters=10):
+    """attn_bwd on one of the configurations: the forward runs once for out and lse, then
+    the backward call (rowsum, dK/dV and dQ kernels) is timed. Algorithmic work: the five
+    products of the backward, 10*d flops per visible (row, key) pair (the kernels execute
+    14*d: S and dP are computed in both the dK/dV and the dQ kernel)."""
+    import torch
+    import masked_flashattention_forward_amd as mfa
+    import synth
+    p = synth.config(name)
+    r = Runner(p)
+    r()
+    dout = torch.randn(r.q.shape, generator=torch.Generator(device="cuda").manual_seed(7), device="cuda",
+                       dtype=torch.float32).to(r.q.dtype)
+    dq, dk, dv = torch.empty_like(r.q), torch.empty_like(r.k), torch.empty_like(r.v)
+    kw = dict(scale=p.scale, mask_kind=p.mask_kind, window_left=p.window_left,
+              mask=r.mask if p.mask_kind == "dense" else None, zero_hold=r.zh if p.mask_kind == "topk" else None,
+              keep_k=p.keep_k, dq=dq, dk=dk, dv=dv)
+
+    def call():
+        mfa.attn_bwd(r.q, r.k, r.v, r.out, r.lse, dout, **kw)
+
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    ms = r.event_time_ms(iters, call)
+    ms_fwd = r.event_time_ms(iters)
+    pairs = visible_pairs(p)
+    flops = 10.0 * p.d * pairs
+    res = {"workload": p.name, "B": p.B, "Hq": p.Hq, "Hkv": p.Hkv, "Lq": p.Lq, "Lk": p.Lk, "d": p.d,
+           "dtype": p.dtype, "mask": p.mask_kind, "us": round(ms * 1e3, 2), "us_forward": round(ms_fwd * 1e3, 2),
+           "tflops": round(flops / ms / 1e9, 2), "pct_mfma_peak": round(100 * flops / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+           "tflops_executed": round(1.4 * flops / ms / 1e9, 2)}
+    del r, dout, dq, dk, dv
+    torch.cuda.empty_cache()
+    log(f"{name} backward: {json.dumps(res)}")
+    return res
+
+
 def paged_pairs_and_keys(p):
     """Visible (row, key) pairs over all query heads, and distinct visible keys per KV
     head, of a varlen problem (each sequence bottom-right aligned)."""
@@ -416,6 +455,9 @@ def main():
         for name in synth.EX_NAMES:
             log(f"config {name} (attn_fwd_ex)")
             configs[name] = bench_ex_config(name)
+        for name in ("c4_d128_bf16", "c4_d64_bf16", "c4_d128_fp16", "c4_d64_fp16", "c3p"):
+            log(f"config {name} (attn_bwd)")
+            configs[f"{name}_bwd"] = bench_bwd_config(name)
         line["configs"] = configs
         d = configs["c3d"]
         line["decode"] = {"workload": d["workload"], "value": d["gbs"], "unit": "GB/s",

@@ -259,11 +259,13 @@ int attn_fwd_ex(const attn_fwd_args_t* args, void* stream);
  *   dq, dk, dv          device, written (not accumulated), layouts of q, k and v. They
  *                       must not overlap the inputs.
  *   B .. keep_k, dtype  as in attn_fwd (the top-k kind selects causally, as attn_fwd).
- *   stream              as in attn_fwd. Temporary device memory: rowsum(dout * out),
- *                       4 bytes per query row, plus the top-k ranks for that kind.
+ *   stream              as in attn_fwd. Temporary device memory: 12 bytes per query
+ *                       row (its LSE, rowsum(dout * out) and a mask index), plus the
+ *                       top-k ranks for that kind.
  *
  *   fp16/bf16 only (fp32 returns MI_ATTN_EUNSUPPORTED), head dims 64 and 128, at most
- *   128 query heads per KV head, Hq * Lq * d * 2 below 2^31 bytes. Products take fp16/bf16
+ *   128 query heads per KV head, Hq * Lq * d * 2 below 2^31 bytes, B * Hq * Lq * 12 below
+ *   2^31. Products take fp16/bf16
  *   operands (P and dZ are rounded to the input type before the second products) with
  *   fp32 accumulation; dq, dk and dv are rounded to nearest-even in the input type.
  *   Returns attn_fwd's codes.

@@ -351,6 +351,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
   if (G > 128) return fail(MI_ATTN_EUNSUPPORTED, "attn_bwd supports at most 128 query heads per KV head");
   if (static_cast<double>(Hq) * Lq * d * 2 > 2147483647.0)
     return fail(MI_ATTN_EUNSUPPORTED, "Hq * Lq * d * 2 must stay below 2^31 bytes");
+  if (static_cast<double>(B) * Hq * Lq * 12 > 2147483647.0)
+    return fail(MI_ATTN_EUNSUPPORTED, "B * Hq * Lq must stay below 2^31 / 12 query rows");
   const void* in[6] = {q, k, v, out, dout, lse};
   const void* gr[3] = {dq, dk, dv};
   for (const void* x : in)
@@ -361,7 +363,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
   const long rows = static_cast<long>(B) * Hq * Lq;
   const long bh = static_cast<long>(B) * Hkv;
   size_t off = 0;
-  const size_t off_dsum = off; off = align256(off + sizeof(float) * rows);
+  const size_t off_side = off; off = align256(off + 3 * sizeof(float) * rows);
   size_t off_rank = 0, off_tau = 0;
   if (mask_kind == MI_ATTN_MASK_TOPK) {
     off_rank = off; off = align256(off + sizeof(int32_t) * bh * Lk);
@@ -375,7 +377,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
   AttnParams p{};
   p.q = q; p.k = k; p.v = v; p.out = const_cast<void*>(out); p.lse = const_cast<float*>(lse);
   p.dout = dout; p.dq = dq; p.dk = dk; p.dv = dv;
-  p.dsum = reinterpret_cast<float*>(ws + off_dsum);
+  p.bwd_side = reinterpret_cast<float*>(ws + off_side);
   p.mask = mask_kind == MI_ATTN_MASK_DENSE ? mask : nullptr;
   p.ms[2] = Lk;
   p.ms[3] = 1;

@@ -126,13 +126,16 @@ struct AttnParams {
   const float* alibi;      // [Hq] slopes or nullptr: logit -= slope_h * |p_i - j|
   float softcap;           // > 0: logit -> softcap * tanh(logit / softcap) before the bias
   int topk_causal;         // top-k among causally allowed keys (1) or among all keys (0)
-  // backward (attn_bwd): the output gradient and the gradients, laid out like out, q, k, v;
-  // dsum = rowsum(dout * out), fp32 [B, Hq, Lq]
+  // backward (attn_bwd): the output gradient and the gradients, laid out like out, q, k, v.
+  // bwd_side: three arrays of B*Hq*Lq 4-byte values, each [B, Hkv, Lq * G] with the rows
+  // of one KV head query-major (row r = i * G + (h - g * G)): -lse * log2(e) (-inf for a
+  // row that sees no key), rowsum(dout * out), and the row's top-k threshold (top-k) or
+  // query index i (dense mask). The dQ kernel writes them; the dK/dV kernel reads them.
   const void* dout;
   void* dq;
   void* dk;
   void* dv;
-  float* dsum;
+  float* bwd_side;
 };
 
 // Whether a call carries a per-element score modifier (every tile is then modified).
@@ -166,7 +169,8 @@ __host__ __device__ inline void key_range(int mask_kind, int window_left, int Lk
 
 // ------------------------------------------------------------------ launchers
 hipError_t launch_row_kernel(const AttnParams& p, int dtype, hipStream_t s);
-// backward: dsum, then dK/dV and dQ (contiguous layouts, fp16/bf16, d 64 or 128)
+// backward: the dQ kernel (which also writes the row side arrays), then the dK/dV
+// kernel (contiguous layouts, fp16/bf16, d 64 or 128)
 hipError_t launch_backward(const AttnParams& p, int dtype, hipStream_t s);
 // tile_min (optional, [BH, ceil(Lk / block_n)]) receives the smallest rank of each
 // block_n-key tile; block_n must divide 256 and be at most 64.

@@ -9,16 +9,19 @@
 //   dq_i += scale dS_ij k_j             dk_j += scale dS_ij q_i
 // (the softmax Jacobian; a fully masked row has P = 0 and contributes nothing).
 //
-// Three kernels, no atomics:
-//   dsum_kernel  D_i for every row.
+// Two kernels, no atomics:
+//   dq_kernel    the forward's structure: one workgroup per (batch, KV head, 128 rows of
+//                the G heads, query-major), 64-key K/V tiles in LDS:
+//                S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T. It computes D itself from
+//                the rows it holds and writes the per-row side arrays (-LSE in log2 units,
+//                D, and the top-k threshold or query index) in the row order below.
 //   dkdv_kernel  one workgroup per (batch, KV head, 128 keys); each wavefront owns 32 keys
 //                (K and V as B operands in registers) and loops over 32-row tiles of the
-//                query rows of all G heads that read the KV head (query-major), staged
-//                in LDS:  S = Q K^T, dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS
-//                with dO^T / Q^T from transposed LDS reads and P / dS straight from the
-//                registers (the C layout of S is the B layout these products need).
-//   dq_kernel    the forward's structure: one workgroup per (batch, KV head, 128 rows),
-//                64-key K/V tiles in LDS: S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T.
+//                query rows of all G heads that read the KV head (query-major), staged in
+//                LDS by direct loads three tiles deep: S = Q K^T, dP = dO V^T, then
+//                dV^T += dO^T P and dK^T += Q^T dS with dO^T / Q^T from transposed LDS
+//                reads and P / dS straight from the registers (the C layout of S is the B
+//                layout these products need).
 #include "common.hpp"
 #include "mfma_common.hpp"
 
@@ -41,21 +44,6 @@ struct BTile {
   static constexpr int rounds = bytes / (kBT * 16);        // direct loads per wave
   static_assert(rounds * kBT * 16 == bytes, "tile split evenly over the direct loads");
 };
-
-// ------------------------------------------------------------------ D = rowsum(dO * O)
-template <typename T>
-__global__ __launch_bounds__(256) void dsum_kernel(AttnParams p) {
-  const long rows = static_cast<long>(p.B) * p.Hq * p.Lq;
-  const long row = static_cast<long>(blockIdx.x) * 4 + threadIdx.x / kWave;
-  const int lane = threadIdx.x % kWave;
-  if (row >= rows) return;
-  const T* o = static_cast<const T*>(p.out) + row * p.d;
-  const T* g = static_cast<const T*>(p.dout) + row * p.d;
-  float acc = 0.f;
-  for (int c = lane; c < p.d; c += kWave) acc = fmaf(to_f32(o[c]), to_f32(g[c]), acc);
-  acc = wave_sum(acc);
-  if (lane == 0) p.dsum[row] = acc;
-}
 
 // LDS operand addresses shared by both kernels (see the forward kernel): a row fragment
 // (A operand: lane = row l32, 8 values dc*16 + hf*8) at blk * 32 * rowBytes +
@@ -108,202 +96,10 @@ __device__ __forceinline__ void store_col(T* dst, const f32x16_t& x, int db, int
   }
 }
 
-// ------------------------------------------------------------------ dK, dV
-// Side data of a 32-row tile: per row the LSE (log2 units, +inf for a dead or absent row,
-// so P = 0), D, the absolute position and the top-k threshold.
-struct RowSide {
-  float lse2;
-  float dsum;
-  int pos;
-  int tau;
-};
+// s_waitcnt: at most n vector-memory operations outstanding and no LDS operation
+constexpr int vm_lgkm0_imm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4); }
 
-template <typename T, int D, int MK>
-__global__ __launch_bounds__(kBT, 1) void dkdv_kernel(AttnParams p) {
-  using QT = BTile<D, 32>;
-  constexpr int NDC = D / 16;
-  constexpr int NDB = D / 32;
-  constexpr int kStage = 2 * QT::bytes + 32 * static_cast<int>(sizeof(RowSide));
-  static_assert(kStage % 512 == 0, "stage offsets keep the XOR-ed address bits");
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kStage];
-
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int lane = tid % kWave;
-  const int l32 = lane & 31;
-  const int hf = lane >> 5;
-  const int Lq = p.Lq, Lk = p.Lk, G = p.G;
-
-  const int nkb = (Lk + 127) / 128;
-  const unsigned lb = logical_block(blockIdx.x, gridDim.x);
-  const int kblk = static_cast<int>(lb % nkb);
-  const int bg = static_cast<int>(lb / nkb);
-  const int b = bg / p.Hkv, g = bg % p.Hkv;
-  const int j_lane = kblk * 128 + wave * 32 + l32;  // this lane's key (the column it owns)
-  const bool key_ok = j_lane < Lk;
-  const long kv_row = (static_cast<long>(bg) * Lk + (key_ok ? j_lane : 0)) * D;
-
-  // K^T and V^T B operands of the lane's key
-  u32x4_t kreg[NDC], vreg[NDC];
-#pragma unroll
-  for (int dc = 0; dc < NDC; ++dc) {
-    u32x4_t x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-    if (key_ok) {
-      x = *reinterpret_cast<const u32x4_t*>(static_cast<const T*>(p.k) + kv_row + dc * 16 + hf * 8);
-      y = *reinterpret_cast<const u32x4_t*>(static_cast<const T*>(p.v) + kv_row + dc * 16 + hf * 8);
-    }
-    kreg[dc] = x;
-    vreg[dc] = y;
-  }
-  int32_t rank_lane = 0x7fffffff;
-  float zh_lane = 0.f;
-  if constexpr (MK == MI_ATTN_MASK_TOPK) {
-    if (key_ok) {
-      rank_lane = p.rank[static_cast<long>(bg) * Lk + j_lane];
-      zh_lane = p.zero_hold[static_cast<long>(bg) * Lk + j_lane] * kLog2e;
-    }
-  }
-
-  // query rows that can see a key of this block: rows of all G heads, query-major
-  const int k_first = kblk * 128, k_last = min(Lk, k_first + 128) - 1;
-  int i_lo = 0, i_hi = Lq - 1;
-  if (MK == MI_ATTN_MASK_CAUSAL || MK == MI_ATTN_MASK_WINDOW || MK == MI_ATTN_MASK_TOPK)
-    i_lo = max(0, k_first - (Lk - Lq));
-  if (MK == MI_ATTN_MASK_WINDOW) i_hi = min(Lq - 1, k_last + p.window_left - (Lk - Lq));
-  if (p.no_skip) { i_lo = 0; i_hi = Lq - 1; }
-  const int R = G * Lq;
-  const int t_lo = (i_lo * G) / 32;
-  const int t_hi = i_lo <= i_hi ? ((i_hi + 1) * G + 31) / 32 : t_lo;
-
-  // direct loads: lane fills 16-byte slot ps of row rr of its load rounds; rows of the
-  // batch are addressed through a buffer over all its query heads (past the end: zeros)
-  const T* qb_ptr = static_cast<const T*>(p.q) + static_cast<long>(b) * p.Hq * Lq * D;
-  const T* ob_ptr = static_cast<const T*>(p.dout) + static_cast<long>(b) * p.Hq * Lq * D;
-  const int batch_bytes = p.Hq * Lq * D * 2;  // < 2^31 (checked on the host)
-  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qb_ptr, batch_bytes);
-  const __amdgpu_buffer_rsrc_t ors = make_rsrc(ob_ptr, batch_bytes);
-  const unsigned smem_addr = __builtin_amdgcn_readfirstlane(lds_address(smem));
-  const int ps = lane % (D / 8);
-  RowSide side{};
-  auto issue = [&](int t, int stg) {
-    const int r0 = t * 32;
-#pragma unroll
-    for (int c = 0; c < QT::rounds; ++c) {
-      const int rr = (c * kBW + wave) * QT::rowsPerWaveLoad + lane / (D / 8);
-      const int r = r0 + rr;
-      const int i = r / G;
-      const long row = (static_cast<long>(g) * G + (r - i * G)) * Lq + i;  // within the batch
-      const int off = r < R ? static_cast<int>(row * D * 2) + ((ps ^ swz<D>(rr)) << 4) : batch_bytes;
-      const unsigned dst = smem_addr + stg * kStage + (c * kBW + wave) * 1024;
-      lds_dma16_at(qrs, dst, off, 0);
-      lds_dma16_at(ors, dst + QT::bytes, off, 0);
-    }
-    if (tid < 32) {
-      const int r = r0 + tid;
-      const int i = r / G;
-      side.lse2 = __builtin_inff();
-      side.dsum = 0.f;
-      side.pos = -0x40000000;  // sees no key
-      side.tau = -1;
-      if (r < R) {
-        const long ri = ((static_cast<long>(b) * p.Hq + g * G + (r - i * G)) * Lq) + i;
-        const float l = p.lse[ri];
-        side.lse2 = l == kNegInf ? __builtin_inff() : l * kLog2e;
-        side.dsum = p.dsum[ri];
-        side.pos = Lk - Lq + i;
-        if constexpr (MK == MI_ATTN_MASK_TOPK) side.tau = min(p.tau[static_cast<long>(bg) * Lq + i], Lk - 1);
-      }
-    }
-  };
-  auto finish = [&](int stg) {
-    if (tid < 32) reinterpret_cast<RowSide*>(smem + stg * kStage + 2 * QT::bytes)[tid] = side;
-    __builtin_amdgcn_s_waitcnt(0);
-  };
-
-  const Bases<D> bs(lane);
-  const float cexp = p.scale * kLog2e;  // signed: no sign folded into an operand here
-  f32x16_t dkacc[NDB], dvacc[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    dkacc[db] = f32x16_t{};
-    dvacc[db] = f32x16_t{};
-  }
-
-  int t = t_lo, stg = 0;
-  if (t < t_hi) {
-    issue(t, 0);
-    finish(0);
-  }
-  __syncthreads();
-  while (t < t_hi) {
-    if (t + 1 < t_hi) issue(t + 1, stg ^ 1);
-    const unsigned char* qt = smem + stg * kStage;
-    const unsigned char* ot = qt + QT::bytes;
-    const RowSide* rs = reinterpret_cast<const RowSide*>(qt + 2 * QT::bytes);
-
-    // S = Q K^T and dP = dO V^T (32 rows x 32 keys; lane = key, registers = rows)
-    f32x16_t s = f32x16_t{}, dp = f32x16_t{};
-#pragma unroll
-    for (int dc = 0; dc < NDC; ++dc) s = mfma32(T{}, row_frag(qt, bs.row_base, 0, dc, QT::rowBytes), kreg[dc], s);
-#pragma unroll
-    for (int dc = 0; dc < NDC; ++dc) dp = mfma32(T{}, row_frag(ot, bs.row_base, 0, dc, QT::rowBytes), vreg[dc], dp);
-
-    // P = exp2(logit - lse) with the mask of the (row, key) pair; dS = P (dP - D)
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int rr = r4 * 8 + hf * 4 + e;
-        const RowSide sd = rs[rr];
-        float x = s[r4 * 4 + e] * cexp;
-        bool vis = key_ok;
-        if constexpr (MK == MI_ATTN_MASK_CAUSAL) vis = vis && j_lane <= sd.pos;
-        if constexpr (MK == MI_ATTN_MASK_WINDOW) vis = vis && j_lane <= sd.pos && j_lane >= sd.pos - p.window_left;
-        if constexpr (MK == MI_ATTN_MASK_DENSE) {
-          const int i = sd.pos - (Lk - Lq);
-          vis = vis && i >= 0;
-          const float mv = vis ? p.mask[static_cast<long>(i) * Lk + j_lane] : 0.f;
-          x = fmaf(mv, kLog2e, x);
-        }
-        if constexpr (MK == MI_ATTN_MASK_TOPK) {
-          vis = vis && j_lane <= sd.pos && rank_lane <= sd.tau;
-          x += zh_lane;
-        }
-        const float pv = vis ? fast_exp2(x - sd.lse2) : 0.f;
-        s[r4 * 4 + e] = pv;
-        dp[r4 * 4 + e] = pv * (dp[r4 * 4 + e] - sd.dsum);
-      }
-    }
-
-    // dV^T += dO^T P and dK^T += Q^T dS (d x 32 keys; contraction over the 32 rows)
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const u32x4_t pb = pack_half<T>(s, half);
-      const u32x4_t sb = pack_half<T>(dp, half);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        dvacc[db] = mfma32(T{}, tr_frag(ot, bs.tr0, bs.tr1, half, db, QT::rowBytes), pb, dvacc[db]);
-        dkacc[db] = mfma32(T{}, tr_frag(qt, bs.tr0, bs.tr1, half, db, QT::rowBytes), sb, dkacc[db]);
-      }
-    }
-
-    if (t + 1 < t_hi) finish(stg ^ 1);
-    __syncthreads();
-    ++t;
-    stg ^= 1;
-  }
-
-  if (!key_ok) return;
-  T* dk = static_cast<T*>(p.dk) + kv_row;
-  T* dv = static_cast<T*>(p.dv) + kv_row;
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    store_col<T>(dk, dkacc[db], db, hf, p.scale);
-    store_col<T>(dv, dvacc[db], db, hf, 1.f);
-  }
-}
-
-// ------------------------------------------------------------------ dQ
+// ------------------------------------------------------------------ dQ (+ row side arrays)
 template <typename T, int D, int MK>
 __global__ __launch_bounds__(kBT, 2) void dq_kernel(AttnParams p) {
   constexpr int BN = 64;
@@ -339,24 +135,41 @@ __global__ __launch_bounds__(kBT, 2) void dq_kernel(AttnParams p) {
   const long row_index = (static_cast<long>(b) * p.Hq + h_row) * Lq + i_row;
 
   u32x4_t qreg[NDC], oreg[NDC];  // Q^T and dO^T B operands of the lane's row
+  float dpart = 0.f;             // this lane half's part of D = rowsum(dO * O)
 #pragma unroll
   for (int dc = 0; dc < NDC; ++dc) {
-    u32x4_t x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+    u32x4_t x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u}, z = {0u, 0u, 0u, 0u};
     if (row_ok) {
-      x = *reinterpret_cast<const u32x4_t*>(static_cast<const T*>(p.q) + row_index * D + dc * 16 + hf * 8);
-      y = *reinterpret_cast<const u32x4_t*>(static_cast<const T*>(p.dout) + row_index * D + dc * 16 + hf * 8);
+      const long e = row_index * D + dc * 16 + hf * 8;
+      x = *reinterpret_cast<const u32x4_t*>(static_cast<const T*>(p.q) + e);
+      y = *reinterpret_cast<const u32x4_t*>(static_cast<const T*>(p.dout) + e);
+      z = *reinterpret_cast<const u32x4_t*>(static_cast<const T*>(p.out) + e);
     }
     qreg[dc] = x;
     oreg[dc] = y;
+    const T* yt = reinterpret_cast<const T*>(&y);
+    const T* zt = reinterpret_cast<const T*>(&z);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) dpart = fmaf(to_f32(yt[c]), to_f32(zt[c]), dpart);
   }
-  const float cexp = p.scale * kLog2e;  // signed
+  const float dsum = sum_halves(dpart);
+  const float cexp = p.scale * kLog2e;  // signed: no sign folded into an operand here
   const float lse = row_ok ? p.lse[row_index] : kNegInf;
   const float lse2 = lse == kNegInf ? __builtin_inff() : lse * kLog2e;  // dead rows: P = 0
-  const float dsum = row_ok ? p.dsum[row_index] : 0.f;
   const Mods md = make_mods<false>(p, cexp, b, h_row, i_row, pos, MK == MI_ATTN_MASK_DENSE);
   int32_t tau_row = 0;
   if constexpr (MK == MI_ATTN_MASK_TOPK) tau_row = min(p.tau[static_cast<long>(bg) * Lq + i_row], Lk - 1);
   const long bgk = static_cast<long>(bg) * Lk;
+
+  // side arrays of the dK/dV kernel, at row r = i * G + hh of this KV head
+  if (row_ok && hf == 0) {
+    const long nr = static_cast<long>(p.B) * p.Hq * Lq;
+    const long si = static_cast<long>(bg) * G * Lq + static_cast<long>(i_first) * G + rloc;
+    p.bwd_side[si] = -lse2;
+    p.bwd_side[nr + si] = dsum;
+    if constexpr (MK == MI_ATTN_MASK_TOPK) reinterpret_cast<int32_t*>(p.bwd_side)[2 * nr + si] = tau_row;
+    if constexpr (MK == MI_ATTN_MASK_DENSE) reinterpret_cast<int32_t*>(p.bwd_side)[2 * nr + si] = i_row;
+  }
 
   int lo, hi;
   key_range(MK, p.window_left, Lk, P0, P1, &lo, &hi);
@@ -452,19 +265,252 @@ __global__ __launch_bounds__(kBT, 2) void dq_kernel(AttnParams p) {
   for (int db = 0; db < NDB; ++db) store_col<T>(dq, dqacc[db], db, hf, p.scale);
 }
 
+// ------------------------------------------------------------------ dK, dV
+template <typename T, int D, int MK>
+__global__ __launch_bounds__(kBT, (D == 128 ? 1 : 2)) void dkdv_kernel(AttnParams p) {
+  using QT = BTile<D, 32>;
+  constexpr int NDC = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr bool kAux = MK == MI_ATTN_MASK_DENSE || MK == MI_ATTN_MASK_TOPK;
+  constexpr bool kCausal = MK == MI_ATTN_MASK_CAUSAL || MK == MI_ATTN_MASK_WINDOW || MK == MI_ATTN_MASK_TOPK;
+  constexpr int kStages = 3;
+  // stage: Q tile, dO tile, then the side values of its 32 rows: -LSE2 [32], D [32],
+  // threshold or query index [32], 128 bytes unused
+  constexpr int kSide = 512;
+  constexpr int kStage = 2 * QT::bytes + kSide;
+  static_assert(kStage % 512 == 0, "stage offsets keep the XOR-ed address bits");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages * kStage];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave;
+  const int l32 = lane & 31;
+  const int hf = lane >> 5;
+  const int Lq = p.Lq, Lk = p.Lk, G = p.G;
+  const int R = G * Lq;  // query rows of the KV head
+
+  const int nkb = (Lk + 127) / 128;
+  const unsigned lb = logical_block(blockIdx.x, gridDim.x);
+  const int kblk = static_cast<int>(lb % nkb);
+  const int bg = static_cast<int>(lb / nkb);
+  const int b = bg / p.Hkv, g = bg % p.Hkv;
+  const int j_lane = kblk * 128 + wave * 32 + l32;  // this lane's key (the column it owns)
+  const bool key_ok = j_lane < Lk;
+  const long kv_row = (static_cast<long>(bg) * Lk + (key_ok ? j_lane : 0)) * D;
+
+  // K^T and V^T B operands of the lane's key
+  u32x4_t kreg[NDC], vreg[NDC];
+#pragma unroll
+  for (int dc = 0; dc < NDC; ++dc) {
+    u32x4_t x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+    if (key_ok) {
+      x = *reinterpret_cast<const u32x4_t*>(static_cast<const T*>(p.k) + kv_row + dc * 16 + hf * 8);
+      y = *reinterpret_cast<const u32x4_t*>(static_cast<const T*>(p.v) + kv_row + dc * 16 + hf * 8);
+    }
+    kreg[dc] = x;
+    vreg[dc] = y;
+  }
+  int32_t rank_lane = 0x7fffffff;
+  float zh_lane = 0.f;
+  if constexpr (MK == MI_ATTN_MASK_TOPK) {
+    if (key_ok) {
+      rank_lane = p.rank[static_cast<long>(bg) * Lk + j_lane];
+      zh_lane = p.zero_hold[static_cast<long>(bg) * Lk + j_lane] * kLog2e;
+    }
+  }
+
+  // Rows that see the lane's key: r in [r_lo, r_hi). Row r = i * G + hh sits at position
+  // Lk - Lq + i, so "i >= j - (Lk - Lq)" is "r >= (j - (Lk - Lq)) * G".
+  const long off = static_cast<long>(Lk) - Lq;
+  auto row_at = [&](long i) { return static_cast<int>(min(static_cast<long>(R), max(0L, i * G))); };
+  int r_lo = key_ok ? 0 : R, r_hi = key_ok ? R : 0;
+  if (kCausal && key_ok) r_lo = row_at(j_lane - off);
+  if (MK == MI_ATTN_MASK_WINDOW && key_ok) r_hi = row_at(j_lane + static_cast<long>(p.window_left) - off + 1);
+  // the same for the block's keys together (row tiles to visit) and for all of them
+  // (tiles that need no per-element mask)
+  const int k_first = kblk * 128, k_last = min(Lk, k_first + 128) - 1;
+  int blk_lo = 0, blk_hi = R, all_lo = 0, all_hi = R;
+  if (kCausal) {
+    blk_lo = row_at(k_first - off);
+    all_lo = row_at(k_last - off);
+  }
+  if (MK == MI_ATTN_MASK_WINDOW) {
+    blk_hi = row_at(k_last + static_cast<long>(p.window_left) - off + 1);
+    all_hi = row_at(k_first + static_cast<long>(p.window_left) - off + 1);
+  }
+  const bool full_block = k_first + 128 <= Lk;
+  if (p.no_skip) { blk_lo = 0; blk_hi = R; }
+  const int t_lo = blk_lo / 32;
+  const int t_hi = blk_hi > blk_lo ? (blk_hi + 31) / 32 : t_lo;
+
+  // direct loads: lane fills 16-byte slot ps of row rr of its load rounds; rows of the
+  // batch are addressed through a buffer over all its query heads (past the end: zeros)
+  const T* qb_ptr = static_cast<const T*>(p.q) + static_cast<long>(b) * p.Hq * Lq * D;
+  const T* ob_ptr = static_cast<const T*>(p.dout) + static_cast<long>(b) * p.Hq * Lq * D;
+  const int batch_bytes = p.Hq * Lq * D * 2;  // < 2^31 (checked on the host)
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qb_ptr, batch_bytes);
+  const __amdgpu_buffer_rsrc_t ors = make_rsrc(ob_ptr, batch_bytes);
+  const long nr = static_cast<long>(p.B) * p.Hq * Lq;
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(p.bwd_side, static_cast<int>(nr * (kAux ? 12 : 8)));
+  const int side_base = static_cast<int>(static_cast<long>(bg) * R * 4);
+  // wave 0: lanes 0-31 load -LSE2 and lanes 32-63 D of the tile's rows; wave 1 (lanes
+  // 0-31): the thresholds or query indices
+  const int side_lane = wave == 0 ? (hf ? static_cast<int>(nr * 4) : 0) + side_base + l32 * 4
+                                  : static_cast<int>(nr * 8) + side_base + l32 * 4;
+  const unsigned smem_addr = __builtin_amdgcn_readfirstlane(lds_address(smem));
+  const int ps = lane % (D / 8);
+  auto issue = [&](int t, int stg) {
+    const int r0 = t * 32;
+    const unsigned sb = smem_addr + stg * kStage;
+#pragma unroll
+    for (int c = 0; c < QT::rounds; ++c) {
+      const int rr = (c * kBW + wave) * QT::rowsPerWaveLoad + lane / (D / 8);
+      const int r = r0 + rr;
+      const int i = r / G;
+      const long row = (static_cast<long>(g) * G + (r - i * G)) * Lq + i;  // within the batch
+      const int o = r < R ? static_cast<int>(row * D * 2) + ((ps ^ swz<D>(rr)) << 4) : batch_bytes;
+      const unsigned dst = sb + (c * kBW + wave) * 1024;
+      lds_dma16_at(qrs, dst, o, 0);
+      lds_dma16_at(ors, dst + QT::bytes, o, 0);
+    }
+    if (wave == 0) lds_dma4_at(srs, sb + 2 * QT::bytes, side_lane, r0 * 4);
+    if (kAux && wave == 1 && lane < 32) lds_dma4_at(srs, sb + 2 * QT::bytes + 256, side_lane, r0 * 4);
+  };
+  // direct loads one tile issues in this wave (the waits below count them)
+  const bool one_more = wave == 0 || (kAux && wave == 1);
+  auto wait_all_but_one_tile = [&]() {
+    if (one_more) __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(2 * QT::rounds + 1));
+    else __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(2 * QT::rounds));
+  };
+
+  const Bases<D> bs(lane);
+  const float cexp = p.scale * kLog2e;  // signed: no sign folded into an operand here
+  f32x16_t dkacc[NDB], dvacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dkacc[db] = f32x16_t{};
+    dvacc[db] = f32x16_t{};
+  }
+
+  // three-stage ring: tiles t + 1 and t + 2 load while tile t is computed
+  if (t_lo < t_hi) issue(t_lo, 0);
+  if (t_lo + 1 < t_hi) {
+    issue(t_lo + 1, 1);
+    wait_all_but_one_tile();
+  } else {
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+  __syncthreads();
+  int stg = 0;
+  for (int t = t_lo; t < t_hi; ++t) {
+    if (t + 2 < t_hi) issue(t + 2, stg == 0 ? 2 : stg - 1);
+    const unsigned char* qt = smem + stg * kStage;
+    const unsigned char* ot = qt + QT::bytes;
+    const float* side_m = reinterpret_cast<const float*>(qt + 2 * QT::bytes);
+    const float* side_d = side_m + 32;
+    const int32_t* side_a = reinterpret_cast<const int32_t*>(side_m + 64);
+    const int r0 = t * 32;
+
+    // S = Q K^T and dP = dO V^T (32 rows x 32 keys; lane = key, registers = rows)
+    f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc) s = mfma32(T{}, row_frag(qt, bs.row_base, 0, dc, QT::rowBytes), kreg[dc], s);
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc) dp = mfma32(T{}, row_frag(ot, bs.row_base, 0, dc, QT::rowBytes), vreg[dc], dp);
+
+    // P = exp2(logit - LSE2) where the pair is visible; dS = P (dP - D). Tiles whose rows
+    // all see every key of the block skip the per-element mask (a uniform branch).
+    const bool interior = !kAux && full_block && r0 >= all_lo && r0 + 32 <= all_hi && !p.no_skip;
+    const int lo = r_lo - r0, hi = r_hi - r0;  // visible rows of the lane's key, tile-relative
+    float4 mlv[4], ddv[4];
+    int4 axv[4];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int rb = r4 * 8 + hf * 4;  // first of the 4 consecutive rows of these registers
+      mlv[r4] = *reinterpret_cast<const float4*>(side_m + rb);
+      ddv[r4] = *reinterpret_cast<const float4*>(side_d + rb);
+      axv[r4] = kAux ? *reinterpret_cast<const int4*>(side_a + rb) : int4{0, 0, 0, 0};
+    }
+    if (__builtin_amdgcn_readfirstlane(static_cast<int>(interior))) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const float mls[4] = {mlv[r4].x, mlv[r4].y, mlv[r4].z, mlv[r4].w};
+        const float dds[4] = {ddv[r4].x, ddv[r4].y, ddv[r4].z, ddv[r4].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float pv = fast_exp2(fmaf(s[r4 * 4 + e], cexp, mls[e]));
+          dp[r4 * 4 + e] = pv * (dp[r4 * 4 + e] - dds[e]);
+          s[r4 * 4 + e] = pv;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int rb = r4 * 8 + hf * 4;
+        const float mls[4] = {mlv[r4].x, mlv[r4].y, mlv[r4].z, mlv[r4].w};
+        const float dds[4] = {ddv[r4].x, ddv[r4].y, ddv[r4].z, ddv[r4].w};
+        const int axs[4] = {axv[r4].x, axv[r4].y, axv[r4].z, axv[r4].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float x = fmaf(s[r4 * 4 + e], cexp, mls[e]);
+          bool vis = rb + e >= lo && rb + e < hi;
+          if constexpr (MK == MI_ATTN_MASK_DENSE) {
+            const float mv = vis ? p.mask[static_cast<long>(axs[e]) * Lk + j_lane] : 0.f;
+            x = fmaf(mv, kLog2e, x);
+          }
+          if constexpr (MK == MI_ATTN_MASK_TOPK) {
+            vis = vis && rank_lane <= axs[e];
+            x += zh_lane;
+          }
+          // selects, not branches; hidden rows past the last one read other rows' side
+          // values, and nothing of them may reach dS
+          const float pv = fast_exp2(vis ? x : kNegInf);
+          dp[r4 * 4 + e] = vis ? pv * (dp[r4 * 4 + e] - dds[e]) : 0.f;
+          s[r4 * 4 + e] = pv;
+        }
+      }
+    }
+
+    // dV^T += dO^T P and dK^T += Q^T dS (d x 32 keys; contraction over the 32 rows)
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const u32x4_t pb = pack_half<T>(s, half);
+      const u32x4_t sb = pack_half<T>(dp, half);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        dvacc[db] = mfma32(T{}, tr_frag(ot, bs.tr0, bs.tr1, half, db, QT::rowBytes), pb, dvacc[db]);
+        dkacc[db] = mfma32(T{}, tr_frag(qt, bs.tr0, bs.tr1, half, db, QT::rowBytes), sb, dkacc[db]);
+      }
+    }
+
+    // tile t + 1 has landed (this wave's part); every wave is done with this stage
+    if (t + 2 < t_hi) wait_all_but_one_tile();
+    else __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    stg = stg == 2 ? 0 : stg + 1;
+  }
+
+  if (!key_ok) return;
+  T* dk = static_cast<T*>(p.dk) + kv_row;
+  T* dv = static_cast<T*>(p.dv) + kv_row;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    store_col<T>(dk, dkacc[db], db, hf, p.scale);
+    store_col<T>(dv, dvacc[db], db, hf, 1.f);
+  }
+}
+
 template <typename T, int D>
 hipError_t launch_bwd_t(const AttnParams& p, hipStream_t s) {
-  const long rows = static_cast<long>(p.B) * p.Hq * p.Lq;
-  hipLaunchKernelGGL(dsum_kernel<T>, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, s, p);
-  const long nkb = (p.Lk + 127) / 128;
-  const dim3 g1(static_cast<unsigned>(static_cast<long>(p.B) * p.Hkv * nkb));
   const long nqb = (p.Lq + p.q_per_block - 1) / p.q_per_block;
-  const dim3 g2(static_cast<unsigned>(static_cast<long>(p.B) * p.Hkv * nqb));
+  const dim3 gq(static_cast<unsigned>(static_cast<long>(p.B) * p.Hkv * nqb));
+  const long nkb = (p.Lk + 127) / 128;
+  const dim3 gk(static_cast<unsigned>(static_cast<long>(p.B) * p.Hkv * nkb));
   switch (p.mask_kind) {
 #define MI_BWD_CASE(KIND)                                                              \
   case KIND:                                                                           \
-    hipLaunchKernelGGL((dkdv_kernel<T, D, KIND>), g1, dim3(kBT), 0, s, p);             \
-    hipLaunchKernelGGL((dq_kernel<T, D, KIND>), g2, dim3(kBT), 0, s, p);               \
+    hipLaunchKernelGGL((dq_kernel<T, D, KIND>), gq, dim3(kBT), 0, s, p);               \
+    hipLaunchKernelGGL((dkdv_kernel<T, D, KIND>), gk, dim3(kBT), 0, s, p);             \
     break;
     MI_BWD_CASE(MI_ATTN_MASK_NONE)
     MI_BWD_CASE(MI_ATTN_MASK_CAUSAL)

@@ -127,6 +127,16 @@ __device__ __forceinline__ void lds_dma16_at(__amdgpu_buffer_rsrc_t rs, unsigned
                : "memory", "m0");
 }
 
+// 4-byte form (buffer_load_dword ... lds): lane i's dword lands at lds_addr + 4 * i.
+__device__ __forceinline__ void lds_dma4_at(__amdgpu_buffer_rsrc_t rs, unsigned lds_addr, int voffset, int soffset) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_addr);
+  const int so = __builtin_amdgcn_readfirstlane(soffset);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :
+               : "s"(m0), "v"(voffset), "s"(rs), "s"(so)
+               : "memory", "m0");
+}
+
 // The same from a per-lane 64-bit global address (global_load_lds_dwordx4): lane i's 16
 // bytes from src land at lds_addr + 16 * i. Used where the rows of one tile come from
 // unrelated places (cache pages), which a 32-bit buffer offset cannot always reach.
