@@ -359,19 +359,42 @@ __global__ __launch_bounds__(kBT, (D == 128 ? 1 : 2)) void dkdv_kernel(AttnParam
                                   : static_cast<int>(nr * 8) + side_base + l32 * 4;
   const unsigned smem_addr = __builtin_amdgcn_readfirstlane(lds_address(smem));
   const int ps = lane % (D / 8);
+  // The lane's row in load round c of the next tile to load, r = i * G + hh, kept as (i,
+  // hh, byte offset of the row in the batch) and advanced by 32 rows per tile without a
+  // division. Tiles are loaded in order from t_lo.
+  int st_i[QT::rounds], st_h[QT::rounds];
+  unsigned st_o[QT::rounds];
+  int sw[QT::rounds];
+#pragma unroll
+  for (int c = 0; c < QT::rounds; ++c) {
+    const int rr = (c * kBW + wave) * QT::rowsPerWaveLoad + lane / (D / 8);
+    const int r = t_lo * 32 + rr;
+    st_i[c] = r / G;
+    st_h[c] = r - st_i[c] * G;
+    st_o[c] = static_cast<unsigned>(((static_cast<long>(g) * G + st_h[c]) * Lq + st_i[c]) * D * 2);
+    sw[c] = (ps ^ swz<D>(rr)) << 4;
+  }
+  const int adv_i = 32 / G, adv_h = 32 % G;
+  const unsigned adv_o = static_cast<unsigned>((adv_i + static_cast<long>(adv_h) * Lq) * D * 2);
+  const unsigned wrap_o = static_cast<unsigned>((1 - static_cast<long>(G) * Lq) * D * 2);
   auto issue = [&](int t, int stg) {
     const int r0 = t * 32;
     const unsigned sb = smem_addr + stg * kStage;
 #pragma unroll
     for (int c = 0; c < QT::rounds; ++c) {
-      const int rr = (c * kBW + wave) * QT::rowsPerWaveLoad + lane / (D / 8);
-      const int r = r0 + rr;
-      const int i = r / G;
-      const long row = (static_cast<long>(g) * G + (r - i * G)) * Lq + i;  // within the batch
-      const int o = r < R ? static_cast<int>(row * D * 2) + ((ps ^ swz<D>(rr)) << 4) : batch_bytes;
+      // rows past the last one (i >= Lq) read zeros (the offset is past the buffer)
+      const int o = st_i[c] < Lq ? static_cast<int>(st_o[c]) + sw[c] : batch_bytes;
       const unsigned dst = sb + (c * kBW + wave) * 1024;
       lds_dma16_at(qrs, dst, o, 0);
       lds_dma16_at(ors, dst + QT::bytes, o, 0);
+      st_h[c] += adv_h;
+      st_i[c] += adv_i;
+      st_o[c] += adv_o;
+      if (st_h[c] >= G) {
+        st_h[c] -= G;
+        st_i[c] += 1;
+        st_o[c] += wrap_o;
+      }
     }
     if (wave == 0) lds_dma4_at(srs, sb + 2 * QT::bytes, side_lane, r0 * 4);
     if (kAux && wave == 1 && lane < 32) lds_dma4_at(srs, sb + 2 * QT::bytes + 256, side_lane, r0 * 4);
@@ -414,9 +437,19 @@ __global__ __launch_bounds__(kBT, (D == 128 ? 1 : 2)) void dkdv_kernel(AttnParam
     // S = Q K^T and dP = dO V^T (32 rows x 32 keys; lane = key, registers = rows)
     f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll
-    for (int dc = 0; dc < NDC; ++dc) s = mfma32(T{}, row_frag(qt, bs.row_base, 0, dc, QT::rowBytes), kreg[dc], s);
+    for (int dc = 0; dc < NDC; ++dc) {
+      s = mfma32(T{}, row_frag(qt, bs.row_base, 0, dc, QT::rowBytes), kreg[dc], s);
+      dp = mfma32(T{}, row_frag(ot, bs.row_base, 0, dc, QT::rowBytes), vreg[dc], dp);
+    }
+    // each MFMA overlaps the LDS read of the operand two MFMAs ahead
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
 #pragma unroll
-    for (int dc = 0; dc < NDC; ++dc) dp = mfma32(T{}, row_frag(ot, bs.row_base, 0, dc, QT::rowBytes), vreg[dc], dp);
+    for (int i = 0; i < 2 * NDC - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
 
     // P = exp2(logit - LSE2) where the pair is visible; dS = P (dP - D). Tiles whose rows
     // all see every key of the block skip the per-element mask (a uniform branch).
@@ -472,6 +505,7 @@ __global__ __launch_bounds__(kBT, (D == 128 ? 1 : 2)) void dkdv_kernel(AttnParam
     }
 
     // dV^T += dO^T P and dK^T += Q^T dS (d x 32 keys; contraction over the 32 rows)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const u32x4_t pb = pack_half<T>(s, half);
@@ -482,6 +516,15 @@ __global__ __launch_bounds__(kBT, (D == 128 ? 1 : 2)) void dkdv_kernel(AttnParam
         dkacc[db] = mfma32(T{}, tr_frag(qt, bs.tr0, bs.tr1, half, db, QT::rowBytes), sb, dkacc[db]);
       }
     }
+    // the transposed reads (two per MFMA) run two MFMAs ahead
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 4 * NDB - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
 
     // tile t + 1 has landed (this wave's part); every wave is done with this stage
     if (t + 2 < t_hi) wait_all_but_one_tile();
