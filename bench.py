@@ -10,7 +10,8 @@ The same line carries:
                 timed with events on the stream the library launches on;
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload;
   configs       every other workload (decode GB/s, long causal, top-k, dense window,
-                tiny fp32), the paged serving batch of attn_fwd_varlen and the attn_fwd_ex
+                tiny fp32), the paged serving batch of attn_fwd_varlen (plain, and with ALiBi +
+                softcap) and the attn_fwd_ex
                 workloads (transposed KV cache, ALiBi + softcap, non-causal top-k, per-head
                 mask; each with the plain call's time on the same data) and the backward
                 (attn_bwd) on the long causal and prefill workloads. Parity at these
@@ -303,9 +304,10 @@ def paged_pairs_and_keys(p):
     return pairs * p.Hq, keys
 
 
-def bench_paged_config(name, iters=20):
+def bench_paged_config(name, iters=20, modifiers=False):
     """attn_fwd_varlen on a paged serving batch: time, algorithmic TFLOP/s and GB/s, and
-    the fraction of the roofline time max(flops / MFMA peak, bytes / HBM peak)."""
+    the fraction of the roofline time max(flops / MFMA peak, bytes / HBM peak). With
+    ``modifiers`` the call also applies ALiBi (the geometric slopes) and softcap 30."""
     import torch
     import masked_flashattention_forward_amd as mfa
     import synth
@@ -324,11 +326,13 @@ def bench_paged_config(name, iters=20):
     bt = None if p.block_table is None else torch.from_numpy(p.block_table).cuda()
     out = torch.empty_like(q)
     lse = torch.empty((p.total_q, p.Hq), dtype=torch.float32, device="cuda")
+    sl = torch.from_numpy(synth.alibi_slopes(p.Hq)).cuda() if modifiers else None
+    cap = 30.0 if modifiers else 0.0
 
     def call():
         mfa.attn_fwd_varlen(q, k, v, cu_q, cu_k, max_seqlen_q=p.max_seqlen_q, max_seqlen_k=p.max_seqlen_k,
                             block_table=bt, k_new=kn, v_new=vn, scale=p.scale, mask_kind=p.mask_kind,
-                            window_left=p.window_left, out=out, lse=lse)
+                            window_left=p.window_left, alibi_slopes=sl, softcap=cap, out=out, lse=lse)
 
     for _ in range(4):
         call()
@@ -347,6 +351,7 @@ def bench_paged_config(name, iters=20):
     t_roof = max(flops / (PEAK_BF16_TFLOPS * 1e12), byts / (PEAK_HBM_GBS * 1e9)) * 1e3
     res = {"workload": p.name, "num_seqs": p.num_seqs, "total_q": p.total_q, "total_k": int(p.k_lens.sum()),
            "Hq": p.Hq, "Hkv": p.Hkv, "d": p.d, "page_size": p.page_size, "dtype": p.dtype, "mask": p.mask_kind,
+           "alibi": modifiers, "softcap": cap,
            "us": round(ms * 1e3, 2), "tflops": round(flops / ms / 1e9, 2),
            "pct_mfma_peak": round(100 * flops / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
            "gbs": round(byts / ms / 1e6, 1), "pct_hbm_peak": round(100 * byts / ms / 1e6 / PEAK_HBM_GBS, 2),
@@ -452,6 +457,8 @@ def main():
             configs[name] = bench_config(name)
         log("config serve (paged varlen)")
         configs["serve"] = bench_paged_config("serve")
+        log("config serve with ALiBi + softcap (paged varlen)")
+        configs["serve_alibi_softcap"] = bench_paged_config("serve", modifiers=True)
         for name in synth.EX_NAMES:
             log(f"config {name} (attn_fwd_ex)")
             configs[name] = bench_ex_config(name)

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define MI_ATTN_ABI_VERSION 5
+#define MI_ATTN_ABI_VERSION 6
 
 /* element types of q, k, v, out */
 #define MI_ATTN_F32 0
@@ -150,6 +150,10 @@ int dynamic_mask_topk(const float* zero_hold, int B, int H, int Lq, int Lk, int 
  *   page_size     keys per page, a power of two (paged form; ignored when packed).
  *   kv_rows       pages (paged) or rows (packed) held by k and v, >= 1.
  *   mask_kind     MI_ATTN_MASK_NONE, _CAUSAL or _WINDOW (window_left >= 0).
+ *   alibi_slopes, softcap  the score modifiers the vLLM page lists in the varlen call it
+ *                 quotes, as in attn_fwd_ex (device fp32 [Hq] or NULL; softcap finite,
+ *                 >= 0, 0 = off), with each sequence's own positions: key j of sequence
+ *                 s gets -slope_h * |Lk_s - Lq_s + i - j|.
  *   dtype         MI_ATTN_F16 or MI_ATTN_BF16, d 64 or 128; fp32 accumulation.
  *
  *   The int32 device arrays are not read on the host. If they break the rules above,
@@ -161,7 +165,7 @@ int dynamic_mask_topk(const float* zero_hold, int B, int H, int Lq, int Lk, int 
  *   values.
  *   Returns MI_ATTN_OK, MI_ATTN_EINVAL (negative sizes, Hq % Hkv != 0, a required pointer
  *   NULL, exactly one of k_new/v_new given, page_size not a power of two, non-finite
- *   scale, window_left < 0, unknown dtype or mask_kind), MI_ATTN_EUNSUPPORTED (fp32, the
+ *   scale, window_left < 0, softcap negative or not finite, unknown dtype or mask_kind), MI_ATTN_EUNSUPPORTED (fp32, the
  *   dense or top-k mask, head dim other than 64/128) or MI_ATTN_EHIP.
  */
 int attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
@@ -170,7 +174,8 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, floa
                     int num_seqs, int total_q, int Hq, int Hkv, int d, float scale,
                     int mask_kind, int window_left,
                     const int32_t* block_table, int max_pages, int page_size, int kv_rows,
-                    const void* k_new, const void* v_new, int dtype, void* stream);
+                    const void* k_new, const void* v_new, const float* alibi_slopes, float softcap,
+                    int dtype, void* stream);
 
 /*
  * attn_fwd_ex: attn_fwd with general layouts, per-head masks and score modifiers.

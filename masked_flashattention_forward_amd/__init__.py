@@ -26,7 +26,7 @@ class MiAttnError(RuntimeError):
         self.code = code
 
 
-ABI_VERSION = 5  # MI_ATTN_ABI_VERSION of include/mi_attn.h that this binding matches
+ABI_VERSION = 6  # MI_ATTN_ABI_VERSION of include/mi_attn.h that this binding matches
 
 
 class AttnPlan(ctypes.Structure):
@@ -58,7 +58,7 @@ _SIGS = {
                           + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "attn_fwd_varlen": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_void_p, ctypes.c_int] * 2
                         + [ctypes.c_int] * 5 + [ctypes.c_float] + [ctypes.c_int] * 2
-                        + [ctypes.c_void_p] + [ctypes.c_int] * 3 + [ctypes.c_void_p] * 2
+                        + [ctypes.c_void_p] + [ctypes.c_int] * 3 + [ctypes.c_void_p] * 3 + [ctypes.c_float]
                         + [ctypes.c_int, ctypes.c_void_p]),
     "attn_fwd_ex": (ctypes.c_int, [ctypes.POINTER(AttnFwdArgs), ctypes.c_void_p]),
     "attn_bwd": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_void_p] + [ctypes.c_void_p] * 4
@@ -304,7 +304,7 @@ def attn_bwd(q, k, v, out, lse, dout, *, scale=None, mask_kind="causal", window_
 
 def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, *, max_seqlen_q=None, max_seqlen_k=None,
                     block_table=None, k_new=None, v_new=None, scale=None, mask_kind="causal", window_left=0,
-                    out=None, lse=None, return_lse=True, stream=None):
+                    alibi_slopes=None, softcap=0.0, out=None, lse=None, return_lse=True, stream=None):
     """Masked attention over a batch of sequences of different lengths (attn_fwd_varlen).
 
     q ``[total_q, Hq, d]`` token-major; cu_seqlens_q/k int32 ``[num_seqs + 1]`` on q's
@@ -312,8 +312,9 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, *, max_seqlen_q=None, m
     ``[num_pages, page_size, Hkv, d]``; without it they are packed ``[total_k, Hkv, d]``.
     ``k_new``/``v_new`` ``[total_q, Hkv, d]`` select the two-source form (the last Lq keys
     of each sequence). ``max_seqlen_q/k`` are host ints; when None they are read from the
-    cu_seqlens tensors, which synchronises with the device. Returns ``(out, lse)``, lse
-    fp32 ``[total_q, Hq]``.
+    cu_seqlens tensors, which synchronises with the device. ``alibi_slopes`` fp32 ``[Hq]``
+    and ``softcap`` as in attn_fwd_ex, on each sequence's own positions. Returns
+    ``(out, lse)``, lse fp32 ``[total_q, Hq]``.
     """
     import torch
 
@@ -364,12 +365,17 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, *, max_seqlen_q=None, m
     if lse is not None and (tuple(lse.shape) != (total_q, Hq) or lse.dtype != torch.float32
                             or not lse.is_contiguous()):
         raise ValueError("lse must be a contiguous fp32 [total_q, Hq] tensor")
+    if alibi_slopes is not None:
+        dev_tensor("alibi_slopes", alibi_slopes, 1, torch.float32)
+        if alibi_slopes.numel() != Hq:
+            raise ValueError("alibi_slopes must be [Hq]")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     rc = lib().attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
                                int(max_seqlen_q), _ptr(cu_seqlens_k), int(max_seqlen_k), num_seqs, total_q, Hq,
                                Hkv, d, float(scale), mk, int(window_left), _ptr(block_table), int(max_pages),
-                               int(page_size), int(kv_rows), _ptr(k_new), _ptr(v_new), _dtype_code(q),
+                               int(page_size), int(kv_rows), _ptr(k_new), _ptr(v_new), _ptr(alibi_slopes),
+                               float(softcap), _dtype_code(q),
                                _stream_handle(q.device, stream))
     _check(rc)
     return out, lse

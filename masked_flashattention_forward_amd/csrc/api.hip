@@ -409,7 +409,7 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, floa
                     const int32_t* cu_seqlens_q, int max_seqlen_q, const int32_t* cu_seqlens_k, int max_seqlen_k,
                     int num_seqs, int total_q, int Hq, int Hkv, int d, float scale, int mask_kind, int window_left,
                     const int32_t* block_table, int max_pages, int page_size, int kv_rows, const void* k_new,
-                    const void* v_new, int dtype, void* stream) {
+                    const void* v_new, const float* alibi_slopes, float softcap, int dtype, void* stream) {
   g_err.clear();
   if (num_seqs < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
     return fail(MI_ATTN_EINVAL, "num_seqs, total_q and max_seqlen_q/k must be >= 0");
@@ -422,6 +422,7 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, floa
     return fail(MI_ATTN_EINVAL, "window_left must be >= 0 (got %d)", window_left);
   if (!std::isfinite(scale)) return fail(MI_ATTN_EINVAL, "scale must be finite");
   if ((k_new == nullptr) != (v_new == nullptr)) return fail(MI_ATTN_EINVAL, "give both k_new and v_new, or neither");
+  if (!std::isfinite(softcap) || softcap < 0.f) return fail(MI_ATTN_EINVAL, "softcap must be finite and >= 0");
   if (kv_rows < 1) return fail(MI_ATTN_EINVAL, "kv_rows must be >= 1 (got %d)", kv_rows);
   int page_shift = 0;
   if (block_table != nullptr) {
@@ -490,6 +491,8 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, floa
   p.q = q; p.k = k; p.v = v; p.out = out; p.lse = lse;
   p.B = 1; p.Hq = Hq; p.Hkv = Hkv; p.Lq = 0; p.Lk = 0; p.d = d; p.G = G;
   p.scale = scale; p.mask_kind = mask_kind; p.window_left = window_left;
+  p.alibi = alibi_slopes;
+  p.softcap = softcap;
   p.no_skip = g_no_skip;
   p.splits = 1;
   p.block_n = prefill_block_n(d);

@@ -388,14 +388,20 @@ void launch_decode_d(const AttnParams& p, hipStream_t s) {
 }
 
 // varlen items of decode type: grid = items x KV heads, no split dimension
-template <typename T, int D>
-void launch_decode_varlen_d(const AttnParams& p, hipStream_t s) {
+template <typename T, int D, bool EXT>
+void launch_decode_varlen_e(const AttnParams& p, hipStream_t s) {
   dim3 grid(static_cast<unsigned>(static_cast<long>(p.vl_items_cap) * p.Hkv)), block(kDecThreads);
   switch (p.mask_kind) {
-    case MI_ATTN_MASK_NONE: hipLaunchKernelGGL((decode_kernel<T, D, 0, true>), grid, block, 0, s, p); break;
-    case MI_ATTN_MASK_CAUSAL: hipLaunchKernelGGL((decode_kernel<T, D, 1, true>), grid, block, 0, s, p); break;
-    default: hipLaunchKernelGGL((decode_kernel<T, D, 2, true>), grid, block, 0, s, p); break;
+    case MI_ATTN_MASK_NONE: hipLaunchKernelGGL((decode_kernel<T, D, 0, true, EXT>), grid, block, 0, s, p); break;
+    case MI_ATTN_MASK_CAUSAL: hipLaunchKernelGGL((decode_kernel<T, D, 1, true, EXT>), grid, block, 0, s, p); break;
+    default: hipLaunchKernelGGL((decode_kernel<T, D, 2, true, EXT>), grid, block, 0, s, p); break;
   }
+}
+template <typename T, int D>
+void launch_decode_varlen_d(const AttnParams& p, hipStream_t s) {
+  // score modifiers (ALiBi, softcap) run the EXT instances
+  if (has_mods(p)) launch_decode_varlen_e<T, D, true>(p, s);
+  else launch_decode_varlen_e<T, D, false>(p, s);
 }
 
 }  // namespace

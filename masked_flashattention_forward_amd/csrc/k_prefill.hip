@@ -694,7 +694,7 @@ hipError_t launch_prefill_t(const AttnParams& p, hipStream_t s) {
 
 // Varlen items of prefill type (query runs longer than 32 rows per KV head); the LSE
 // merge of split units runs separately.
-template <typename T>
+template <typename T, bool EXT>
 hipError_t launch_prefill_varlen_t(const AttnParams& p, hipStream_t s) {
   const long blocks = (static_cast<long>(p.vl_items_cap) * p.Hkv + 7) / 8 * 8;  // whole rounds of 8 XCDs
   if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
@@ -702,22 +702,22 @@ hipError_t launch_prefill_varlen_t(const AttnParams& p, hipStream_t s) {
   if (p.d == 128) {
     switch (p.mask_kind) {
       case MI_ATTN_MASK_NONE:
-        hipLaunchKernelGGL((prefill_kernel<T, 128, 64, 0, false, true>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((prefill_kernel<T, 128, 64, 0, false, true, EXT>), grid, block, 0, s, p);
         break;
       case MI_ATTN_MASK_CAUSAL:
-        hipLaunchKernelGGL((prefill_kernel<T, 128, 64, 1, false, true>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((prefill_kernel<T, 128, 64, 1, false, true, EXT>), grid, block, 0, s, p);
         break;
-      default: hipLaunchKernelGGL((prefill_kernel<T, 128, 64, 2, false, true>), grid, block, 0, s, p); break;
+      default: hipLaunchKernelGGL((prefill_kernel<T, 128, 64, 2, false, true, EXT>), grid, block, 0, s, p); break;
     }
   } else {
     switch (p.mask_kind) {
       case MI_ATTN_MASK_NONE:
-        hipLaunchKernelGGL((prefill_kernel<T, 64, 64, 0, false, true>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((prefill_kernel<T, 64, 64, 0, false, true, EXT>), grid, block, 0, s, p);
         break;
       case MI_ATTN_MASK_CAUSAL:
-        hipLaunchKernelGGL((prefill_kernel<T, 64, 64, 1, false, true>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((prefill_kernel<T, 64, 64, 1, false, true, EXT>), grid, block, 0, s, p);
         break;
-      default: hipLaunchKernelGGL((prefill_kernel<T, 64, 64, 2, false, true>), grid, block, 0, s, p); break;
+      default: hipLaunchKernelGGL((prefill_kernel<T, 64, 64, 2, false, true, EXT>), grid, block, 0, s, p); break;
     }
   }
   return hipGetLastError();
@@ -726,8 +726,10 @@ hipError_t launch_prefill_varlen_t(const AttnParams& p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_prefill_varlen(const AttnParams& p, int dtype, hipStream_t s) {
-  if (dtype == MI_ATTN_BF16) return launch_prefill_varlen_t<bf16_t>(p, s);
-  if (dtype == MI_ATTN_F16) return launch_prefill_varlen_t<f16_t>(p, s);
+  // score modifiers (ALiBi, softcap) run the EXT instances
+  const bool ext = has_mods(p);
+  if (dtype == MI_ATTN_BF16) return ext ? launch_prefill_varlen_t<bf16_t, true>(p, s) : launch_prefill_varlen_t<bf16_t, false>(p, s);
+  if (dtype == MI_ATTN_F16) return ext ? launch_prefill_varlen_t<f16_t, true>(p, s) : launch_prefill_varlen_t<f16_t, false>(p, s);
   return hipErrorInvalidValue;
 }
 

@@ -24,12 +24,16 @@ Readings (the page names the arguments only; everything below is the plainest re
   holds the first ``Lk - Lq``. A sequence with fewer keys than queries has no such
   split; its rows are returned fully masked (output 0, LSE -inf).
 * LSE is returned token-major, ``[total_q, Hq]``.
+* The score modifiers of the same call (``alibi_slopes``, ``softcap``) apply as in
+  ``general.py``, on each sequence's own positions: the ALiBi distance of key ``j`` from
+  query ``i`` of sequence ``s`` is ``|Lk_s - Lq_s + i - j|``.
 """
 from __future__ import annotations
 
 import numpy as np
 
 from .attention import attention_ref
+from .general import general_attention_ref
 
 
 def gather_sequence_kv(cache: np.ndarray, table_row, page_size: int, n: int) -> np.ndarray:
@@ -48,12 +52,13 @@ def _sequence_kv(cache, block_table, page_size, cu_k, s, n):
 
 
 def paged_attention_ref(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, block_table, page_size, scale, kind,
-                        *, window_left=0, k_new=None, v_new=None):
+                        *, window_left=0, k_new=None, v_new=None, alibi_slopes=None, softcap=0.0):
     """q ``[total_q, Hq, d]``; returns out ``[total_q, Hq, d]`` and lse ``[total_q, Hq]``.
 
     ``block_table`` ``[num_seqs, max_pages]`` (or None for packed K/V); ``kind`` is one of
-    the key-position masks ("none", "causal", "window").
+    the key-position masks ("none", "causal", "window"); ``alibi_slopes`` ``[Hq]`` or None.
     """
+    mods = alibi_slopes is not None or softcap > 0.0
     q = np.asarray(q, dtype=np.float64)
     total_q, Hq, d = q.shape
     cu_q = np.asarray(cu_seqlens_q, dtype=np.int64)
@@ -80,8 +85,12 @@ def paged_attention_ref(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, block_t
         if Lk == 0:
             continue  # no key at all: every row is fully masked
         Q = q[q0:q1].transpose(1, 0, 2)[None]
-        o, l = attention_ref(Q, K.reshape(1, Hkv, Lk, d), V.reshape(1, Hkv, Lk, d), scale, kind,
-                             window_left=window_left)
+        if mods:
+            o, l = general_attention_ref(Q, K.reshape(1, Hkv, Lk, d), V.reshape(1, Hkv, Lk, d), scale, kind,
+                                         window_left=window_left, alibi_slopes=alibi_slopes, softcap=softcap)
+        else:
+            o, l = attention_ref(Q, K.reshape(1, Hkv, Lk, d), V.reshape(1, Hkv, Lk, d), scale, kind,
+                                 window_left=window_left)
         out[q0:q1] = o[0].transpose(1, 0, 2)
         lse[q0:q1] = l[0].T
     return out, lse

@@ -83,7 +83,7 @@ def compare(p: synth.Problem, out, lse, ref_out, ref_lse, rows=None, heads=None,
 
 
 # ---------------------------------------------------------------- varlen / paged problems
-def run_gpu_paged(p: synth.PagedProblem, *, out_fill=None, max_seqlen_k=None):
+def run_gpu_paged(p: synth.PagedProblem, *, out_fill=None, max_seqlen_k=None, alibi=None, softcap=0.0):
     import torch
     import masked_flashattention_forward_amd as mfa
     q, k, v = (to_device(getattr(p, n), p.dtype) for n in ("q", "k", "v"))
@@ -98,21 +98,26 @@ def run_gpu_paged(p: synth.PagedProblem, *, out_fill=None, max_seqlen_k=None):
     if out_fill is not None:
         out.fill_(out_fill)
         lse.fill_(out_fill)
+    sl = None if alibi is None else torch.from_numpy(np.asarray(alibi, dtype=np.float32)).cuda()
     mfa.attn_fwd_varlen(q, k, v, cu_q, cu_k, max_seqlen_q=p.max_seqlen_q,
                         max_seqlen_k=p.max_seqlen_k if max_seqlen_k is None else max_seqlen_k,
                         block_table=bt, k_new=kn, v_new=vn, scale=p.scale, mask_kind=p.mask_kind,
-                        window_left=p.window_left, out=out, lse=lse)
+                        window_left=p.window_left, alibi_slopes=sl, softcap=softcap, out=out, lse=lse)
     torch.cuda.synchronize()
     return out_to_f64(out, p.dtype), lse.cpu().numpy().astype(np.float64)
 
 
-def run_oracle_paged(p: synth.PagedProblem, seqs=None):
+def run_oracle_paged(p: synth.PagedProblem, seqs=None, alibi=None, softcap=0.0):
     """fp64 oracle; with ``seqs`` only those sequences are computed (their K/V rows are
-    gathered from the cache in storage form first) and the other rows are NaN."""
+    gathered from the cache in storage form first) and the other rows are NaN. ``alibi``
+    (fp32 slopes) and ``softcap`` as passed to the GPU call."""
+    mods = dict(alibi_slopes=None if alibi is None else np.asarray(alibi, dtype=np.float32).astype(np.float64),
+                softcap=float(np.float32(softcap)))
     if seqs is None:
         return oracle.paged_attention_ref(p.f64("q"), p.f64("k"), p.f64("v"), p.cu_seqlens_q, p.cu_seqlens_k,
                                           p.block_table, p.page_size, p.scale, p.mask_kind,
-                                          window_left=p.window_left, k_new=p.f64("k_new"), v_new=p.f64("v_new"))
+                                          window_left=p.window_left, k_new=p.f64("k_new"), v_new=p.f64("v_new"),
+                                          **mods)
     out = np.full((p.total_q, p.Hq, p.d), np.nan)
     lse = np.full((p.total_q, p.Hq), np.nan)
     for s in seqs:
@@ -135,6 +140,6 @@ def run_oracle_paged(p: synth.PagedProblem, seqs=None):
             f(p.q[q0:q1]), f(kk), f(vv), [0, q1 - q0], [0, Lk], None, 0, p.scale, p.mask_kind,
             window_left=p.window_left,
             k_new=None if not p.two_source else f(p.k_new[q0:q1]),
-            v_new=None if not p.two_source else f(p.v_new[q0:q1]))
+            v_new=None if not p.two_source else f(p.v_new[q0:q1]), **mods)
         out[q0:q1], lse[q0:q1] = o, l
     return out, lse

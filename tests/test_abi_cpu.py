@@ -244,7 +244,8 @@ def varlen_rc(lib, **kw):
     """attn_fwd_varlen with NULL device pointers: only host validation can run."""
     a = dict(q=None, k=None, v=None, out=None, lse=None, cu_q=None, max_q=1, cu_k=None, max_k=8, num_seqs=2,
              total_q=0, Hq=4, Hkv=2, d=128, scale=0.1, mask_kind=1, window_left=0, block_table=None,
-             max_pages=4, page_size=16, kv_rows=8, k_new=None, v_new=None, dtype=2, stream=None)
+             max_pages=4, page_size=16, kv_rows=8, k_new=None, v_new=None, alibi_slopes=None, softcap=0.0, dtype=2,
+             stream=None)
     a.update(kw)
     return lib.attn_fwd_varlen(*a.values())
 
@@ -258,6 +259,7 @@ def varlen_rc(lib, **kw):
     (dict(block_table=ctypes.c_void_p(16), page_size=0), -1),
     (dict(block_table=ctypes.c_void_p(16), max_pages=0), -1),
     (dict(kv_rows=0), -1),
+    (dict(softcap=-1.0), -1), (dict(softcap=float("nan")), -1),
     (dict(dtype=0), -2), (dict(d=96), -2), (dict(mask_kind=3), -2), (dict(mask_kind=4), -2),
     (dict(Hq=256, Hkv=1), -2),                                              # more heads per KV head than rows
     (dict(total_q=5), -1),                                                  # NULL tensors with work to do

@@ -23,10 +23,10 @@ def gpu():
     mfa.set_debug()
 
 
-def check(p, **kw):
+def check(p, alibi=None, softcap=0.0, **kw):
     say(p.name)
-    out, lse = run_gpu_paged(p, out_fill=float("nan"), **kw)
-    ref_o, ref_l = run_oracle_paged(p)
+    out, lse = run_gpu_paged(p, out_fill=float("nan"), alibi=alibi, softcap=softcap, **kw)
+    ref_o, ref_l = run_oracle_paged(p, alibi=alibi, softcap=softcap)
     compare(p, out, lse, ref_o, ref_l, label=p.name)
 
 
@@ -74,6 +74,33 @@ def test_forced_splits(splits):
     mfa.set_debug(force_splits=splits)
     try:
         check(p)
+    finally:
+        mfa.set_debug()
+
+
+SLOPES8 = [2.0 ** -(i + 1) for i in range(8)]
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp16", 64)])
+@pytest.mark.parametrize("kind", ["none", "causal", "window"])
+@pytest.mark.parametrize("mods", ["alibi", "softcap", "both"])
+def test_score_modifiers(dtype, d, kind, mods):
+    """ALiBi and softcap on every sequence's own positions, on the prefill-type and the
+    decode-type kernels of one batch (N(0,1) inputs, a cap that bends the scores)."""
+    p = synth.make_paged_problem(f"varlen {mods} {kind} {dtype} d{d}", Q_LENS, K_LENS, 8, 2, d, dtype, kind,
+                                 800 + d, page_size=16, window_left=45)
+    check(p, alibi=SLOPES8 if mods != "softcap" else None, softcap=0.8 if mods != "alibi" else 0.0)
+
+
+@pytest.mark.parametrize("form", ["two_source", "split"])
+def test_score_modifiers_two_source_and_split(form):
+    import masked_flashattention_forward_amd as mfa
+    q_lens, k_lens = [1, 37, 1, 130, 0, 64, 3], [300, 200, 1, 130, 50, 64, 2]
+    p = synth.make_paged_problem(f"varlen modifiers {form}", q_lens, k_lens, 8, 2, 128, "bf16", "causal", 820,
+                                 page_size=16, two_source=form == "two_source")
+    mfa.set_debug(force_splits=3 if form == "split" else 0)
+    try:
+        check(p, alibi=SLOPES8, softcap=1.3)
     finally:
         mfa.set_debug()
 
@@ -126,6 +153,19 @@ def test_serving_batch_sampled_sequences():
     seqs = [0, 3, 4, 17, 40, 63]   # two prefill chunks and four decode steps
     ref_o, ref_l = run_oracle_paged(p, seqs=seqs)
     compare(p, out, lse, ref_o, ref_l, label=p.name + " (sampled sequences)")
+    assert not np.isnan(out).any() and not np.isnan(lse).any()
+
+
+@pytest.mark.slow
+def test_serving_batch_with_modifiers_sampled():
+    """The serving batch with ALiBi + softcap as bench.py times it, on sampled sequences."""
+    p = synth.paged_config("serve")
+    say(p.name + " + ALiBi + softcap 30")
+    alibi = synth.alibi_slopes(p.Hq)
+    out, lse = run_gpu_paged(p, out_fill=float("nan"), alibi=alibi, softcap=30.0)
+    seqs = [0, 3, 4, 17, 40, 63]
+    ref_o, ref_l = run_oracle_paged(p, seqs=seqs, alibi=alibi, softcap=30.0)
+    compare(p, out, lse, ref_o, ref_l, label=p.name + " + modifiers (sampled sequences)")
     assert not np.isnan(out).any() and not np.isnan(lse).any()
 
 

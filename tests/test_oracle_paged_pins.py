@@ -195,3 +195,53 @@ def test_sequences_without_queries_or_keys():
     np.testing.assert_array_equal(out[:3], 0)          # sequence 1 has no keys
     assert np.all(np.isneginf(lse[:3]))
     assert np.all(np.isfinite(lse[3:]))
+
+
+def test_alibi_on_causal_sequences_is_a_key_bias_per_head():
+    """Causal ALiBi: -slope * (p_i - j) = slope * j - slope * p_i. The row constant leaves
+    the softmax unchanged and shifts the LSE by -slope * p_i; slope * j is a key bias, which
+    an extra query coordinate 1 against a key coordinate slope * j / scale adds to the
+    plain (pinned) paged attention. Positions are each sequence's own, so a sequence-level
+    mistake (global key index, shared position) fails here."""
+    q_lens, k_lens = [2, 5, 1, 3], [9, 5, 14, 3]
+    Hq, Hkv, d = 4, 2, 6
+    p = synth.make_paged_problem("pin", q_lens, k_lens, Hq, Hkv, d, "fp32", "causal", 31, page_size=4, scale=0.35)
+    slopes = np.array([0.5, 0.25, 0.125, 0.0625])
+    out, lse = paged_attention_ref(f64(p, "q"), f64(p, "k"), f64(p, "v"), p.cu_seqlens_q, p.cu_seqlens_k,
+                                   p.block_table, p.page_size, p.scale, "causal", alibi_slopes=slopes)
+    G = Hq // Hkv
+    for h in range(Hq):
+        # one head at a time: its slope goes into the key coordinate of its KV head
+        q1 = np.concatenate([f64(p, "q")[:, h:h + 1], np.ones((p.total_q, 1, 1))], axis=2)
+        kx = np.zeros(p.k.shape[:3] + (1,))
+        for s in range(p.num_seqs):
+            for j in range(int(k_lens[s])):
+                kx[p.block_table[s][j // p.page_size], j % p.page_size, :, 0] = slopes[h] * j / p.scale
+        k1 = np.concatenate([f64(p, "k")[:, :, h // G:h // G + 1], kx[:, :, h // G:h // G + 1]], axis=3)
+        v1 = np.concatenate([f64(p, "v")[:, :, h // G:h // G + 1], np.zeros(kx.shape[:3] + (1,))[:, :, :1]], axis=3)
+        o1, l1 = paged_attention_ref(q1, k1, v1, p.cu_seqlens_q, p.cu_seqlens_k, p.block_table, p.page_size,
+                                     p.scale, "causal")
+        np.testing.assert_allclose(out[:, h], o1[:, 0, :d], rtol=0, atol=1e-12)
+        pos = np.concatenate([np.arange(lq) + lk - lq for lq, lk in zip(q_lens, k_lens)])
+        np.testing.assert_allclose(lse[:, h], l1[:, 0] - slopes[h] * pos, rtol=0, atol=1e-11)
+
+
+def test_softcap_limits_on_paged_sequences():
+    """softcap -> infinity is no softcap; a tiny cap flattens every score to ~0 (uniform
+    weights over the visible keys: the mean of their values)."""
+    p = synth.make_paged_problem("pin", [3, 2], [7, 4], 2, 1, 5, "fp32", "causal", 33, page_size=2, scale=0.4)
+    args = (f64(p, "q"), f64(p, "k"), f64(p, "v"), p.cu_seqlens_q, p.cu_seqlens_k, p.block_table, p.page_size,
+            p.scale, "causal")
+    o0, l0 = paged_attention_ref(*args)
+    o1, l1 = paged_attention_ref(*args, softcap=1e9)
+    np.testing.assert_allclose(o1, o0, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l1, l0, rtol=0, atol=1e-12)
+    o2, l2 = paged_attention_ref(*args, softcap=1e-9)
+    vv = f64(p, "v")
+    for s, (lq, lk) in enumerate(zip([3, 2], [7, 4])):
+        for i in range(lq):
+            n = lk - lq + i + 1
+            keys = [vv[p.block_table[s][j // 2], j % 2, 0] for j in range(n)]
+            t = int(p.cu_seqlens_q[s]) + i
+            np.testing.assert_allclose(o2[t, 0], np.mean(keys, axis=0), rtol=0, atol=1e-7)
+            np.testing.assert_allclose(l2[t, 0], math.log(n), rtol=0, atol=1e-7)
