@@ -22,6 +22,8 @@
 //                dV^T += dO^T P and dK^T += Q^T dS with dO^T / Q^T from transposed LDS
 //                reads and P / dS straight from the registers (the C layout of S is the B
 //                layout these products need).
+#include <type_traits>
+
 #include "common.hpp"
 #include "mfma_common.hpp"
 
@@ -267,19 +269,27 @@ __global__ __launch_bounds__(kBT, 2) void dq_kernel(AttnParams p) {
 
 // ------------------------------------------------------------------ dK, dV
 template <typename T, int D, int MK>
-__global__ __launch_bounds__(kBT, (D == 128 ? 1 : 2)) void dkdv_kernel(AttnParams p) {
+__global__ __launch_bounds__(kBT, 2) void dkdv_kernel(AttnParams p) {
   using QT = BTile<D, 32>;
+  using KT = BTile<D, 128>;
   constexpr int NDC = D / 16;
   constexpr int NDB = D / 32;
   constexpr bool kAux = MK == MI_ATTN_MASK_DENSE || MK == MI_ATTN_MASK_TOPK;
   constexpr bool kCausal = MK == MI_ATTN_MASK_CAUSAL || MK == MI_ATTN_MASK_WINDOW || MK == MI_ATTN_MASK_TOPK;
-  constexpr int kStages = 3;
+  // d = 128: the block's K tile lives in LDS (read like Q each tile) instead of 64
+  // registers, so two workgroups fit per CU (two wavefronts per SIMD); LDS then holds a
+  // two-stage ring. d = 64 keeps K in registers and a three-stage ring.
+  constexpr bool kKLds = D == 128;
+  constexpr int kStages = kKLds ? 2 : 3;
+  constexpr int kDist = kStages - 1;  // tiles loaded ahead
   // stage: Q tile, dO tile, then the side values of its 32 rows: -LSE2 [32], D [32],
   // threshold or query index [32], 128 bytes unused
   constexpr int kSide = 512;
   constexpr int kStage = 2 * QT::bytes + kSide;
   static_assert(kStage % 512 == 0, "stage offsets keep the XOR-ed address bits");
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages * kStage];
+  constexpr int kKBytes = kKLds ? KT::bytes : 0;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages * kStage + kKBytes];
+  unsigned char* const ktile = smem + kStages * kStage;  // d = 128: keys kblk * 128 + r
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -298,16 +308,16 @@ __global__ __launch_bounds__(kBT, (D == 128 ? 1 : 2)) void dkdv_kernel(AttnParam
   const bool key_ok = j_lane < Lk;
   const long kv_row = (static_cast<long>(bg) * Lk + (key_ok ? j_lane : 0)) * D;
 
-  // K^T and V^T B operands of the lane's key
-  u32x4_t kreg[NDC], vreg[NDC];
+  // K^T and V^T B operands of the lane's key (K from LDS at d = 128)
+  u32x4_t kreg[kKLds ? 1 : NDC], vreg[NDC];
 #pragma unroll
   for (int dc = 0; dc < NDC; ++dc) {
     u32x4_t x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
     if (key_ok) {
-      x = *reinterpret_cast<const u32x4_t*>(static_cast<const T*>(p.k) + kv_row + dc * 16 + hf * 8);
+      if (!kKLds) x = *reinterpret_cast<const u32x4_t*>(static_cast<const T*>(p.k) + kv_row + dc * 16 + hf * 8);
       y = *reinterpret_cast<const u32x4_t*>(static_cast<const T*>(p.v) + kv_row + dc * 16 + hf * 8);
     }
-    kreg[dc] = x;
+    if (!kKLds) kreg[dc] = x;
     vreg[dc] = y;
   }
   int32_t rank_lane = 0x7fffffff;
@@ -399,11 +409,16 @@ __global__ __launch_bounds__(kBT, (D == 128 ? 1 : 2)) void dkdv_kernel(AttnParam
     if (wave == 0) lds_dma4_at(srs, sb + 2 * QT::bytes, side_lane, r0 * 4);
     if (kAux && wave == 1 && lane < 32) lds_dma4_at(srs, sb + 2 * QT::bytes + 256, side_lane, r0 * 4);
   };
-  // direct loads one tile issues in this wave (the waits below count them)
+  // direct loads one tile issues in this wave; "the tile after next may still be in
+  // flight" (three stages) or "nothing may" (two stages)
   const bool one_more = wave == 0 || (kAux && wave == 1);
-  auto wait_all_but_one_tile = [&]() {
-    if (one_more) __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(2 * QT::rounds + 1));
-    else __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(2 * QT::rounds));
+  auto wait_next_tile = [&]() {
+    if constexpr (kDist == 1) {
+      __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(0));
+    } else {
+      if (one_more) __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(2 * QT::rounds + 1));
+      else __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(2 * QT::rounds));
+    }
   };
 
   const Bases<D> bs(lane);
@@ -415,18 +430,30 @@ __global__ __launch_bounds__(kBT, (D == 128 ? 1 : 2)) void dkdv_kernel(AttnParam
     dvacc[db] = f32x16_t{};
   }
 
-  // three-stage ring: tiles t + 1 and t + 2 load while tile t is computed
+  // d = 128: the block's K tile (keys past Lk read as zeros), before the first ring tile
+  if constexpr (kKLds) {
+    const T* Kb = static_cast<const T*>(p.k) + static_cast<long>(bg) * Lk * D;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kb, Lk * D * 2);  // < 2^31 (host check)
+#pragma unroll
+    for (int c = 0; c < KT::rounds; ++c) {
+      const int rr = (c * kBW + wave) * KT::rowsPerWaveLoad + lane / (D / 8);
+      const int o = (kblk * 128 + rr) * D * 2 + ((ps ^ swz<D>(rr)) << 4);
+      lds_dma16_at(krs, smem_addr + kStages * kStage + (c * kBW + wave) * 1024, o, 0);
+    }
+  }
+
+  // ring: tiles t + 1 .. t + kDist load while tile t is computed
   if (t_lo < t_hi) issue(t_lo, 0);
-  if (t_lo + 1 < t_hi) {
+  if (kDist == 2 && t_lo + 1 < t_hi) {
     issue(t_lo + 1, 1);
-    wait_all_but_one_tile();
+    wait_next_tile();
   } else {
     __builtin_amdgcn_s_waitcnt(0);
   }
   __syncthreads();
   int stg = 0;
   for (int t = t_lo; t < t_hi; ++t) {
-    if (t + 2 < t_hi) issue(t + 2, stg == 0 ? 2 : stg - 1);
+    if (t + kDist < t_hi) issue(t + kDist, stg + kDist < kStages ? stg + kDist : stg + kDist - kStages);
     const unsigned char* qt = smem + stg * kStage;
     const unsigned char* ot = qt + QT::bytes;
     const float* side_m = reinterpret_cast<const float*>(qt + 2 * QT::bytes);
@@ -438,15 +465,17 @@ __global__ __launch_bounds__(kBT, (D == 128 ? 1 : 2)) void dkdv_kernel(AttnParam
     f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll
     for (int dc = 0; dc < NDC; ++dc) {
-      s = mfma32(T{}, row_frag(qt, bs.row_base, 0, dc, QT::rowBytes), kreg[dc], s);
+      const u32x4_t kf = kKLds ? row_frag(ktile, bs.row_base, wave, dc, QT::rowBytes) : kreg[kKLds ? 0 : dc];
+      s = mfma32(T{}, row_frag(qt, bs.row_base, 0, dc, QT::rowBytes), kf, s);
       dp = mfma32(T{}, row_frag(ot, bs.row_base, 0, dc, QT::rowBytes), vreg[dc], dp);
     }
-    // each MFMA overlaps the LDS read of the operand two MFMAs ahead
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    // each MFMA overlaps the LDS read of the operand(s) two MFMAs ahead
+    constexpr int kRd = kKLds ? 3 : 2;  // reads per S/dP MFMA pair
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kRd, 0);
 #pragma unroll
-    for (int i = 0; i < 2 * NDC - 2; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    for (int i = 0; i < NDC - 1; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kRd, 0);
     }
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -455,37 +484,27 @@ __global__ __launch_bounds__(kBT, (D == 128 ? 1 : 2)) void dkdv_kernel(AttnParam
     // all see every key of the block skip the per-element mask (a uniform branch).
     const bool interior = !kAux && full_block && r0 >= all_lo && r0 + 32 <= all_hi && !p.no_skip;
     const int lo = r_lo - r0, hi = r_hi - r0;  // visible rows of the lane's key, tile-relative
-    float4 mlv[4], ddv[4];
-    int4 axv[4];
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
+    const bool uniform_interior = __builtin_amdgcn_readfirstlane(static_cast<int>(interior));
+    // P and dS of the 4 consecutive rows rb .. rb + 3 held in registers r4 * 4 .. + 3, with
+    // their side values read from LDS just before (short live ranges)
+    auto rows4 = [&](int r4, auto masked_c) {
+      constexpr bool MASKED = decltype(masked_c)::value;
       const int rb = r4 * 8 + hf * 4;  // first of the 4 consecutive rows of these registers
-      mlv[r4] = *reinterpret_cast<const float4*>(side_m + rb);
-      ddv[r4] = *reinterpret_cast<const float4*>(side_d + rb);
-      axv[r4] = kAux ? *reinterpret_cast<const int4*>(side_a + rb) : int4{0, 0, 0, 0};
-    }
-    if (__builtin_amdgcn_readfirstlane(static_cast<int>(interior))) {
+      const float4 ml = *reinterpret_cast<const float4*>(side_m + rb);
+      const float4 dd = *reinterpret_cast<const float4*>(side_d + rb);
+      const float mls[4] = {ml.x, ml.y, ml.z, ml.w};
+      const float dds[4] = {dd.x, dd.y, dd.z, dd.w};
+      int4 ax = {0, 0, 0, 0};
+      if constexpr (kAux) ax = *reinterpret_cast<const int4*>(side_a + rb);
+      const int axs[4] = {ax.x, ax.y, ax.z, ax.w};
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const float mls[4] = {mlv[r4].x, mlv[r4].y, mlv[r4].z, mlv[r4].w};
-        const float dds[4] = {ddv[r4].x, ddv[r4].y, ddv[r4].z, ddv[r4].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float pv = fast_exp2(fmaf(s[r4 * 4 + e], cexp, mls[e]));
+      for (int e = 0; e < 4; ++e) {
+        float x = fmaf(s[r4 * 4 + e], cexp, mls[e]);
+        if constexpr (!MASKED) {
+          const float pv = fast_exp2(x);
           dp[r4 * 4 + e] = pv * (dp[r4 * 4 + e] - dds[e]);
           s[r4 * 4 + e] = pv;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int rb = r4 * 8 + hf * 4;
-        const float mls[4] = {mlv[r4].x, mlv[r4].y, mlv[r4].z, mlv[r4].w};
-        const float dds[4] = {ddv[r4].x, ddv[r4].y, ddv[r4].z, ddv[r4].w};
-        const int axs[4] = {axv[r4].x, axv[r4].y, axv[r4].z, axv[r4].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float x = fmaf(s[r4 * 4 + e], cexp, mls[e]);
+        } else {
           bool vis = rb + e >= lo && rb + e < hi;
           if constexpr (MK == MI_ATTN_MASK_DENSE) {
             const float mv = vis ? p.mask[static_cast<long>(axs[e]) * Lk + j_lane] : 0.f;
@@ -502,6 +521,13 @@ __global__ __launch_bounds__(kBT, (D == 128 ? 1 : 2)) void dkdv_kernel(AttnParam
           s[r4 * 4 + e] = pv;
         }
       }
+    };
+    if (uniform_interior) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) rows4(r4, std::false_type{});
+    } else {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) rows4(r4, std::true_type{});
     }
 
     // dV^T += dO^T P and dK^T += Q^T dS (d x 32 keys; contraction over the 32 rows)
@@ -527,10 +553,10 @@ __global__ __launch_bounds__(kBT, (D == 128 ? 1 : 2)) void dkdv_kernel(AttnParam
     __builtin_amdgcn_sched_barrier(0);
 
     // tile t + 1 has landed (this wave's part); every wave is done with this stage
-    if (t + 2 < t_hi) wait_all_but_one_tile();
+    if (t + kDist < t_hi) wait_next_tile();
     else __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    stg = stg == 2 ? 0 : stg + 1;
+    stg = stg + 1 == kStages ? 0 : stg + 1;
   }
 
   if (!key_ok) return;
