@@ -217,3 +217,23 @@ def test_backward_full_size_sampled(name):
     got = run_gpu_bwd(p, dout_s)
     ref, bnd = oracle_with_bounds(p, synth.storage_to_f64(dout_s, p.dtype), heads=BENCH_SAMPLES[name])
     compare_grads(p, got, ref, bnd, f"{name} (sampled heads)")
+
+
+@pytest.mark.parametrize("kind,Lq,Lk,extra", [
+    ("causal", 1, 1, {}),                      # one row, one key
+    ("none", 5, 1, {}),                        # a single key for every row
+    ("window", 40, 90, {"window_left": 0}),    # each row sees only its own position
+    ("dense", 9, 33, {"mask": "all -inf"}),    # every row dead: all gradients zero
+    ("topk", 64, 64, {"keep_k": 1}),           # one kept key per row
+])
+def test_backward_edge_cases(kind, Lq, Lk, extra):
+    mask = None
+    if extra.get("mask") == "all -inf":
+        mask = np.full((Lq, Lk), -np.inf, dtype=np.float32)
+    p = synth.make_problem(f"bwd edge {kind} {Lq}x{Lk} {extra}", 2, 4, 2, Lq, Lk, 128, "bf16", kind, 2200 + Lq,
+                           window_left=extra.get("window_left", 0), keep_k=extra.get("keep_k", 0),
+                           with_zero_hold=kind == "topk", mask=mask)
+    got = check(p, 2201)
+    if mask is not None:
+        for g in got:
+            assert np.all(g == 0.0)
