@@ -6,8 +6,9 @@
 // range ("split"); its 4 wavefronts stream disjoint 32-key tiles of that range
 // independently, each with its own online-softmax state for all G * Lq rows:
 //   K tile   loaded straight into registers in the 32x32x16 MFMA A-operand layout;
-//   V tile   loaded straight into a private 2-stage LDS ring (buffer_load ... lds) and read
-//            back transposed (ds_read_b64_tr_b16) as the V^T operand;
+//   V tile   loaded straight into a private 2-stage LDS ring (buffer_load ... lds, with the
+//            non-temporal hint) and read back transposed (ds_read_b64_tr_b16) as the V^T
+//            operand;
 //   S^T = K Q^T and O^T += V^T P^T on MFMA, softmax guarded as in the prefill kernel.
 // No workgroup barrier is needed while streaming; at the end the four states are merged
 // through LDS by log-sum-exp, giving the split's partial (o, lse) or, with one split, the
@@ -185,7 +186,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(AttnParams p) {
         const int ps = lane % (D / 8);
         bool nv;
         const long ev = varlen_row<D>(p, vs, g, j0 + r, __shfl(page, r, kWave), (ps ^ swz<D>(r)) << 3, &nv);
-        lds_dma16_global(lds_address(dst + c * 1024), pick(nv, v_fresh, v_cache) + ev);
+        lds_dma16_global_nt(lds_address(dst + c * 1024), pick(nv, v_fresh, v_cache) + ev);
       }
       if (p.block_table != nullptr) page_next = varlen_page(p, vs, j0 + kDecWaves * kDecBN + l32);
       return;
@@ -194,13 +195,13 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(AttnParams p) {
 #pragma unroll
     for (int dc = 0; dc < TL::kLoads; ++dc)
       kr[dc] = buffer_load16(krs, static_cast<int>(((j0 + l32) * ksr + dc * 16 + hf * 8) * 2));
-    // V: 1 KB direct loads into the swizzled [key][d] tile
+    // V: 1 KB direct loads into the swizzled [key][d] tile, non-temporal (read once, whole rows)
 #pragma unroll
     for (int c = 0; c < TL::vLoads; ++c) {
       const int r = c * (1024 / (D * 2)) + lane / (D / 8);
       const int ps = lane % (D / 8);
       const int gofs = static_cast<int>(((j0 + r) * vsr + ((ps ^ swz<D>(r)) << 3)) * 2);
-      lds_dma16(vrs, dst + c * 1024, gofs);
+      lds_dma16_nt(vrs, dst + c * 1024, gofs);
     }
   };
   constexpr int kLoadsPerTile = TL::kLoads + TL::vLoads;
