@@ -459,17 +459,18 @@ __global__ __launch_bounds__(256) void mask_summary_kernel(AttnParams p, int blo
   const int j1 = (j0 + block_n) < p.Lk ? (j0 + block_n) : p.Lk;
   const int w = j1 - j0;
   const int nh = p.flag_g > 1 ? p.G : 1;  // query heads of the KV head (one when shared)
-  const long nrow = static_cast<long>(i1 - i0) * nh;
   const float* mb = p.mask + fb * p.ms[0] + static_cast<long>(fg) * p.G * p.ms[1];
-  bool live = false;
-  for (long e = lane; e < nrow * w; e += kWave) {
-    const long r = e / w;
-    const int j = j0 + static_cast<int>(e % w);
-    const int i = i0 + static_cast<int>(r / nh);
-    const int hh = static_cast<int>(r % nh);
-    live |= mb[hh * p.ms[1] + i * p.ms[2] + j * p.ms[3]] > kNegInf;
+  // lanes take consecutive keys, the wavefront walks the rows (query position, head) and
+  // stops at the first row with a visible key
+  bool any = false;
+  for (int i = i0; i < i1 && !any; ++i) {
+    for (int hh = 0; hh < nh && !any; ++hh) {
+      const float* row = mb + hh * p.ms[1] + i * p.ms[2];
+      bool live = false;
+      for (int jj = lane; jj < w; jj += kWave) live |= row[(j0 + jj) * p.ms[3]] > kNegInf;
+      any = __any(live);
+    }
   }
-  const bool any = __any(live);
   if (lane == 0) flags[f] = any ? 1 : 0;
 }
 
