@@ -22,7 +22,9 @@ int q_per_block_for(int G) { return prefill_block_m() / G; }
 
 int auto_splits(int blocks, int Lk, int bn) {
   if (blocks >= kTargetBlocks / 2) return 1;
-  const int max_by_len = (Lk + bn * kMinTilesPerSplit - 1) / (bn * kMinTilesPerSplit);
+  // every split keeps at least kMinTilesPerSplit tiles (a shorter one does not repay the
+  // merge kernel)
+  const int max_by_len = ((Lk + bn - 1) / bn) / kMinTilesPerSplit;
   int s = (kTargetBlocks + blocks - 1) / blocks;
   if (s > max_by_len) s = max_by_len;
   return s < 1 ? 1 : s;
