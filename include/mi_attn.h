@@ -262,7 +262,8 @@ int attn_fwd_ex(const attn_fwd_args_t* args, void* stream);
  *                       be the one attn_fwd wrote for these inputs, not NULL).
  *   dout                device, [B, Hq, Lq, d] `dtype`: the gradient of out.
  *   dq, dk, dv          device, written (not accumulated), layouts of q, k and v. They
- *                       must not overlap the inputs.
+ *                       must not overlap the inputs. q, k, v, out, dout, dq, dk and dv
+ *                       are 16-byte aligned, lse 4-byte aligned (else MI_ATTN_EINVAL).
  *   B .. keep_k, dtype  as in attn_fwd (the top-k kind selects causally, as attn_fwd).
  *   stream              as in attn_fwd. Temporary device memory: 12 bytes per query
  *                       row (its LSE, rowsum(dout * out) and a mask index), plus the

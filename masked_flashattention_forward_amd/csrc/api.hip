@@ -353,12 +353,12 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
     return fail(MI_ATTN_EUNSUPPORTED, "Hq * Lq * d * 2 must stay below 2^31 bytes");
   if (static_cast<double>(B) * Hq * Lq * 12 > 2147483647.0)
     return fail(MI_ATTN_EUNSUPPORTED, "B * Hq * Lq must stay below 2^31 / 12 query rows");
-  const void* in[6] = {q, k, v, out, dout, lse};
-  const void* gr[3] = {dq, dk, dv};
-  for (const void* x : in)
-    if (reinterpret_cast<uintptr_t>(x) % 16 != 0) return fail(MI_ATTN_EINVAL, "inputs must be 16-byte aligned");
-  for (const void* x : gr)
-    if (reinterpret_cast<uintptr_t>(x) % 16 != 0) return fail(MI_ATTN_EINVAL, "dq, dk and dv must be 16-byte aligned");
+  // the kernels move 16-byte vectors of the tensors and 4-byte values of lse
+  const void* vec[8] = {q, k, v, out, dout, dq, dk, dv};
+  for (const void* x : vec)
+    if (reinterpret_cast<uintptr_t>(x) % 16 != 0)
+      return fail(MI_ATTN_EINVAL, "q, k, v, out, dout, dq, dk and dv must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(lse) % 4 != 0) return fail(MI_ATTN_EINVAL, "lse must be 4-byte aligned");
 
   const long rows = static_cast<long>(B) * Hq * Lq;
   const long bh = static_cast<long>(B) * Hkv;
