@@ -1,7 +1,10 @@
 """Randomised shapes on the GPU against the fp64 oracle: forward (attn_fwd) and backward
 (attn_bwd) over seeded draws of batch, head counts and grouping, lengths (Lq above, equal to
-and below Lk, one-row and one-key cases), head dim, dtype and mask kind with its parameters.
-Every draw is printed before it runs, so a failure names its case."""
+and below Lk, one-row and one-key cases), head dim, dtype and mask kind with its parameters;
+varlen batches (attn_fwd_varlen) over seeded draws of sequence count and lengths (empty
+queries, no keys, fewer keys than queries), page size, the cache/new-token split, ALiBi,
+softcap and forced KV splits. Every draw is printed before it runs, so a failure names its
+case."""
 import numpy as np
 import pytest
 
@@ -70,3 +73,40 @@ def test_backward_random(i):
     if c["Hq"] // c["Hkv"] > 128:
         pytest.skip("more than 128 query heads per KV head")
     check(problem(c, f"random bwd #{i}"), 7000 + i)
+
+
+def draw_varlen(i):
+    rng = np.random.default_rng(9000 + i)
+    S = int(rng.integers(1, 9))
+    q_lens = [int(rng.choice([0, 1, 1, 2, 5, 37, 64, 65, 130, 257])) for _ in range(S)]
+    if max(q_lens) == 0:
+        q_lens[0] = 1
+    k_lens = [int(rng.choice([0, 1, 3])) if rng.random() < 0.15 else q + int(rng.integers(0, 700)) for q in q_lens]
+    Hkv = int(rng.integers(1, 4))
+    Hq = Hkv * int(rng.choice([1, 2, 4, 8, 16]))
+    dtype = ["bf16", "fp16"][rng.integers(2)]
+    d = int(rng.choice([64, 128]))
+    kind = ["none", "causal", "window"][rng.integers(3)]
+    wl = int(rng.integers(0, 150))
+    page = int(rng.choice([0, 1, 8, 16, 32, 128]))
+    two = bool(rng.random() < 0.3)
+    alibi = [float(2.0 ** -rng.uniform(0.5, 8.0)) for _ in range(Hq)] if rng.random() < 0.3 else None
+    softcap = float(rng.uniform(5.0, 50.0)) if rng.random() < 0.3 else 0.0
+    splits = int(rng.integers(2, 8)) if rng.random() < 0.2 else 0
+    name = (f"random varlen #{i} {dtype} d{d} H{Hq}/{Hkv} q{q_lens} k{k_lens} {kind} wl{wl} page{page} "
+            f"two{int(two)} alibi{int(alibi is not None)} softcap{softcap:.1f} splits{splits}")
+    p = synth.make_paged_problem(name, q_lens, k_lens, Hq, Hkv, d, dtype, kind, 9500 + i, page_size=page,
+                                 two_source=two, window_left=wl)
+    return p, alibi, softcap, splits
+
+
+@pytest.mark.parametrize("i", range(40))
+def test_varlen_random(i):
+    import masked_flashattention_forward_amd as mfa
+    from test_gpu_varlen import check
+    p, alibi, softcap, splits = draw_varlen(i)
+    mfa.set_debug(force_splits=splits)
+    try:
+        check(p, alibi=alibi, softcap=softcap)
+    finally:
+        mfa.set_debug()
