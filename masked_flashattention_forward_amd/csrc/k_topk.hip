@@ -458,7 +458,9 @@ __global__ __launch_bounds__(256) void mask_summary_kernel(AttnParams p, int blo
   const int j0 = t * block_n;
   const int j1 = (j0 + block_n) < p.Lk ? (j0 + block_n) : p.Lk;
   const int w = j1 - j0;
-  const int nh = p.flag_g > 1 ? p.G : 1;  // query heads of the KV head (one when shared)
+  // query heads of the KV head whose mask rows differ (one when the mask is shared over
+  // heads); with a single KV head flag_g is 1 even when the rows differ per query head
+  const int nh = (p.Hq > 1 && p.ms[1] != 0) ? p.G : 1;
   const float* mb = p.mask + fb * p.ms[0] + static_cast<long>(fg) * p.G * p.ms[1];
   // lanes take consecutive keys, the wavefront walks the rows (query position, head) and
   // stops at the first row with a visible key

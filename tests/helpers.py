@@ -60,9 +60,10 @@ def run_oracle(p: synth.Problem, rows=None, heads=None):
                                 keep_k=p.keep_k, rows=rows, heads=heads)
 
 
-def compare(p: synth.Problem, out, lse, ref_out, ref_lse, rows=None, heads=None, label=""):
-    """Element-wise comparison on the computed (rows, heads) subset; returns the errors."""
-    tol_o, tol_l = TOL[p.dtype]
+def compare(p: synth.Problem, out, lse, ref_out, ref_lse, rows=None, heads=None, label="", tol=None):
+    """Element-wise comparison on the computed (rows, heads) subset; returns the errors.
+    ``tol`` = (output, LSE) overrides the dtype's tolerances where a case derives its own."""
+    tol_o, tol_l = TOL[p.dtype] if tol is None else tol
     sel = ~np.isnan(ref_lse)
     if rows is not None or heads is not None:
         assert sel.any()

@@ -81,10 +81,10 @@ def run(p, *, qlay="bhld", klay="bhld", olay="bhld", mask=None, topk_causal=True
     return out_to_f64(out, p.dtype), lse.cpu().numpy().astype(np.float64), ref_o, ref_l
 
 
-def check(p, label, **kw):
+def check(p, label, tol=None, **kw):
     say(label)
     out, lse, ref_o, ref_l = run(p, **kw)
-    compare(p, out, lse, ref_o, ref_l, label=label)
+    compare(p, out, lse, ref_o, ref_l, label=label, tol=tol)
 
 
 # (dtype, d, Lq, Lk, Hq, Hkv, forced path, forced splits): prefill, split prefill, decode,
@@ -188,3 +188,15 @@ def test_ex_workloads_full_size_sampled(name):
                                  mask=o["mask"] if o["mask"] is not None else p.mask, topk_causal=o["topk_causal"],
                                  alibi=o["alibi"], softcap=o["softcap"], heads=heads)
     compare(p, out, lse, ref_o, ref_l, heads=heads, label=f"{name} (sampled heads)")
+
+
+@pytest.mark.parametrize("Lq,path", [(1, 2), (1, 1), (33, 1), (33, None)])
+def test_mqa_per_head_mask_first_head_hidden(Lq, path):
+    # One KV head and mask rows per query head, head 0 seeing no key at all: the dense-mask
+    # tile summary must scan every query head of the group, not only the first (a tile
+    # hidden from head 0 is still visible to the others).
+    Hq, Lk = 8, 513
+    m = per_head_mask(21 + Lq, (1, Hq), Lq, Lk)
+    m[0, 0] = -np.inf
+    p = synth.make_problem(f"MQA per-head mask Lq{Lq}", 1, Hq, 1, Lq, Lk, 128, "bf16", "dense", 970 + Lq)
+    check(p, f"MQA per-head mask, head 0 hidden, Lq {Lq} path {path}", mask=m, path=path)

@@ -3,7 +3,9 @@
 and below Lk, one-row and one-key cases), head dim, dtype and mask kind with its parameters;
 varlen batches (attn_fwd_varlen) over seeded draws of sequence count and lengths (empty
 queries, no keys, fewer keys than queries), page size, the cache/new-token split, ALiBi,
-softcap and forced KV splits. Every draw is printed before it runs, so a failure names its
+softcap and forced KV splits; attn_fwd_ex over seeded draws of memory layouts (transposed
+cache, padded rows), dense masks broadcast over batch and head, top-k over causal or all
+keys, ALiBi and softcap on every mask kind, and forced paths and splits. Every draw is printed before it runs, so a failure names its
 case."""
 import numpy as np
 import pytest
@@ -110,3 +112,49 @@ def test_varlen_random(i):
         check(p, alibi=alibi, softcap=softcap)
     finally:
         mfa.set_debug()
+
+
+def draw_ex(i):
+    from test_gpu_ex import per_head_mask
+    rng = np.random.default_rng(11000 + i)
+    c = draw_case(300 + i, ["bf16", "fp16", "fp32"])
+    c["Hq"] = c["Hkv"] * int(rng.choice([1, 2, 4, 8]))
+    c["B"] = int(rng.integers(1, 3))
+    if c["kind"] == "dense":
+        shape = [(), (c["B"], 1), (1, c["Hq"]), (c["B"], c["Hq"])][rng.integers(4)]
+        c["mask"] = per_head_mask(12000 + i, shape, c["Lq"], c["Lk"])
+    lays = ["bhld", "blhd", "pad"]
+    kw = dict(qlay=lays[rng.integers(3)], klay=lays[rng.integers(3)], olay=lays[rng.integers(3)],
+              mask=c["mask"], topk_causal=bool(rng.random() < 0.5))
+    if rng.random() < 0.35:
+        kw["alibi"] = [float(2.0 ** -rng.uniform(0.5, 8.0)) for _ in range(c["Hq"])]
+    if rng.random() < 0.35:
+        kw["softcap"] = float(rng.uniform(5.0, 50.0))
+    G = c["Hq"] // c["Hkv"]
+    r = rng.random()
+    if c["dtype"] != "fp32" and r < 0.2:
+        kw["path"] = 1
+    elif c["dtype"] != "fp32" and r < 0.35 and G * c["Lq"] <= 32:
+        kw["path"] = 2
+    elif r < 0.45:
+        kw["path"] = 0
+    if kw.get("path") in (1, 2) and rng.random() < 0.5:
+        kw["splits"] = int(rng.integers(2, 8))
+    p = problem(c, f"random ex #{i}")
+    if c["dtype"] == "fp32" and "alibi" in kw:
+        # fp32 rounds each logit's ALiBi term, up to slope * (Lk + Lq) in size, to about u32
+        # of it (a few roundings: 4 u32); that moves LSE by as much and the output by that
+        # times the largest |v|
+        db = 4 * 2.0 ** -24 * max(kw["alibi"]) * (c["Lk"] + c["Lq"])
+        kw["tol"] = (1e-5 + db * float(np.abs(p.v).max()), 1e-5 + db)
+    label = (f"{p.name} lay {kw['qlay']}/{kw['klay']}/{kw['olay']} topk_causal{int(kw['topk_causal'])} "
+             f"alibi{int('alibi' in kw)} softcap{kw.get('softcap', 0.0):.1f} path{kw.get('path')} "
+             f"splits{kw.get('splits', 0)}")
+    return p, label, kw
+
+
+@pytest.mark.parametrize("i", range(40))
+def test_ex_random(i):
+    from test_gpu_ex import check
+    p, label, kw = draw_ex(i)
+    check(p, label, **kw)
