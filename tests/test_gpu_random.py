@@ -5,7 +5,9 @@ varlen batches (attn_fwd_varlen) over seeded draws of sequence count and lengths
 queries, no keys, fewer keys than queries), page size, the cache/new-token split, ALiBi,
 softcap and forced KV splits; attn_fwd_ex over seeded draws of memory layouts (transposed
 cache, padded rows), dense masks broadcast over batch and head, top-k over causal or all
-keys, ALiBi and softcap on every mask kind, and forced paths and splits. Every draw is printed before it runs, so a failure names its
+keys, ALiBi and softcap on every mask kind, and forced paths and splits; dynamic_mask_topk
+over seeded draws of lengths on both sides of the merge/count switch, keep counts and tie-heavy
+zero_hold values (bit-exact). Every draw is printed before it runs, so a failure names its
 case."""
 import numpy as np
 import pytest
@@ -158,3 +160,28 @@ def test_ex_random(i):
     from test_gpu_ex import check
     p, label, kw = draw_ex(i)
     check(p, label, **kw)
+
+
+def draw_topk(i):
+    rng = np.random.default_rng(13000 + i)
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+    Lk = int(np.exp(rng.uniform(0.0, np.log(20000.0))))
+    Lq = int(rng.integers(1, min(2 * Lk, 40_000_000 // Lk) + 1))
+    keep = int(rng.integers(1, Lk + 6))
+    causal = bool(rng.random() < 0.5)
+    style = int(rng.integers(3))
+    if style == 0:    # few distinct values: long tie runs, -0.0 beside +0.0
+        zh = rng.choice(np.array([-1.0, -0.0, 0.0, 0.5, 2.0], dtype=np.float32), size=(B, H, Lk))
+    elif style == 1:  # continuous values
+        zh = rng.standard_normal((B, H, Lk)).astype(np.float32)
+    else:             # continuous with a share of repeated values
+        zh = rng.standard_normal((B, H, Lk)).astype(np.float32)
+        zh[rng.random(zh.shape) < 0.3] = np.float32(0.25)
+    return zh, Lq, keep, causal, f"random topk #{i} B{B} H{H} Lq{Lq} Lk{Lk} keep{keep} causal{int(causal)} style{style}"
+
+
+@pytest.mark.parametrize("i", range(30))
+def test_topk_random(i):
+    from test_gpu_topk import check_topk
+    zh, Lq, keep, causal, label = draw_topk(i)
+    check_topk(zh, Lq, keep, causal, label)
