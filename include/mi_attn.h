@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define MI_ATTN_ABI_VERSION 6
+#define MI_ATTN_ABI_VERSION 7
 
 /* element types of q, k, v, out */
 #define MI_ATTN_F32 0
@@ -316,10 +316,39 @@ int attn_fwd_plan(int B, int Hq, int Hkv, int Lq, int Lk, int d, int mask_kind,
  */
 void attn_set_debug(int no_skip, int force_path, int force_splits);
 
-/* message for the last non-zero return on the calling thread ("" if none) */
+/*
+ * attn_read_stream: read `bytes` bytes at device pointer `src` once, as a plain stream of
+ * 16-byte loads (with the non-temporal cache hint when `nontemporal` != 0, the hint the
+ * split-KV decode kernel puts on its V loads), and write one XOR of the data per
+ * MI_ATTN_READ_STREAM_CHUNK bytes to sink[0 .. ceil(bytes / MI_ATTN_READ_STREAM_CHUNK) - 1]
+ * (device memory, caller-owned). No page defines this operation: it is a measurement aid,
+ * the practical HBM read ceiling that the decode path's bandwidth is reported against.
+ * `src` must be 16-byte aligned and `bytes` a positive multiple of 16, else MI_ATTN_EINVAL
+ * (nothing enqueued). MI_ATTN_EHIP if the launch fails. Enqueued on `stream`, no sync.
+ */
+#define MI_ATTN_READ_STREAM_CHUNK 2097152
+int attn_read_stream(const void* src, size_t bytes, int nontemporal, uint32_t* sink, void* stream);
+
+/*
+ * attn_last_error: message for the last non-zero return on the calling thread ("" if
+ * none). Every rejected argument (a mask kind without its pointer, an unsupported head
+ * dimension, Hq % Hkv != 0, ...) returns an error code with a message here instead of
+ * being ignored or silently replaced: the InfiniTrain pull request #193 page ("TODO",
+ * and the review comment under it) notes that its flash path ignored a parsed mask and
+ * asks for an error or a fallback in that case.
+ * Ownership: the string is owned by the library (thread-local storage) and stays valid
+ * until the next call on the same thread. Never fails.
+ */
 const char* attn_last_error(void);
 
-/* MI_ATTN_ABI_VERSION of the loaded library, for the caller to assert semantics */
+/*
+ * attn_abi_version: MI_ATTN_ABI_VERSION of the loaded library. A caller compiled against
+ * this header asserts that the loaded library has the same version before relying on
+ * its semantics (argument lists, mask conventions such as the bottom-right alignment),
+ * as the FastChat pull request #2315 page does with an assert on the flash-attn version
+ * so that the corrected q_len != kv_len causal behaviour is guaranteed to be present.
+ * Host-only; never fails.
+ */
 int attn_abi_version(void);
 
 #ifdef __cplusplus

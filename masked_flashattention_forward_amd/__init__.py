@@ -26,7 +26,7 @@ class MiAttnError(RuntimeError):
         self.code = code
 
 
-ABI_VERSION = 6  # MI_ATTN_ABI_VERSION of include/mi_attn.h that this binding matches
+ABI_VERSION = 7  # MI_ATTN_ABI_VERSION of include/mi_attn.h that this binding matches
 
 
 class AttnPlan(ctypes.Structure):
@@ -69,6 +69,8 @@ _SIGS = {
     "attn_set_debug": (None, [ctypes.c_int] * 3),
     "attn_last_error": (ctypes.c_char_p, []),
     "attn_abi_version": (ctypes.c_int, []),
+    "attn_read_stream": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
+                                        ctypes.c_void_p]),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -104,6 +106,29 @@ def _check(rc: int):
 
 def abi_version() -> int:
     return lib().attn_abi_version()
+
+
+READ_STREAM_CHUNK = 2097152  # MI_ATTN_READ_STREAM_CHUNK
+
+
+def read_stream(src, nontemporal: bool = True, sink=None, stream=None):
+    """attn_read_stream: read every byte of the contiguous GPU tensor ``src`` once (a plain
+    16-byte load stream; the measured HBM read ceiling for the decode roofline). Returns
+    the int32 sink tensor the kernel writes (one word per 2 MiB)."""
+    import torch
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous GPU tensor")
+    nbytes = src.numel() * src.element_size()
+    words = (nbytes + READ_STREAM_CHUNK - 1) // READ_STREAM_CHUNK
+    if sink is None:
+        sink = torch.empty(words, dtype=torch.int32, device=src.device)
+    elif sink.numel() < words or sink.dtype != torch.int32:
+        raise ValueError(f"sink must be int32 with at least {words} entries")
+    if stream is None:
+        stream = torch.cuda.current_stream(src.device)
+    _check(lib().attn_read_stream(ctypes.c_void_p(src.data_ptr()), nbytes, int(bool(nontemporal)),
+                                  ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream.cuda_stream)))
+    return sink
 
 
 def set_debug(no_skip: bool = False, force_path: int = -1, force_splits: int = 0):

@@ -286,10 +286,17 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN, EXT>)) void pr
       pg_lane = p.block_table[static_cast<long>(sq.seq) * p.max_pages + idx];
     }
   };
+  // The fast form needs every row it forms to lie in its array: new-token rows always do
+  // (q_start and Lq are clamped to total_q), paged rows sit in a clamped page, and packed
+  // rows only when the sequence's slice [k_start + j0, k_start + j0 + BN) lies inside the
+  // kv_rows rows of the cache (the lengths are caller data; anything else takes the
+  // clamped per-row form).
   auto tile_direct = [&](int j0) -> bool {
     if (j0 + BN > sq.Lk) return false;
     if (j0 >= sq.ctx) return true;  // new-token rows (two-source form)
-    return j0 + BN <= sq.ctx && (p.block_table == nullptr || p.page_shift >= kLog2RoundKeys<D>);
+    if (j0 + BN > sq.ctx) return false;
+    if (p.block_table != nullptr) return p.page_shift >= kLog2RoundKeys<D>;
+    return sq.k_start >= 0 && sq.k_start <= p.kv_rows - (j0 + BN);
   };
   auto load_gidx = [&](int t) {
     if constexpr (GATHER) {

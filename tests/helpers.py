@@ -69,17 +69,25 @@ def compare(p: synth.Problem, out, lse, ref_out, ref_lse, rows=None, heads=None,
         assert sel.any()
     go, gl = out[sel], lse[sel]
     ro, rl = ref_out[sel], ref_lse[sel]
+    # per-row tolerances (arrays shaped like the LSE) or one number for every row
+    to = np.broadcast_to(np.asarray(tol_o, dtype=np.float64), ref_lse.shape)[sel]
+    tl = np.broadcast_to(np.asarray(tol_l, dtype=np.float64), ref_lse.shape)[sel]
     assert not np.isnan(go).any(), f"{label}: NaN in output"
     assert not np.isnan(gl).any(), f"{label}: NaN in LSE"
     dead = rl == -np.inf
     assert np.array_equal(gl == -np.inf, dead), f"{label}: -inf LSE pattern differs"
     assert np.all(go[dead] == 0.0), f"{label}: fully masked rows must be 0"
-    err_o = float(np.abs(go - ro).max()) if go.size else 0.0
-    err_l = float(np.abs(gl[~dead] - rl[~dead]).max()) if (~dead).any() else 0.0
-    print(f"[parity] {label or p.name}: max|out err|={err_o:.3e} (tol {tol_o}) "
-          f"max|lse err|={err_l:.3e} (tol {tol_l}) dead_rows={int(dead.sum())}", flush=True)
-    assert err_o <= tol_o, f"{label}: output error {err_o} > {tol_o}"
-    assert err_l <= tol_l, f"{label}: LSE error {err_l} > {tol_l}"
+    row_o = np.abs(go - ro).reshape(go.shape[0], -1).max(axis=1) if go.size else np.zeros(0)
+    row_l = np.where(dead, 0.0, np.abs(gl - np.where(dead, 0.0, rl)))
+    err_o = float(row_o.max()) if row_o.size else 0.0
+    err_l = float(row_l.max()) if row_l.size else 0.0
+    ratio_o = float((row_o / to).max()) if row_o.size else 0.0
+    ratio_l = float((row_l / tl).max()) if row_l.size else 0.0
+    print(f"[parity] {label or p.name}: max|out err|={err_o:.3e} (tol {float(to.min()):.3g}..{float(to.max()):.3g}) "
+          f"max|lse err|={err_l:.3e} (tol {float(tl.min()):.3g}..{float(tl.max()):.3g}) "
+          f"worst err/tol out {ratio_o:.3f} lse {ratio_l:.3f} dead_rows={int(dead.sum())}", flush=True)
+    assert ratio_o <= 1.0, f"{label}: output error {err_o} exceeds its row's tolerance (worst ratio {ratio_o})"
+    assert ratio_l <= 1.0, f"{label}: LSE error {err_l} exceeds its row's tolerance (worst ratio {ratio_l})"
     return err_o, err_l
 
 

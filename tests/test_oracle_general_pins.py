@@ -233,3 +233,70 @@ def test_modifiers_compose_in_order():
     o4, l4 = general_attention_ref(q, k, v, 0.4, "dense", mask=m, alibi_slopes=slopes, softcap=0.9)
     np.testing.assert_allclose(o3, o4, rtol=0, atol=1e-14)
     np.testing.assert_allclose(l3, l4 + 2.5, rtol=0, atol=1e-13)
+
+
+def one_key_mask(Lq, Lk, keys):
+    """Dense mask that leaves key keys[i] visible to row i and hides every other key."""
+    m = np.full((Lq, Lk), -np.inf)
+    m[np.arange(Lq), keys] = 0.0
+    return m
+
+
+def test_softcap_then_alibi_single_key_closed_form():
+    """One visible key at distance delta from the row: LSE = cap*tanh(t/cap) - slope*delta
+    and the output is that key's V row. Applying ALiBi inside the tanh (the other order)
+    gives cap*tanh((t - slope*delta)/cap) instead, which differs here by more than 0.1."""
+    q, k, v = problem(61, B=1, Hq=2, Hkv=1, Lq=4, Lk=10)
+    Lq, Lk = 4, 10
+    pos = query_positions(Lq, Lk)
+    keys = np.array([0, 2, 9, 5])  # distances 6, 5, 2 (a key after the row) and 4
+    cap, scale = 0.8, 0.9
+    slopes = np.array([0.35, 0.6])
+    o, lse = general_attention_ref(q, k, v, scale, "dense", mask=one_key_mask(Lq, Lk, keys), alibi_slopes=slopes,
+                                   softcap=cap)
+    for h in range(2):
+        t = scale * np.einsum("id,id->i", q[0, h], k[0, 0, keys])
+        delta = np.abs(pos - keys)
+        np.testing.assert_array_equal(o[0, h], v[0, 0, keys])
+        np.testing.assert_allclose(lse[0, h], cap * np.tanh(t / cap) - slopes[h] * delta, rtol=0, atol=1e-15)
+        swapped = cap * np.tanh((t - slopes[h] * delta) / cap)
+        assert np.abs(swapped - lse[0, h]).min() > 0.1
+
+
+def test_softcap_then_alibi_two_keys_weights():
+    """Two visible keys a and b: the output is w*v_a + (1-w)*v_b with
+    w = 1 / (1 + exp(z_b - z_a)), z = cap*tanh(t/cap) - slope*|p - j|, and
+    LSE = z_a + log(1 + exp(z_b - z_a))."""
+    q, k, v = problem(62, B=1, Hq=1, Hkv=1, Lq=1, Lk=8)
+    p = 7
+    a, b = 1, 6
+    m = np.full((1, 8), -np.inf)
+    m[0, [a, b]] = 0.0
+    cap, scale, slope = 0.5, 1.1, 0.4
+    o, lse = general_attention_ref(q, k, v, scale, "dense", mask=m, alibi_slopes=np.array([slope]), softcap=cap)
+    za = cap * np.tanh(scale * q[0, 0, 0] @ k[0, 0, a] / cap) - slope * (p - a)
+    zb = cap * np.tanh(scale * q[0, 0, 0] @ k[0, 0, b] / cap) - slope * (p - b)
+    w = 1.0 / (1.0 + np.exp(zb - za))
+    np.testing.assert_allclose(o[0, 0, 0], w * v[0, 0, a] + (1 - w) * v[0, 0, b], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse[0, 0, 0], za + np.log1p(np.exp(zb - za)), rtol=0, atol=1e-14)
+
+
+def test_softcap_and_alibi_match_torch_with_both_in_the_mask():
+    """Library route with both modifiers: torch's fp64 attention over the scaled scores with
+    an additive mask that replaces each score by its capped value (built from
+    torch.sigmoid) and subtracts the ALiBi distance term, under the causal mask."""
+    q, k, v = problem(63, B=1, Hq=2, Hkv=2, Lq=5, Lk=9, d=16)
+    cap, scale = 1.1, 0.7
+    slopes = np.array([0.45, 0.15])
+    o, lse = general_attention_ref(q, k, v, scale, "causal", alibi_slopes=slopes, softcap=cap)
+    tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+    t = scale * (tq @ tk.transpose(-1, -2))
+    capped = cap * (2 * torch.sigmoid(2 * t / cap) - 1)
+    pos = torch.from_numpy(query_positions(5, 9)).double()[:, None]
+    j = torch.arange(9, dtype=torch.float64)[None, :]
+    bias = -torch.from_numpy(slopes)[:, None, None] * (pos - j).abs()[None]
+    causal = torch.where(j <= pos, 0.0, -torch.inf)[None]
+    z = capped + bias[None] + causal[None]
+    ref = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=z - t, scale=scale)
+    np.testing.assert_allclose(o, ref.numpy(), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, torch.logsumexp(z, dim=-1).numpy(), rtol=0, atol=1e-13)
