@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define MI_ATTN_ABI_VERSION 7
+#define MI_ATTN_ABI_VERSION 8
 
 /* element types of q, k, v, out */
 #define MI_ATTN_F32 0
@@ -281,6 +281,28 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
              int B, int Hq, int Hkv, int Lq, int Lk, int d, float scale,
              int mask_kind, int window_left, const float* mask, const float* zero_hold,
              int keep_k, int dtype, void* stream);
+
+/*
+ * attn_fwd_noalloc: attn_fwd for callers that cannot allocate device memory during the
+ * call (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). Same arguments, same kernels and the same results as attn_fwd, but the
+ * temporary memory (split-KV partials, top-k ranks, thresholds, sorted key chunks and
+ * kept-key lists, dense-mask tile flags) comes from a fixed scratch array of
+ * MI_ATTN_NOALLOC_MAX_WORKSPACE bytes that the library holds on each GPU it runs on until
+ * the process ends; the call itself allocates and frees nothing.
+ *  - A call whose plan needs more than MI_ATTN_NOALLOC_MAX_WORKSPACE bytes (see
+ *    attn_plan_t.workspace_bytes) returns MI_ATTN_EUNSUPPORTED before enqueuing anything.
+ *  - Every call on one GPU shares that GPU's array, which keeps the last call's contents
+ *    (nothing in it needs to start at zero): calls that overlap on one GPU (different
+ *    streams, or different host threads) race and must be serialised by the caller.
+ *  - The first call on a device looks up the array's device address there (on the
+ *    device `stream` belongs to); it fails with MI_ATTN_EHIP if that lookup fails.
+ */
+#define MI_ATTN_NOALLOC_MAX_WORKSPACE 33554432
+int attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out, float* lse,
+                     int B, int Hq, int Hkv, int Lq, int Lk, int d, float scale,
+                     int mask_kind, int window_left, const float* mask, const float* zero_hold,
+                     int keep_k, int dtype, void* stream);
 
 /* which kernels attn_fwd would run for a shape (host-only query, no GPU work) */
 typedef struct {

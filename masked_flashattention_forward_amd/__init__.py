@@ -26,7 +26,7 @@ class MiAttnError(RuntimeError):
         self.code = code
 
 
-ABI_VERSION = 7  # MI_ATTN_ABI_VERSION of include/mi_attn.h that this binding matches
+ABI_VERSION = 8  # MI_ATTN_ABI_VERSION of include/mi_attn.h that this binding matches
 
 
 class AttnPlan(ctypes.Structure):
@@ -54,6 +54,9 @@ _SIGS = {
     "attn_fwd": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_void_p] + [ctypes.c_int] * 6 + [ctypes.c_float]
                  + [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                     ctypes.c_void_p]),
+    "attn_fwd_noalloc": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_void_p] + [ctypes.c_int] * 6
+                         + [ctypes.c_float] + [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                               ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
     "dynamic_mask_topk": (ctypes.c_int, [ctypes.c_void_p] + [ctypes.c_int] * 6
                           + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "attn_fwd_varlen": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_void_p, ctypes.c_int] * 2
@@ -109,6 +112,7 @@ def abi_version() -> int:
 
 
 READ_STREAM_CHUNK = 2097152  # MI_ATTN_READ_STREAM_CHUNK
+NOALLOC_MAX_WORKSPACE = 33554432  # MI_ATTN_NOALLOC_MAX_WORKSPACE
 
 
 def read_stream(src, nontemporal: bool = True, sink=None, stream=None):
@@ -164,8 +168,9 @@ def _stream_handle(device, stream):
 
 
 def attn_fwd(q, k, v, *, scale=None, mask_kind="causal", window_left=0, mask=None, zero_hold=None,
-             keep_k=0, out=None, lse=None, return_lse=True, stream=None):
-    """Masked attention forward.
+             keep_k=0, out=None, lse=None, return_lse=True, stream=None, noalloc=False):
+    """Masked attention forward (``noalloc=True``: attn_fwd_noalloc, the same call with its
+    temporary memory taken from the library's fixed per-GPU scratch instead of allocated).
 
     q ``[B,Hq,Lq,d]``, k/v ``[B,Hkv,Lk,d]`` (fp32, fp16 or bf16, contiguous, on one
     GPU); mask ``[Lq,Lk]`` fp32 for ``mask_kind="dense"``; zero_hold ``[B,Hkv,Lk]``
@@ -204,9 +209,10 @@ def attn_fwd(q, k, v, *, scale=None, mask_kind="causal", window_left=0, mask=Non
         raise ValueError("lse must be a contiguous fp32 [B, Hq, Lq] tensor")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    rc = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Lq, Lk, d,
-                        float(scale), mk, int(window_left), _ptr(mask), _ptr(zero_hold), int(keep_k),
-                        _dtype_code(q), _stream_handle(q.device, stream))
+    fn = lib().attn_fwd_noalloc if noalloc else lib().attn_fwd
+    rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Lq, Lk, d,
+            float(scale), mk, int(window_left), _ptr(mask), _ptr(zero_hold), int(keep_k),
+            _dtype_code(q), _stream_handle(q.device, stream))
     _check(rc)
     return out, lse
 

@@ -3,6 +3,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "common.hpp"
@@ -73,7 +74,7 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 struct Plan {
   attn_plan_t pub;
   int q_per_block;     // query positions per workgroup (dense-mask summary granularity)
-  size_t off_rank, off_tau, off_tmin, off_flags, off_pout, off_plse;
+  size_t off_rank, off_tau, off_tmin, off_sort, off_flags, off_pout, off_plse;
   int list_cap;        // top-k gathered form: entries per kept-key list (0 when not used)
   size_t off_lidx, off_lrank, off_lzh, off_lcnt;
 };
@@ -126,6 +127,7 @@ int make_plan(const Shape& s, Plan* pl) {
     pl->off_rank = off; off = align256(off + sizeof(int32_t) * bh * s.Lk);
     pl->off_tau = off;  off = align256(off + sizeof(int32_t) * bh * s.Lq);
     pl->off_tmin = off; off = align256(off + sizeof(int32_t) * bh * ((s.Lk + p.block_n - 1) / p.block_n));
+    pl->off_sort = off; off = align256(off + topk_sort_ws_bytes(static_cast<int>(bh), s.Lk));
     if (path == 1 && !g_no_skip) pl->list_cap = topk_list_cap(s.keep_k, pl->q_per_block, s.Lk);
     if (pl->list_cap > 0) {
       const size_t nl = static_cast<size_t>(bh) * ((s.Lq + pl->q_per_block - 1) / pl->q_per_block);
@@ -179,8 +181,17 @@ int attn_fwd_plan(int B, int Hq, int Hkv, int Lq, int Lk, int d, int mask_kind, 
   return MI_ATTN_OK;
 }
 
-int attn_fwd_ex(const attn_fwd_args_t* a, void* stream) {
-  g_err.clear();
+}  // extern "C"
+
+// Fixed scratch of attn_fwd_noalloc (see scratch_for below).
+static __device__ __align__(256) unsigned char scratch[MI_ATTN_NOALLOC_MAX_WORKSPACE];
+
+namespace {
+
+// The forward call behind attn_fwd_ex / attn_fwd / attn_fwd_noalloc. Temporary device
+// memory comes from a stream-ordered allocation when fixed_ws is null, else from fixed_ws
+// (fixed_cap bytes), and the call is refused when its plan needs more.
+int fwd_impl(const attn_fwd_args_t* a, void* stream, char* fixed_ws, size_t fixed_cap) {
   if (a == nullptr) return fail(MI_ATTN_EINVAL, "args must not be NULL");
   Shape s{a->B, a->Hq, a->Hkv, a->Lq, a->Lk, a->d, a->mask_kind, a->window_left, a->keep_k, a->dtype};
   int rc = validate(s);
@@ -231,7 +242,13 @@ int attn_fwd_ex(const attn_fwd_args_t* a, void* stream) {
 
   hipStream_t st_ = static_cast<hipStream_t>(stream);
   char* ws = nullptr;
-  if (pl.pub.workspace_bytes > 0) {
+  const bool own_ws = fixed_ws == nullptr;
+  if (!own_ws) {
+    if (pl.pub.workspace_bytes > fixed_cap)
+      return fail(MI_ATTN_EUNSUPPORTED, "the call needs %zu bytes of temporary memory, above the %zu-byte fixed scratch",
+                  pl.pub.workspace_bytes, fixed_cap);
+    ws = fixed_ws;
+  } else if (pl.pub.workspace_bytes > 0) {
     hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&ws), pl.pub.workspace_bytes, st_);
     if (e != hipSuccess) return hip_fail(e, "hipMallocAsync(workspace)");
   }
@@ -271,7 +288,7 @@ int attn_fwd_ex(const attn_fwd_args_t* a, void* stream) {
     int32_t* tmin = reinterpret_cast<int32_t*>(ws + pl.off_tmin);
     what = "top-k selection";
     e = launch_topk(a->zero_hold, B * Hkv, Lq, Lk, a->keep_k, p.topk_causal, rank, tau, nullptr, tmin, pl.pub.block_n,
-                    st_);
+                    st_, topk_sort_ws_bytes(B * Hkv, Lk) > 0 ? ws + pl.off_sort : nullptr);
     p.rank = rank; p.tau = tau; p.tile_min_rank = tmin;
     if (e == hipSuccess && pl.list_cap > 0) {
       int32_t* lidx = reinterpret_cast<int32_t*>(ws + pl.off_lidx);
@@ -299,7 +316,7 @@ int attn_fwd_ex(const attn_fwd_args_t* a, void* stream) {
     what = "attention kernel";
     e = (pl.pub.path == 0) ? launch_row_kernel(p, a->dtype, st_) : launch_half_path(pl.pub.path, p, a->dtype, st_);
   }
-  if (ws != nullptr) {
+  if (own_ws && ws != nullptr) {
     const hipError_t ef = hipFreeAsync(ws, st_);
     if (e == hipSuccess && ef != hipSuccess) return hip_fail(ef, "hipFreeAsync(workspace)");
   }
@@ -307,10 +324,11 @@ int attn_fwd_ex(const attn_fwd_args_t* a, void* stream) {
   return MI_ATTN_OK;
 }
 
-int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv, int Lq,
-             int Lk, int d, float scale, int mask_kind, int window_left, const float* mask, const float* zero_hold,
-             int keep_k, int dtype, void* stream) {
-  // the contiguous layouts, the single [Lq, Lk] mask (dense kind only), causal top-k
+// attn_fwd's argument list as an argument block (contiguous layouts, the single [Lq, Lk]
+// mask for the dense kind, causal top-k)
+attn_fwd_args_t contiguous_args(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
+                                int Hkv, int Lq, int Lk, int d, float scale, int mask_kind, int window_left,
+                                const float* mask, const float* zero_hold, int keep_k, int dtype) {
   attn_fwd_args_t a{};
   a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Lq = Lq; a.Lk = Lk; a.d = d;
@@ -327,7 +345,77 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
   a.mask_stride[3] = 1;
   a.zero_hold = zero_hold; a.keep_k = keep_k; a.topk_causal = 1;
   a.dtype = dtype;
-  return attn_fwd_ex(&a, stream);
+  return a;
+}
+
+// ---- fixed scratch for attn_fwd_noalloc: one copy of this array per GPU, for the life of
+// the process. Host code never passes the array's name to a kernel (on the host it is only
+// a stand-in for the symbol); it uses the device address hipGetSymbolAddress returns, looked
+// up once per device with that device current and kept here.
+constexpr size_t kScratchBytes = MI_ATTN_NOALLOC_MAX_WORKSPACE;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// device address of `scratch` on the device `stream` belongs to (the current device for
+// the null stream)
+int scratch_for(hipStream_t stream, char** out) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  int dev = cur;
+  if (stream != nullptr) {
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+  }
+  if (dev < 0 || dev >= kMaxDevices) return fail(MI_ATTN_EUNSUPPORTED, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail(e, "hipSetDevice");
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || ptr == nullptr) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = static_cast<char*>(g_scratch_ptr[dev]);
+  return MI_ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_ex(const attn_fwd_args_t* a, void* stream) {
+  g_err.clear();
+  return fwd_impl(a, stream, nullptr, 0);
+}
+
+int attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv,
+                     int Lq, int Lk, int d, float scale, int mask_kind, int window_left, const float* mask,
+                     const float* zero_hold, int keep_k, int dtype, void* stream) {
+  g_err.clear();
+  const attn_fwd_args_t a = contiguous_args(q, k, v, out, lse, B, Hq, Hkv, Lq, Lk, d, scale, mask_kind, window_left,
+                                            mask, zero_hold, keep_k, dtype);
+  // validate and plan first, so that a refused call touches no device state
+  {
+    Shape sh{B, Hq, Hkv, Lq, Lk, d, mask_kind, window_left, keep_k, dtype};
+    int rc = validate(sh);
+    if (rc != MI_ATTN_OK) return rc;
+  }
+  char* ws = nullptr;
+  const int rc = scratch_for(static_cast<hipStream_t>(stream), &ws);
+  if (rc != MI_ATTN_OK) return rc;
+  return fwd_impl(&a, stream, ws, kScratchBytes);
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv, int Lq,
+             int Lk, int d, float scale, int mask_kind, int window_left, const float* mask, const float* zero_hold,
+             int keep_k, int dtype, void* stream) {
+  g_err.clear();
+  const attn_fwd_args_t a = contiguous_args(q, k, v, out, lse, B, Hq, Hkv, Lq, Lk, d, scale, mask_kind, window_left,
+                                            mask, zero_hold, keep_k, dtype);
+  return fwd_impl(&a, stream, nullptr, 0);
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse, const void* dout,

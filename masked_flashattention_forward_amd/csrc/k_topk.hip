@@ -478,23 +478,34 @@ __global__ __launch_bounds__(256) void mask_summary_kernel(AttnParams p, int blo
 
 }  // namespace
 
+size_t topk_sort_ws_bytes(int BH, int Lk) {
+  if (Lk > kMergeMaxKeys) return 0;
+  const int nchunks = (Lk + kChunk - 1) / kChunk;
+  return sizeof(u64) * static_cast<size_t>(BH) * nchunks * kChunk;
+}
+
 hipError_t launch_topk(const float* zh, int BH, int Lq, int Lk, int keep_k, int causal, int32_t* rank,
-                       int32_t* tau, uint32_t* keep_bits, int32_t* tile_min, int block_n, hipStream_t s) {
+                       int32_t* tau, uint32_t* keep_bits, int32_t* tile_min, int block_n, hipStream_t s,
+                       void* sort_ws) {
   if (tile_min != nullptr && (block_n <= 0 || block_n > kWave || kRankThreads % block_n != 0))
     return hipErrorInvalidValue;
   hipError_t e = hipSuccess;
   if (Lk <= kMergeMaxKeys) {
-    // sorted chunks live in a stream-ordered scratch buffer
+    // sorted chunks: the caller's workspace, or a stream-ordered scratch buffer
     const int nchunks = (Lk + kChunk - 1) / kChunk;
-    u64* sorted = nullptr;
-    e = hipMallocAsync(reinterpret_cast<void**>(&sorted), sizeof(u64) * static_cast<size_t>(BH) * nchunks * kChunk, s);
-    if (e != hipSuccess) return e;
+    u64* sorted = static_cast<u64*>(sort_ws);
+    if (sorted == nullptr) {
+      e = hipMallocAsync(reinterpret_cast<void**>(&sorted), topk_sort_ws_bytes(BH, Lk), s);
+      if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(chunk_sort_kernel, dim3(BH, nchunks), dim3(kChunkThreads), 0, s, zh, Lk, nchunks, sorted);
     hipLaunchKernelGGL(rank_merge_kernel, dim3(BH, (Lk + kRankThreads - 1) / kRankThreads), dim3(kRankThreads),
                        sizeof(u64) * nchunks * kChunk, s, zh, sorted, Lk, nchunks, rank, tile_min, block_n);
     e = hipGetLastError();
-    const hipError_t ef = hipFreeAsync(sorted, s);
-    if (e == hipSuccess) e = ef;
+    if (sort_ws == nullptr) {
+      const hipError_t ef = hipFreeAsync(sorted, s);
+      if (e == hipSuccess) e = ef;
+    }
   } else {
     hipLaunchKernelGGL(rank_count_kernel, dim3(BH, (Lk + 255) / 256), dim3(256), 0, s, zh, Lk, rank);
     e = hipGetLastError();
