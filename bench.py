@@ -256,6 +256,21 @@ def bench_config(name, iters=20, with_oracle=False):
     return res
 
 
+def bench_topk_select(B=2, H=16, L=32768, keep_k=1024, iters=10) -> dict:
+    """dynamic_mask_topk alone over a long cache (c5's selection at L keys and L query
+    rows, zero_hold N(0,1) from seed 5): ranks by chunk sort and run merge, then the
+    per-row thresholds."""
+    import torch
+    import masked_flashattention_forward_amd as mfa
+    zh = torch.from_numpy(np.random.default_rng(5).standard_normal((B, H, L), dtype=np.float32)).cuda()
+    tm = time_calls(lambda: mfa.dynamic_mask_topk(zh, L, keep_k), iters)
+    res = {"workload": f"dynamic_mask_topk zero_hold [{B},{H},{L}], {L} query rows, keep {keep_k}", **tm}
+    del zh
+    torch.cuda.empty_cache()
+    log(f"topk select {L}: {json.dumps(res)}")
+    return res
+
+
 def bench_read_stream(nbytes: int, iters=20) -> dict:
     """The plain HBM read stream (attn_read_stream) over a buffer the size of the decode
     workload's K and V, with and without the non-temporal hint: the practical ceiling the
@@ -534,6 +549,8 @@ def main():
                      "c1"):
             log(f"config {name}")
             configs[name] = bench_config(name, with_oracle=oracle_on and name != "c2w")
+        log("config c5 selection at 32768 keys")
+        configs["c5_topk_select_32k"] = bench_topk_select()
         log("config serve (paged varlen)")
         configs["serve"] = bench_paged_config("serve")
         log("config serve with ALiBi + softcap (paged varlen)")

@@ -8,8 +8,8 @@
 //      Caches of up to 8192 keys: every 512-key chunk is bitonic-sorted by one workgroup
 //      (in registers and wavefront shuffles, LDS only for the cross-wavefront stages),
 //      then each key's rank is the sum over chunks of the number of smaller words, found
-//      by a binary search in the sorted chunks staged in LDS. Longer caches use an
-//      O(Lk^2) counting kernel.
+//      by a binary search in the sorted chunks staged in LDS. Longer caches first merge
+//      the chunks into sorted runs of 8192 keys the same way, then search the runs.
 //   2. tau: per query row, the keep_k-th smallest rank among the row's allowed keys. One
 //      wavefront sweeps 32 consecutive rows, holding a bitmap of the ranks seen so far in
 //      registers. Under the causal mask a row allows one key more than the row before,
@@ -154,23 +154,111 @@ __global__ __launch_bounds__(kRankThreads) void rank_merge_kernel(const float* z
   }
 }
 
-// O(Lk^2) rank for caches longer than the merge path: rank_j = #keys ordered before j.
-__global__ __launch_bounds__(256) void rank_count_kernel(const float* zh, int Lk, int32_t* rank) {
-  __shared__ u64 tile[256];
+// Caches longer than kMergeMaxKeys: the sorted 512-key chunks are first merged into
+// sorted runs of kRunChunks chunks (8192 keys, staged in LDS like the merge above), then
+// each key's rank is the sum over the runs of a binary search in global memory
+// (log2(8192) + 1 probes per run, the runs of one (b,h) read from L2).
+constexpr int kRunChunks = kMergeMaxKeys / kChunk;  // chunks per run
+constexpr int kRunKeys = kMergeMaxKeys;
+
+// Run blockIdx.y of (b,h) = blockIdx.x: each key of the run moves to its place among the
+// run's keys (the count of smaller words over the run's sorted chunks). Slots at or past
+// the run's real keys (the padding of the last chunk) receive kPadKey.
+__global__ __launch_bounds__(kRankThreads) void run_merge_kernel(const u64* sorted, int Lk, int nchunks,
+                                                                   u64* runs) {
+  extern __shared__ u64 srt[];
   const int bh = blockIdx.x;
-  const float* z = zh + static_cast<long>(bh) * Lk;
-  const int j = blockIdx.y * 256 + threadIdx.x;
-  const u64 mine = (j < Lk) ? order_key(z, j) : kPadKey;
-  int cnt = 0;
-  for (int m0 = 0; m0 < Lk; m0 += 256) {
-    const int m = m0 + threadIdx.x;
-    tile[threadIdx.x] = (m < Lk) ? order_key(z, m) : kPadKey;
-    __syncthreads();
-    const int n = (Lk - m0) < 256 ? (Lk - m0) : 256;
-    for (int t = 0; t < n; ++t) cnt += (tile[t] < mine) ? 1 : 0;
-    __syncthreads();
+  const int run = blockIdx.y;
+  const int c0 = run * kRunChunks;
+  const int rc = (nchunks - c0) < kRunChunks ? (nchunks - c0) : kRunChunks;  // chunks in this run
+  const int n = rc * kChunk;
+  const u64* base = sorted + (static_cast<long>(bh) * nchunks + c0) * kChunk;
+  const uint4* src = reinterpret_cast<const uint4*>(base);
+  uint4* dst = reinterpret_cast<uint4*>(srt);
+  for (int t = threadIdx.x; t < n / 2; t += kRankThreads) dst[t] = src[t];
+  __syncthreads();
+  const int local = blockIdx.z * kRankThreads + threadIdx.x;  // slot in the run
+  if (local >= n) return;
+  u64* out = runs + (static_cast<long>(bh) * nchunks + c0) * kChunk;
+  const long real = static_cast<long>(Lk) - static_cast<long>(c0) * kChunk;  // real keys from the run start
+  if (local >= real) {
+    out[local] = kPadKey;
+    return;
   }
-  if (j < Lk) rank[static_cast<long>(bh) * Lk + j] = cnt;
+  // the run's keys are those of its chunks; a real key's place is the number of words
+  // below it over all of them (its own chunk included)
+  const u64 key = srt[local];
+  int cnt = 0;
+  for (int c = 0; c < rc; c += 4) {
+    const u64* sp[4];
+    int pos[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      sp[u] = srt + (c + u < rc ? c + u : 0) * kChunk;
+      pos[u] = 0;
+    }
+#pragma unroll
+    for (int step = kChunk / 2; step > 0; step >>= 1)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (sp[u][pos[u] + step - 1] < key) pos[u] += step;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (c + u < rc) cnt += pos[u] + (sp[u][pos[u]] < key ? 1 : 0);
+  }
+  out[cnt] = key;
+}
+
+// rank_j = sum over the sorted runs of the number of words below key_j (lower bound by
+// binary search over each run's kRunKeys or fewer slots), plus the per-tile minimum rank
+// when tile_min is given (as in rank_merge_kernel).
+__global__ __launch_bounds__(kRankThreads) void rank_runs_kernel(const float* zh, const u64* runs, int Lk,
+                                                                   int nchunks, int32_t* rank, int32_t* tile_min,
+                                                                   int block_n) {
+  __shared__ int32_t rk_s[kRankThreads];
+  const int bh = blockIdx.x;
+  const int nruns = (nchunks + kRunChunks - 1) / kRunChunks;
+  const u64* rb = runs + static_cast<long>(bh) * nchunks * kChunk;
+  const int j = blockIdx.y * kRankThreads + threadIdx.x;
+  int cnt = kAllKept;
+  if (j < Lk) {
+    const u64 key = order_key(zh + static_cast<long>(bh) * Lk, j);
+    cnt = 0;
+    for (int r = 0; r < nruns; r += 4) {
+      const u64* sp[4];
+      int len[4], pos[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int rr = r + u < nruns ? r + u : 0;
+        sp[u] = rb + static_cast<long>(rr) * kRunKeys;
+        const int rcn = (nchunks - rr * kRunChunks) < kRunChunks ? (nchunks - rr * kRunChunks) : kRunChunks;
+        len[u] = rcn * kChunk;
+        pos[u] = 0;
+      }
+#pragma unroll
+      for (int step = kRunKeys / 2; step > 0; step >>= 1)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (pos[u] + step <= len[u] && sp[u][pos[u] + step - 1] < key) pos[u] += step;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (r + u < nruns) cnt += pos[u] + (pos[u] < len[u] && sp[u][pos[u]] < key ? 1 : 0);
+    }
+    rank[static_cast<long>(bh) * Lk + j] = cnt;
+  }
+  if (tile_min == nullptr) return;
+  rk_s[threadIdx.x] = cnt;
+  __syncthreads();
+  const int ntiles = (Lk + block_n - 1) / block_n;
+  const int tile = blockIdx.y * (kRankThreads / block_n) + static_cast<int>(threadIdx.x);
+  if (static_cast<int>(threadIdx.x) < kRankThreads / block_n && tile < ntiles) {
+    int32_t mn = kAllKept;
+    for (int e = 0; e < block_n; ++e) {
+      const int32_t rv = rk_s[threadIdx.x * block_n + e];
+      mn = rv < mn ? rv : mn;
+    }
+    tile_min[static_cast<long>(bh) * ntiles + tile] = mn;
+  }
 }
 
 constexpr int kTauRowsPerWave = 32;
@@ -340,24 +428,6 @@ __global__ void keep_bits_kernel(const int32_t* rank, const int32_t* tau, int BH
   bits[t] = x;
 }
 
-// One wavefront per tile of block_n <= 64 keys: the smallest rank in it.
-__global__ __launch_bounds__(256) void tile_min_rank_kernel(const int32_t* rank, int BH, int Lk, int block_n,
-                                                              int32_t* out) {
-  const int nt = (Lk + block_n - 1) / block_n;
-  const long t = static_cast<long>(blockIdx.x) * 4 + threadIdx.x / kWave;
-  const int lane = threadIdx.x % kWave;
-  if (t >= static_cast<long>(BH) * nt) return;
-  const long bh = t / nt;
-  const int j = static_cast<int>(t % nt) * block_n + lane;
-  int32_t mn = (lane < block_n && j < Lk) ? rank[bh * Lk + j] : kAllKept;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const int32_t y = __shfl_xor(mn, o, kWave);
-    mn = y < mn ? y : mn;
-  }
-  if (lane == 0) out[t] = mn;
-}
-
 // Kept-key list of one (b, KV head, query block): the keys j <= p of the block's last row
 // whose rank is at most the threshold of its first row (thresholds do not grow with the
 // row position, so every row of the block keeps a subset), ascending, padded to a whole
@@ -479,9 +549,9 @@ __global__ __launch_bounds__(256) void mask_summary_kernel(AttnParams p, int blo
 }  // namespace
 
 size_t topk_sort_ws_bytes(int BH, int Lk) {
-  if (Lk > kMergeMaxKeys) return 0;
   const int nchunks = (Lk + kChunk - 1) / kChunk;
-  return sizeof(u64) * static_cast<size_t>(BH) * nchunks * kChunk;
+  const size_t one = sizeof(u64) * static_cast<size_t>(BH) * nchunks * kChunk;
+  return Lk > kMergeMaxKeys ? 2 * one : one;  // sorted chunks (and the merged runs)
 }
 
 hipError_t launch_topk(const float* zh, int BH, int Lq, int Lk, int keep_k, int causal, int32_t* rank,
@@ -490,31 +560,31 @@ hipError_t launch_topk(const float* zh, int BH, int Lq, int Lk, int keep_k, int 
   if (tile_min != nullptr && (block_n <= 0 || block_n > kWave || kRankThreads % block_n != 0))
     return hipErrorInvalidValue;
   hipError_t e = hipSuccess;
+  // sorted chunks (and, past kMergeMaxKeys, the merged runs): the caller's workspace, or
+  // a stream-ordered scratch buffer
+  const int nchunks = (Lk + kChunk - 1) / kChunk;
+  const size_t chunk_words = static_cast<size_t>(BH) * nchunks * kChunk;
+  u64* sorted = static_cast<u64*>(sort_ws);
+  if (sorted == nullptr) {
+    e = hipMallocAsync(reinterpret_cast<void**>(&sorted), topk_sort_ws_bytes(BH, Lk), s);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(chunk_sort_kernel, dim3(BH, nchunks), dim3(kChunkThreads), 0, s, zh, Lk, nchunks, sorted);
   if (Lk <= kMergeMaxKeys) {
-    // sorted chunks: the caller's workspace, or a stream-ordered scratch buffer
-    const int nchunks = (Lk + kChunk - 1) / kChunk;
-    u64* sorted = static_cast<u64*>(sort_ws);
-    if (sorted == nullptr) {
-      e = hipMallocAsync(reinterpret_cast<void**>(&sorted), topk_sort_ws_bytes(BH, Lk), s);
-      if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(chunk_sort_kernel, dim3(BH, nchunks), dim3(kChunkThreads), 0, s, zh, Lk, nchunks, sorted);
     hipLaunchKernelGGL(rank_merge_kernel, dim3(BH, (Lk + kRankThreads - 1) / kRankThreads), dim3(kRankThreads),
                        sizeof(u64) * nchunks * kChunk, s, zh, sorted, Lk, nchunks, rank, tile_min, block_n);
-    e = hipGetLastError();
-    if (sort_ws == nullptr) {
-      const hipError_t ef = hipFreeAsync(sorted, s);
-      if (e == hipSuccess) e = ef;
-    }
   } else {
-    hipLaunchKernelGGL(rank_count_kernel, dim3(BH, (Lk + 255) / 256), dim3(256), 0, s, zh, Lk, rank);
-    e = hipGetLastError();
-    if (e == hipSuccess && tile_min != nullptr) {
-      const long n = static_cast<long>(BH) * ((Lk + block_n - 1) / block_n);
-      hipLaunchKernelGGL(tile_min_rank_kernel, dim3(static_cast<unsigned>((n + 3) / 4)), dim3(256), 0, s, rank, BH,
-                         Lk, block_n, tile_min);
-      e = hipGetLastError();
-    }
+    u64* runs = sorted + chunk_words;
+    const int nruns = (nchunks + kRunChunks - 1) / kRunChunks;
+    hipLaunchKernelGGL(run_merge_kernel, dim3(BH, nruns, kRunKeys / kRankThreads), dim3(kRankThreads),
+                       sizeof(u64) * kRunKeys, s, sorted, Lk, nchunks, runs);
+    hipLaunchKernelGGL(rank_runs_kernel, dim3(BH, (Lk + kRankThreads - 1) / kRankThreads), dim3(kRankThreads), 0, s,
+                       zh, runs, Lk, nchunks, rank, tile_min, block_n);
+  }
+  e = hipGetLastError();
+  if (sort_ws == nullptr) {
+    const hipError_t ef = hipFreeAsync(sorted, s);
+    if (e == hipSuccess) e = ef;
   }
   if (e == hipSuccess) {
     if (!causal) {

@@ -202,7 +202,7 @@ def test_ex_random(i):
 def draw_topk(i):
     rng = np.random.default_rng(13000 + i)
     B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
-    Lk = int(np.exp(rng.uniform(0.0, np.log(20000.0))))
+    Lk = int(np.exp(rng.uniform(0.0, np.log(33000.0))))
     Lq = int(rng.integers(1, min(2 * Lk, 40_000_000 // Lk) + 1))
     keep = int(rng.integers(1, Lk + 6))
     causal = bool(rng.random() < 0.5)

@@ -63,3 +63,32 @@ def test_topk_c5_full_size():
     """Every (batch, head) of the top-k workload at its full size."""
     p = synth.config("c5")
     check_topk(p.zero_hold, p.Lq, p.keep_k, True, "c5 zero_hold [2,16,4096] k=1024, all 32 heads")
+
+
+@pytest.mark.parametrize("Lk", [8193, 16391, 32768])
+@pytest.mark.parametrize("causal", [True, False])
+def test_topk_long_caches(Lk, causal):
+    """Past 8192 keys the 512-key sorted chunks are merged into sorted runs of 8192 keys
+    before the ranks are counted: ranks, thresholds and keep bits bit-exact, with long
+    runs of tied values and -0.0 beside +0.0, including a partial last run and a partial
+    last chunk."""
+    rng = np.random.default_rng(Lk + int(causal))
+    zh = rng.standard_normal((1, 2, Lk)).astype(np.float32)
+    zh[0, 0, rng.random(Lk) < 0.4] = np.float32(0.75)
+    zh[0, 1, : Lk // 3] = -0.0
+    zh[0, 1, Lk // 3: Lk // 2] = 0.0
+    Lq = 40
+    check_topk(zh, Lq, 3000, causal, f"long cache Lk{Lk} causal{int(causal)}")
+
+
+def test_topk_attention_over_a_long_cache():
+    """Top-k attention (kept-key lists) over 20000 keys, against the oracle."""
+    from helpers import compare, run_gpu, run_oracle
+    import masked_flashattention_forward_amd as mfa
+    p = synth.make_problem("top-k attention Lk 20000", 1, 4, 2, 300, 20000, 128, "bf16", "topk", 1601, keep_k=700,
+                           with_zero_hold=True)
+    assert mfa.plan(p.B, p.Hq, p.Hkv, p.Lq, p.Lk, p.d, "topk", keep_k=p.keep_k)["topk_list_cap"] > 0
+    say(p.name)
+    out, lse = run_gpu(p, out_fill=float("nan"))
+    ref_o, ref_l = run_oracle(p)
+    compare(p, out, lse, ref_o, ref_l, label=p.name)
