@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define MI_ATTN_ABI_VERSION 8
+#define MI_ATTN_ABI_VERSION 9
 
 /* element types of q, k, v, out */
 #define MI_ATTN_F32 0
@@ -244,6 +244,31 @@ typedef struct {
 } attn_fwd_args_t;
 
 int attn_fwd_ex(const attn_fwd_args_t* args, void* stream);
+
+/*
+ * attn_fwd_dump: attn_fwd_ex (same arguments and results) that also writes the
+ * intermediates of ONE key tile of ONE workgroup of the MFMA prefill kernel, so that a
+ * single block can be compared with a reference step by step, as the
+ * flash-sparse-attention issue #11 page proposes for locating a wrong mask application
+ * ("Next Steps": dump the intermediate logits, mask values and output of one block).
+ * The workgroup is the one of batch b, KV head kv_head and query block query_block
+ * (attn_fwd_plan's block_m rows: the query rows of the KV head's G query heads, row
+ * r = (i - query_block * block_m / G) * G + (h - kv_head * G), query-major); tile is the
+ * 64-key tile index (key range [64 tile, 64 tile + 64)), or the tile of the block's
+ * kept-key list when topk_list_cap > 0. dump (device, fp32, MI_ATTN_DUMP_FLOATS) receives
+ *   S[128][64]   scale * q k^T + mask of the tile, natural-log units (-inf where hidden)
+ *   P[128][64]   exp(S - m), fp32 before rounding to the 16-bit type of the P V product
+ *   m[128]       the reference maximum m of the running softmax after this tile (natural
+ *                log units; it trails the true running maximum by less than 8 ln 2)
+ *   l[128]       the running sum after this tile, so l exp(m) = sum of exp(S) over the
+ *                keys visited so far
+ * Rows past the block's rows and tiles the kernel skips (hidden entirely) are not written.
+ * MI_ATTN_EUNSUPPORTED when the call does not take the MFMA prefill path (see
+ * attn_fwd_plan), MI_ATTN_EINVAL for an index out of range or a NULL dump.
+ */
+#define MI_ATTN_DUMP_FLOATS (2 * 128 * 64 + 2 * 128)
+int attn_fwd_dump(const attn_fwd_args_t* args, int b, int kv_head, int query_block, int tile, float* dump,
+                  void* stream);
 
 /*
  * attn_bwd: gradients of attn_fwd, as the InfiniTrain pull request #193 page pairs the

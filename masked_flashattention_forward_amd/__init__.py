@@ -26,7 +26,7 @@ class MiAttnError(RuntimeError):
         self.code = code
 
 
-ABI_VERSION = 8  # MI_ATTN_ABI_VERSION of include/mi_attn.h that this binding matches
+ABI_VERSION = 9  # MI_ATTN_ABI_VERSION of include/mi_attn.h that this binding matches
 
 
 class AttnPlan(ctypes.Structure):
@@ -64,6 +64,8 @@ _SIGS = {
                         + [ctypes.c_void_p] + [ctypes.c_int] * 3 + [ctypes.c_void_p] * 3 + [ctypes.c_float]
                         + [ctypes.c_int, ctypes.c_void_p]),
     "attn_fwd_ex": (ctypes.c_int, [ctypes.POINTER(AttnFwdArgs), ctypes.c_void_p]),
+    "attn_fwd_dump": (ctypes.c_int, [ctypes.POINTER(AttnFwdArgs)] + [ctypes.c_int] * 4
+                      + [ctypes.c_void_p, ctypes.c_void_p]),
     "attn_bwd": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_void_p] + [ctypes.c_void_p] * 4
                  + [ctypes.c_int] * 6 + [ctypes.c_float]
                  + [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
@@ -113,6 +115,7 @@ def abi_version() -> int:
 
 READ_STREAM_CHUNK = 2097152  # MI_ATTN_READ_STREAM_CHUNK
 NOALLOC_MAX_WORKSPACE = 33554432  # MI_ATTN_NOALLOC_MAX_WORKSPACE
+DUMP_FLOATS = 2 * 128 * 64 + 2 * 128  # MI_ATTN_DUMP_FLOATS
 
 
 def read_stream(src, nontemporal: bool = True, sink=None, stream=None):
@@ -218,7 +221,8 @@ def attn_fwd(q, k, v, *, scale=None, mask_kind="causal", window_left=0, mask=Non
 
 
 def attn_fwd_ex(q, k, v, *, scale=None, mask_kind="causal", window_left=0, mask=None, zero_hold=None, keep_k=0,
-                topk_causal=True, alibi_slopes=None, softcap=0.0, out=None, lse=None, return_lse=True, stream=None):
+                topk_causal=True, alibi_slopes=None, softcap=0.0, out=None, lse=None, return_lse=True, stream=None,
+                dump_at=None):
     """Masked attention forward with general layouts and score modifiers (attn_fwd_ex).
 
     q ``[B,Hq,Lq,d]`` and k/v ``[B,Hkv,Lk,d]`` may be any strided views whose last
@@ -227,7 +231,9 @@ def attn_fwd_ex(q, k, v, *, scale=None, mask_kind="causal", window_left=0, mask=
     ``[B,Hq,Lq,Lk]`` (dense kind; with ``"topk"`` it is optional and added to the kept
     keys). ``topk_causal=False`` selects the top-k among all keys. ``alibi_slopes`` fp32
     ``[Hq]``; ``softcap`` > 0 caps the scaled scores. ``out`` may be strided too.
-    Returns ``(out, lse)``.
+    Returns ``(out, lse)``. ``dump_at=(b, kv_head, query_block, tile)`` runs attn_fwd_dump
+    instead and returns ``(out, lse, dump)`` with dump a dict of the tile's intermediates
+    (``S``, ``P`` ``[128, 64]``, ``m``, ``l`` ``[128]``, NaN where not written).
     """
     import torch
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -282,8 +288,17 @@ def attn_fwd_ex(q, k, v, *, scale=None, mask_kind="causal", window_left=0, mask=
     a.alibi_slopes = None if alibi_slopes is None else alibi_slopes.data_ptr()
     a.softcap = float(softcap)
     a.dtype = _dtype_code(q)
-    _check(lib().attn_fwd_ex(ctypes.byref(a), _stream_handle(q.device, stream)))
-    return out, lse
+    if dump_at is None:
+        _check(lib().attn_fwd_ex(ctypes.byref(a), _stream_handle(q.device, stream)))
+        return out, lse
+    buf = torch.full((DUMP_FLOATS,), float("nan"), dtype=torch.float32, device=q.device)
+    b, g, qb, tile = (int(x) for x in dump_at)
+    _check(lib().attn_fwd_dump(ctypes.byref(a), b, g, qb, tile, ctypes.c_void_p(buf.data_ptr()),
+                               _stream_handle(q.device, stream)))
+    rows, keys = 128, 64
+    dump = {"S": buf[:rows * keys].view(rows, keys), "P": buf[rows * keys:2 * rows * keys].view(rows, keys),
+            "m": buf[2 * rows * keys:2 * rows * keys + rows], "l": buf[2 * rows * keys + rows:]}
+    return out, lse, dump
 
 
 def attn_bwd(q, k, v, out, lse, dout, *, scale=None, mask_kind="causal", window_left=0, mask=None, zero_hold=None,

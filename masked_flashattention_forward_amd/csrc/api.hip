@@ -71,6 +71,8 @@ int validate(const Shape& s) {
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+constexpr int kSummaryMinTiles = 32;  // dense-mask summary from this many key tiles up
+
 struct Plan {
   attn_plan_t pub;
   int q_per_block;     // query positions per workgroup (dense-mask summary granularity)
@@ -137,7 +139,12 @@ int make_plan(const Shape& s, Plan* pl) {
       pl->off_lcnt = off;  off = align256(off + sizeof(int32_t) * nl);
     }
   }
-  if (s.mask_kind == MI_ATTN_MASK_DENSE && path != 0) {
+  // Dense masks: per-tile summary flags let the kernels skip tiles the mask hides
+  // entirely. For short key ranges the separate summary pass and its buffer cost more than
+  // visiting every tile (each visited tile reads its mask entries anyway), so the flags
+  // are only built from kSummaryMinTiles key tiles up.
+  const int key_tiles = (s.Lk + p.block_n - 1) / p.block_n;
+  if (s.mask_kind == MI_ATTN_MASK_DENSE && path != 0 && key_tiles >= kSummaryMinTiles) {
     p.mask_summary = 1;
     pl->off_flags = off;
     off = align256(off + static_cast<size_t>(s.flag_b) * s.flag_g *
@@ -191,7 +198,13 @@ namespace {
 // The forward call behind attn_fwd_ex / attn_fwd / attn_fwd_noalloc. Temporary device
 // memory comes from a stream-ordered allocation when fixed_ws is null, else from fixed_ws
 // (fixed_cap bytes), and the call is refused when its plan needs more.
-int fwd_impl(const attn_fwd_args_t* a, void* stream, char* fixed_ws, size_t fixed_cap) {
+struct DumpReq {
+  float* buf;
+  int b, kv_head, query_block, tile;
+};
+
+int fwd_impl(const attn_fwd_args_t* a, void* stream, char* fixed_ws, size_t fixed_cap,
+             const DumpReq* dump = nullptr) {
   if (a == nullptr) return fail(MI_ATTN_EINVAL, "args must not be NULL");
   Shape s{a->B, a->Hq, a->Hkv, a->Lq, a->Lk, a->d, a->mask_kind, a->window_left, a->keep_k, a->dtype};
   int rc = validate(s);
@@ -239,6 +252,17 @@ int fwd_impl(const attn_fwd_args_t* a, void* stream, char* fixed_ws, size_t fixe
   Plan pl;
   rc = make_plan(s, &pl);
   if (rc != MI_ATTN_OK) return rc;
+  if (dump != nullptr) {
+    if (pl.pub.path != 1)
+      return fail(MI_ATTN_EUNSUPPORTED, "the one-tile dump runs on the MFMA prefill path only (this call takes path %d)",
+                  pl.pub.path);
+    const int nqb = (a->Lq + pl.q_per_block - 1) / pl.q_per_block;
+    const int ntiles = pl.list_cap > 0 ? pl.list_cap / 64 : (a->Lk + pl.pub.block_n - 1) / pl.pub.block_n;
+    if (dump->buf == nullptr || dump->b < 0 || dump->b >= a->B || dump->kv_head < 0 || dump->kv_head >= a->Hkv ||
+        dump->query_block < 0 || dump->query_block >= nqb || dump->tile < 0 || dump->tile >= ntiles)
+      return fail(MI_ATTN_EINVAL, "dump: need a buffer, b < %d, kv_head < %d, query_block < %d and tile < %d", a->B,
+                  a->Hkv, nqb, ntiles);
+  }
 
   hipStream_t st_ = static_cast<hipStream_t>(stream);
   char* ws = nullptr;
@@ -279,6 +303,12 @@ int fwd_impl(const attn_fwd_args_t* a, void* stream, char* fixed_ws, size_t fixe
   }
   p.block_n = pl.pub.block_n;
   p.q_per_block = pl.q_per_block;
+  if (dump != nullptr) {
+    p.dump = dump->buf;
+    p.dump_bg = dump->b * Hkv + dump->kv_head;
+    p.dump_qb = dump->query_block;
+    p.dump_tile = dump->tile;
+  }
 
   hipError_t e = hipSuccess;
   const char* what = "";
@@ -389,6 +419,13 @@ extern "C" {
 int attn_fwd_ex(const attn_fwd_args_t* a, void* stream) {
   g_err.clear();
   return fwd_impl(a, stream, nullptr, 0);
+}
+
+int attn_fwd_dump(const attn_fwd_args_t* a, int b, int kv_head, int query_block, int tile, float* dump,
+                  void* stream) {
+  g_err.clear();
+  const DumpReq req{dump, b, kv_head, query_block, tile};
+  return fwd_impl(a, stream, nullptr, 0, &req);
 }
 
 int attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv,

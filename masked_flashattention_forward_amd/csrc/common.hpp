@@ -131,6 +131,11 @@ struct AttnParams {
   // of one KV head query-major (row r = i * G + (h - g * G)): -lse * log2(e) (-inf for a
   // row that sees no key), rowsum(dout * out), and the row's top-k threshold (top-k) or
   // query index i (dense mask). The dQ kernel writes them; the dK/dV kernel reads them.
+  // one-tile dump (attn_fwd_dump): when dump != nullptr, the workgroup of (batch * Hkv +
+  // KV head) = dump_bg and query block dump_qb writes the intermediates of key tile
+  // dump_tile (see MI_ATTN_DUMP_FLOATS); nullptr otherwise
+  float* dump;
+  int dump_bg, dump_qb, dump_tile;
   const void* dout;
   void* dq;
   void* dk;

@@ -151,7 +151,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(AttnParams p) {
       (static_cast<long>(p.flag_b > 1 ? b : 0) * p.flag_g + (p.flag_g > 1 ? g : 0)) * ntiles_all;
   auto tile_live = [&](int t) -> bool {
     if (p.no_skip) return true;
-    if constexpr (MK == MI_ATTN_MASK_DENSE) return p.tile_live[flag_base + t] != 0;
+    if constexpr (MK == MI_ATTN_MASK_DENSE) return p.tile_live == nullptr || p.tile_live[flag_base + t] != 0;
     if constexpr (MK == MI_ATTN_MASK_TOPK) return p.tile_min_rank[static_cast<long>(bg) * ntiles_all + t] <= tau_blk;
     return true;
   };

@@ -32,6 +32,7 @@ using namespace mfma;
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kBlockM = 32 * kWaves;  // query rows per workgroup
+constexpr int kDumpRows = kBlockM;      // rows of a one-tile dump
 static_assert(kBlockM == kVarlenPrefillRows, "varlen partial slots hold one workgroup's rows");
 
 template <int D, int BN>
@@ -218,9 +219,50 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN, EXT>)) void pr
   // dense-mask summary flags of this (batch, KV head), query block
   const long flag_base = ((static_cast<long>(p.flag_b > 1 ? b : 0) * p.flag_g + (p.flag_g > 1 ? g : 0)) * nqb + qb) *
                          ntiles_all;
+  // Dense masks over short key ranges come without summary flags (no separate pass):
+  // the workgroup reads its own rows' mask entries over its tiles (at most 32 of them)
+  // once, up front, and keeps one live bit per tile.
+  uint32_t live_bits = 0xffffffffu;
+  if constexpr (MK == MI_ATTN_MASK_DENSE) {
+    if (p.tile_live == nullptr && !p.no_skip && t_hi > t_lo && t_hi - t_lo <= 32) {
+      __shared__ uint32_t live_shared;
+      if (tid == 0) live_shared = 0u;
+      // rows whose entries differ: the block's positions, times its query heads when the
+      // mask varies with the head
+      const int nh = (p.Hq > 1 && p.ms[1] != 0) ? p.G : 1;
+      const int j_lo = t_lo * BN;
+      const int nk = min(t_hi * BN, Lk) - j_lo;
+      const int total = (i_last - i_first + 1) * nh * nk;
+      const float* mb = p.mask + b * p.ms[0] + static_cast<long>(g) * p.G * p.ms[1];
+      uint32_t bits = 0u;
+      // eight independent loads per pass, so their latencies overlap
+      constexpr int kUnroll = 8;
+      for (int e0 = tid; e0 < total; e0 += kUnroll * kThreads) {
+        float mv[kUnroll];
+        int tj[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          const int e = e0 + u * kThreads;
+          const int r = e / nk;
+          const int j = j_lo + (e - r * nk);
+          tj[u] = (j - j_lo) / BN;
+          mv[u] = e < total ? mb[(r % nh) * p.ms[1] + static_cast<long>(i_first + r / nh) * p.ms[2] + j * p.ms[3]]
+                            : kNegInf;
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+          if (mv[u] > kNegInf) bits |= 1u << tj[u];
+      }
+      __syncthreads();
+      if (bits != 0u) atomicOr(&live_shared, bits);
+      __syncthreads();
+      live_bits = live_shared;
+    }
+  }
   auto tile_live = [&](int t) -> bool {
     if (GATHER || p.no_skip) return true;
-    if constexpr (MK == MI_ATTN_MASK_DENSE) return p.tile_live[flag_base + t] != 0;
+    if constexpr (MK == MI_ATTN_MASK_DENSE)
+      return p.tile_live == nullptr ? ((live_bits >> (t - t_lo)) & 1u) != 0 : p.tile_live[flag_base + t] != 0;
     if constexpr (MK == MI_ATTN_MASK_TOPK)
       return p.tile_min_rank[static_cast<long>(bg) * ntiles_all + t] <= tau_blk;
     return true;
@@ -504,6 +546,16 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN, EXT>)) void pr
       cm = 1.f;
     }
 
+    // one-tile dump (a debug call): the scaled, masked logits in natural-log units
+    const bool dump_here = p.dump != nullptr && bg == p.dump_bg && qb == p.dump_qb && t == p.dump_tile;
+    if (dump_here && row_ok) {
+      float* ds = p.dump + static_cast<long>(rloc) * BN;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ds[kb * 32 + (e / 4) * 8 + hf * 4 + e % 4] = sacc[kb][e] * cm * kLn2;
+    }
+
     // online softmax (log2 domain), guarded against all -inf tiles and rows
     float mx4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};  // four independent chains
 #pragma unroll
@@ -537,6 +589,21 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN, EXT>)) void pr
     }
     l_run = fmaf(l_run, alpha, (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]));
     m_run = m_next;
+    if (dump_here) {
+      // P (fp32, before rounding to 16 bits) against the reference max m, that max and
+      // the running sum after this tile, both in natural-log units (rows of the block only)
+      const float l_all = sum_halves(l_run);  // every lane: a cross-lane exchange
+      float* dp = p.dump + kDumpRows * BN + static_cast<long>(rloc) * BN;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (row_ok) dp[kb * 32 + (e / 4) * 8 + hf * 4 + e % 4] = fast_exp2(fmaf(sacc[kb][e], cm, -m_use));
+      if (hf == 0 && row_ok) {
+        p.dump[2 * kDumpRows * BN + rloc] = m_use * kLn2;
+        p.dump[2 * kDumpRows * BN + kDumpRows + rloc] = l_all;
+      }
+    }
     if (!__all(alpha == 1.f)) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;

@@ -190,12 +190,14 @@ def test_ex_workloads_full_size_sampled(name):
     compare(p, out, lse, ref_o, ref_l, heads=heads, label=f"{name} (sampled heads)")
 
 
+@pytest.mark.parametrize("Lk", [513, 2100])
 @pytest.mark.parametrize("Lq,path", [(1, 2), (1, 1), (33, 1), (33, None)])
-def test_mqa_per_head_mask_first_head_hidden(Lq, path):
+def test_mqa_per_head_mask_first_head_hidden(Lq, path, Lk):
     # One KV head and mask rows per query head, head 0 seeing no key at all: the dense-mask
     # tile summary must scan every query head of the group, not only the first (a tile
-    # hidden from head 0 is still visible to the others).
-    Hq, Lk = 8, 513
+    # hidden from head 0 is still visible to the others). 2100 keys build the summary
+    # flags on both paths, 513 keys visit every tile without them.
+    Hq = 8
     m = per_head_mask(21 + Lq, (1, Hq), Lq, Lk)
     m[0, 0] = -np.inf
     p = synth.make_problem(f"MQA per-head mask Lq{Lq}", 1, Hq, 1, Lq, Lk, 128, "bf16", "dense", 970 + Lq)

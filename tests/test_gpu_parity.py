@@ -80,6 +80,29 @@ def test_small_configs_full(name):
                                        rtol=0, atol=1e-2)
 
 
+@pytest.mark.parametrize("Lq,Lk,path", [(16, 2900, 1), (3, 2900, 2), (130, 4100, 1), (16, 700, 1)])
+def test_dense_mask_with_and_without_summary(Lq, Lk, path):
+    """Dense masks over long key ranges build per-tile summary flags and skip the tiles
+    the mask hides (mostly hidden here: a window of 200 keys, and a block of keys near
+    the start visible to a few rows); short ranges visit every tile. Both against the
+    oracle, on the prefill and decode paths."""
+    import masked_flashattention_forward_amd as mfa
+    m = synth.window_dense_mask(Lq, Lk, Lk - Lq, 200)
+    m[: max(1, Lq // 3), 70:90] = 0.5
+    p = synth.make_problem(f"dense summary Lq{Lq} Lk{Lk} path{path}", 2, 8, 2, Lq, Lk, 128, "bf16", "dense",
+                           1500 + Lk + Lq, mask=m)
+    pl = mfa.plan(p.B, p.Hq, p.Hkv, p.Lq, p.Lk, p.d, "dense")
+    assert pl["mask_summary"] == (Lk >= 2048), pl
+    say(p.name)
+    try:
+        mfa.set_debug(force_path=path)
+        out, lse = run_gpu(p, out_fill=float("nan"))
+    finally:
+        mfa.set_debug()
+    ref_o, ref_l = run_oracle(p)
+    compare(p, out, lse, ref_o, ref_l, label=p.name)
+
+
 def test_c2_dense_equals_window_kind():
     """Two routes on the GPU: the dense window mask over 700 keys and the window kind
     over the first 576 keys give the same result."""

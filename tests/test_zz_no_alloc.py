@@ -67,9 +67,11 @@ PAIRS = [
     # split-KV decode partials, then a smaller decode
     (("decode big", 4, 32, 8, 1, 8192, 128, "bf16", "causal", 1403, {}),
      ("decode small", 2, 8, 2, 1, 3000, 128, "bf16", "causal", 1404, {})),
-    # dense-mask tile flags, then smaller flags
-    (("dense big", 4, 32, 8, 16, 700, 128, "bf16", "dense", 1405, dict(mask=synth.window_dense_mask(16, 700, 560, 60))),
-     ("dense small", 1, 4, 2, 9, 300, 64, "bf16", "dense", 1406, dict(mask=synth.window_dense_mask(9, 300, 250, 20)))),
+    # dense-mask tile flags (built from 2048 keys up), then smaller flags
+    (("dense big", 4, 32, 8, 16, 2900, 128, "bf16", "dense", 1405,
+      dict(mask=synth.window_dense_mask(16, 2900, 2884, 300))),
+     ("dense small", 1, 4, 2, 9, 2100, 64, "bf16", "dense", 1406,
+      dict(mask=synth.window_dense_mask(9, 2100, 2091, 200)))),
 ]
 
 
