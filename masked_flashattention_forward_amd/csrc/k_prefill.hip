@@ -61,6 +61,13 @@ constexpr int kLog2BN = 6;  // 64-key tiles
 template <int D, int MK, bool VARLEN, bool EXT>
 constexpr int kMinBlocks = D == 128 ? 2 : (MK == MI_ATTN_MASK_TOPK || EXT) ? 2 : VARLEN ? 3 : 4;
 
+// Softmax against the running max without a per-tile max reduction (see the tile loop).
+// Its second code path does not fit the registers at d = 64 (4 workgroups per CU, 128
+// VGPRs) nor beside the score modifiers' state, and for a dense mask it would read the
+// mask entries of a tile twice; those reduce the max first.
+template <int D, int MK, bool EXT>
+constexpr bool kRunningMaxExps = D == 128 && !EXT && MK != MI_ATTN_MASK_DENSE;
+
 // GATHER (top-k only): tiles are consecutive 64-key runs of the block's kept-key list
 // (AttnParams::list_*) instead of consecutive keys, so only keys some row of the block
 // keeps are loaded and multiplied.
@@ -490,9 +497,11 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN, EXT>)) void pr
     const int j0 = t * BN;
 
     // S^T = K Q^T. The first 32-key block's K fragments are read before its first MFMA;
-    // afterwards each MFMA overlaps the read of one fragment of the next block.
+    // afterwards each MFMA overlaps the read of one fragment of the next block. (A lambda,
+    // as are the mask below: the rare tile that moves the running max computes its logits
+    // a second time, K still being in LDS, rather than keeping them live.)
     f32x16_t sacc[NKB];
-    {
+    auto qk = [&]() {
       constexpr int NDC = D / 16;
       u32x4_t kf[NKB][NDC];
 #pragma unroll
@@ -515,11 +524,13 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN, EXT>)) void pr
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
       }
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, NDC, 0);
-    }
+    };
+    qk();
 
     // mask (tiles the mask does not cover entirely); masked tiles move to the log2
     // domain here (cm = 1), unmasked ones are scaled inside the exponent (cm = cexp)
     float cm = cexp;
+    auto apply_mask = [&]() {
     if constexpr (GATHER) {
       const int32_t* xr = reinterpret_cast<const int32_t*>(vs + TL::vBytes);
       const float* xzl = reinterpret_cast<const float*>(xr + BN);
@@ -545,6 +556,8 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN, EXT>)) void pr
       mods_tile<NKB>(sacc, j0, hf, md);  // a tile every row sees: the score modifiers alone
       cm = 1.f;
     }
+    };
+    apply_mask();
 
     // one-tile dump (a debug call): the scaled, masked logits in natural-log units
     const bool dump_here = p.dump != nullptr && bg == p.dump_bg && qb == p.dump_qb && t == p.dump_tile;
@@ -556,57 +569,132 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN, EXT>)) void pr
         for (int e = 0; e < 16; ++e) ds[kb * 32 + (e / 4) * 8 + hf * 4 + e % 4] = sacc[kb][e] * cm * kLn2;
     }
 
-    // online softmax (log2 domain), guarded against all -inf tiles and rows
-    float mx4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};  // four independent chains
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx4[e & 3] = fmaxf(mx4[e & 3], sacc[kb][e]);
-    float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
-    mx = max_halves(mx) * cm;
-    const float m_next = (mx > m_run + kRescaleThreshold) ? mx : m_run;
-    const float m_use = (m_next == kNegInf) ? 0.f : m_next;
-    const float alpha = fast_exp2(m_run - m_use);  // 1 when the max did not move, 0 from -inf
-    float ps4[4] = {0.f, 0.f, 0.f, 0.f};  // four independent chains
     u32x4_t preg[BN / 16];
+    if constexpr (kRunningMaxExps<D, MK, EXT>) {
+      // Online softmax (log2 domain) against the running max m_run as it stands, with no
+      // per-tile max reduction. That is exact online softmax as long as no exponential
+      // exceeds 2^kRescaleThreshold, which holds whenever this lane's sum of them does
+      // (the sum also fails for inf / NaN, i.e. a row with no visible key so far). Only
+      // when some lane's sum fails does the wave compute the tile's logits again, reduce
+      // their row maxima, move m to the exact running max, rescale l and O and take the
+      // exponentials again; a dump takes that exact path too.
+      auto exps = [&](float m_ref) -> float {  // P packed for the PV operand; the lane's sum
+        float ps4[4] = {0.f, 0.f, 0.f, 0.f};  // four independent chains
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
+        for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        float pv[8];
+          for (int half = 0; half < 2; ++half) {
+            float pv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pv[e] = fast_exp2(fmaf(sacc[kb][half * 8 + e], cm, -m_use));
-          ps4[e & 3] += pv[e];
+            for (int e = 0; e < 8; ++e) {
+              pv[e] = fast_exp2(fmaf(sacc[kb][half * 8 + e], cm, -m_ref));
+              ps4[e & 3] += pv[e];
+            }
+            u32x4_t pk;
+            pk.x = pack2(T{}, pv[0], pv[1]);
+            pk.y = pack2(T{}, pv[2], pv[3]);
+            pk.z = pack2(T{}, pv[4], pv[5]);
+            pk.w = pack2(T{}, pv[6], pv[7]);
+            preg[kb * 2 + half] = pk;
+          }
         }
-        u32x4_t pk;
-        pk.x = pack2(T{}, pv[0], pv[1]);
-        pk.y = pack2(T{}, pv[2], pv[3]);
-        pk.z = pack2(T{}, pv[4], pv[5]);
-        pk.w = pack2(T{}, pv[6], pv[7]);
-        preg[kb * 2 + half] = pk;
+        return (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
+      };
+      float m_ref = m_run;
+      float lsum = exps(m_ref);
+      if (!__all(lsum <= kFastSumLimit) || dump_here) {
+        // a compiler-only memory barrier: K is read from LDS again, not kept in registers
+        asm volatile("" ::: "memory");
+        qk();
+        cm = cexp;
+        apply_mask();
+        float mx4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};  // four independent chains
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mx4[e & 3] = fmaxf(mx4[e & 3], sacc[kb][e]);
+        const float mx = max_halves(fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]))) * cm;
+        const float m_next = fmaxf(m_run, mx);
+        m_ref = (m_next == kNegInf) ? 0.f : m_next;
+        const float alpha = fast_exp2(m_run - m_ref);  // 0 from -inf
+        if (dump_here) {
+          // P (fp32, before rounding to 16 bits) against the reference max m
+          float* dp = p.dump + kDumpRows * BN + static_cast<long>(rloc) * BN;
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+              if (row_ok) dp[kb * 32 + (e / 4) * 8 + hf * 4 + e % 4] = fast_exp2(fmaf(sacc[kb][e], cm, -m_ref));
+        }
+        lsum = exps(m_ref);
+        l_run *= alpha;
+        if (!__all(alpha == 1.f)) {
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+        }
+        m_run = m_next;
       }
-    }
-    l_run = fmaf(l_run, alpha, (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]));
-    m_run = m_next;
-    if (dump_here) {
-      // P (fp32, before rounding to 16 bits) against the reference max m, that max and
-      // the running sum after this tile, both in natural-log units (rows of the block only)
-      const float l_all = sum_halves(l_run);  // every lane: a cross-lane exchange
-      float* dp = p.dump + kDumpRows * BN + static_cast<long>(rloc) * BN;
+      l_run += lsum;
+      if (dump_here) {
+        // that max and the running sum after this tile, in natural-log units
+        const float l_all = sum_halves(l_run);  // every lane: a cross-lane exchange
+        if (hf == 0 && row_ok) {
+          p.dump[2 * kDumpRows * BN + rloc] = m_ref * kLn2;
+          p.dump[2 * kDumpRows * BN + kDumpRows + rloc] = l_all;
+        }
+      }
+    } else {
+      // online softmax (log2 domain), guarded against all -inf tiles and rows
+      float mx4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};  // four independent chains
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (row_ok) dp[kb * 32 + (e / 4) * 8 + hf * 4 + e % 4] = fast_exp2(fmaf(sacc[kb][e], cm, -m_use));
-      if (hf == 0 && row_ok) {
-        p.dump[2 * kDumpRows * BN + rloc] = m_use * kLn2;
-        p.dump[2 * kDumpRows * BN + kDumpRows + rloc] = l_all;
-      }
-    }
-    if (!__all(alpha == 1.f)) {
+        for (int e = 0; e < 16; ++e) mx4[e & 3] = fmaxf(mx4[e & 3], sacc[kb][e]);
+      float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
+      mx = max_halves(mx) * cm;
+      const float m_next = (mx > m_run + kRescaleThreshold) ? mx : m_run;
+      const float m_use = (m_next == kNegInf) ? 0.f : m_next;
+      const float alpha = fast_exp2(m_run - m_use);  // 1 when the max did not move, 0 from -inf
+      float ps4[4] = {0.f, 0.f, 0.f, 0.f};  // four independent chains
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          float pv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            pv[e] = fast_exp2(fmaf(sacc[kb][half * 8 + e], cm, -m_use));
+            ps4[e & 3] += pv[e];
+          }
+          u32x4_t pk;
+          pk.x = pack2(T{}, pv[0], pv[1]);
+          pk.y = pack2(T{}, pv[2], pv[3]);
+          pk.z = pack2(T{}, pv[4], pv[5]);
+          pk.w = pack2(T{}, pv[6], pv[7]);
+          preg[kb * 2 + half] = pk;
+        }
+      }
+      l_run = fmaf(l_run, alpha, (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]));
+      m_run = m_next;
+      if (dump_here) {
+        // P (fp32, before rounding to 16 bits) against the reference max m, that max and
+        // the running sum after this tile, both in natural-log units (rows of the block only)
+        const float l_all = sum_halves(l_run);  // every lane: a cross-lane exchange
+        float* dp = p.dump + kDumpRows * BN + static_cast<long>(rloc) * BN;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (row_ok) dp[kb * 32 + (e / 4) * 8 + hf * 4 + e % 4] = fast_exp2(fmaf(sacc[kb][e], cm, -m_use));
+        if (hf == 0 && row_ok) {
+          p.dump[2 * kDumpRows * BN + rloc] = m_use * kLn2;
+          p.dump[2 * kDumpRows * BN + kDumpRows + rloc] = l_all;
+        }
+      }
+      if (!__all(alpha == 1.f)) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+      }
     }
 
     // O^T += V^T P^T. The V^T operand comes from two transposed reads: lane (16 * g + i)

@@ -88,6 +88,9 @@ constexpr int kSchedDsRead = 0x100;
 // without loss of relative precision; l and the output use the same m, so the result is
 // unchanged up to rounding, and most tiles skip rescaling the output accumulator.
 constexpr float kRescaleThreshold = 8.0f;
+// A lane's sum of exponentials up to this bound (2^kRescaleThreshold) proves that none of
+// them exceeds it: the prefill kernel's test for keeping the running max of a tile.
+constexpr float kFastSumLimit = 256.0f;
 
 // Workgroup -> (KV group, query block). Workgroups are handed to the 8 XCDs round-robin;
 // the remap gives each XCD a contiguous run of KV groups (their K/V stays in that XCD's
