@@ -162,6 +162,10 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN, EXT>)) void pr
   const float cexp = fabsf(p.scale) * kLog2e;
   // score modifiers and the dense mask row of this lane (rows past the block read row i_first)
   const Mods md = make_mods<EXT>(p, cexp, b, h_row, i_row, pos, MK == MI_ATTN_MASK_DENSE || MK == MI_ATTN_MASK_TOPK);
+  // dense: every lane's mask row is contiguous and 16-byte aligned (the strides of the
+  // dimensions in use and the base are multiples of 4 floats)
+  const bool dense_vec = MK == MI_ATTN_MASK_DENSE && p.mask != nullptr && p.ms[3] == 1 && (p.ms[2] & 3) == 0 &&
+                         (p.ms[1] & 3) == 0 && (p.ms[0] & 3) == 0 && (reinterpret_cast<uintptr_t>(p.mask) & 15) == 0;
   u32x4_t qreg[D / 16];
 #pragma unroll
   for (int dc = 0; dc < D / 16; ++dc) {
@@ -239,26 +243,45 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN, EXT>)) void pr
       const int nh = (p.Hq > 1 && p.ms[1] != 0) ? p.G : 1;
       const int j_lo = t_lo * BN;
       const int nk = min(t_hi * BN, Lk) - j_lo;
-      const int total = (i_last - i_first + 1) * nh * nk;
+      const int nrows = (i_last - i_first + 1) * nh;
       const float* mb = p.mask + b * p.ms[0] + static_cast<long>(g) * p.G * p.ms[1];
       uint32_t bits = 0u;
-      // eight independent loads per pass, so their latencies overlap
-      constexpr int kUnroll = 8;
-      for (int e0 = tid; e0 < total; e0 += kUnroll * kThreads) {
-        float mv[kUnroll];
-        int tj[kUnroll];
+      // A thread takes a group of keys (4 consecutive ones when rows are contiguous and
+      // aligned, else 1) of every row, consecutive threads consecutive groups. Rows advance
+      // as (position, head) pairs with wave-uniform offsets, sixteen independent loads per
+      // pass so their latencies overlap. A group never straddles a tile.
+      constexpr int kUnroll = 16;
+      const int gk = dense_vec ? 4 : 1;
+      for (int kk = tid * gk; kk < nk; kk += kThreads * gk) {
+        const float* col = mb + static_cast<long>(j_lo + kk) * p.ms[3];
+        const bool whole = dense_vec && kk + 3 < nk;  // a 16-byte load covers the group
+        int h = 0;
+        long roff = static_cast<long>(i_first) * p.ms[2];  // offset of row (i_first, head 0)
+        bool live = false;
+        for (int r0 = 0; r0 < nrows; r0 += kUnroll) {
+          float mv[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-          const int e = e0 + u * kThreads;
-          const int r = e / nk;
-          const int j = j_lo + (e - r * nk);
-          tj[u] = (j - j_lo) / BN;
-          mv[u] = e < total ? mb[(r % nh) * p.ms[1] + static_cast<long>(i_first + r / nh) * p.ms[2] + j * p.ms[3]]
-                            : kNegInf;
+          for (int u = 0; u < kUnroll; ++u) {
+            const float* a = col + roff + h * p.ms[1];
+            float m = kNegInf;
+            if (r0 + u < nrows) {
+              if (whole) {
+                const float4 q4 = *reinterpret_cast<const float4*>(a);
+                m = fmaxf(fmaxf(q4.x, q4.y), fmaxf(q4.z, q4.w));
+              } else {
+                for (int e = 0; e < gk && kk + e < nk; ++e) m = fmaxf(m, a[e * p.ms[3]]);
+              }
+            }
+            mv[u] = m;
+            if (++h == nh) {
+              h = 0;
+              roff += p.ms[2];
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < kUnroll; ++u) live = live || mv[u] > kNegInf;
         }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-          if (mv[u] > kNegInf) bits |= 1u << tj[u];
+        if (live) bits |= 1u << (kk / BN);
       }
       __syncthreads();
       if (bits != 0u) atomicOr(&live_shared, bits);
@@ -496,6 +519,13 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN, EXT>)) void pr
     const unsigned char* vs = smem + vs_ofs;
     const int j0 = t * BN;
 
+    // dense, d = 128: this tile's mask entries of the lane's row, requested before the S
+    // MFMAs so their latency overlaps them (at d = 64 the 32 extra registers do not fit the
+    // 128 of four workgroups per CU; mask_tile reads them itself there)
+    constexpr bool kDensePre = MK == MI_ATTN_MASK_DENSE && D == 128;
+    float4 dmask[kDensePre ? NKB * 4 : 1];
+    if constexpr (kDensePre) load_dense_tile<NKB>(dmask, md, Lk, j0, hf, dense_vec);
+
     // S^T = K Q^T. The first 32-key block's K fragments are read before its first MFMA;
     // afterwards each MFMA overlaps the read of one fragment of the next block. (A lambda,
     // as are the mask below: the rare tile that moves the running max computes its logits
@@ -550,7 +580,8 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN, EXT>)) void pr
         mask_tile_topk<NKB, false, EXT>(sacc, j0, hf, pos, tau_row, md, xr, xzl);
       cm = 1.f;
     } else if (tile_needs_mask<MK, BN>(p, Lk, j0, P0, P1)) {
-      mask_tile<MK, NKB, EXT>(sacc, p, Lk, j0, hf, pos, tau_row, md, nullptr, nullptr);
+      mask_tile<MK, NKB, EXT>(sacc, p, Lk, j0, hf, pos, tau_row, md, nullptr, nullptr,
+                              kDensePre ? dmask : nullptr);
       cm = 1.f;
     } else if constexpr (EXT) {
       mods_tile<NKB>(sacc, j0, hf, md);  // a tile every row sees: the score modifiers alone

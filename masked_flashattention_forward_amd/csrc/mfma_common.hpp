@@ -44,8 +44,17 @@ __device__ __forceinline__ float sum_halves(float x) {
 }
 
 // Buffer resource over `bytes` bytes at `base`: loads past the end return zeros.
+// Every caller's base and size are wave-uniform. They are passed through readfirstlane so
+// the descriptor is built in SGPRs whatever the compiler's uniformity analysis concludes:
+// the inline-asm direct loads take it with an "s" constraint, which a VGPR copy would not
+// satisfy.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes, 0x00020000);
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  void* ub = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, static_cast<short>(0), __builtin_amdgcn_readfirstlane(bytes),
+                                           0x00020000);
 }
 __device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, int byte_offset) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, 0));
@@ -310,9 +319,12 @@ __device__ __forceinline__ void mods_tile(f32x16_t* sacc, int j0, int hf, const 
 // zero_hold values (index = key - j0); a dense mask given with the top-k kind is added to
 // the kept keys. Lk is the key count of the (batch or sequence) the tile belongs to; tau_row
 // is clamped to Lk - 1 by the caller, so keys past Lk (rank INT32_MAX) are never kept.
+// (dense kind: pre, when given, holds the lane's 4 NKB groups of 4 entries, loaded ahead by
+// load_dense_tile; otherwise the entries are read here)
 template <int MK, int NKB, bool EXT>
 __device__ __forceinline__ void mask_tile(f32x16_t* sacc, const AttnParams& p, int Lk, int j0, int hf, int pos,
-                                          int32_t tau_row, const Mods& md, const int32_t* xr, const float* xz) {
+                                          int32_t tau_row, const Mods& md, const int32_t* xr, const float* xz,
+                                          const float4* pre = nullptr) {
   const float base = EXT ? static_cast<float>(j0 + hf * 4 - pos) : 0.f;  // distance of the lane's first key
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
@@ -328,7 +340,13 @@ __device__ __forceinline__ void mask_tile(f32x16_t* sacc, const AttnParams& p, i
         if constexpr (MK == MI_ATTN_MASK_WINDOW) vis = vis && j <= pos && j >= pos - p.window_left;
         // side reads use key j0 (always < Lk in a visited tile) in place of keys past Lk
         if constexpr (MK == MI_ATTN_MASK_DENSE) {
-          const float mv = md.mrow[(vis ? j : j0) * md.msj];
+          float mv;
+          if (pre != nullptr) {
+            const float4 q4 = pre[kb * 4 + r4];
+            mv = e == 0 ? q4.x : e == 1 ? q4.y : e == 2 ? q4.z : q4.w;
+          } else {
+            mv = md.mrow[(vis ? j : j0) * md.msj];
+          }
           s = fmaf(vis ? mv : 0.f, kLog2e, s);
         }
         if constexpr (MK == MI_ATTN_MASK_TOPK) {
@@ -342,6 +360,28 @@ __device__ __forceinline__ void mask_tile(f32x16_t* sacc, const AttnParams& p, i
       }
     }
   }
+}
+
+// The dense-mask entries a lane's mask_tile needs for the tile at key j0: group kb * 4 + r4
+// holds keys j0 + kb * 32 + r4 * 8 + hf * 4 + 0..3 of its row. One 16-byte load per group
+// when vec (the caller's test that the row is contiguous and 16-byte aligned) and the group
+// lies below Lk; otherwise four loads with keys clamped to the tile's first key.
+template <int NKB>
+__device__ __forceinline__ void load_dense_tile(float4* out, const Mods& md, int Lk, int j0, int hf, bool vec) {
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int j = j0 + kb * 32 + r4 * 8 + hf * 4;
+      if (vec && j + 3 < Lk) {
+        out[kb * 4 + r4] = *reinterpret_cast<const float4*>(md.mrow + j);
+      } else {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = md.mrow[(j + e < Lk ? j + e : j0) * md.msj];
+        out[kb * 4 + r4] = float4{v[0], v[1], v[2], v[3]};
+      }
+    }
 }
 
 // Top-k mask of one tile whose side data sits in LDS, padded to the full tile:
