@@ -12,9 +12,14 @@
  *    pointer after a call returns.
  *  - Every call validates its arguments on the host first. On a non-zero return nothing
  *    has been enqueued and no output was touched; attn_last_error() gives a message.
- *  - Work is enqueued on `stream` (a hipStream_t; NULL means the default stream). The
- *    library never synchronises the stream. Temporary device memory (split-KV partial
- *    results, top-k ranks) is taken with hipMallocAsync/hipFreeAsync on that stream.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL means the default stream).
+ *    Temporary device memory (split-KV partial results, top-k ranks, kept-key lists) is a
+ *    block the library allocates once per GPU and reuses across calls, holding it until
+ *    the process ends. A call on another stream than the block's previous user first
+ *    makes its stream wait, on the device, for that user's work; host threads calling
+ *    concurrently take turns while enqueueing. The library does not synchronise with the
+ *    host, except when a call needs a larger block than it holds: it then waits for the
+ *    earlier calls' use of the old block to end before freeing it.
  *  - Layouts are row-major and contiguous:
  *      q, out      [B, Hq,  Lq, d]   elements of `dtype`
  *      k, v        [B, Hkv, Lk, d]   elements of `dtype`

@@ -190,6 +190,95 @@ int attn_fwd_plan(int B, int Hq, int Hkv, int Lq, int Lk, int d, int mask_kind, 
 
 }  // extern "C"
 
+namespace mi_attn {
+
+// ---- per-device workspace arena. A call's temporary memory is one block per device, kept
+// and reused by later calls (grown when a call needs more) instead of a stream-ordered
+// allocation per call: on this runtime hipMallocAsync / hipFreeAsync wait for the device,
+// which left the device idle ~16 us between back-to-back c5 calls. Calls on one stream use
+// the block in stream order; a call on another stream first makes its stream wait (on the
+// device) for the event recorded after the previous call's work. A host thread holds the
+// arena's mutex while its call enqueues, so concurrent callers take turns. The block is
+// held until the process ends.
+constexpr int kArenaDevices = 64;
+struct Arena {
+  std::mutex mu;
+  char* ptr = nullptr;
+  size_t cap = 0;
+  hipStream_t last = nullptr;  // stream of the previous call that used the block
+  hipEvent_t done = nullptr;   // recorded on `last` after that call's work
+  bool recorded = false;
+};
+Arena g_arena[kArenaDevices];
+
+// RAII: acquire() locks the device's arena and returns a block of at least `bytes` that
+// no earlier call's work still uses on another stream; the destructor records the event
+// after this call's work and unlocks.
+class ArenaLease {
+ public:
+  ~ArenaLease() {
+    if (a_ == nullptr) return;
+    if (hipEventRecord(a_->done, s_) == hipSuccess) {
+      a_->last = s_;
+      a_->recorded = true;
+    } else {
+      // nothing to wait for later: make sure the work enqueued so far has finished
+      (void)hipStreamSynchronize(s_);
+      a_->recorded = false;
+    }
+    a_->mu.unlock();
+  }
+  hipError_t acquire(size_t bytes, hipStream_t s, char** out) {
+    *out = nullptr;
+    if (bytes == 0) return hipSuccess;
+    int cur = 0, dev = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    dev = cur;
+    if (s != nullptr && (e = hipStreamGetDevice(s, &dev)) != hipSuccess) return e;
+    if (dev < 0 || dev >= kArenaDevices) return hipErrorInvalidDevice;
+    Arena& a = g_arena[dev];
+    a.mu.lock();
+    const bool switch_dev = dev != cur;
+    if (switch_dev && (e = hipSetDevice(dev)) != hipSuccess) {
+      a.mu.unlock();
+      return e;
+    }
+    if (a.done == nullptr) e = hipEventCreateWithFlags(&a.done, hipEventDisableTiming);
+    if (e == hipSuccess && a.cap < bytes) {
+      // grow: the old block may still be in use by queued work
+      if (a.ptr != nullptr) {
+        if (a.recorded) e = hipEventSynchronize(a.done);
+        if (e == hipSuccess) e = hipFree(a.ptr);
+        a.ptr = nullptr;
+        a.cap = 0;
+        a.recorded = false;
+      }
+      size_t want = size_t{1} << 20;
+      while (want < bytes) want <<= 1;
+      if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&a.ptr), want);
+      if (e == hipSuccess) a.cap = want;
+      else a.ptr = nullptr;
+    }
+    if (e == hipSuccess && a.recorded && a.last != s) e = hipStreamWaitEvent(s, a.done, 0);
+    if (switch_dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess) {
+      a.mu.unlock();
+      return e;
+    }
+    a_ = &a;
+    s_ = s;
+    *out = a.ptr;
+    return hipSuccess;
+  }
+
+ private:
+  Arena* a_ = nullptr;
+  hipStream_t s_ = nullptr;
+};
+
+}  // namespace mi_attn
+
 // Fixed scratch of attn_fwd_noalloc (see scratch_for below).
 static __device__ __align__(256) unsigned char scratch[MI_ATTN_NOALLOC_MAX_WORKSPACE];
 
@@ -266,15 +355,15 @@ int fwd_impl(const attn_fwd_args_t* a, void* stream, char* fixed_ws, size_t fixe
 
   hipStream_t st_ = static_cast<hipStream_t>(stream);
   char* ws = nullptr;
-  const bool own_ws = fixed_ws == nullptr;
-  if (!own_ws) {
+  ArenaLease lease;
+  if (fixed_ws != nullptr) {
     if (pl.pub.workspace_bytes > fixed_cap)
       return fail(MI_ATTN_EUNSUPPORTED, "the call needs %zu bytes of temporary memory, above the %zu-byte fixed scratch",
                   pl.pub.workspace_bytes, fixed_cap);
     ws = fixed_ws;
   } else if (pl.pub.workspace_bytes > 0) {
-    hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&ws), pl.pub.workspace_bytes, st_);
-    if (e != hipSuccess) return hip_fail(e, "hipMallocAsync(workspace)");
+    const hipError_t e = lease.acquire(pl.pub.workspace_bytes, st_, &ws);
+    if (e != hipSuccess) return hip_fail(e, "workspace");
   }
 
   const int B = a->B, Hq = a->Hq, Hkv = a->Hkv, Lq = a->Lq, Lk = a->Lk;
@@ -317,18 +406,30 @@ int fwd_impl(const attn_fwd_args_t* a, void* stream, char* fixed_ws, size_t fixe
     int32_t* tau = reinterpret_cast<int32_t*>(ws + pl.off_tau);
     int32_t* tmin = reinterpret_cast<int32_t*>(ws + pl.off_tmin);
     what = "top-k selection";
+    // gathered tiles: the kept-key lists, written by the causal threshold kernel itself
+    // or by a list kernel after the constant thresholds of the non-causal selection
+    TopkListArgs la{};
+    if (pl.list_cap > 0) {
+      la.zh = a->zero_hold;
+      la.q_per_block = pl.q_per_block;
+      la.nqb = (Lq + pl.q_per_block - 1) / pl.q_per_block;
+      la.cap = pl.list_cap;
+      la.lidx = reinterpret_cast<int32_t*>(ws + pl.off_lidx);
+      la.lrank = reinterpret_cast<int32_t*>(ws + pl.off_lrank);
+      la.lzh = reinterpret_cast<float*>(ws + pl.off_lzh);
+      la.lcount = reinterpret_cast<int32_t*>(ws + pl.off_lcnt);
+    }
+    const bool fused_lists = pl.list_cap > 0 && p.topk_causal;
     e = launch_topk(a->zero_hold, B * Hkv, Lq, Lk, a->keep_k, p.topk_causal, rank, tau, nullptr, tmin, pl.pub.block_n,
-                    st_, topk_sort_ws_bytes(B * Hkv, Lk) > 0 ? ws + pl.off_sort : nullptr);
+                    st_, topk_sort_ws_bytes(B * Hkv, Lk) > 0 ? ws + pl.off_sort : nullptr, fused_lists ? &la : nullptr);
     p.rank = rank; p.tau = tau; p.tile_min_rank = tmin;
     if (e == hipSuccess && pl.list_cap > 0) {
-      int32_t* lidx = reinterpret_cast<int32_t*>(ws + pl.off_lidx);
-      int32_t* lrank = reinterpret_cast<int32_t*>(ws + pl.off_lrank);
-      float* lzh = reinterpret_cast<float*>(ws + pl.off_lzh);
-      int32_t* lcnt = reinterpret_cast<int32_t*>(ws + pl.off_lcnt);
-      what = "top-k kept-key lists";
-      e = launch_topk_lists(rank, tau, a->zero_hold, B * Hkv, Lq, Lk, pl.q_per_block, pl.list_cap, p.topk_causal,
-                            lidx, lrank, lzh, lcnt, st_);
-      p.list_idx = lidx; p.list_rank = lrank; p.list_zh = lzh; p.list_count = lcnt;
+      if (!fused_lists) {
+        what = "top-k kept-key lists";
+        e = launch_topk_lists(rank, tau, a->zero_hold, B * Hkv, Lq, Lk, pl.q_per_block, pl.list_cap, p.topk_causal,
+                              la.lidx, la.lrank, la.lzh, la.lcount, st_);
+      }
+      p.list_idx = la.lidx; p.list_rank = la.lrank; p.list_zh = la.lzh; p.list_count = la.lcount;
       p.list_cap = pl.list_cap;
     }
   }
@@ -345,10 +446,6 @@ int fwd_impl(const attn_fwd_args_t* a, void* stream, char* fixed_ws, size_t fixe
     }
     what = "attention kernel";
     e = (pl.pub.path == 0) ? launch_row_kernel(p, a->dtype, st_) : launch_half_path(pl.pub.path, p, a->dtype, st_);
-  }
-  if (own_ws && ws != nullptr) {
-    const hipError_t ef = hipFreeAsync(ws, st_);
-    if (e == hipSuccess && ef != hipSuccess) return hip_fail(ef, "hipFreeAsync(workspace)");
   }
   if (e != hipSuccess) return hip_fail(e, what);
   return MI_ATTN_OK;
@@ -490,14 +587,17 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
   size_t off = 0;
   const size_t off_side = off; off = align256(off + 3 * sizeof(float) * rows);
   size_t off_rank = 0, off_tau = 0;
+  size_t off_sort = 0;
   if (mask_kind == MI_ATTN_MASK_TOPK) {
     off_rank = off; off = align256(off + sizeof(int32_t) * bh * Lk);
     off_tau = off;  off = align256(off + sizeof(int32_t) * bh * Lq);
+    off_sort = off; off = align256(off + topk_sort_ws_bytes(static_cast<int>(bh), Lk));
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* ws = nullptr;
-  hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&ws), off, st);
-  if (e != hipSuccess) return hip_fail(e, "hipMallocAsync(workspace)");
+  ArenaLease lease;
+  hipError_t e = lease.acquire(off, st, &ws);
+  if (e != hipSuccess) return hip_fail(e, "workspace");
 
   AttnParams p{};
   p.q = q; p.k = k; p.v = v; p.out = const_cast<void*>(out); p.lse = const_cast<float*>(lse);
@@ -518,15 +618,13 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
     int32_t* rank = reinterpret_cast<int32_t*>(ws + off_rank);
     int32_t* tau = reinterpret_cast<int32_t*>(ws + off_tau);
     what = "top-k selection";
-    e = launch_topk(zero_hold, B * Hkv, Lq, Lk, keep_k, 1, rank, tau, nullptr, nullptr, 0, st);
+    e = launch_topk(zero_hold, B * Hkv, Lq, Lk, keep_k, 1, rank, tau, nullptr, nullptr, 0, st, ws + off_sort);
     p.rank = rank;
     p.tau = tau;
     if (e == hipSuccess) what = "attention backward kernels";
   }
   if (e == hipSuccess) e = launch_backward(p, dtype, st);
-  const hipError_t ef = hipFreeAsync(ws, st);
   if (e != hipSuccess) return hip_fail(e, what);
-  if (ef != hipSuccess) return hip_fail(ef, "hipFreeAsync(workspace)");
   return MI_ATTN_OK;
 }
 
@@ -601,8 +699,9 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, floa
   const size_t off_pdl = off;   off = align256(off + sizeof(float) * ic * 32);
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* ws = nullptr;
-  hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&ws), off, st);
-  if (e != hipSuccess) return hip_fail(e, "hipMallocAsync(workspace)");
+  ArenaLease lease;
+  hipError_t e = lease.acquire(off, st, &ws);
+  if (e != hipSuccess) return hip_fail(e, "workspace");
   b.units = reinterpret_cast<int4*>(ws + off_units);
   b.items_p = reinterpret_cast<int4*>(ws + off_ip);
   b.items_d = reinterpret_cast<int4*>(ws + off_id);
@@ -631,9 +730,7 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, floa
   (void)max_seqlen_q;
   (void)max_seqlen_k;
   e = launch_varlen(p, dtype, b, st);
-  const hipError_t ef = hipFreeAsync(ws, st);
   if (e != hipSuccess) return hip_fail(e, "varlen attention kernels");
-  if (ef != hipSuccess) return hip_fail(ef, "hipFreeAsync(workspace)");
   return MI_ATTN_OK;
 }
 
@@ -647,8 +744,12 @@ int dynamic_mask_topk(const float* zero_hold, int B, int H, int Lq, int Lk, int 
     return fail(MI_ATTN_EINVAL, "zero_hold, rank and tau must not be NULL");
   if (Lk > 65536) return fail(MI_ATTN_EUNSUPPORTED, "Lk must be <= 65536 (got %d)", Lk);
   if (static_cast<double>(B) * H * Lq * ((Lk + 31) / 32) > 2.0e9) return fail(MI_ATTN_EINVAL, "tensor too large");
-  const hipError_t e = launch_topk(zero_hold, B * H, Lq, Lk, keep_k, causal ? 1 : 0, rank, tau, keep_bits, nullptr, 0,
-                                   static_cast<hipStream_t>(stream));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = nullptr;
+  ArenaLease lease;
+  hipError_t e = lease.acquire(topk_sort_ws_bytes(B * H, Lk), st, &ws);
+  if (e != hipSuccess) return hip_fail(e, "workspace");
+  e = launch_topk(zero_hold, B * H, Lq, Lk, keep_k, causal ? 1 : 0, rank, tau, keep_bits, nullptr, 0, st, ws);
   if (e != hipSuccess) return hip_fail(e, "dynamic_mask_topk");
   return MI_ATTN_OK;
 }

@@ -179,11 +179,18 @@ hipError_t launch_row_kernel(const AttnParams& p, int dtype, hipStream_t s);
 hipError_t launch_backward(const AttnParams& p, int dtype, hipStream_t s);
 // tile_min (optional, [BH, ceil(Lk / block_n)]) receives the smallest rank of each
 // block_n-key tile; block_n must divide 256 and be at most 64.
-// sort_ws (optional): topk_sort_ws_bytes(BH, Lk) bytes of device memory for the sorted
-// key chunks; nullptr takes a stream-ordered allocation instead.
+// sort_ws: topk_sort_ws_bytes(BH, Lk) bytes of device memory for the sorted key chunks.
+// lists (optional, causal only): the kept-key lists of the gathered attention, written by
+// the threshold kernel itself (see launch_topk_lists for their layout).
+struct TopkListArgs {
+  const float* zh;
+  int q_per_block, nqb, cap;
+  int32_t *lidx, *lrank, *lcount;
+  float* lzh;
+};
 hipError_t launch_topk(const float* zh, int BH, int Lq, int Lk, int keep_k, int causal,
                        int32_t* rank, int32_t* tau, uint32_t* keep_bits, int32_t* tile_min, int block_n,
-                       hipStream_t s, void* sort_ws = nullptr);
+                       hipStream_t s, void* sort_ws, const TopkListArgs* lists = nullptr);
 size_t topk_sort_ws_bytes(int BH, int Lk);
 // Kept-key lists of the gathered top-k attention (see AttnParams::list_*).
 // causal == 0: every row may keep any key (the lists hold the keys of rank <= tau).

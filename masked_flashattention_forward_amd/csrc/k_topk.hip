@@ -16,6 +16,8 @@
 //      so tau can only fall: it is found once by a wavefront prefix count and afterwards
 //      moves, when the new key ranks below it, to the largest set rank below the old tau.
 //   3. optional keep bitmask and per-tile minimum rank (tile skipping in attention).
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace mi_attn {
@@ -261,6 +263,93 @@ __global__ __launch_bounds__(kRankThreads) void rank_runs_kernel(const float* zh
   }
 }
 
+// Kept-key list of one (b, KV head, query block): the keys j < n (n: keys 0 .. p of the
+// block's last row, or every key when rows may keep any) whose rank is at most the
+// threshold tf of the block's first row (thresholds do not grow with the row position, so
+// every row of the block keeps a subset), ascending, padded to a whole number of 64-key
+// tiles with key Lk. Exactly keep_k keys up to the first row's position pass the test when
+// its threshold is finite, and every key when it is not (then that position is below
+// keep_k), so a list never holds more than keep_k + q_per_block - 1 keys. Run by all
+// kListThreads threads of a workgroup.
+constexpr int kListThreads = 256;
+constexpr int kListWaves = kListThreads / kWave;
+constexpr int kListSub = 16;  // 256-key sub-passes per pass (4096 keys per pass)
+__device__ __forceinline__ void build_topk_list(const int32_t* rk, const float* z, int32_t tf, int n, int Lk,
+                                                long base, int cap, int32_t* lidx, int32_t* lrank, float* lzh,
+                                                int32_t* lcount) {
+  __shared__ int sub_cnt[kListSub][kListWaves];
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid % kWave;
+  int cnt = 0;
+  // a pass covers 4096 keys: sub-pass u holds keys j0 + 256 u + (0..255), so the loads are
+  // coalesced and all 16 are in flight together; per-wavefront ballot counts of every
+  // sub-pass go to LDS and one barrier later each lane knows where its keys go
+  for (int j0 = 0; j0 < n; j0 += kListThreads * kListSub) {
+    int32_t r[kListSub];
+#pragma unroll
+    for (int u = 0; u < kListSub; ++u) {
+      const int j = j0 + u * kListThreads + tid;
+      r[u] = j < n ? rk[j] : kAllKept;
+    }
+    unsigned long long ball[kListSub];
+#pragma unroll
+    for (int u = 0; u < kListSub; ++u) {
+      const int j = j0 + u * kListThreads + tid;
+      ball[u] = __ballot(j < n && r[u] <= tf);
+      if (lane == 0) sub_cnt[u][wave] = __popcll(ball[u]);
+    }
+    __syncthreads();
+    int run = cnt;  // kept keys before sub-pass u
+#pragma unroll
+    for (int u = 0; u < kListSub; ++u) {
+      int before = run;
+#pragma unroll
+      for (int w = 0; w < kListWaves; ++w) {
+        const int c = sub_cnt[u][w];
+        before += w < wave ? c : 0;
+        run += c;
+      }
+      const unsigned long long b_u = ball[u];
+      if ((b_u >> lane) & 1ull) {
+        const int e = before + __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(b_u >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(b_u), 0));
+        const int j = j0 + u * kListThreads + tid;
+        if (e < cap) {
+          lidx[base + e] = j;
+          lrank[base + e] = r[u];
+          lzh[base + e] = z[j] * kLog2e;
+        }
+      }
+    }
+    cnt = run;
+    __syncthreads();  // sub_cnt is rewritten by the next pass
+  }
+  cnt = cnt < cap ? cnt : cap;  // the bound above makes this a no-op
+  const int padded = ((cnt + 63) / 64) * 64;
+  for (int e = cnt + tid; e < padded; e += kListThreads) {
+    lidx[base + e] = Lk;
+    lrank[base + e] = kAllKept;
+    lzh[base + e] = 0.f;
+  }
+  if (tid == 0) *lcount = cnt;
+}
+
+// One workgroup per (b, KV head, query block).
+__global__ __launch_bounds__(kListThreads) void topk_list_kernel(const int32_t* rank, const int32_t* tau,
+                                                                   const float* zh, int Lq, int Lk, int q_per_block,
+                                                                   int nqb, int cap, int causal, int32_t* lidx,
+                                                                   int32_t* lrank, float* lzh, int32_t* lcount) {
+  const int qb = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int i_first = qb * q_per_block;
+  const int i_last = min(Lq, i_first + q_per_block) - 1;
+  const int n = causal ? Lk - Lq + i_last + 1 : Lk;
+  build_topk_list(rank + static_cast<long>(bh) * Lk, zh + static_cast<long>(bh) * Lk,
+                  tau[static_cast<long>(bh) * Lq + i_first], n, Lk, (static_cast<long>(bh) * nqb + qb) * cap, cap,
+                  lidx, lrank, lzh, lcount + static_cast<long>(bh) * nqb + qb);
+}
+
 constexpr int kTauRowsPerWave = 32;
 constexpr int kTauWaves = 4;
 
@@ -316,10 +405,12 @@ __device__ __forceinline__ int set_rank_below(const uint32_t (&words)[WPL], int 
 
 // Causal tau. WPL = 32-bit bitmap words per lane; one wavefront covers 64 * 32 * WPL ranks.
 // Workgroup = 4 wavefronts = 128 consecutive rows of one (b,h). Every global load of the
-// kernel is issued before the first barrier, so their latencies overlap.
-template <int WPL>
+// kernel is issued before the first barrier, so their latencies overlap. LISTS: the
+// workgroup then builds the kept-key lists of the query blocks its rows start (their
+// first rows' thresholds are in LDS by then).
+template <int WPL, bool LISTS>
 __global__ __launch_bounds__(kTauWaves * kWave) void tau_kernel(const int32_t* rank, int Lq, int Lk, int keep_k,
-                                                                  int32_t* tau) {
+                                                                  int32_t* tau, TopkListArgs la) {
   constexpr int NW = kWave * WPL;
   constexpr int kThreads = kTauWaves * kWave;
   constexpr int kBuild = (8 * WPL) < 16 ? (8 * WPL) : 16;  // keys per thread per pass of the shared bitmap
@@ -375,7 +466,8 @@ __global__ __launch_bounds__(kTauWaves * kWave) void tau_kernel(const int32_t* r
   for (int u = 0; u < kExtra; ++u)
     if (xr[u] >= 0) atomicOr(&wave_bm[wave][xr[u] >> 5], 1u << (xr[u] & 31));
   __syncthreads();
-  if (n == 0) return;
+  __shared__ int32_t tau_s[LISTS ? kTauWaves * kTauRowsPerWave : 1];
+  if (!LISTS && n == 0) return;
 
   uint32_t words[WPL];
 #pragma unroll
@@ -400,6 +492,20 @@ __global__ __launch_bounds__(kTauWaves * kWave) void tau_kernel(const int32_t* r
     if (lane == i) my_tau = cur;
   }
   if (lane < n) tau[static_cast<long>(bh) * Lq + r0 + lane] = my_tau;
+  if constexpr (LISTS) {
+    if (lane < kTauRowsPerWave) tau_s[wave * kTauRowsPerWave + lane] = my_tau;
+    __syncthreads();
+    // query blocks whose first row lies in this workgroup's rows
+    const int qb0 = (rb + la.q_per_block - 1) / la.q_per_block;
+    const int qb1 = min(la.nqb, (rb + kTauWaves * kTauRowsPerWave + la.q_per_block - 1) / la.q_per_block);
+    for (int qb = qb0; qb < qb1; ++qb) {
+      const int i_first = qb * la.q_per_block;
+      const int i_last = min(Lq, i_first + la.q_per_block) - 1;
+      build_topk_list(rk, la.zh + static_cast<long>(bh) * Lk, tau_s[i_first - rb], Lk - Lq + i_last + 1, Lk,
+                      (static_cast<long>(bh) * la.nqb + qb) * la.cap, la.cap, la.lidx, la.lrank, la.lzh,
+                      la.lcount + static_cast<long>(bh) * la.nqb + qb);
+    }
+  }
 }
 
 __global__ void tau_const_kernel(int n, int32_t value, int32_t* tau) {
@@ -426,88 +532,6 @@ __global__ void keep_bits_kernel(const int32_t* rank, const int32_t* tau, int BH
     if (j < Lk && (!causal || j <= pos) && rank[bh * Lk + j] <= th) x |= 1u << bit;
   }
   bits[t] = x;
-}
-
-// Kept-key list of one (b, KV head, query block): the keys j <= p of the block's last row
-// whose rank is at most the threshold of its first row (thresholds do not grow with the
-// row position, so every row of the block keeps a subset), ascending, padded to a whole
-// number of 64-key tiles with key Lk. Exactly keep_k keys up to the first row's position
-// pass the test when its threshold is finite, and every key when it is not (then that
-// position is below keep_k), so a list never holds more than keep_k + q_per_block - 1
-// keys.
-constexpr int kListThreads = 256;
-constexpr int kListWaves = kListThreads / kWave;
-constexpr int kListSub = 16;  // 256-key sub-passes per pass (4096 keys per pass)
-__global__ __launch_bounds__(kListThreads) void topk_list_kernel(const int32_t* rank, const int32_t* tau,
-                                                                   const float* zh, int Lq, int Lk, int q_per_block,
-                                                                   int nqb, int cap, int causal, int32_t* lidx,
-                                                                   int32_t* lrank, float* lzh, int32_t* lcount) {
-  __shared__ int sub_cnt[kListSub][kListWaves];
-  const int qb = blockIdx.x;
-  const int bh = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int wave = tid / kWave;
-  const int lane = tid % kWave;
-  const int i_first = qb * q_per_block;
-  const int i_last = min(Lq, i_first + q_per_block) - 1;
-  // keys 0 .. p of the last row (may be <= 0), or every key when rows may keep any
-  const int n = causal ? Lk - Lq + i_last + 1 : Lk;
-  const int32_t tf = tau[static_cast<long>(bh) * Lq + i_first];
-  const int32_t* rk = rank + static_cast<long>(bh) * Lk;
-  const float* z = zh + static_cast<long>(bh) * Lk;
-  const long base = (static_cast<long>(bh) * nqb + qb) * cap;
-  int cnt = 0;
-  // a pass covers 4096 keys: sub-pass u holds keys j0 + 256 u + (0..255), so the loads are
-  // coalesced and all 16 are in flight together; per-wavefront ballot counts of every
-  // sub-pass go to LDS and one barrier later each lane knows where its keys go
-  for (int j0 = 0; j0 < n; j0 += kListThreads * kListSub) {
-    int32_t r[kListSub];
-#pragma unroll
-    for (int u = 0; u < kListSub; ++u) {
-      const int j = j0 + u * kListThreads + tid;
-      r[u] = j < n ? rk[j] : kAllKept;
-    }
-    unsigned long long ball[kListSub];
-#pragma unroll
-    for (int u = 0; u < kListSub; ++u) {
-      const int j = j0 + u * kListThreads + tid;
-      ball[u] = __ballot(j < n && r[u] <= tf);
-      if (lane == 0) sub_cnt[u][wave] = __popcll(ball[u]);
-    }
-    __syncthreads();
-    int run = cnt;  // kept keys before sub-pass u
-#pragma unroll
-    for (int u = 0; u < kListSub; ++u) {
-      int before = run;
-#pragma unroll
-      for (int w = 0; w < kListWaves; ++w) {
-        const int c = sub_cnt[u][w];
-        before += w < wave ? c : 0;
-        run += c;
-      }
-      const unsigned long long b_u = ball[u];
-      if ((b_u >> lane) & 1ull) {
-        const int e = before + __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(b_u >> 32),
-                                                        __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(b_u), 0));
-        const int j = j0 + u * kListThreads + tid;
-        if (e < cap) {
-          lidx[base + e] = j;
-          lrank[base + e] = r[u];
-          lzh[base + e] = z[j] * kLog2e;
-        }
-      }
-    }
-    cnt = run;
-    __syncthreads();  // sub_cnt is rewritten by the next pass
-  }
-  cnt = cnt < cap ? cnt : cap;  // the bound above makes this a no-op
-  const int padded = ((cnt + 63) / 64) * 64;
-  for (int e = cnt + tid; e < padded; e += kListThreads) {
-    lidx[base + e] = Lk;
-    lrank[base + e] = kAllKept;
-    lzh[base + e] = 0.f;
-  }
-  if (tid == 0) lcount[static_cast<long>(bh) * nqb + qb] = cnt;
 }
 
 // One wavefront per flag (batch, KV head, query block, key tile) of a dense mask that may
@@ -556,19 +580,16 @@ size_t topk_sort_ws_bytes(int BH, int Lk) {
 
 hipError_t launch_topk(const float* zh, int BH, int Lq, int Lk, int keep_k, int causal, int32_t* rank,
                        int32_t* tau, uint32_t* keep_bits, int32_t* tile_min, int block_n, hipStream_t s,
-                       void* sort_ws) {
+                       void* sort_ws, const TopkListArgs* lists) {
+  if (lists != nullptr && (!causal || lists->cap % 64 != 0 || lists->q_per_block <= 0)) return hipErrorInvalidValue;
   if (tile_min != nullptr && (block_n <= 0 || block_n > kWave || kRankThreads % block_n != 0))
     return hipErrorInvalidValue;
   hipError_t e = hipSuccess;
-  // sorted chunks (and, past kMergeMaxKeys, the merged runs): the caller's workspace, or
-  // a stream-ordered scratch buffer
+  // sorted chunks (and, past kMergeMaxKeys, the merged runs): the caller's workspace
   const int nchunks = (Lk + kChunk - 1) / kChunk;
   const size_t chunk_words = static_cast<size_t>(BH) * nchunks * kChunk;
   u64* sorted = static_cast<u64*>(sort_ws);
-  if (sorted == nullptr) {
-    e = hipMallocAsync(reinterpret_cast<void**>(&sorted), topk_sort_ws_bytes(BH, Lk), s);
-    if (e != hipSuccess) return e;
-  }
+  if (sorted == nullptr && topk_sort_ws_bytes(BH, Lk) > 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(chunk_sort_kernel, dim3(BH, nchunks), dim3(kChunkThreads), 0, s, zh, Lk, nchunks, sorted);
   if (Lk <= kMergeMaxKeys) {
     hipLaunchKernelGGL(rank_merge_kernel, dim3(BH, (Lk + kRankThreads - 1) / kRankThreads), dim3(kRankThreads),
@@ -582,10 +603,6 @@ hipError_t launch_topk(const float* zh, int BH, int Lq, int Lk, int keep_k, int 
                        zh, runs, Lk, nchunks, rank, tile_min, block_n);
   }
   e = hipGetLastError();
-  if (sort_ws == nullptr) {
-    const hipError_t ef = hipFreeAsync(sorted, s);
-    if (e == hipSuccess) e = ef;
-  }
   if (e == hipSuccess) {
     if (!causal) {
       const int32_t v = (Lk > keep_k) ? keep_k - 1 : kAllKept;
@@ -596,12 +613,18 @@ hipError_t launch_topk(const float* zh, int BH, int Lq, int Lk, int keep_k, int 
       const dim3 grid(BH, (Lq + kTauWaves * kTauRowsPerWave - 1) / (kTauWaves * kTauRowsPerWave));
       const dim3 block(kTauWaves * kWave);
       const int wpl = (Lk + 64 * 32 - 1) / (64 * 32);
-      if (wpl <= 1) hipLaunchKernelGGL(tau_kernel<1>, grid, block, 0, s, rank, Lq, Lk, keep_k, tau);
-      else if (wpl <= 2) hipLaunchKernelGGL(tau_kernel<2>, grid, block, 0, s, rank, Lq, Lk, keep_k, tau);
-      else if (wpl <= 4) hipLaunchKernelGGL(tau_kernel<4>, grid, block, 0, s, rank, Lq, Lk, keep_k, tau);
-      else if (wpl <= 8) hipLaunchKernelGGL(tau_kernel<8>, grid, block, 0, s, rank, Lq, Lk, keep_k, tau);
-      else if (wpl <= 16) hipLaunchKernelGGL(tau_kernel<16>, grid, block, 0, s, rank, Lq, Lk, keep_k, tau);
-      else hipLaunchKernelGGL(tau_kernel<32>, grid, block, 0, s, rank, Lq, Lk, keep_k, tau);
+      const TopkListArgs la = lists != nullptr ? *lists : TopkListArgs{};
+      auto go = [&](auto wpl_tag) {
+        constexpr int W = decltype(wpl_tag)::value;
+        if (lists != nullptr) hipLaunchKernelGGL((tau_kernel<W, true>), grid, block, 0, s, rank, Lq, Lk, keep_k, tau, la);
+        else hipLaunchKernelGGL((tau_kernel<W, false>), grid, block, 0, s, rank, Lq, Lk, keep_k, tau, la);
+      };
+      if (wpl <= 1) go(std::integral_constant<int, 1>{});
+      else if (wpl <= 2) go(std::integral_constant<int, 2>{});
+      else if (wpl <= 4) go(std::integral_constant<int, 4>{});
+      else if (wpl <= 8) go(std::integral_constant<int, 8>{});
+      else if (wpl <= 16) go(std::integral_constant<int, 16>{});
+      else go(std::integral_constant<int, 32>{});
     }
     e = hipGetLastError();
   }
