@@ -19,6 +19,8 @@
 //                    lane's eight keys match the ones its P registers hold.
 // Tiles that the mask hides entirely are never loaded: their range comes from the causal
 // / window bounds, the dense-mask summary or the top-k minimum rank per tile.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma_common.hpp"
@@ -56,10 +58,14 @@ constexpr int kLog2RoundKeys = (D == 128) ? 4 : 5;
 constexpr int kLog2BN = 6;  // 64-key tiles
 
 // resident workgroups per CU: LDS allows 2 for d = 128 and 4 for d = 64. At d = 64 the
-// top-k variant's extra state and the score modifiers (EXT) keep it at 2 and the varlen
-// variant's per-row addressing at 3 (4 would cap them at 128 VGPRs and spill).
+// top-k variant's extra state and the score modifiers (EXT) keep it at 2, and the varlen
+// variant's per-row addressing and the dense mask's liveness scan at 3 (4 would cap them
+// at 128 VGPRs and spill).
 template <int D, int MK, bool VARLEN, bool EXT>
-constexpr int kMinBlocks = D == 128 ? 2 : (MK == MI_ATTN_MASK_TOPK || EXT) ? 2 : VARLEN ? 3 : 4;
+constexpr int kMinBlocks = D == 128 ? 2
+                           : (MK == MI_ATTN_MASK_TOPK || EXT) ? 2
+                           : (VARLEN || MK == MI_ATTN_MASK_DENSE) ? 3
+                                                                   : 4;
 
 // Softmax against the running max without a per-tile max reduction (see the tile loop).
 // Its second code path does not fit the registers at d = 64 (4 workgroups per CU, 128
@@ -490,6 +496,20 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN, EXT>)) void pr
     v_base1 = (tr_row + 8) * TL::rowBytes | ((sl ^ swz<D>(tr_row + 8)) << 4) | (8 * (lane & 1));
   }
   static_assert(TL::stage % 512 == 0 && TL::kBytes % 512 == 0, "stage offsets keep the XOR-ed address bits");
+  // The tile loop runs unrolled by two (kUnroll2) at d = 128 for the position masks: the
+  // stage is then a constant in each copy. Byte offsets in smem of a lane's K fragment (dim
+  // chunk dc) and V^T fragment (dim block db) in the stage at byte offset ofs: adding a
+  // multiple of 512 commutes with the XOR, so unrolled, the XOR-ed base is loop-invariant
+  // and the stage offset an immediate. The other instances (d = 64 at 128 VGPRs; dense,
+  // top-k and score modifiers, whose extra state leaves no room for the 16 invariant
+  // addresses) keep the form that needs no extra live registers.
+  constexpr bool kUnroll2 = D == 128 && MK <= MI_ATTN_MASK_WINDOW && !EXT;
+  auto k_addr = [&](int dc, int ofs) -> int {
+    return kUnroll2 ? (k_base ^ (dc << 5)) + ofs : ((k_base + ofs) ^ (dc << 5));
+  };
+  auto v_addr = [&](int vbase, int db, int ofs) -> int {
+    return kUnroll2 ? (vbase ^ (db << 6)) + ofs : ((vbase + ofs) ^ (db << 6));
+  };
 
   // ---- running state
   constexpr int NKB = BN / 32;  // 32-key blocks per tile
@@ -501,7 +521,6 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN, EXT>)) void pr
   float l_run = 0.f;      // this lane's partial running sum
 
   int t = next_live(t_lo);
-  int stage = 0;
   if (t < t_hi) {
     load_gidx(t);
     load_pages(t);
@@ -510,7 +529,10 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN, EXT>)) void pr
   }
   __syncthreads();
 
-  while (t < t_hi) {
+  // One key tile; `stage_c` is the LDS stage it sits in (an integral_constant when the loop
+  // is unrolled by two, see kUnroll2; otherwise an int).
+  auto tile_step = [&](auto stage_c) {
+    const int stage = stage_c;
     const int tn = next_live(t + 1);
     if (tn < t_hi) issue_tile(tn, stage ^ 1);  // lands in the other stage while this tile computes
 
@@ -538,8 +560,7 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN, EXT>)) void pr
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int dc = 0; dc < NDC; ++dc)
-          kf[kb][dc] = *reinterpret_cast<const u32x4_t*>(smem + kb * 32 * TL::rowBytes +
-                                                         ((k_base + ks_ofs) ^ (dc << 5)));
+          kf[kb][dc] = *reinterpret_cast<const u32x4_t*>(smem + kb * 32 * TL::rowBytes + k_addr(dc, ks_ofs));
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         f32x16_t acc = f32x16_t{};
@@ -740,15 +761,15 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN, EXT>)) void pr
     __builtin_amdgcn_s_setprio(1);
     {
       constexpr int NKC = BN / 16;
-      const int vb0 = v_base0 + vs_ofs, vb1 = v_base1 + vs_ofs;
+
       u32x4_t vf[NKC][NDB];
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           const unsigned char* row = smem + kc * 16 * TL::rowBytes;
-          const u32x2_t lo = lds_read_tr16(row + (vb0 ^ (db << 6)));
-          const u32x2_t hi2 = lds_read_tr16(row + (vb1 ^ (db << 6)));
+          const u32x2_t lo = lds_read_tr16(row + v_addr(v_base0, db, vs_ofs));
+          const u32x2_t hi2 = lds_read_tr16(row + v_addr(v_base1, db, vs_ofs));
           vf[kc][db] = u32x4_t{lo.x, lo.y, hi2.x, hi2.y};
         }
 #pragma unroll
@@ -768,7 +789,15 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN, EXT>)) void pr
     if (tn < t_hi) finish_tile(stage ^ 1);
     __syncthreads();
     t = tn;
-    stage ^= 1;
+  };
+  if constexpr (kUnroll2) {
+    while (t < t_hi) {
+      tile_step(std::integral_constant<int, 0>{});
+      if (t >= t_hi) break;
+      tile_step(std::integral_constant<int, 1>{});
+    }
+  } else {
+    for (int stage = 0; t < t_hi; stage ^= 1) tile_step(stage);
   }
 
   // ---- epilogue: combine the two lane halves' partial sums, normalise, store
