@@ -175,6 +175,18 @@ def blas_threads() -> int:
         return len(os.sched_getaffinity(0))
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), for the oracle baseline record."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
 def cpu_oracle(p, heads=None, label="") -> dict:
     """The fp64 oracle, as it stands, timed on this host's cores: every (batch, head) of the
     workload, or only ``heads`` (then scaled up to the whole workload and labelled
@@ -205,12 +217,13 @@ def cpu_oracle(p, heads=None, label="") -> dict:
     flops = 4.0 * p.d * visible_pairs(p)
     dt = elapsed / frac
     res = {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
-           "seconds": round(dt, 3)}
+           "cpu": cpu_model(), "seconds": round(dt, 3)}
     if heads is None:
         res["sample"] = f"fp64 oracle on all {len(pairs)} (b,h) heads of {label or p.name}, {elapsed:.1f} s"
     else:
         res["sample"] = (f"fp64 oracle on {len(sample)} of {len(pairs)} (b,h) heads of {label or p.name} "
-                         f"(all {p.Lq} rows each), {elapsed:.1f} s, scaled x{len(pairs) / len(sample):g}")
+                         f"(all {p.Lq} rows each), {elapsed:.1f} s, scaled x{len(pairs) / len(sample):g}: "
+                         f"extrapolated")
         res["extrapolated"] = True
     log(f"cpu oracle {label or p.name}: {json.dumps(res)}")
     return res
