@@ -264,12 +264,13 @@ int attn_fwd_ex(const attn_fwd_args_t* args, void* stream);
  *   S[128][64]   scale * q k^T + mask of the tile, natural-log units (-inf where hidden)
  *   P[128][64]   exp(S - m), fp32 before rounding to the 16-bit type of the P V product
  *   m[128]       the reference maximum m of the running softmax after this tile (natural
- *                log units; it trails the true running maximum by less than 8 ln 2)
+ *                log units; it trails the true running maximum by at most 8 ln 2)
  *   l[128]       the running sum after this tile, so l exp(m) = sum of exp(S) over the
  *                keys visited so far
  * Rows past the block's rows and tiles the kernel skips (hidden entirely) are not written.
- * MI_ATTN_EUNSUPPORTED when the call does not take the MFMA prefill path (see
- * attn_fwd_plan), MI_ATTN_EINVAL for an index out of range or a NULL dump.
+ * MI_ATTN_EUNSUPPORTED when the call does not take the MFMA prefill path with 64-key tiles
+ * (see attn_fwd_plan: path 1 and block_n 64; d = 64 with the none / causal / window kinds
+ * takes 128-key tiles), MI_ATTN_EINVAL for an index out of range or a NULL dump.
  */
 #define MI_ATTN_DUMP_FLOATS (2 * 128 * 64 + 2 * 128)
 int attn_fwd_dump(const attn_fwd_args_t* args, int b, int kv_head, int query_block, int tile, float* dump,
@@ -339,7 +340,8 @@ typedef struct {
   int path;          /* 0 fp32 row kernel; 1 MFMA prefill (split over keys, with an LSE merge,
                         when there are few workgroups); 2 split-KV decode + LSE merge        */
   int block_m;       /* query rows per workgroup (rows of all heads sharing a KV head)   */
-  int block_n;       /* keys per KV tile                                                 */
+  int block_n;       /* keys per KV tile (128 for d = 64 with the none / causal / window
+                        kinds on path 1, else 64; 32 on path 2)                           */
   int splits;        /* key-range splits merged by log-sum-exp (paths 1, 2); 1 if unsplit */
   int grid;          /* workgroups of the main kernel                                    */
   int mask_summary;  /* 1 when a per-tile dense-mask summary kernel runs first            */

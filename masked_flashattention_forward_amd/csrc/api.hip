@@ -345,6 +345,9 @@ int fwd_impl(const attn_fwd_args_t* a, void* stream, char* fixed_ws, size_t fixe
     if (pl.pub.path != 1)
       return fail(MI_ATTN_EUNSUPPORTED, "the one-tile dump runs on the MFMA prefill path only (this call takes path %d)",
                   pl.pub.path);
+    if (pl.pub.block_n != 64)
+      return fail(MI_ATTN_EUNSUPPORTED, "the one-tile dump covers 64-key tiles (this call takes %d-key tiles)",
+                  pl.pub.block_n);
     const int nqb = (a->Lq + pl.q_per_block - 1) / pl.q_per_block;
     const int ntiles = pl.list_cap > 0 ? pl.list_cap / 64 : (a->Lk + pl.pub.block_n - 1) / pl.pub.block_n;
     if (dump->buf == nullptr || dump->b < 0 || dump->b >= a->B || dump->kv_head < 0 || dump->kv_head >= a->Hkv ||
@@ -719,7 +722,7 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, floa
   p.softcap = softcap;
   p.no_skip = g_no_skip;
   p.splits = 1;
-  p.block_n = prefill_block_n(d);
+  p.block_n = 64;  // varlen instances take 64-key tiles
   p.q_per_block = qpb;
   p.cu_q = cu_seqlens_q; p.cu_k = cu_seqlens_k;
   p.block_table = block_table; p.k_new = k_new; p.v_new = v_new;

@@ -57,22 +57,30 @@ template <int D>
 constexpr int kLog2RoundKeys = (D == 128) ? 4 : 5;
 constexpr int kLog2BN = 6;  // 64-key tiles
 
-// resident workgroups per CU: LDS allows 2 for d = 128 and 4 for d = 64. At d = 64 the
-// top-k variant's extra state and the score modifiers (EXT) keep it at 2, and the varlen
-// variant's per-row addressing and the dense mask's liveness scan at 3 (4 would cap them
-// at 128 VGPRs and spill).
-template <int D, int MK, bool VARLEN, bool EXT>
-constexpr int kMinBlocks = D == 128 ? 2
+// resident workgroups per CU: LDS allows 2 for d = 128 and for 128-key tiles at d = 64,
+// and 4 for 64-key tiles at d = 64. There the top-k variant's extra state and the score
+// modifiers (EXT) keep it at 2, and the varlen variant's per-row addressing and the dense
+// mask's liveness scan at 3 (4 would cap them at 128 VGPRs and spill).
+template <int D, int MK, bool VARLEN, bool EXT, int BN>
+constexpr int kMinBlocks = (D == 128 || BN == 128) ? 2
                            : (MK == MI_ATTN_MASK_TOPK || EXT) ? 2
                            : (VARLEN || MK == MI_ATTN_MASK_DENSE) ? 3
                                                                    : 4;
 
+// Keys per tile of the position-mask (none / causal / window) instances: 128 at d = 64,
+// where the tile's fixed costs (barrier, loads, bookkeeping) would otherwise be spread
+// over half the MFMA work of d = 128 (c4 d64: 654 -> 609 us with the max still reduced
+// first); 64 at d = 128 (two 64 KB stages per workgroup leave room for two per CU). The
+// dense, top-k and varlen instances take 64-key tiles.
+template <int D>
+constexpr int kPosBN = D == 64 ? 128 : 64;
+
 // Softmax against the running max without a per-tile max reduction (see the tile loop).
-// Its second code path does not fit the registers at d = 64 (4 workgroups per CU, 128
-// VGPRs) nor beside the score modifiers' state, and for a dense mask it would read the
-// mask entries of a tile twice; those reduce the max first.
-template <int D, int MK, bool EXT>
-constexpr bool kRunningMaxExps = D == 128 && !EXT && MK != MI_ATTN_MASK_DENSE;
+// Its second code path does not fit the registers with 64-key tiles at d = 64 (4
+// workgroups per CU, 128 VGPRs) nor beside the score modifiers' state, and for a dense
+// mask it would read the mask entries of a tile twice; those reduce the max first.
+template <int D, int BN, int MK, bool EXT>
+constexpr bool kRunningMaxExps = (D == 128 || BN == 128) && !EXT && MK != MI_ATTN_MASK_DENSE;
 
 // GATHER (top-k only): tiles are consecutive 64-key runs of the block's kept-key list
 // (AttnParams::list_*) instead of consecutive keys, so only keys some row of the block
@@ -83,7 +91,7 @@ constexpr bool kRunningMaxExps = D == 128 && !EXT && MK != MI_ATTN_MASK_DENSE;
 // and each K/V row is fetched from its own cache page (or packed row, or the new-token
 // array of the two-source form) with a per-lane 64-bit address.
 template <typename T, int D, int BN, int MK, bool GATHER = false, bool VARLEN = false, bool EXT = false>
-__global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN, EXT>)) void prefill_kernel(AttnParams p) {
+__global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN, EXT, BN>)) void prefill_kernel(AttnParams p) {
   static_assert(!GATHER || (MK == MI_ATTN_MASK_TOPK && BN == 64), "gathered tiles are top-k lists of 64 keys");
   static_assert(!VARLEN || (!GATHER && MK <= MI_ATTN_MASK_WINDOW), "varlen takes the key-position masks");
   using TL = Tile<D, BN>;
@@ -496,14 +504,15 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN, EXT>)) void pr
     v_base1 = (tr_row + 8) * TL::rowBytes | ((sl ^ swz<D>(tr_row + 8)) << 4) | (8 * (lane & 1));
   }
   static_assert(TL::stage % 512 == 0 && TL::kBytes % 512 == 0, "stage offsets keep the XOR-ed address bits");
-  // The tile loop runs unrolled by two (kUnroll2) at d = 128 for the position masks: the
+  // The tile loop runs unrolled by two (kUnroll2) for the position masks at d = 128 and
+  // with 128-key tiles at d = 64: the
   // stage is then a constant in each copy. Byte offsets in smem of a lane's K fragment (dim
   // chunk dc) and V^T fragment (dim block db) in the stage at byte offset ofs: adding a
   // multiple of 512 commutes with the XOR, so unrolled, the XOR-ed base is loop-invariant
   // and the stage offset an immediate. The other instances (d = 64 at 128 VGPRs; dense,
   // top-k and score modifiers, whose extra state leaves no room for the 16 invariant
   // addresses) keep the form that needs no extra live registers.
-  constexpr bool kUnroll2 = D == 128 && MK <= MI_ATTN_MASK_WINDOW && !EXT;
+  constexpr bool kUnroll2 = (D == 128 || BN == 128) && MK <= MI_ATTN_MASK_WINDOW && !EXT;
   auto k_addr = [&](int dc, int ofs) -> int {
     return kUnroll2 ? (k_base ^ (dc << 5)) + ofs : ((k_base + ofs) ^ (dc << 5));
   };
@@ -612,7 +621,7 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN, EXT>)) void pr
     apply_mask();
 
     // one-tile dump (a debug call): the scaled, masked logits in natural-log units
-    const bool dump_here = p.dump != nullptr && bg == p.dump_bg && qb == p.dump_qb && t == p.dump_tile;
+    const bool dump_here = BN == 64 && p.dump != nullptr && bg == p.dump_bg && qb == p.dump_qb && t == p.dump_tile;
     if (dump_here && row_ok) {
       float* ds = p.dump + static_cast<long>(rloc) * BN;
 #pragma unroll
@@ -622,7 +631,7 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN, EXT>)) void pr
     }
 
     u32x4_t preg[BN / 16];
-    if constexpr (kRunningMaxExps<D, MK, EXT>) {
+    if constexpr (kRunningMaxExps<D, BN, MK, EXT>) {
       // Online softmax (log2 domain) against the running max m_run as it stands, with no
       // per-tile max reduction. That is exact online softmax as long as no exponential
       // exceeds 2^kRescaleThreshold, which holds whenever this lane's sum of them does
@@ -882,9 +891,9 @@ template <typename T, int D, bool EXT>
 void launch_prefill_d(dim3 grid, const AttnParams& p, hipStream_t s) {
   const dim3 block(kThreads);
   switch (p.mask_kind) {
-    case MI_ATTN_MASK_NONE: hipLaunchKernelGGL((prefill_kernel<T, D, 64, 0, false, false, EXT>), grid, block, 0, s, p); break;
-    case MI_ATTN_MASK_CAUSAL: hipLaunchKernelGGL((prefill_kernel<T, D, 64, 1, false, false, EXT>), grid, block, 0, s, p); break;
-    case MI_ATTN_MASK_WINDOW: hipLaunchKernelGGL((prefill_kernel<T, D, 64, 2, false, false, EXT>), grid, block, 0, s, p); break;
+    case MI_ATTN_MASK_NONE: hipLaunchKernelGGL((prefill_kernel<T, D, kPosBN<D>, 0, false, false, EXT>), grid, block, 0, s, p); break;
+    case MI_ATTN_MASK_CAUSAL: hipLaunchKernelGGL((prefill_kernel<T, D, kPosBN<D>, 1, false, false, EXT>), grid, block, 0, s, p); break;
+    case MI_ATTN_MASK_WINDOW: hipLaunchKernelGGL((prefill_kernel<T, D, kPosBN<D>, 2, false, false, EXT>), grid, block, 0, s, p); break;
     case MI_ATTN_MASK_DENSE: hipLaunchKernelGGL((prefill_kernel<T, D, 64, 3, false, false, EXT>), grid, block, 0, s, p); break;
     default:
       if (p.list_idx != nullptr)
@@ -955,7 +964,9 @@ hipError_t launch_prefill_varlen(const AttnParams& p, int dtype, hipStream_t s) 
   return hipErrorInvalidValue;
 }
 
-int prefill_block_n(int) { return 64; }
+int prefill_block_n(int d, int mask_kind) {
+  return mask_kind <= MI_ATTN_MASK_WINDOW ? (d == 64 ? kPosBN<64> : kPosBN<128>) : 64;
+}
 int prefill_block_m() { return kBlockM; }
 
 hipError_t launch_lse_merge(const AttnParams& p, int dtype, hipStream_t s) {

@@ -23,7 +23,8 @@ hipError_t launch_half_path(int path, const AttnParams& p, int dtype, hipStream_
 
 // MFMA prefill tile shape: query rows and keys per workgroup tile.
 int prefill_block_m();
-int prefill_block_n(int d);
+// keys per tile of the MFMA prefill kernel for head dim d and a mask kind
+int prefill_block_n(int d, int mask_kind);
 
 // Varlen / paged forward (attn_fwd_varlen): device-built work lists (units and items, see
 // k_varlen.hip), the MFMA prefill and split-KV decode kernels over them, and the LSE

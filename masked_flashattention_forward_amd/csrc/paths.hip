@@ -59,7 +59,7 @@ int choose_half_path(int B, int Hkv, int G, int Lq, int Lk, int d, int /*mask_ki
   return 1;
 }
 
-HalfPlan plan_half_path(int path, int B, int Hkv, int G, int Lq, int Lk, int d, int /*mask_kind*/,
+HalfPlan plan_half_path(int path, int B, int Hkv, int G, int Lq, int Lk, int d, int mask_kind,
                         int /*window_left*/, int force_splits) {
   HalfPlan h{};
   int splits = 1;
@@ -71,7 +71,7 @@ HalfPlan plan_half_path(int path, int B, int Hkv, int G, int Lq, int Lk, int d, 
     splits = force_splits > 0 ? force_splits : decode_splits(h.grid, Lk);
   } else {
     h.block_m = prefill_block_m();
-    h.block_n = prefill_block_n(d);
+    h.block_n = prefill_block_n(d, mask_kind);
     h.q_per_block = q_per_block_for(G);
     const long blocks = prefill_blocks(B, Hkv, G, Lq);
     h.grid = static_cast<int>(blocks < 0x7fffffff ? blocks : 0x7fffffff);
