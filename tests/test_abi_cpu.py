@@ -84,6 +84,22 @@ def test_plan_accepts_supported_shapes(lib):
         assert p.path in (0, 1, 2) and p.grid >= 1 and p.splits >= 1
 
 
+def test_key_tile_sizes(lib):
+    # d = 64 with the position masks takes 128-key tiles; every other prefill instance 64
+    for kind in ("none", "causal", "window"):
+        assert mfa.plan(4, 16, 16, 8192, 8192, 64, kind, window_left=100)["block_n"] == 128, kind
+        assert mfa.plan(4, 16, 16, 8192, 8192, 128, kind, window_left=100)["block_n"] == 64, kind
+    assert mfa.plan(4, 16, 16, 2048, 2048, 64, "dense")["block_n"] == 64
+    assert mfa.plan(2, 16, 16, 4096, 4096, 64, "topk", keep_k=1024)["block_n"] == 64
+    # splits of a short prefill fall on 128-key tile boundaries: keys per split is a
+    # multiple of the tile
+    p = mfa.plan(1, 4, 4, 128, 16384, 64, "causal")
+    assert p["path"] == "mfma_prefill" and p["splits"] > 1
+    tiles = (16384 + 127) // 128
+    per = (tiles + p["splits"] - 1) // p["splits"]
+    assert (tiles + per - 1) // per == p["splits"]
+
+
 def test_fp32_takes_the_row_kernel(lib):
     assert mfa.plan(1, 2, 2, 128, 128, 64, "causal", dtype=mfa.F32)["path"] == "row"
 

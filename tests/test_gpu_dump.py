@@ -106,4 +106,10 @@ def test_dump_rejects_bad_requests():
     with pytest.raises(mfa.MiAttnError) as e:
         mfa.attn_fwd_ex(q2, k2, v2, mask_kind="causal", dump_at=(0, 0, 0, 0))
     assert e.value.code == mfa.EUNSUPPORTED
+    # d = 64 with a position mask takes 128-key tiles: the 64-key dump refuses it
+    p3 = synth.make_problem("dump d64 causal", 1, 4, 2, 200, 600, 64, "bf16", "causal", 1712)
+    q3, k3, v3 = (to_device(getattr(p3, n), p3.dtype) for n in ("q", "k", "v"))
+    with pytest.raises(mfa.MiAttnError) as e:
+        mfa.attn_fwd_ex(q3, k3, v3, mask_kind="causal", dump_at=(0, 0, 0, 0))
+    assert e.value.code == mfa.EUNSUPPORTED
     torch.cuda.synchronize()
