@@ -6,19 +6,24 @@
 // all G heads (InfiniTrain page, "Transformer integration": the flash path keeps the
 // original KV heads instead of expanding them).
 //
-// Per KV tile of BN keys (ExecuTorch page, "Summary": chunks along the key dimension,
-// online softmax finalised at the end):
+// Per KV tile of BN keys (64; 128 for the position masks at d = 64) (ExecuTorch page,
+// "Summary": chunks along the key dimension, online softmax finalised at the end):
 //   S^T = K Q^T      v_mfma_f32_32x32x16 (K from LDS as the A operand, Q^T from registers).
 //                    Each lane then holds one query column and 16 keys per 32-key block,
 //                    so the row max/sum is in-lane plus one exchange with lane ^ 32.
 //   mask             only on tiles the mask does not cover entirely (boundary tiles).
 //   online softmax   running max m and sum l per row in the log2 domain, guarded so an
-//                    all -inf tile (or row) never produces exp(-inf - -inf).
+//                    all -inf tile (or row) never produces exp(-inf - -inf); where the
+//                    registers allow, the exponentials are taken against the running max
+//                    as it stands and the max is reduced only on the rare tile that moves
+//                    it (see kRunningMaxExps).
 //   O^T += V^T P^T   P^T straight from the S^T registers (packed to 16 bit) as the B
-//                    operand; V is written to LDS transposed, with keys permuted so each
-//                    lane's eight keys match the ones its P registers hold.
+//                    operand; V stays in LDS row-major and its A operand comes from
+//                    transposed reads (ds_read_b64_tr_b16) whose lane-to-key map matches
+//                    the keys each lane's P registers hold.
 // Tiles that the mask hides entirely are never loaded: their range comes from the causal
-// / window bounds, the dense-mask summary or the top-k minimum rank per tile.
+// / window bounds, the dense-mask summary flags or in-kernel scan, or the top-k kept-key
+// lists and minimum rank per tile.
 #include <type_traits>
 
 #include "common.hpp"
