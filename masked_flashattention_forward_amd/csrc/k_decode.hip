@@ -270,7 +270,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(AttnParams p) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
     }
-    float ps4[4] = {0.f, 0.f, 0.f, 0.f};
+    float ps4[4] = {-0.f, -0.f, -0.f, -0.f};  // (-0 + x is x: the first adds fold away)
     u32x4_t preg[2];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {

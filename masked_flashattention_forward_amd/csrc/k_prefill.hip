@@ -645,7 +645,7 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN, EXT, BN>)) voi
       // their row maxima, move m to the exact running max, rescale l and O and take the
       // exponentials again; a dump takes that exact path too.
       auto exps = [&](float m_ref) -> float {  // P packed for the PV operand; the lane's sum
-        float ps4[4] = {0.f, 0.f, 0.f, 0.f};  // four independent chains
+        float ps4[4] = {-0.f, -0.f, -0.f, -0.f};  // four independent chains (-0 + x is x: no add)
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -721,7 +721,7 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN, EXT, BN>)) voi
       const float m_next = (mx > m_run + kRescaleThreshold) ? mx : m_run;
       const float m_use = (m_next == kNegInf) ? 0.f : m_next;
       const float alpha = fast_exp2(m_run - m_use);  // 1 when the max did not move, 0 from -inf
-      float ps4[4] = {0.f, 0.f, 0.f, 0.f};  // four independent chains
+      float ps4[4] = {-0.f, -0.f, -0.f, -0.f};  // four independent chains (-0 + x is x: no add)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
