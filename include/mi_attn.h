@@ -343,7 +343,10 @@ typedef struct {
   int block_n;       /* keys per KV tile (128 for d = 64 with the none / causal / window
                         kinds on path 1, else 64; 32 on path 2)                           */
   int splits;        /* key-range splits merged by log-sum-exp (paths 1, 2); 1 if unsplit */
-  int grid;          /* workgroups of the main kernel                                    */
+  int grid;          /* query blocks of the main kernel, one workgroup each; on path 1 with
+                        the none / causal / window kinds and one split, more blocks than the
+                        GPU holds at once run on that many resident workgroups, each taking
+                        several blocks                                                    */
   int mask_summary;  /* 1 when a per-tile dense-mask summary kernel runs first            */
   size_t workspace_bytes; /* temporary device memory the call takes                     */
   int topk_list_cap; /* top-k on path 1: keys per query block's kept-key list (the block's

@@ -136,6 +136,10 @@ struct AttnParams {
   // dump_tile (see MI_ATTN_DUMP_FLOATS); nullptr otherwise
   float* dump;
   int dump_bg, dump_qb, dump_tile;
+  // query blocks of the prefill grid. For the key-position masks with one split, when it
+  // exceeds gridDim.x the grid holds only the workgroups the device runs at once and each
+  // takes several blocks (see prefill_kernel); otherwise it equals gridDim.x.
+  unsigned n_blocks;
   const void* dout;
   void* dq;
   void* dk;

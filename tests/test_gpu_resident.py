@@ -1,0 +1,64 @@
+"""Resident prefill workgroups: when a prefill grid has more query blocks than the GPU
+holds at once, attn_fwd launches only the resident workgroups and each takes several
+blocks (the blocks of its XCD's list in zigzag rounds). The cases have more blocks than
+two workgroups per CU on 256 CUs and cover each mask kind on this path (none, causal,
+window, dense, gathered top-k), both head dims and both half types, with ragged query
+blocks (Lq not a multiple of the block). The outputs start as NaN, so a block that no
+workgroup takes fails; the first and last row of every query block, over every (batch,
+head), are compared with the oracle, and a second call must give the same bits."""
+import numpy as np
+import pytest
+
+import synth
+from helpers import compare, run_gpu, run_oracle, say
+
+pytestmark = pytest.mark.gpu
+
+RESIDENT = 2 * 256  # two workgroups per CU on 256 CUs: every grid below is larger
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import masked_flashattention_forward_amd as mfa
+    mfa.lib()
+    mfa.set_debug()
+    yield
+    mfa.set_debug()
+
+
+def problems():
+    rng = np.random.default_rng(4301)
+    dense = np.where(rng.random((1000, 1000)) < 0.2, -np.inf, rng.standard_normal((1000, 1000))).astype(np.float32)
+    return [
+        synth.make_problem("resident causal bf16 d128 4x16 2000", 4, 16, 16, 2000, 2000, 128, "bf16", "causal", 4201),
+        synth.make_problem("resident none fp16 d64 GQA 2x32/8 2100x3000", 2, 32, 8, 2100, 3000, 64, "fp16", "none",
+                           4202),
+        synth.make_problem("resident window bf16 d64 4x16 2048", 4, 16, 16, 2048, 2048, 64, "bf16", "window", 4203,
+                           window_left=300),
+        synth.make_problem("resident dense fp16 d128 8x16 1000", 8, 16, 16, 1000, 1000, 128, "fp16", "dense", 4204,
+                           mask=dense),
+        synth.make_problem("resident top-k bf16 d128 2x16 4000", 2, 16, 16, 4000, 4000, 128, "bf16", "topk", 4205,
+                           keep_k=1024, with_zero_hold=True),
+    ]
+
+
+@pytest.mark.parametrize("idx", range(5))
+def test_resident_workgroups(idx):
+    import masked_flashattention_forward_amd as mfa
+    p = problems()[idx]
+    plan = mfa.plan(p.B, p.Hq, p.Hkv, p.Lq, p.Lk, p.d, p.mask_kind, p.window_left, p.keep_k,
+                    synth.DTYPE_CODES[p.dtype])
+    assert plan["path"] == "mfma_prefill" and plan["splits"] == 1 and plan["grid"] > RESIDENT, plan
+    say(f"{p.name}: {plan['grid']} query blocks")
+    out, lse = run_gpu(p, out_fill=float("nan"))
+    assert not np.isnan(out).any() and not np.isnan(lse).any(), f"{p.name}: a block was not computed"
+    qpb = plan["block_m"] // (p.Hq // p.Hkv)
+    rows = sorted({r for qb0 in range(0, p.Lq, qpb) for r in (qb0, min(p.Lq, qb0 + qpb) - 1)})
+    ref_o, ref_l = run_oracle(p, rows=rows)
+    compare(p, out, lse, ref_o, ref_l, rows=rows, label=f"{p.name}, first and last row of every block")
+    out2, lse2 = run_gpu(p, out_fill=float("nan"))
+    np.testing.assert_array_equal(out2, out, err_msg=f"{p.name}: second call differs")
+    np.testing.assert_array_equal(lse2, lse, err_msg=f"{p.name}: second call differs (LSE)")
