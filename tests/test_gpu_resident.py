@@ -1,11 +1,12 @@
-"""Resident prefill workgroups: when a prefill grid has more query blocks than the GPU
-holds at once, attn_fwd launches only the resident workgroups and each takes several
-blocks (the blocks of its XCD's list in zigzag rounds). The cases have more blocks than
-two workgroups per CU on 256 CUs and cover each mask kind on this path (none, causal,
-window, dense, gathered top-k), both head dims and both half types, with ragged query
-blocks (Lq not a multiple of the block). The outputs start as NaN, so a block that no
-workgroup takes fails; the first and last row of every query block, over every (batch,
-head), are compared with the oracle, and a second call must give the same bits."""
+"""Resident prefill workgroups: when a prefill grid of a key-position mask (none, causal,
+window) has more query blocks than the GPU holds at once, attn_fwd launches only the
+resident workgroups and each takes several blocks (the blocks of its XCD's list in zigzag
+rounds). The cases have more blocks than two workgroups per CU on 256 CUs and cover the
+three position kinds, both head dims and both half types, with ragged query blocks (Lq
+not a multiple of the block); a dense and a gathered top-k case of the same size check
+the one-workgroup-per-block launch those kinds keep. The outputs start as NaN, so a block
+that no workgroup takes fails; the first and last row of every query block, over every
+(batch, head), are compared with the oracle, and a second call must give the same bits."""
 import numpy as np
 import pytest
 
