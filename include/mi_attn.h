@@ -270,7 +270,10 @@ int attn_fwd_ex(const attn_fwd_args_t* args, void* stream);
  * Rows past the block's rows and tiles the kernel skips (hidden entirely) are not written.
  * MI_ATTN_EUNSUPPORTED when the call does not take the MFMA prefill path with 64-key tiles
  * (see attn_fwd_plan: path 1 and block_n 64; d = 64 with the none / causal / window kinds
- * takes 128-key tiles), MI_ATTN_EINVAL for an index out of range or a NULL dump.
+ * takes 128-key tiles) or carries a score modifier (ALiBi slopes, softcap > 0, or a dense
+ * mask added to top-k), MI_ATTN_EINVAL for an index out of range or a NULL dump. The dump
+ * runs its own kernel instances (one workgroup per query block); the results are those
+ * of attn_fwd_ex.
  */
 #define MI_ATTN_DUMP_FLOATS (2 * 128 * 64 + 2 * 128)
 int attn_fwd_dump(const attn_fwd_args_t* args, int b, int kv_head, int query_block, int tile, float* dump,

@@ -348,6 +348,10 @@ int fwd_impl(const attn_fwd_args_t* a, void* stream, char* fixed_ws, size_t fixe
     if (pl.pub.block_n != 64)
       return fail(MI_ATTN_EUNSUPPORTED, "the one-tile dump covers 64-key tiles (this call takes %d-key tiles)",
                   pl.pub.block_n);
+    if (a->alibi_slopes != nullptr || a->softcap > 0.f ||
+        (a->mask_kind == MI_ATTN_MASK_TOPK && a->mask != nullptr))
+      return fail(MI_ATTN_EUNSUPPORTED,
+                  "the one-tile dump covers calls without score modifiers (ALiBi, softcap, a mask added to top-k)");
     const int nqb = (a->Lq + pl.q_per_block - 1) / pl.q_per_block;
     const int ntiles = pl.list_cap > 0 ? pl.list_cap / 64 : (a->Lk + pl.pub.block_n - 1) / pl.pub.block_n;
     if (dump->buf == nullptr || dump->b < 0 || dump->b >= a->B || dump->kv_head < 0 || dump->kv_head >= a->Hkv ||

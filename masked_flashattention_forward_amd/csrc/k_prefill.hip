@@ -101,10 +101,15 @@ constexpr bool kRunningMaxExps = (D == 128 || BN == 128) && !EXT && MK != MI_ATT
 // one item of the device-built work list (a key range of one (sequence, query block)),
 // and each K/V row is fetched from its own cache page (or packed row, or the new-token
 // array of the two-source form) with a per-lane 64-bit address.
-template <typename T, int D, int BN, int MK, bool GATHER = false, bool VARLEN = false, bool EXT = false>
+// DUMP: the instance attn_fwd_dump runs (AttnParams::dump set): one workgroup writes the
+// intermediates of one tile. The checks live only in these instances, so the others
+// carry no per-tile test for it (it cost 1.5% at c4 d128).
+template <typename T, int D, int BN, int MK, bool GATHER = false, bool VARLEN = false, bool EXT = false,
+          bool DUMP = false>
 __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN, EXT, BN>)) void prefill_kernel(AttnParams p) {
   static_assert(!GATHER || (MK == MI_ATTN_MASK_TOPK && BN == 64), "gathered tiles are top-k lists of 64 keys");
   static_assert(!VARLEN || (!GATHER && MK <= MI_ATTN_MASK_WINDOW), "varlen takes the key-position masks");
+  static_assert(!DUMP || (BN == 64 && !VARLEN && !EXT), "the dump covers 64-key tiles without score modifiers");
   using TL = Tile<D, BN>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * TL::stage];
 
@@ -634,7 +639,7 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN, EXT, BN>)) voi
       apply_mask();
 
       // one-tile dump (a debug call): the scaled, masked logits in natural-log units
-      const bool dump_here = BN == 64 && p.dump != nullptr && bg == p.dump_bg && qb == p.dump_qb && t == p.dump_tile;
+      const bool dump_here = DUMP && bg == p.dump_bg && qb == p.dump_qb && t == p.dump_tile;
       if (dump_here && row_ok) {
         float* ds = p.dump + static_cast<long>(rloc) * BN;
 #pragma unroll
@@ -969,6 +974,38 @@ void launch_prefill_d(dim3 grid, const AttnParams& p, hipStream_t s) {
   }
 }
 
+// The dump instances (64-key tiles, no score modifiers), one workgroup per block.
+template <typename T, int D>
+hipError_t launch_prefill_dump(dim3 grid, const AttnParams& p, hipStream_t s) {
+  AttnParams a = p;
+  a.n_blocks = grid.x;
+  const dim3 block(kThreads);
+  switch (p.mask_kind) {
+    case MI_ATTN_MASK_NONE:
+    case MI_ATTN_MASK_CAUSAL:
+    case MI_ATTN_MASK_WINDOW:
+      if constexpr (kPosBN<D> == 64) {
+        if (p.mask_kind == MI_ATTN_MASK_NONE)
+          hipLaunchKernelGGL((prefill_kernel<T, D, 64, 0, false, false, false, true>), grid, block, 0, s, a);
+        else if (p.mask_kind == MI_ATTN_MASK_CAUSAL)
+          hipLaunchKernelGGL((prefill_kernel<T, D, 64, 1, false, false, false, true>), grid, block, 0, s, a);
+        else
+          hipLaunchKernelGGL((prefill_kernel<T, D, 64, 2, false, false, false, true>), grid, block, 0, s, a);
+        break;
+      } else {
+        return hipErrorInvalidValue;  // these kinds take 128-key tiles at this head dim
+      }
+    case MI_ATTN_MASK_DENSE: hipLaunchKernelGGL((prefill_kernel<T, D, 64, 3, false, false, false, true>), grid, block, 0, s, a); break;
+    default:
+      if (p.list_idx != nullptr)
+        hipLaunchKernelGGL((prefill_kernel<T, D, 64, 4, true, false, false, true>), grid, block, 0, s, a);
+      else
+        hipLaunchKernelGGL((prefill_kernel<T, D, 64, 4, false, false, false, true>), grid, block, 0, s, a);
+      break;
+  }
+  return hipSuccess;
+}
+
 template <typename T>
 hipError_t launch_prefill_t(const AttnParams& p, hipStream_t s) {
   const int nqb = (p.Lq + p.q_per_block - 1) / p.q_per_block;
@@ -976,7 +1013,11 @@ hipError_t launch_prefill_t(const AttnParams& p, hipStream_t s) {
   if (blocks > 0x7fffffffL || p.splits > 65535) return hipErrorInvalidValue;
   dim3 grid(static_cast<unsigned>(blocks), p.splits);
   const bool ext = needs_ext(p);
-  if (p.d == 128) {
+  if (p.dump != nullptr) {
+    if (ext) return hipErrorInvalidValue;
+    const hipError_t e = p.d == 128 ? launch_prefill_dump<T, 128>(grid, p, s) : launch_prefill_dump<T, 64>(grid, p, s);
+    if (e != hipSuccess) return e;
+  } else if (p.d == 128) {
     if (ext) launch_prefill_d<T, 128, true>(grid, p, s);
     else launch_prefill_d<T, 128, false>(grid, p, s);
   } else {

@@ -41,12 +41,14 @@ def block_logits(p, b, g, qb, qpb):
     return S, rows
 
 
-@pytest.mark.parametrize("kind,tile", [("causal", 3), ("causal", 4), ("causal", 0), ("window", 4), ("dense", 2)])
-def test_dump_matches_the_block_logits(kind, tile):
+@pytest.mark.parametrize("kind,tile,d", [("causal", 3, 128), ("causal", 4, 128), ("causal", 0, 128),
+                                         ("window", 4, 128), ("dense", 2, 128), ("dense", 3, 64),
+                                         ("none", 1, 128)])
+def test_dump_matches_the_block_logits(kind, tile, d):
     import masked_flashattention_forward_amd as mfa
-    B, Hq, Hkv, Lq, Lk, d = 2, 4, 2, 100, 300, 128
+    B, Hq, Hkv, Lq, Lk = 2, 4, 2, 100, 300
     mask = synth.window_dense_mask(Lq, Lk, Lk - Lq, 90) if kind == "dense" else None
-    p = synth.make_problem(f"dump {kind} tile {tile}", B, Hq, Hkv, Lq, Lk, d, "bf16", kind, 1700 + tile,
+    p = synth.make_problem(f"dump {kind} d{d} tile {tile}", B, Hq, Hkv, Lq, Lk, d, "bf16", kind, 1700 + tile,
                            window_left=90, mask=mask)
     plan = mfa.plan(B, Hq, Hkv, Lq, Lk, d, kind, window_left=90)
     qpb = plan["block_m"] // (Hq // Hkv)
@@ -112,4 +114,10 @@ def test_dump_rejects_bad_requests():
     with pytest.raises(mfa.MiAttnError) as e:
         mfa.attn_fwd_ex(q3, k3, v3, mask_kind="causal", dump_at=(0, 0, 0, 0))
     assert e.value.code == mfa.EUNSUPPORTED
+    # score modifiers: the dump instances have none
+    slopes = torch.full((p.Hq,), 0.25, dtype=torch.float32, device="cuda")
+    for kw in (dict(alibi_slopes=slopes), dict(softcap=20.0)):
+        with pytest.raises(mfa.MiAttnError) as e:
+            mfa.attn_fwd_ex(q, k, v, mask_kind="causal", dump_at=(0, 0, 0, 0), **kw)
+        assert e.value.code == mfa.EUNSUPPORTED
     torch.cuda.synchronize()
