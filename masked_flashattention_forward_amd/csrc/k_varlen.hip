@@ -106,28 +106,68 @@ __device__ void block_scan(const long long (&v)[NV], long long (&excl)[NV], long
   __syncthreads();  // wsum is reused by the next call
 }
 
-// One workgroup. Pass 1 sums the tiles of each type and fixes the item length per type;
-// pass 2 numbers units and items sequence by sequence (256 sequences a round) and writes
-// them. Units of a sequence are written longest key range first. Writes stop at the
-// caps, which consistent lengths never reach.
+// One workgroup. Sequences are taken in rounds of 256: their lengths and unit offsets go
+// to LDS, and each thread then takes units of the round (not whole sequences, so a long
+// prefill sequence's units do not run one after another on a single lane). Pass 1 sums
+// the tiles of each type and fixes the item length per type; pass 2 numbers units and
+// items in sequence order and writes them. Units of a sequence are written longest key
+// range first. Writes stop at the caps, which consistent lengths never reach.
 __global__ __launch_bounds__(kPlanThreads) void varlen_plan_kernel(AttnParams p, int4* units, int4* items_p,
                                                                    int4* items_d, int32_t* counts, int units_cap,
                                                                    int items_cap, int target_items, int force) {
   __shared__ long long wsum[3][kPlanWaves];
+  __shared__ int s_lq[kPlanThreads], s_lk[kPlanThreads], s_ctx[kPlanThreads], s_off[kPlanThreads + 1];
   const int tid = threadIdx.x;
+
+  // the round of sequences [base, base + kPlanThreads): lengths and the offsets of their
+  // units within the round; returns the round's unit count
+  auto load_round = [&](int base) {
+    const int s = base + tid;
+    long long nu[1] = {0}, ex[1], tot[1];
+    s_lq[tid] = s_lk[tid] = s_ctx[tid] = 0;
+    if (s < p.num_seqs) {
+      const VarlenSeq v = varlen_seq(p, s);
+      s_lq[tid] = v.Lq;
+      s_lk[tid] = v.Lk;
+      s_ctx[tid] = v.ctx;
+      nu[0] = units_of(p, v);
+    }
+    block_scan<1>(nu, ex, tot, wsum);
+    s_off[tid] = static_cast<int>(ex[0]);
+    if (tid == 0) s_off[kPlanThreads] = static_cast<int>(tot[0]);
+    __syncthreads();
+    return static_cast<int>(tot[0]);
+  };
+  // unit j of the round: its sequence's slot in the round, lengths and query block
+  auto unit_at = [&](int j, int* ls, int* qb, VarlenSeq* v) {
+    int lo = 0, hi = kPlanThreads;  // the last slot whose offset is <= j (a non-empty one)
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) / 2;
+      if (s_off[mid] <= j) lo = mid;
+      else hi = mid;
+    }
+    *ls = lo;
+    *qb = s_off[lo + 1] - 1 - j;  // the round's units run longest key range first
+    *v = VarlenSeq{};
+    v->Lq = s_lq[lo];
+    v->Lk = s_lk[lo];
+    v->ctx = s_ctx[lo];
+  };
 
   // tiles of prefill-type and decode-type units, and the prefill-type unit count
   long long t3[3] = {0, 0, 0};
-  for (int s = tid; s < p.num_seqs; s += kPlanThreads) {
-    const VarlenSeq v = varlen_seq(p, s);
-    const int nu = units_of(p, v);
-    const bool dec = decode_type(p, v);
-    if (!dec) t3[2] += nu;
-    for (int qb = 0; qb < nu; ++qb) {
-      int lo, hi;
+  for (int base = 0; base < p.num_seqs; base += kPlanThreads) {
+    const int nunits = load_round(base);
+    for (int j = tid; j < nunits; j += kPlanThreads) {
+      int ls, qb, lo, hi;
+      VarlenSeq v;
+      unit_at(j, &ls, &qb, &v);
+      const bool dec = decode_type(p, v);
+      if (!dec) t3[2] += 1;
       unit_keys(p, v, qb, &lo, &hi);
       t3[dec ? 1 : 0] += tiles_of(lo, hi);
     }
+    __syncthreads();  // the next round rewrites the LDS arrays
   }
   long long ex3[3], tot3[3];
   block_scan<3>(t3, ex3, tot3, wsum);
@@ -143,43 +183,40 @@ __global__ __launch_bounds__(kPlanThreads) void varlen_plan_kernel(AttnParams p,
 
   long long carry[3] = {0, 0, 0};  // units, prefill-type items, decode-type items so far
   for (int base = 0; base < p.num_seqs; base += kPlanThreads) {
-    const int s = base + tid;
-    VarlenSeq v{};
-    int nu = 0;
-    bool dec = false;
-    long long cnt[3] = {0, 0, 0};
-    if (s < p.num_seqs) {
-      v = varlen_seq(p, s);
-      nu = units_of(p, v);
-      dec = decode_type(p, v);
-      for (int qb = 0; qb < nu; ++qb) {
-        int lo, hi, n, per_u;
+    const int nunits = load_round(base);
+    for (int j0 = 0; j0 < nunits; j0 += kPlanThreads) {
+      const int j = j0 + tid;
+      int ls = 0, qb = 0, lo = 0, hi = 0, n = 0, per_u = 0;
+      bool dec = false;
+      long long cnt[3] = {0, 0, 0};
+      if (j < nunits) {
+        VarlenSeq v;
+        unit_at(j, &ls, &qb, &v);
+        dec = decode_type(p, v);
         unit_keys(p, v, qb, &lo, &hi);
         split_unit(tiles_of(lo, hi), dec ? per_d : per_p, force, &n, &per_u);
-        cnt[dec ? 2 : 1] += n;
+        cnt[0] = 1;
+        cnt[dec ? 2 : 1] = n;
       }
-      cnt[0] = nu;
-    }
-    long long ex[3], tot[3];
-    block_scan<3>(cnt, ex, tot, wsum);
-    long long u = carry[0] + ex[0];
-    long long it = carry[dec ? 2 : 1] + ex[dec ? 2 : 1];
-    int4* items = dec ? items_d : items_p;
-    for (int qb = nu - 1; qb >= 0; --qb, ++u) {
-      int lo, hi, n, per_u;
-      unit_keys(p, v, qb, &lo, &hi);
-      split_unit(tiles_of(lo, hi), dec ? per_d : per_p, force, &n, &per_u);
-      if (u < units_cap)
-        units[u] = make_int4(s, qb, static_cast<int>(it < items_cap ? it : items_cap), n | (dec ? kDecodeFlag : 0));
-      const long long t0 = lo / kItemTile;
-      for (int k = 0; k < n; ++k, ++it) {
-        const long long a = k == 0 ? lo : max(static_cast<long long>(lo), (t0 + k * per_u) * kItemTile);
-        const long long b = min(static_cast<long long>(hi), (t0 + (k + 1) * static_cast<long long>(per_u)) * kItemTile);
-        if (it < items_cap && u < units_cap)
-          items[it] = make_int4(static_cast<int>(u), static_cast<int>(a), static_cast<int>(max(a, b)), 0);
+      long long ex[3], tot[3];
+      block_scan<3>(cnt, ex, tot, wsum);
+      if (j < nunits) {
+        const long long u = carry[0] + ex[0];
+        long long it = carry[dec ? 2 : 1] + ex[dec ? 2 : 1];
+        int4* items = dec ? items_d : items_p;
+        if (u < units_cap)
+          units[u] = make_int4(base + ls, qb, static_cast<int>(it < items_cap ? it : items_cap), n | (dec ? kDecodeFlag : 0));
+        const long long t0 = lo / kItemTile;
+        for (int k = 0; k < n; ++k, ++it) {
+          const long long a = k == 0 ? lo : max(static_cast<long long>(lo), (t0 + k * per_u) * kItemTile);
+          const long long b = min(static_cast<long long>(hi), (t0 + (k + 1) * static_cast<long long>(per_u)) * kItemTile);
+          if (it < items_cap && u < units_cap)
+            items[it] = make_int4(static_cast<int>(u), static_cast<int>(a), static_cast<int>(max(a, b)), 0);
+        }
       }
+      for (int k = 0; k < 3; ++k) carry[k] += tot[k];
     }
-    for (int k = 0; k < 3; ++k) carry[k] += tot[k];
+    __syncthreads();  // the next round rewrites the LDS arrays
   }
   if (tid == 0) {
     counts[0] = static_cast<int32_t>(min(carry[0], static_cast<long long>(units_cap)));
