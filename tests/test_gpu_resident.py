@@ -63,3 +63,43 @@ def test_resident_workgroups(idx):
     out2, lse2 = run_gpu(p, out_fill=float("nan"))
     np.testing.assert_array_equal(out2, out, err_msg=f"{p.name}: second call differs")
     np.testing.assert_array_equal(lse2, lse, err_msg=f"{p.name}: second call differs (LSE)")
+
+
+def test_two_streams_at_once():
+    """Resident grids of two calls launched on two streams with no ordering between them
+    (the library takes no workspace for them, so nothing serialises the calls): the
+    workgroups of one grid wait for the other's slots, and every block is still computed
+    once, with the bits of the calls run alone."""
+    import torch
+    import masked_flashattention_forward_amd as mfa
+    from helpers import to_device
+    ps = problems()[:3]
+    dev = []
+    for p in ps:
+        q, k, v = (to_device(getattr(p, n), p.dtype) for n in ("q", "k", "v"))
+        dev.append((p, q, k, v))
+
+    def run(p, q, k, v, stream=None):
+        with torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream()):
+            out = torch.full(q.shape, float("nan"), dtype=q.dtype, device="cuda")
+            lse = torch.full((p.B, p.Hq, p.Lq), float("nan"), dtype=torch.float32, device="cuda")
+        mfa.attn_fwd(q, k, v, scale=p.scale, mask_kind=p.mask_kind, window_left=p.window_left, out=out, lse=lse,
+                     stream=stream)
+        return out, lse
+
+    ref = []
+    for p, q, k, v in dev:
+        o, l = run(p, q, k, v)
+        torch.cuda.synchronize()
+        ref.append((o.view(torch.int16).cpu().numpy(), l.cpu().numpy()))
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for rnd in range(3):
+        say(f"resident grids on two streams at once, round {rnd}")
+        torch.cuda.synchronize()
+        res = [run(*d, stream=s1 if i % 2 == 0 else s2) for i, d in enumerate(dev)]
+        torch.cuda.synchronize()
+        for (p, *_), (o, l), (o_ref, l_ref) in zip(dev, res, ref):
+            np.testing.assert_array_equal(o.view(torch.int16).cpu().numpy(), o_ref,
+                                          err_msg=f"{p.name}: output differs on two streams")
+            np.testing.assert_array_equal(l.cpu().numpy(), l_ref, err_msg=f"{p.name}: LSE differs on two streams")
+    print("[resident] three resident grids on two streams at once, three rounds: bit-identical", flush=True)
