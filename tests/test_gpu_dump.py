@@ -121,3 +121,74 @@ def test_dump_rejects_bad_requests():
             mfa.attn_fwd_ex(q, k, v, mask_kind="causal", dump_at=(0, 0, 0, 0), **kw)
         assert e.value.code == mfa.EUNSUPPORTED
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("keep,tile", [(100, 1), (400, 5)])
+def test_dump_topk(keep, tile):
+    """The top-k instances: with keep 100 the block's tiles are runs of its kept-key list
+    (keys up to the block's last position whose rank is at most the first row's
+    threshold, ascending, padded with key Lk); with keep 400 the list would not save
+    enough and the tiles are consecutive keys. S holds scale q k^T + zero_hold on the keys
+    a row keeps and -inf elsewhere (padding included), against the oracle's ranks and
+    thresholds."""
+    import torch
+    import masked_flashattention_forward_amd as mfa
+    from oracle.topk import topk_rank_ref, topk_tau_ref, kept_from_rank_tau
+    B, Hq, Hkv, Lq, Lk, d = 1, 4, 2, 200, 600, 128
+    G = Hq // Hkv
+    p = synth.make_problem(f"dump top-k keep {keep} tile {tile}", B, Hq, Hkv, Lq, Lk, d, "bf16", "topk", 1720 + keep,
+                           keep_k=keep, with_zero_hold=True)
+    plan = mfa.plan(B, Hq, Hkv, Lq, Lk, d, "topk", keep_k=keep)
+    gathered = plan["topk_list_cap"] > 0
+    assert gathered == (keep == 100), plan
+    qpb = plan["block_m"] // G
+    b, g, qb = 0, 1, 2
+    say(p.name)
+    q, k, v = (to_device(getattr(p, n), p.dtype) for n in ("q", "k", "v"))
+    zh = torch.from_numpy(p.zero_hold).cuda()
+    out, lse, dump = mfa.attn_fwd_ex(q, k, v, scale=p.scale, mask_kind="topk", zero_hold=zh, keep_k=keep,
+                                     dump_at=(b, g, qb, tile))
+    torch.cuda.synchronize()
+    zrow = p.zero_hold[b, g].astype(np.float64)
+    rank = topk_rank_ref(zrow)
+    tau = topk_tau_ref(rank, Lq, keep)
+    kept = kept_from_rank_tau(rank, tau, Lq)
+    i0, i1 = qb * qpb, min(Lq, qb * qpb + qpb)
+    rows = (i1 - i0) * G
+    pos_last = Lk - Lq + i1 - 1
+    if gathered:
+        keys = [j for j in range(pos_last + 1) if rank[j] <= tau[i0]]
+        keys += [Lk] * (-len(keys) % 64)
+    else:
+        keys = list(range(Lk)) + [Lk] * (-Lk % 64)
+    qf, kf = p.f64("q"), p.f64("k")
+    S_all = np.full((rows, len(keys)), -np.inf)
+    for r in range(rows):
+        i, h = i0 + r // G, g * G + r % G
+        for c, j in enumerate(keys):
+            if j < Lk and kept[i, j]:
+                S_all[r, c] = p.scale64 * (kf[b, g, j] @ qf[b, h, i]) + zrow[j]
+    c0 = 64 * tile
+    assert c0 < len(keys)
+    Sr = S_all[:, c0:c0 + 64]
+    S = dump["S"].cpu().numpy().astype(np.float64)[:rows]
+    P = dump["P"].cpu().numpy().astype(np.float64)[:rows]
+    m = dump["m"].cpu().numpy().astype(np.float64)[:rows]
+    l = dump["l"].cpu().numpy().astype(np.float64)[:rows]
+    np.testing.assert_array_equal(np.isneginf(S), np.isneginf(Sr))
+    fin = np.isfinite(Sr)
+    assert fin.any()
+    np.testing.assert_allclose(S[fin], Sr[fin], rtol=1e-5, atol=1e-4)
+    with np.errstate(invalid="ignore"):
+        ref_p = np.exp(S - m[:, None])
+    ref_p[~fin] = 0.0
+    np.testing.assert_allclose(P, ref_p, rtol=1e-5, atol=1e-30)
+    seen = S_all[:, :c0 + 64]
+    run_max = np.max(seen, axis=1)
+    live = np.isfinite(run_max)
+    assert np.all(m[live] <= run_max[live] + 1e-4)
+    assert np.all(m[live] >= run_max[live] - 8 * np.log(2) - 1e-4)
+    z = np.exp(seen - m[:, None]).sum(axis=1)
+    np.testing.assert_allclose(l[live], z[live], rtol=1e-3)
+    print(f"[dump] {p.name}: {'kept-key list' if gathered else 'key'} tile {tile}, {rows} rows, "
+          f"{int(fin.sum())} visible logits match the oracle", flush=True)
