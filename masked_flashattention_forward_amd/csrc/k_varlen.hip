@@ -247,20 +247,41 @@ __global__ __launch_bounds__(256) void varlen_merge_kernel(AttnParams p, const i
   const float* po = dec ? pd_out : pp_out;
   const float* pl = dec ? pd_lse : pp_lse;
   constexpr int kPerRow = D / 4;
+  constexpr int kBatch = 8;  // items whose partials are loaded together (their latencies overlap)
   for (int idx = threadIdx.x; idx < rows * kPerRow; idx += blockDim.x) {
     const int r = idx / kPerRow;
     const int d0 = (idx % kPerRow) * 4;
+    auto slot_of = [&](int k) { return (static_cast<long>(un.z + k) * p.Hkv + g) * rpb + r; };
     float mx = kNegInf;
-    for (int k = 0; k < n; ++k) mx = fmaxf(mx, pl[(static_cast<long>(un.z + k) * p.Hkv + g) * rpb + r]);
+    for (int k0 = 0; k0 < n; k0 += kBatch) {
+      float ls[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) ls[k] = k0 + k < n ? pl[slot_of(k0 + k)] : kNegInf;
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) mx = fmaxf(mx, ls[k]);
+    }
     float4 acc = {0.f, 0.f, 0.f, 0.f};
     float tot = 0.f;
     if (mx != kNegInf) {
-      for (int k = 0; k < n; ++k) {
-        const long slot = (static_cast<long>(un.z + k) * p.Hkv + g) * rpb + r;
-        const float w = __expf(pl[slot] - mx);
-        const float4 o = *reinterpret_cast<const float4*>(po + slot * D + d0);
-        acc.x += w * o.x; acc.y += w * o.y; acc.z += w * o.z; acc.w += w * o.w;
-        tot += w;
+      for (int k0 = 0; k0 < n; k0 += kBatch) {
+        float ls[kBatch];
+        float4 os[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          ls[k] = kNegInf;
+          os[k] = float4{0.f, 0.f, 0.f, 0.f};
+          if (k0 + k < n) {
+            const long slot = slot_of(k0 + k);
+            ls[k] = pl[slot];
+            os[k] = *reinterpret_cast<const float4*>(po + slot * D + d0);
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          const float w = __expf(ls[k] - mx);  // 0 for the items past n
+          acc.x += w * os[k].x; acc.y += w * os[k].y; acc.z += w * os[k].z; acc.w += w * os[k].w;
+          tot += w;
+        }
       }
     }
     const bool dead = !(tot > 0.f);
