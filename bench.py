@@ -486,6 +486,32 @@ def copy_calibration(nbytes: int, iters: int):
     log(f"copied {nbytes} bytes x {iters}")
 
 
+def headline_roofline(name, p, plan, flops, kern, warm_ms):
+    """The roofline object of the timed workload: MFMA-bound (TFLOP/s of the visible pairs)
+    on the prefill path, HBM-bound (algorithmic bytes) on the split-KV decode path, with
+    the calibrated HBM traffic when the committed counters belong to this workload and the
+    current kernel sources."""
+    kern_ms = float(kern.mean())
+    med_ms = float(np.median(kern))
+    nbytes = algorithmic_bytes(p)
+    common = {"algorithmic_bytes": nbytes, "avg_kernel_us": round(kern_ms * 1e3, 2),
+              "median_kernel_us": round(med_ms * 1e3, 2), "min_kernel_us": round(float(kern.min()) * 1e3, 2),
+              "warmup_ms": round(warm_ms, 1)}
+    if plan["path"] == "splitkv_decode":
+        achieved = nbytes / kern_ms / 1e6
+        return {"bound": "hbm", "kernel": f"decode_kernel<{p.dtype},{p.d},{p.mask_kind}> + lse_merge_kernel",
+                "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": measured_traffic("decode_kernel<bf16,128,causal> c3 decode") if name == "c3d" else None,
+                **common, "frac_at_median": round(nbytes / med_ms / 1e6 / PEAK_HBM_GBS, 4)}
+    achieved = flops / kern_ms / 1e9
+    return {"bound": "mfma", "kernel": f"prefill_kernel<{p.dtype},{p.d},{plan['block_n']},{p.mask_kind}>",
+            "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": measured_traffic("prefill_kernel<bf16,128,64,causal> c3 prefill") if name == "c3p" else None,
+            **common, "frac_at_median": round(flops / med_ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -542,16 +568,12 @@ def main():
         "config": {"workload": p.name, "B": p.B, "Hq": p.Hq, "Hkv": p.Hkv, "Lq": p.Lq, "Lk": p.Lk, "d": p.d,
                    "mask": p.mask_kind, "seed": p.meta.get("seed"), "flops_per_step": flops,
                    "plan": plan},
-        "roofline": {"bound": "mfma", "kernel": "prefill_kernel<bf16,128,64,causal>", "achieved": round(achieved, 2),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic("prefill_kernel<bf16,128,64,causal> c3 prefill") if args.only == "c3p" else None,
-                     "algorithmic_bytes": algorithmic_bytes(p), "avg_kernel_us": round(kern_ms * 1e3, 2),
-                     "median_kernel_us": round(float(np.median(kern)) * 1e3, 2),
-                     "min_kernel_us": round(float(kern.min()) * 1e3, 2),
-                     "frac_at_median": round(flops / float(np.median(kern)) / 1e9 / PEAK_BF16_TFLOPS, 4),
-                     "warmup_ms": round(warm_ms, 1)},
-        "parity": "tests/test_gpu_parity.py::test_full_size_every_element compares every element of this workload "
-                  "at this size against the oracle",
+        "roofline": headline_roofline(args.only, p, plan, flops, kern, warm_ms),
+        "parity": ("tests/test_gpu_parity.py::test_full_size_every_element compares every element of this "
+                   "workload at this size against the oracle" if args.only in ("c3p", "c3d", "c5") else
+                   "tests/test_gpu_parity.py::test_full_size_long_causal_16_heads compares 16 (batch, head) pairs of "
+                   "this workload at this size against the oracle, every row" if args.only.startswith("c4") else
+                   "tests/test_gpu_parity.py compares this workload against the oracle"),
     }
     del r
     torch.cuda.empty_cache()

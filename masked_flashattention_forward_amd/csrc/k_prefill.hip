@@ -901,16 +901,37 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(AttnParams p) {
   if (t >= rows_all * per_row) return;
   const long row = t / per_row;
   const int d0 = static_cast<int>(t % per_row) * 4;
+  constexpr int kBatch = 8;  // splits whose partials are loaded together (their latencies overlap)
   float mx = kNegInf;
-  for (int s = 0; s < p.splits; ++s) mx = fmaxf(mx, p.part_lse[s * rows_all + row]);
+  for (int s0 = 0; s0 < p.splits; s0 += kBatch) {
+    float ls[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) ls[k] = s0 + k < p.splits ? p.part_lse[(s0 + k) * rows_all + row] : kNegInf;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) mx = fmaxf(mx, ls[k]);
+  }
   float4 acc = {0.f, 0.f, 0.f, 0.f};
   float tot = 0.f;
   if (mx != kNegInf) {
-    for (int s = 0; s < p.splits; ++s) {
-      const float w = __expf(p.part_lse[s * rows_all + row] - mx);
-      const float4 o = *reinterpret_cast<const float4*>(p.part_out + (s * rows_all + row) * D + d0);
-      acc.x += w * o.x; acc.y += w * o.y; acc.z += w * o.z; acc.w += w * o.w;
-      tot += w;
+    for (int s0 = 0; s0 < p.splits; s0 += kBatch) {
+      float ls[kBatch];
+      float4 os[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        ls[k] = kNegInf;
+        os[k] = float4{0.f, 0.f, 0.f, 0.f};
+        if (s0 + k < p.splits) {
+          const long slot = (s0 + k) * rows_all + row;
+          ls[k] = p.part_lse[slot];
+          os[k] = *reinterpret_cast<const float4*>(p.part_out + slot * D + d0);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const float w = __expf(ls[k] - mx);  // 0 for the splits past the last
+        acc.x += w * os[k].x; acc.y += w * os[k].y; acc.z += w * os[k].z; acc.w += w * os[k].w;
+        tot += w;
+      }
     }
   }
   const bool dead = !(tot > 0.f);
