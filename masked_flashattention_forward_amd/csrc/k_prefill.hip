@@ -558,7 +558,9 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN, EXT, BN>)) voi
 
     // One key tile; `stage_c` is the LDS stage it sits in (an integral_constant when the loop
     // is unrolled by two, see kUnroll2; otherwise an int).
-    auto tile_step = [&](auto stage_c) {
+    // first_c: the block's first tile (every row's running max still -inf), peeled off the
+    // unrolled loop so that it can take the exact softmax path directly
+    auto tile_step = [&](auto stage_c, auto first_c) {
       const int stage = stage_c;
       const int tn = next_live(t + 1);
       if (tn < t_hi) issue_tile(tn, stage ^ 1);  // lands in the other stage while this tile computes
@@ -683,7 +685,7 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN, EXT, BN>)) voi
         // a row with no running max yet (its first live tile) fails the check for sure: with
         // 128-key tiles go straight to the exact path, with the logits still in the
         // registers (d = 64: 1.2% faster; at d = 128 the registers that keeps live cost more)
-        const bool fresh = BN == 128 && !__all(m_run != kNegInf);
+        const bool fresh = decltype(first_c)::value || (BN == 128 && !__all(m_run != kNegInf));
         float lsum = fresh ? 0.f : exps(m_ref);
         if (fresh || !__all(lsum <= kFastSumLimit) || dump_here) {
           if (!fresh) {
@@ -824,13 +826,15 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN, EXT, BN>)) voi
       t = tn;
     };
     if constexpr (kUnroll2) {
+      using F = std::false_type;
+      if (t < t_hi) tile_step(std::integral_constant<int, 0>{}, std::true_type{});
       while (t < t_hi) {
-        tile_step(std::integral_constant<int, 0>{});
+        tile_step(std::integral_constant<int, 1>{}, F{});
         if (t >= t_hi) break;
-        tile_step(std::integral_constant<int, 1>{});
+        tile_step(std::integral_constant<int, 0>{}, F{});
       }
     } else {
-      for (int stage = 0; t < t_hi; stage ^= 1) tile_step(stage);
+      for (int stage = 0; t < t_hi; stage ^= 1) tile_step(stage, std::false_type{});
     }
 
     // ---- epilogue: combine the two lane halves' partial sums, normalise, store
