@@ -833,6 +833,13 @@ __global__ __launch_bounds__(kThreads, (kMinBlocks<D, MK, VARLEN, EXT, BN>)) voi
         if (t >= t_hi) break;
         tile_step(std::integral_constant<int, 0>{}, F{});
       }
+    } else if constexpr (kRunningMaxExps<D, BN, MK, EXT>) {
+      int stage = 0;
+      if (t < t_hi) {
+        tile_step(0, std::true_type{});
+        stage = 1;
+      }
+      for (; t < t_hi; stage ^= 1) tile_step(stage, std::false_type{});
     } else {
       for (int stage = 0; t < t_hi; stage ^= 1) tile_step(stage, std::false_type{});
     }
