@@ -512,6 +512,29 @@ def headline_roofline(name, p, plan, flops, kern, warm_ms):
             **common, "frac_at_median": round(flops / med_ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
 
 
+FWD_CONFIGS = ("c3d", "c4_d128_bf16", "c4_d64_bf16", "c4_d128_fp16", "c4_d64_fp16", "c5", "c2", "c2w", "c1")
+BWD_CONFIGS = ("c4_d128_bf16", "c4_d64_bf16", "c4_d128_fp16", "c4_d64_fp16", "c3p")
+
+
+def config_entries(oracle_on):
+    """The per-configuration entries of the JSON line in their order: (key, progress label,
+    function that measures it)."""
+    import synth
+    out = [(n, f"config {n}", lambda n=n: bench_config(n, with_oracle=oracle_on and n != "c2w"))
+           for n in FWD_CONFIGS]
+    out.append(("c5_topk_select_32k", "config c5 selection at 32768 keys", bench_topk_select))
+    out.append(("serve", "config serve (paged varlen)", lambda: bench_paged_config("serve")))
+    out.append(("serve_alibi_softcap", "config serve with ALiBi + softcap (paged varlen)",
+                lambda: bench_paged_config("serve", modifiers=True)))
+    out += [(n, f"config {n} (attn_fwd_ex)", lambda n=n: bench_ex_config(n)) for n in synth.EX_NAMES]
+    out += [(f"{n}_bwd", f"config {n} (attn_bwd)", lambda n=n: bench_bwd_config(n)) for n in BWD_CONFIGS]
+    return out
+
+
+def config_entry_names():
+    return [key for key, _, _ in config_entries(False)]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -521,6 +544,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0)
+    ap.add_argument("--configs", default="",
+                    help="comma-separated subset of the per-configuration entries to run (default: all of them)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -530,6 +555,12 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, max(1, args.steps))
         return
+    wanted = [n for n in args.configs.split(",") if n]
+    unknown = sorted(set(wanted) - set(config_entry_names()))
+    if unknown:
+        print(f"unknown --configs entries: {', '.join(unknown)} (known: {', '.join(config_entry_names())})",
+              file=sys.stderr)
+        sys.exit(2)
 
     import torch
     import masked_flashattention_forward_amd as mfa
@@ -580,32 +611,22 @@ def main():
     oracle_on = not args.no_cpu_baseline
     if not args.no_configs:
         configs = {}
-        for name in ("c3d", "c4_d128_bf16", "c4_d64_bf16", "c4_d128_fp16", "c4_d64_fp16", "c5", "c2", "c2w",
-                     "c1"):
-            log(f"config {name}")
-            configs[name] = bench_config(name, with_oracle=oracle_on and name != "c2w")
-        log("config c5 selection at 32768 keys")
-        configs["c5_topk_select_32k"] = bench_topk_select()
-        log("config serve (paged varlen)")
-        configs["serve"] = bench_paged_config("serve")
-        log("config serve with ALiBi + softcap (paged varlen)")
-        configs["serve_alibi_softcap"] = bench_paged_config("serve", modifiers=True)
-        for name in synth.EX_NAMES:
-            log(f"config {name} (attn_fwd_ex)")
-            configs[name] = bench_ex_config(name)
-        for name in ("c4_d128_bf16", "c4_d64_bf16", "c4_d128_fp16", "c4_d64_fp16", "c3p"):
-            log(f"config {name} (attn_bwd)")
-            configs[f"{name}_bwd"] = bench_bwd_config(name)
+        for key, label, run in config_entries(oracle_on):
+            if wanted and key not in wanted:
+                continue
+            log(label)
+            configs[key] = run()
         line["configs"] = configs
-        d = configs["c3d"]
-        rs = bench_read_stream(2 * d["B"] * d["Hkv"] * d["Lk"] * d["d"] * 2)
-        line["decode"] = {"workload": d["workload"], "value": d["gbs"], "unit": "GB/s",
-                          "frac_hbm_peak": round(d["gbs"] / PEAK_HBM_GBS, 4),
-                          "read_stream": rs, "frac_of_read_stream": round(d["gbs"] / rs["best_gbs"], 4),
-                          "roofline": {"bound": "hbm", "kernel": "decode_kernel<bf16,128> + lse_merge_kernel",
-                                       "achieved": d["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                       "frac": round(d["gbs"] / PEAK_HBM_GBS, 4),
-                                       "traffic": measured_traffic("decode_kernel<bf16,128,causal> c3 decode")}}
+        if "c3d" in configs:
+            d = configs["c3d"]
+            rs = bench_read_stream(2 * d["B"] * d["Hkv"] * d["Lk"] * d["d"] * 2)
+            line["decode"] = {"workload": d["workload"], "value": d["gbs"], "unit": "GB/s",
+                              "frac_hbm_peak": round(d["gbs"] / PEAK_HBM_GBS, 4),
+                              "read_stream": rs, "frac_of_read_stream": round(d["gbs"] / rs["best_gbs"], 4),
+                              "roofline": {"bound": "hbm", "kernel": "decode_kernel<bf16,128> + lse_merge_kernel",
+                                           "achieved": d["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                           "frac": round(d["gbs"] / PEAK_HBM_GBS, 4),
+                                           "traffic": measured_traffic("decode_kernel<bf16,128,causal> c3 decode")}}
     if oracle_on:
         log("cpu baseline (fp64 oracle) on the headline workload")
         line["cpu_baseline"] = cpu_oracle(p, label=args.only)

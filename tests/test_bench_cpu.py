@@ -64,3 +64,16 @@ def test_algorithmic_bytes_count_distinct_visible_keys(kind):
     if kind == "dense":
         expect += mask.nbytes
     assert bench.algorithmic_bytes(p) == expect
+
+
+def test_configs_subset_option():
+    """--configs names entries of the per-configuration list; an unknown name stops the run
+    before anything is measured (exit status 2, the known names listed)."""
+    import subprocess
+    import sys
+    names = bench.config_entry_names()
+    assert len(names) == len(set(names))
+    assert {"c3d", "c5", "serve", "c4_d128_bf16_bwd", "c3p_bwd"} <= set(names)
+    r = subprocess.run([sys.executable, "bench.py", "--configs", "c3d,not_a_config"], capture_output=True, text=True,
+                       cwd=bench.__file__.rsplit("/", 1)[0], timeout=120)
+    assert r.returncode == 2 and "not_a_config" in r.stderr and "c4_d128_bf16_bwd" in r.stderr
