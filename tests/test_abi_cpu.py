@@ -68,11 +68,18 @@ def plan_rc(**kw):
     (dict(d=96), -2), (dict(d=256), -2), (dict(d=32), -2),
     (dict(dtype=0, d=260), -2), (dict(dtype=0, d=66), -2),
     (dict(mask_kind=4, keep_k=4, Lk=70000), -2),
+    (dict(Lk=1 << 23, d=128), -2), (dict(Lk=1 << 24, d=64), -2),   # a K/V slice past 2^31 bytes
 ])
 def test_plan_rejects_invalid_arguments(lib, kw, code):
     rc, _ = plan_rc(**kw)
     assert rc == code
     assert lib.attn_last_error().decode() != ""
+
+
+def test_plan_accepts_the_largest_kv_slice(lib):
+    """One (batch, KV head) slice of K or V just under 2^31 bytes is accepted."""
+    rc, _ = plan_rc(Lk=(1 << 23) - 1, d=128)
+    assert rc == 0, mfa.lib().attn_last_error().decode()
 
 
 def test_plan_accepts_supported_shapes(lib):
