@@ -65,7 +65,7 @@ def test_topk_c5_full_size():
     check_topk(p.zero_hold, p.Lq, p.keep_k, True, "c5 zero_hold [2,16,4096] k=1024, all 32 heads")
 
 
-@pytest.mark.parametrize("Lk", [8193, 16391, 32768])
+@pytest.mark.parametrize("Lk", [8193, 16391, 32768, 40001, 65536])
 @pytest.mark.parametrize("causal", [True, False])
 def test_topk_long_caches(Lk, causal):
     """Past 8192 keys the 512-key sorted chunks are merged into sorted runs of 8192 keys
@@ -79,6 +79,18 @@ def test_topk_long_caches(Lk, causal):
     zh[0, 1, Lk // 3: Lk // 2] = 0.0
     Lq = 40
     check_topk(zh, Lq, 3000, causal, f"long cache Lk{Lk} causal{int(causal)}")
+
+
+def test_topk_attention_at_the_largest_cache():
+    """Top-k attention over 65536 keys, the largest cache the top-k mask takes (eight sorted
+    runs), for the last 64 query positions, against the oracle."""
+    from helpers import compare, run_gpu, run_oracle
+    p = synth.make_problem("top-k attention Lk 65536", 1, 4, 2, 64, 65536, 128, "bf16", "topk", 1602, keep_k=2000,
+                           with_zero_hold=True)
+    say(p.name)
+    out, lse = run_gpu(p, out_fill=float("nan"))
+    ref_o, ref_l = run_oracle(p)
+    compare(p, out, lse, ref_o, ref_l, label=p.name)
 
 
 def test_topk_attention_over_a_long_cache():
