@@ -218,6 +218,9 @@ def ex_args(**kw):
     (dict(mask_kind=3), -1),                       # dense kind without a mask
     (dict(mask_kind=3, mask=0x2000, mask_stride=(0, 0, -8, 1)), -1),
     (dict(k_stride=(1 << 40, 1 << 32, 1 << 28)), -2),  # K rows too far apart for 32-bit offsets
+    # 262144 rows 4096 elements apart end past 2^31 bytes (262143 rows are the largest span taken)
+    (dict(Lk=262144, d=128, k_stride=(1 << 30, 1 << 30, 4096), v_stride=(1 << 30, 1 << 30, 4096)), -2),
+    (dict(Lk=262144, d=128, v_stride=(1 << 30, 1 << 30, 4096), k_stride=(1 << 25, 1 << 25, 128)), -2),
 ])
 def test_attn_fwd_ex_rejects_before_any_gpu_work(lib, kw, code):
     assert lib.attn_fwd_ex(ctypes.byref(ex_args(**kw)), None) == code

@@ -36,7 +36,17 @@ def layout(t, kind):
         buf = torch.full((B, H, L, d + 16), float("nan"), dtype=t.dtype, device=t.device)
         buf[..., :d] = t
         return buf[..., :d]
+    if kind == "far":
+        # rows FAR_ROW_STRIDE elements apart, NaN between them: a long cache slice whose
+        # last row ends just under 2^31 bytes from its first
+        B, H, L, d = t.shape
+        buf = torch.full((B, H, L, FAR_ROW_STRIDE), float("nan"), dtype=t.dtype, device=t.device)
+        buf[..., :d] = t
+        return buf[..., :d]
     raise ValueError(kind)
+
+
+FAR_ROW_STRIDE = 4096  # elements: 8 KB between 16-bit rows
 
 
 def per_head_mask(seed, shape, Lq, Lk):
@@ -188,6 +198,18 @@ def test_ex_workloads_full_size_sampled(name):
                                  mask=o["mask"] if o["mask"] is not None else p.mask, topk_causal=o["topk_causal"],
                                  alibi=o["alibi"], softcap=o["softcap"], heads=heads)
     compare(p, out, lse, ref_o, ref_l, heads=heads, label=f"{name} (sampled heads)")
+
+
+@pytest.mark.parametrize("Lq,path,splits", [(1, None, 0), (16, None, 0), (16, 1, 1)])
+def test_kv_slice_at_the_32bit_offset_limit(Lq, path, splits):
+    """K and V slices whose last row ends just under 2^31 bytes from the first (262143 keys
+    8 KB apart, NaN between the rows): the largest span the 32-bit offsets of the library
+    take, on the decode path, the split prefill and one unsplit workgroup per query block
+    (one key more is refused: tests/test_abi_cpu.py)."""
+    Lk = 262143
+    assert (Lk * FAR_ROW_STRIDE + 128) * 2 <= 2**31 - 1 < ((Lk + 1) * FAR_ROW_STRIDE + 128) * 2
+    p = synth.make_problem(f"far rows Lq{Lq} Lk{Lk}", 1, 8, 1, Lq, Lk, 128, "bf16", "causal", 1701 + Lq)
+    check(p, f"{p.name} path{path} splits{splits}", klay="far", path=path, splits=splits)
 
 
 @pytest.mark.parametrize("Lk", [513, 2100])
