@@ -143,11 +143,12 @@ def dead_row_mask(Lq, Lk, seed):
     return m
 
 
-# (dtype, d, B, Hq, Hkv, Lq, Lk): MHA and GQA/MQA, ragged tails against the 32-row,
-# 64-key and 128-key tiles, Lq below, equal to and above Lk, one-row decode
+# (dtype, d, B, Hq, Hkv, Lq, Lk): MHA and GQA/MQA (up to 128 query heads per KV head, the
+# most attn_bwd takes), ragged tails against the 32-row, 64-key and 128-key tiles, Lq below,
+# equal to and above Lk, one-row decode
 SHAPES = [("bf16", 128, 2, 4, 2, 77, 203), ("fp16", 64, 2, 4, 2, 77, 203), ("bf16", 64, 1, 2, 2, 130, 130),
           ("fp16", 128, 1, 8, 1, 100, 100), ("bf16", 128, 2, 6, 2, 1, 300), ("bf16", 128, 1, 4, 4, 300, 100),
-          ("fp16", 128, 1, 16, 1, 33, 260)]
+          ("fp16", 128, 1, 16, 1, 33, 260), ("bf16", 128, 1, 128, 1, 5, 150)]
 KINDS = ["none", "causal", "window", "dense", "topk"]
 
 

@@ -185,6 +185,22 @@ def test_row_kernel_and_mfma_agree(dtype):
     np.testing.assert_allclose(a[1], b[1], rtol=0, atol=1e-3)
 
 
+@pytest.mark.parametrize("G,Lq,Lk,path", [(96, 7, 300, "mfma_prefill"), (128, 5, 700, "mfma_prefill"),
+                                          (256, 3, 200, "row")])
+@pytest.mark.parametrize("kind", ["causal", "topk"])
+def test_largest_head_groups(G, Lq, Lk, path, kind):
+    """One KV head read by 96, 128 (the most a 128-row prefill block takes: one query
+    position per block) and 256 query heads (more than a block holds: the row kernel)."""
+    import masked_flashattention_forward_amd as mfa
+    p = synth.make_problem(f"G{G} {kind} Lq{Lq} Lk{Lk}", 1, G, 1, Lq, Lk, 128, "bf16", kind, 1800 + G,
+                           keep_k=50, with_zero_hold=kind == "topk")
+    assert mfa.plan(p.B, p.Hq, p.Hkv, p.Lq, p.Lk, p.d, kind, keep_k=p.keep_k)["path"] == path
+    say(p.name)
+    out, lse = run_gpu(p, out_fill=float("nan"))
+    ref_o, ref_l = run_oracle(p)
+    compare(p, out, lse, ref_o, ref_l, label=p.name)
+
+
 @pytest.mark.parametrize("G,Lq", [(4, 1), (8, 4), (32, 1), (1, 32), (6, 5)])
 def test_decode_path_shapes(G, Lq):
     """Shapes the planner sends to the split-KV decode kernel (G * Lq <= 32)."""
