@@ -201,6 +201,30 @@ def test_largest_head_groups(G, Lq, Lk, path, kind):
     compare(p, out, lse, ref_o, ref_l, label=p.name)
 
 
+@pytest.mark.parametrize("dtype,d,Lq,Lk,path", [("bf16", 128, 200, 700, "mfma_prefill"),
+                                               ("fp16", 64, 300, 300, "mfma_prefill"),
+                                               ("bf16", 128, 1, 3000, "splitkv_decode"), ("fp32", 64, 40, 90, "row")])
+def test_zero_scale_weighs_visible_keys_equally(dtype, d, Lq, Lk, path):
+    """scale = 0: every visible key gets the same weight, so each row's output is the mean
+    of its visible V rows and its LSE is ln(number of visible keys) (causal: Lk - Lq + i + 1
+    keys for row i). Checked against that closed form directly, not only the oracle."""
+    import masked_flashattention_forward_amd as mfa
+    p = synth.make_problem(f"zero scale {dtype} d{d} {Lq}x{Lk}", 2, 4, 2, Lq, Lk, d, dtype, "causal", 1900 + Lq,
+                           scale=0.0)
+    assert mfa.plan(p.B, p.Hq, p.Hkv, p.Lq, p.Lk, p.d, "causal", dtype=synth.DTYPE_CODES[dtype])["path"] == path
+    say(p.name)
+    out, lse = run_gpu(p, out_fill=float("nan"))
+    v = p.f64("v")
+    n_vis = Lk - Lq + np.arange(Lq) + 1
+    mean_v = np.cumsum(v, axis=2)[:, :, Lk - Lq:, :] / n_vis[None, None, :, None]
+    ref_o = np.repeat(mean_v, p.Hq // p.Hkv, axis=1)
+    ref_l = np.broadcast_to(np.log(n_vis.astype(np.float64)), lse.shape)
+    compare(p, out, lse, ref_o, ref_l, label=p.name)
+    o2, l2 = run_oracle(p)
+    np.testing.assert_allclose(o2, ref_o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l2, ref_l, rtol=0, atol=1e-12)
+
+
 @pytest.mark.parametrize("G,Lq", [(4, 1), (8, 4), (32, 1), (1, 32), (6, 5)])
 def test_decode_path_shapes(G, Lq):
     """Shapes the planner sends to the split-KV decode kernel (G * Lq <= 32)."""
