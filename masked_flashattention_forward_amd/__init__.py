@@ -142,12 +142,18 @@ def set_debug(no_skip: bool = False, force_path: int = -1, force_splits: int = 0
     lib().attn_set_debug(int(bool(no_skip)), int(force_path), int(force_splits))
 
 
+_DTYPE_CODES = None  # torch dtype -> library dtype code, built on first use
+
+
 def _dtype_code(t) -> int:
-    import torch
-    codes = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
-    if t.dtype not in codes:
+    global _DTYPE_CODES
+    if _DTYPE_CODES is None:
+        import torch
+        _DTYPE_CODES = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+    code = _DTYPE_CODES.get(t.dtype)
+    if code is None:
         raise TypeError(f"unsupported dtype {t.dtype}")
-    return codes[t.dtype]
+    return code
 
 
 def plan(B, Hq, Hkv, Lq, Lk, d, mask_kind="causal", window_left=0, keep_k=0, dtype=BF16) -> dict:
@@ -164,10 +170,22 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+_raw_current_stream = None  # torch's accessor for the current stream's raw handle, looked up once
+
+
 def _stream_handle(device, stream):
+    """The HIP stream the call is enqueued on: ``stream`` (a torch stream), else torch's
+    current stream of ``device``. The current stream's handle is read with torch's raw
+    accessor, which skips building a stream object (about 1.8 us of host time per call)."""
+    global _raw_current_stream
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream)
     import torch
-    s = torch.cuda.current_stream(device) if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    if _raw_current_stream is None:
+        _raw_current_stream = getattr(torch._C, "_cuda_getCurrentRawStream", False)
+    if _raw_current_stream and device.index is not None:
+        return ctypes.c_void_p(_raw_current_stream(device.index))
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
 def attn_fwd(q, k, v, *, scale=None, mask_kind="causal", window_left=0, mask=None, zero_hold=None,
