@@ -28,7 +28,7 @@ using u64 = unsigned long long;
 
 constexpr int kChunk = 512;               // keys bitonic-sorted per workgroup
 constexpr int kChunkThreads = kChunk / 2; // two keys per thread
-constexpr int kMergeMaxKeys = 8192;       // sorted chunks of one (b,h) staged in 64 KiB of LDS
+constexpr int kMergeMaxKeys = 8192;       // sorted chunks of one (b,h) staged in 68 KiB of LDS (padded)
 constexpr int kRankThreads = 256;
 constexpr u64 kPadKey = ~0ull;            // above every real key
 constexpr int32_t kAllKept = 0x7fffffff;  // "no threshold" and the rank past the last key
@@ -101,6 +101,11 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_sort_kernel(const float* 
   dst[e0 + 1] = b;
 }
 
+// LDS slot of staged sorted word g: 16 bytes of padding after every 32 words. The probes of
+// one binary-search level are words s - 1 (mod s) for a step s, so without padding those of
+// the small steps fall on a few banks.
+__host__ __device__ constexpr int pad_slot(int g) { return g + 2 * (g >> 5); }
+
 // rank_j = number of keys before j in the total order = sum over the sorted chunks of the
 // count of words below key_j (branch-free lower bound over 512 entries). When tile_min is
 // given, also the smallest rank of each block_n-key tile (block_n divides kRankThreads).
@@ -112,8 +117,8 @@ __global__ __launch_bounds__(kRankThreads) void rank_merge_kernel(const float* z
   const int bh = blockIdx.x;
   const int n = nchunks * kChunk;
   const uint4* src = reinterpret_cast<const uint4*>(sorted + static_cast<long>(bh) * n);
-  uint4* dst = reinterpret_cast<uint4*>(srt);
-  for (int t = threadIdx.x; t < n / 2; t += kRankThreads) dst[t] = src[t];
+  // words 2t, 2t + 1 stay side by side (16-byte aligned) in the padded layout
+  for (int t = threadIdx.x; t < n / 2; t += kRankThreads) *reinterpret_cast<uint4*>(srt + pad_slot(2 * t)) = src[t];
   __syncthreads();
   const int j = blockIdx.y * kRankThreads + threadIdx.x;
   int cnt = kAllKept;
@@ -121,23 +126,24 @@ __global__ __launch_bounds__(kRankThreads) void rank_merge_kernel(const float* z
     const u64 key = order_key(zh + static_cast<long>(bh) * Lk, j);
     cnt = 0;
     // four independent searches at a time, so their LDS latencies overlap; chunks past
-    // nchunks are searched in chunk 0 and not counted
+    // nchunks are searched in chunk 0 and not counted. A chunk starts on a multiple of 32
+    // words, so its word i sits at its own start plus pad_slot(i).
     for (int c = 0; c < nchunks; c += 4) {
       const u64* s[4];
       int pos[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        s[u] = srt + (c + u < nchunks ? c + u : 0) * kChunk;
+        s[u] = srt + pad_slot((c + u < nchunks ? c + u : 0) * kChunk);
         pos[u] = 0;
       }
 #pragma unroll
       for (int step = kChunk / 2; step > 0; step >>= 1)
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          if (s[u][pos[u] + step - 1] < key) pos[u] += step;
+          if (s[u][pad_slot(pos[u] + step - 1)] < key) pos[u] += step;
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        if (c + u < nchunks) cnt += pos[u] + (s[u][pos[u]] < key ? 1 : 0);
+        if (c + u < nchunks) cnt += pos[u] + (s[u][pad_slot(pos[u])] < key ? 1 : 0);
     }
     rank[static_cast<long>(bh) * Lk + j] = cnt;
   }
@@ -593,7 +599,7 @@ hipError_t launch_topk(const float* zh, int BH, int Lq, int Lk, int keep_k, int 
   hipLaunchKernelGGL(chunk_sort_kernel, dim3(BH, nchunks), dim3(kChunkThreads), 0, s, zh, Lk, nchunks, sorted);
   if (Lk <= kMergeMaxKeys) {
     hipLaunchKernelGGL(rank_merge_kernel, dim3(BH, (Lk + kRankThreads - 1) / kRankThreads), dim3(kRankThreads),
-                       sizeof(u64) * nchunks * kChunk, s, zh, sorted, Lk, nchunks, rank, tile_min, block_n);
+                       sizeof(u64) * pad_slot(nchunks * kChunk), s, zh, sorted, Lk, nchunks, rank, tile_min, block_n);
   } else {
     u64* runs = sorted + chunk_words;
     const int nruns = (nchunks + kRunChunks - 1) / kRunChunks;

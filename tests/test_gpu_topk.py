@@ -65,13 +65,14 @@ def test_topk_c5_full_size():
     check_topk(p.zero_hold, p.Lq, p.keep_k, True, "c5 zero_hold [2,16,4096] k=1024, all 32 heads")
 
 
-@pytest.mark.parametrize("Lk", [8193, 16391, 32768, 40001, 65536])
+@pytest.mark.parametrize("Lk", [8192, 8193, 16391, 32768, 40001, 65536])
 @pytest.mark.parametrize("causal", [True, False])
 def test_topk_long_caches(Lk, causal):
-    """Past 8192 keys the 512-key sorted chunks are merged into sorted runs of 8192 keys
-    before the ranks are counted: ranks, thresholds and keep bits bit-exact, with long
-    runs of tied values and -0.0 beside +0.0, including a partial last run and a partial
-    last chunk."""
+    """At 8192 keys the ranks come from the sixteen sorted 512-key chunks staged in LDS
+    together (the largest staging); past 8192 keys the chunks are merged into sorted runs
+    of 8192 keys before the ranks are counted: ranks, thresholds and keep bits bit-exact,
+    with long runs of tied values and -0.0 beside +0.0, including a partial last run and a
+    partial last chunk."""
     rng = np.random.default_rng(Lk + int(causal))
     zh = rng.standard_normal((1, 2, Lk)).astype(np.float32)
     zh[0, 0, rng.random(Lk) < 0.4] = np.float32(0.75)
